@@ -1,0 +1,378 @@
+"""Pins for the CPU oracle: worked examples from the pages, closed forms, the
+pages' invariances and an independent brute force.  CPU only."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import (
+    brute_decode,
+    brute_prefill,
+    ref_decode,
+    ref_prefill,
+    ref_reshape_and_cache,
+    ref_slot_mapping,
+    widen,
+)
+from workloads import make_case, nan_pool
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "slot_examples.json")
+
+
+def _examples():
+    with open(GOLDEN) as f:
+        return json.load(f)["examples"]
+
+
+# ----------------------------------------------------------------------------
+# helpers: populate a NaN pool through the oracle's own scatter
+# ----------------------------------------------------------------------------
+
+def populate(case, include_new=True):
+    """Oracle pool after writing the cached prefix and (optionally) this step's
+    new tokens, each through ref_slot_mapping + ref_reshape_and_cache."""
+    kc = nan_pool(case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim, case.dtype)
+    vc = kc.copy()
+    kp, vp, cu_pre, lens_pre = case.prefix()
+    slots = ref_slot_mapping(case.block_table, cu_pre, lens_pre, case.block_size)
+    kc, vc = ref_reshape_and_cache(kp, vp, slots, kc, vc)
+    if include_new:
+        kn, vn = case.new_kv()
+        slots = ref_slot_mapping(case.block_table, case.cu_seqlens, case.context_lens, case.block_size)
+        kc, vc = ref_reshape_and_cache(kn, vn, slots, kc, vc)
+    return kc, vc
+
+
+def decode_oracle(case):
+    kc, vc = populate(case)
+    return ref_decode(case.q, kc, vc, case.block_table, case.context_lens, case.scale)
+
+
+def tiny_case(G=2, H_kv=2, D=8, P=4, lens=(5, 1, 17, 9), seed=0, dtype="f32", qlens=None, **kw):
+    return make_case(dtype=dtype, block_size=P, num_q_heads=G * H_kv, num_kv_heads=H_kv, head_dim=D,
+                     context_lens=list(lens), query_lens=qlens, seed=seed, **kw)
+
+
+# ----------------------------------------------------------------------------
+# slot math: the pages' worked examples
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ex", _examples(), ids=lambda e: e["source"][:40])
+def test_slot_mapping_worked_examples(ex):
+    P = ex["block_size"]
+    n = len(ex["positions"])
+    # the whole sequence written as one prefill step
+    got = ref_slot_mapping([ex["block_table"]], [0, n], [n], P)
+    assert got.tolist() == ex["slot"]
+    assert [b * P + o for b, o in zip(ex["physical_block"], ex["offset"])] == ex["slot"]
+
+
+@pytest.mark.parametrize("ex", _examples(), ids=lambda e: e["source"][:40])
+def test_slot_mapping_decode_position_is_length_before_append(ex):
+    # tiny-vllm-py "Design Choices": the new token's position is the cache length
+    # before its K/V is appended; context_lens counts the new token too.
+    P = ex["block_size"]
+    for n in range(1, len(ex["positions"]) + 1):
+        got = ref_slot_mapping([ex["block_table"]], [0, 1], [n], P)
+        assert got.tolist() == [ex["slot"][n - 1]]
+
+
+def test_slot_mapping_chunk_over_prefix():
+    ex = _examples()[2]
+    # 4 tokens cached, a chunk of 6 new tokens: positions 4..9
+    got = ref_slot_mapping([ex["block_table"]], [0, 6], [10], 4)
+    assert got.tolist() == ex["slot"][4:]
+
+
+# ----------------------------------------------------------------------------
+# scatter
+# ----------------------------------------------------------------------------
+
+def test_reshape_and_cache_is_bit_exact_and_touches_only_its_slots():
+    N, P, H, D = 6, 4, 2, 4
+    special = np.array([0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00001, 0xFFBADBAD,
+                        0x00000001, 0x807FFFFF], dtype=np.uint32)
+    rng = np.random.default_rng(5)
+    k = rng.choice(special, size=(5, H, D)).view(np.float32)
+    v = rng.integers(0, 2**32, size=(5, H, D), dtype=np.uint64).astype(np.uint32).view(np.float32)
+    kc = rng.integers(0, 2**32, size=(N, P, H, D), dtype=np.uint64).astype(np.uint32).view(np.float32)
+    vc = kc.copy()
+    slots = np.array([7, 0, 23, -1, 13])
+    nk, nv = ref_reshape_and_cache(k, v, slots, kc, vc)
+    fk = nk.view(np.uint32).reshape(N * P, H, D)
+    fv = nv.view(np.uint32).reshape(N * P, H, D)
+    ok = kc.view(np.uint32).reshape(N * P, H, D)
+    for t, s in enumerate(slots):
+        if s >= 0:
+            assert np.array_equal(fk[s], k[t].view(np.uint32))
+            assert np.array_equal(fv[s], v[t].view(np.uint32))
+    untouched = np.setdiff1d(np.arange(N * P), slots[slots >= 0])
+    assert np.array_equal(fk[untouched], ok[untouched])
+    # inputs are not modified
+    assert np.array_equal(kc.view(np.uint32).reshape(N * P, H, D), ok)
+
+
+def test_reshape_and_cache_bf16_bits_and_duplicates_rejected():
+    kc = nan_pool(3, 2, 1, 4, "bf16")
+    k = np.array([[[0x0001, 0x8000, 0x7F80, 0x1234]]], dtype=np.uint16)
+    nk, _ = ref_reshape_and_cache(k, k, [5], kc, kc)
+    assert nk.reshape(6, 1, 4)[5].tolist() == k[0].tolist()
+    with pytest.raises(AssertionError):
+        ref_reshape_and_cache(np.concatenate([k, k]), np.concatenate([k, k]), [1, 1], kc, kc)
+
+
+# ----------------------------------------------------------------------------
+# decode: brute force and closed forms
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,H_kv,P", [(1, 3, 1), (2, 2, 3), (3, 1, 4), (4, 2, 7)])
+def test_decode_matches_brute_force(G, H_kv, P):
+    case = tiny_case(G=G, H_kv=H_kv, P=P, lens=(5, 1, 17, 9, 30), seed=G * 10 + P)
+    ref = decode_oracle(case)
+    bf = np.array(brute_decode(case.q, case.k_tok, case.v_tok, case.cu_ctx, case.num_kv_heads, case.scale))
+    np.testing.assert_allclose(ref, bf, rtol=0, atol=1e-12)
+
+
+def test_decode_matches_brute_force_bf16():
+    case = tiny_case(G=4, H_kv=2, D=16, P=5, lens=(33, 2, 40), seed=3, dtype="bf16")
+    ref = decode_oracle(case)
+    bf = np.array(brute_decode(case.q, case.k_tok, case.v_tok, case.cu_ctx, case.num_kv_heads, case.scale))
+    np.testing.assert_allclose(ref, bf, rtol=0, atol=1e-12)
+
+
+def test_decode_single_token_returns_its_value_exactly():
+    case = tiny_case(lens=(1, 1, 1), seed=11)
+    out = decode_oracle(case)
+    G = case.num_q_heads // case.num_kv_heads
+    v = widen(case.v_tok)
+    for b in range(case.B):
+        for h in range(case.num_q_heads):
+            assert np.array_equal(out[b, h], v[case.cu_ctx[b], h // G])
+
+
+def test_decode_zero_query_is_mean_of_values():
+    case = tiny_case(lens=(7, 12, 3), seed=12)
+    case.q[:] = 0
+    out = decode_oracle(case)
+    v = widen(case.v_tok)
+    G = case.num_q_heads // case.num_kv_heads
+    for b in range(case.B):
+        rows = v[case.cu_ctx[b]: case.cu_ctx[b + 1]]
+        for h in range(case.num_q_heads):
+            np.testing.assert_allclose(out[b, h], rows[:, h // G].mean(axis=0), rtol=0, atol=1e-14)
+
+
+def test_decode_identical_values_return_that_value():
+    case = tiny_case(lens=(9, 4), seed=13)
+    case.v_tok[:] = case.v_tok[0]
+    out = decode_oracle(case)
+    v0 = widen(case.v_tok[0])
+    G = case.num_q_heads // case.num_kv_heads
+    for b in range(case.B):
+        for h in range(case.num_q_heads):
+            np.testing.assert_allclose(out[b, h], v0[h // G], rtol=1e-15, atol=1e-15)
+
+
+def test_decode_dominant_key_and_two_key_logistic():
+    # one key whose score is 60 above every other: output is that key's value to e^-60
+    case = tiny_case(G=1, H_kv=1, D=4, lens=(6,), seed=14)
+    case.q[:] = 0
+    case.q[0, 0, 0] = 1.0
+    case.k_tok[:] = 0
+    j = 3
+    case.k_tok[j, 0, 0] = 60.0 / case.scale
+    out = decode_oracle(case)
+    np.testing.assert_allclose(out[0, 0], widen(case.v_tok)[j, 0], rtol=0, atol=10 * math.exp(-60) * 6)
+    # two keys: out = sigma(s0 - s1) v0 + sigma(s1 - s0) v1
+    case = tiny_case(G=1, H_kv=1, D=4, lens=(2,), seed=15)
+    q, k, v = widen(case.q)[0, 0], widen(case.k_tok)[:, 0], widen(case.v_tok)[:, 0]
+    s0, s1 = case.scale * (q @ k[0]), case.scale * (q @ k[1])
+    w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    expect = w0 * v[0] + (1.0 - w0) * v[1]
+    np.testing.assert_allclose(decode_oracle(case)[0, 0], expect, rtol=0, atol=1e-14)
+
+
+def test_decode_empty_context_gives_zeros():
+    case = tiny_case(lens=(3, 0, 2), qlens=(1, 0, 1), seed=16)
+    kc, vc = populate(case)
+    out = ref_decode(case.q[[0, 0, 1]], kc, vc, case.block_table, case.context_lens, case.scale)
+    assert np.all(out[1] == 0)
+
+
+# ----------------------------------------------------------------------------
+# decode: the pages' invariances (bitwise in the oracle)
+# ----------------------------------------------------------------------------
+
+def test_decode_block_size_invariance_bitwise():
+    # ember "Correctness": identical output for block_size in {1,2,3,7,16,64}
+    outs = [decode_oracle(tiny_case(G=2, H_kv=2, P=P, lens=(70, 5, 129, 1), seed=21)) for P in (1, 2, 3, 7, 16, 64)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_decode_block_permutation_invariance_bitwise():
+    # tiny-vllm-py "Mental Model": only where the KV entries physically live changes
+    a = tiny_case(P=4, lens=(13, 22, 9), seed=22)
+    kc, vc = populate(a)
+    ref = ref_decode(a.q, kc, vc, a.block_table, a.context_lens, a.scale)
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(a.num_blocks)  # physical block i moves to perm[i]
+    kc2 = np.empty_like(kc)
+    vc2 = np.empty_like(vc)
+    kc2[perm] = kc
+    vc2[perm] = vc
+    bt2 = perm[a.block_table]
+    out = ref_decode(a.q, kc2, vc2, bt2, a.context_lens, a.scale)
+    assert np.array_equal(out, ref)
+
+
+def test_decode_batch_invariance_bitwise():
+    # ember "Correctness": a request alone == alongside others
+    full = tiny_case(lens=(11, 40, 3, 25), seed=23)
+    ref = decode_oracle(full)
+    for b in range(full.B):
+        alone = tiny_case(lens=(int(full.context_lens[b]),), seed=0)
+        # carry request b's own values into the single-request case
+        s, e = full.cu_ctx[b], full.cu_ctx[b + 1]
+        alone.k_tok[:] = full.k_tok[s:e]
+        alone.v_tok[:] = full.v_tok[s:e]
+        alone.q[:] = full.q[b: b + 1]
+        assert np.array_equal(decode_oracle(alone)[0], ref[b])
+
+
+def test_gqa_equals_replicated_mha_bitwise():
+    g = tiny_case(G=4, H_kv=2, lens=(10, 3), seed=24)
+    ref = decode_oracle(g)
+    G = 4
+    m = tiny_case(G=1, H_kv=8, lens=(10, 3), seed=0)
+    m.k_tok[:] = np.repeat(g.k_tok, G, axis=1)
+    m.v_tok[:] = np.repeat(g.v_tok, G, axis=1)
+    m.q[:] = g.q
+    assert np.array_equal(decode_oracle(m), ref)
+
+
+# ----------------------------------------------------------------------------
+# prefill
+# ----------------------------------------------------------------------------
+
+def prefill_oracle(case):
+    kc, vc = populate(case)
+    return ref_prefill(case.q, kc, vc, case.cu_seqlens, case.block_table, case.context_lens, case.scale)
+
+
+@pytest.mark.parametrize("G,H_kv,P", [(1, 2, 1), (2, 2, 3), (4, 1, 16)])
+def test_prefill_matches_brute_force(G, H_kv, P):
+    case = tiny_case(G=G, H_kv=H_kv, P=P, lens=(9, 20, 4, 13), qlens=(9, 6, 1, 13), seed=30 + G)
+    ref = prefill_oracle(case)
+    bf = np.array(brute_prefill(case.q, case.cu_seqlens, case.k_tok, case.v_tok, case.cu_ctx,
+                                case.num_kv_heads, case.scale))
+    np.testing.assert_allclose(ref, bf, rtol=0, atol=1e-12)
+
+
+def test_prefill_without_prefix_is_textbook_causal_attention():
+    # tiny-vllm-py "Mistakes I made": prefill is causal (is_causal=True)
+    case = tiny_case(G=2, H_kv=1, D=8, P=3, lens=(12,), qlens=(12,), seed=31)
+    out = prefill_oracle(case)
+    q = widen(case.q)[:, :, :]
+    k = widen(case.k_tok)[:, 0]
+    v = widen(case.v_tok)[:, 0]
+    T = 12
+    mask = np.triu(np.full((T, T), -np.inf), k=1)
+    for h in range(2):
+        S = case.scale * q[:, h] @ k.T + mask
+        W = np.exp(S - S.max(axis=1, keepdims=True))
+        W /= W.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(out[:, h], W @ v, rtol=0, atol=1e-13)
+
+
+def test_prefill_single_new_token_equals_decode_bitwise():
+    case = tiny_case(lens=(8, 19, 1), seed=32)
+    kc, vc = populate(case)
+    dec = ref_decode(case.q, kc, vc, case.block_table, case.context_lens, case.scale)
+    pre = ref_prefill(case.q, kc, vc, case.cu_seqlens, case.block_table, case.context_lens, case.scale)
+    assert np.array_equal(dec, pre)
+
+
+def test_chunked_prefill_equals_one_shot_bitwise():
+    one = tiny_case(G=2, H_kv=2, P=3, lens=(23,), qlens=(23,), seed=33)
+    ref = prefill_oracle(one)
+    # the same prompt in chunks of 5, 9, 1, 8: each chunk scatters, then attends
+    kc = nan_pool(one.num_blocks, 3, 2, one.head_dim, one.dtype)
+    vc = kc.copy()
+    start = 0
+    pieces = []
+    for T in (5, 9, 1, 8):
+        L = start + T
+        slots = ref_slot_mapping(one.block_table, [0, T], [L], 3)
+        kc, vc = ref_reshape_and_cache(one.k_tok[start:L], one.v_tok[start:L], slots, kc, vc)
+        pieces.append(ref_prefill(one.q[start:L], kc, vc, [0, T], one.block_table, [L], one.scale))
+        start = L
+    assert np.array_equal(np.concatenate(pieces), ref)
+
+
+def test_prefill_rows_subset_matches_full():
+    case = tiny_case(lens=(9, 20), qlens=(4, 7), seed=34)
+    kc, vc = populate(case)
+    full = ref_prefill(case.q, kc, vc, case.cu_seqlens, case.block_table, case.context_lens, case.scale)
+    part = ref_prefill(case.q, kc, vc, case.cu_seqlens, case.block_table, case.context_lens, case.scale,
+                       rows=[1, 5, 10])
+    for r in (1, 5, 10):
+        assert np.array_equal(part[r], full[r])
+    assert np.isnan(part[0]).all()
+
+
+def test_unused_table_entries_are_never_read():
+    # entries past ceil(L/P) may hold anything, even ids outside the pool
+    case = tiny_case(P=4, lens=(5, 9), seed=35)
+    kc, vc = populate(case)
+    ref = ref_decode(case.q, kc, vc, case.block_table, case.context_lens, case.scale)
+    bt = case.block_table.copy()
+    for b in range(case.B):
+        bt[b, (case.context_lens[b] + 3) // 4:] = case.num_blocks + 7
+    assert np.array_equal(ref_decode(case.q, kc, vc, bt, case.context_lens, case.scale), ref)
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each pin above must catch a plausible bug in the oracle
+# ----------------------------------------------------------------------------
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    import oracle.paged_attention as pa
+
+    case = tiny_case(G=2, H_kv=2, P=3, lens=(7, 12), seed=40)
+    bf = np.array(brute_decode(case.q, case.k_tok, case.v_tok, case.cu_ctx, 2, case.scale))
+
+    # 1. wrong GQA head map (h % H_kv instead of h // G)
+    def bad_decode(q, k_cache, v_cache, block_table, context_lens, scale, select=None):
+        qd = pa.widen(q)
+        B, Hq, D = qd.shape
+        Hkv = k_cache.shape[2]
+        out = np.zeros((B, Hq, D))
+        for b in range(B):
+            K = pa.ref_gather(k_cache, block_table[b], context_lens[b], k_cache.shape[1])
+            V = pa.ref_gather(v_cache, block_table[b], context_lens[b], k_cache.shape[1])
+            for h in range(Hq):
+                out[b, h] = pa._attend(qd[b, h], K[:, h % Hkv], V[:, h % Hkv], scale)
+        return out
+
+    kc, vc = populate(case)
+    assert not np.allclose(bad_decode(case.q, kc, vc, case.block_table, case.context_lens, case.scale), bf)
+
+    # 2. slot offset taken from the wrong term (p // P instead of p % P)
+    ex = _examples()[2]
+    bt = np.asarray([ex["block_table"]])
+    pos = np.arange(10)
+    wrong = bt[0, pos // 4] * 4 + pos // 4
+    assert wrong.tolist() != ex["slot"]
+
+    # 3. causal mask off by one (a row does not see itself)
+    pcase = tiny_case(G=1, H_kv=1, P=3, lens=(6,), qlens=(6,), seed=41)
+    kc, vc = populate(pcase)
+    bfp = np.array(brute_prefill(pcase.q, pcase.cu_seqlens, pcase.k_tok, pcase.v_tok, pcase.cu_ctx, 1, pcase.scale))
+    orig = pa._attend
+    monkeypatch.setattr(pa, "_attend", lambda q, K, V, s: orig(q, K[:-1], V[:-1], s))
+    bad = pa.ref_prefill(pcase.q, kc, vc, pcase.cu_seqlens, pcase.block_table, pcase.context_lens, pcase.scale)
+    assert not np.allclose(bad[1:], bfp[1:])
