@@ -1,0 +1,170 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged-attention library
+ * (libpaged_attn.so).
+ *
+ * The operations follow the pages' statement of the problem:
+ *   - weft, "Shapes and symbols" and "Cache layouts": the per-layer paged cache
+ *     view is [N, P, H_kv, D]; writes scatter through slot_mapping, reads gather
+ *     through block_table; H_q / H_kv is the GQA group size G.
+ *   - ember, "The core idea, in one picture": logical position p of a sequence
+ *     lives at block block_table[p / P], offset p % P.
+ *   - tiny-vllm-py, "KV Cache" (Mental Model, Design Choices, Mistakes I made):
+ *     a query at position t attends to every cached token up to and including t;
+ *     a new token's position is the cache length before its K/V is appended;
+ *     prefill is causal and decode is unmasked.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers, dense row-major, owned by the
+ *     caller.  The library keeps no pointer after a call returns and allocates
+ *     no memory; scratch space is a caller-provided workspace.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *     stream).  None synchronises or reads device memory on the host.
+ *   - Element type `dtype`: PA_DTYPE_F32 (float) or PA_DTYPE_BF16 (bfloat16).
+ *     Arithmetic is fp32; outputs are written in the input dtype (bf16 rounded
+ *     to nearest even).  Index arrays are int32.
+ *   - Supported head_dim: 64 and 128.  Any block_size >= 1.  Any
+ *     num_q_heads that is a multiple of num_kv_heads.
+ *   - Scalars are validated before any HIP call; a zero-sized batch is a no-op
+ *     that returns PA_OK.
+ *   - Device metadata that is out of range (a slot outside [0, N*P), a block id
+ *     outside [0, N), context_lens above max_blocks_per_seq * block_size) gives
+ *     unspecified output values but never an out-of-bounds access: such slots
+ *     are skipped, such tokens are masked, such lengths are clamped.
+ *   - Return value: PA_OK (0) or a negative pa_status; pa_last_error() then
+ *     holds a message for the calling thread.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* null pointer, negative size, inconsistent shape  */
+  PA_ERR_UNSUPPORTED = -2, /* well-formed but not provided (head_dim, dtype)    */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the size query */
+  PA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed        */
+} pa_status;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int pa_version(void);
+
+/* Static text for a status code. */
+const char* pa_status_string(int status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * pa_slot_mapping -- slot of every new token (weft "Cache layouts"; ember
+ * "The core idea").  Request b has T_b = cu_seqlens[b+1] - cu_seqlens[b] new
+ * tokens and context_lens[b] cached tokens counting them, so its new token i sits
+ * at position p = context_lens[b] - T_b + i and gets
+ *     slot_mapping[cu_seqlens[b] + i] = block_table[b][p / P] * P + p % P,
+ * the row index into the flattened [N * P] token rows of the pool.  Positions
+ * outside [0, max_blocks_per_seq * P) get slot -1.
+ *   block_table  int32 [num_seqs, max_blocks_per_seq]
+ *   cu_seqlens   int32 [num_seqs + 1], non-decreasing, cu_seqlens[0] = 0,
+ *                cu_seqlens[num_seqs] = num_tokens
+ *   context_lens int32 [num_seqs]
+ *   slot_mapping int32 [num_tokens] (output)
+ */
+int pa_slot_mapping(const int32_t* block_table, const int32_t* cu_seqlens,
+                    const int32_t* context_lens, int32_t* slot_mapping,
+                    int32_t num_seqs, int64_t num_tokens, int32_t block_size,
+                    int32_t max_blocks_per_seq, void* stream);
+
+/*
+ * pa_reshape_and_cache -- scatter new keys and values into the block pool
+ * (weft "Cache layouts": write = scatter via slot_mapping; tiny-vllm-py
+ * "Paged KV Cache", Mental Model: append into the tail block).  For every token
+ * t with 0 <= slot_mapping[t] < num_blocks * block_size the [H_kv, D] row of k
+ * (and of v) is copied bit for bit to row slot_mapping[t] of the pool viewed as
+ * [N * P, H_kv, D].  Negative (padding) and out-of-range slots are skipped.
+ * Slots must be distinct within one call (duplicates race).
+ *   k, v               [num_tokens, num_kv_heads, head_dim]
+ *   slot_mapping       int32 [num_tokens]
+ *   k_cache, v_cache   [num_blocks, block_size, num_kv_heads, head_dim], in place
+ */
+int pa_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mapping,
+                         void* k_cache, void* v_cache, int64_t num_tokens,
+                         int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t dtype, void* stream);
+
+/* Bytes of workspace pa_paged_decode_attention needs for these shapes. */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_blocks_per_seq);
+
+/*
+ * pa_paged_decode_attention -- one query token per request attends, without a
+ * mask, to the context_lens[b] tokens of its request, gathered through the block
+ * table (tiny-vllm-py "KV Cache": the new token sees all earlier tokens and
+ * itself; the scatter of this step's K/V happens before this call).  Query head
+ * h reads KV head h / G, G = num_q_heads / num_kv_heads.
+ *     out[b, h] = sum_j softmax_j(scale * q[b, h] . k_j) v_j,  j < context_lens[b]
+ * context_lens[b] == 0 gives a zero row.
+ *   q, out             [num_seqs, num_q_heads, head_dim] (out must not alias)
+ *   k_cache, v_cache   [num_blocks, block_size, num_kv_heads, head_dim]
+ *   block_table        int32 [num_seqs, max_blocks_per_seq]; only the first
+ *                      ceil(context_lens[b] / block_size) entries are read
+ *   context_lens       int32 [num_seqs]
+ *   workspace          device scratch of at least pa_decode_workspace_size()
+ *                      bytes, not shared with a concurrently running call
+ */
+int pa_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* context_lens,
+                              float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_paged_prefill_attention needs for these shapes. */
+size_t pa_prefill_workspace_size(int32_t num_seqs, int64_t total_q_tokens,
+                                 int32_t num_q_heads, int32_t num_kv_heads);
+
+/*
+ * pa_paged_prefill_attention -- varlen and chunked prefill over the paged cache
+ * (tiny-vllm-py "Mistakes I made": prefill is causal; ember "Deliberately out of
+ * scope": chunked prefill; weft "Shapes and symbols": T_total packing).
+ * k and v ARE the layer's paged pools, already holding this step's chunk
+ * (written by pa_reshape_and_cache).  Request b's chunk has
+ * T_b = cu_seqlens[b+1] - cu_seqlens[b] tokens; its row i sits at absolute
+ * position L_b - T_b + i (L_b = context_lens[b]) and attends causally to keys
+ * 0 .. L_b - T_b + i.  Requests with T_b > L_b produce unspecified rows.
+ *   q, out        [total_q_tokens, num_q_heads, head_dim], packed by request
+ *   k, v          [num_blocks, block_size, num_kv_heads, head_dim]
+ *   cu_seqlens    int32 [num_seqs + 1]
+ *   block_table   int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens  int32 [num_seqs]
+ *   workspace     at least pa_prefill_workspace_size() bytes
+ * dtype must be PA_DTYPE_BF16 (bf16 MFMA); fp32 returns PA_ERR_UNSUPPORTED.
+ */
+int pa_paged_prefill_attention(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens, const int32_t* block_table,
+                               const int32_t* context_lens, float scale, void* out,
+                               int32_t num_seqs, int64_t total_q_tokens, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_set_timing_events -- measurement hook.  While both events are non-NULL
+ * (hipEvent_t handles), each attention call on this thread records `start`
+ * just before and `stop` just after its main kernel (the decode partition
+ * kernel, or the prefill kernel), on the call's stream, so the caller can time
+ * that kernel alone with hipEventElapsedTime.  Pass NULL, NULL to turn it off.
+ */
+int pa_set_timing_events(void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

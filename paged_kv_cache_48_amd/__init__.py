@@ -1,0 +1,267 @@
+"""Paged-attention hot path for MI355X (gfx950): Python binding of libpaged_attn.so.
+
+Only argument marshalling lives here: every step of the computation runs in the
+HIP kernels behind the C ABI declared in ``include/paged_attn.h``.  PyTorch
+supplies device memory and the current stream.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+
+Calls (weft, "Cache layouts": write = scatter via slot_mapping, read = gather by
+block_table; per-layer pool ``[N, P, H_kv, D]``):
+
+* ``slot_mapping(block_table, cu_seqlens, context_lens, block_size)``
+* ``reshape_and_cache(k, v, slot_mapping, k_cache, v_cache)``
+* ``paged_decode_attention(q, k_cache, v_cache, block_table, context_lens, scale, out)``
+* ``paged_prefill_attention(q, k, v, cu_seqlens, block_table, context_lens, scale, out)``
+"""
+
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "LIB_PATH",
+    "PagedAttnError",
+    "load_library",
+    "slot_mapping",
+    "reshape_and_cache",
+    "paged_decode_attention",
+    "paged_prefill_attention",
+    "decode_workspace_size",
+    "prefill_workspace_size",
+    "kernel_timer",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
+
+_c_void_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_size = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/paged_attn.h
+SIGNATURES = {
+    "pa_version": (ctypes.c_int, []),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_set_timing_events": (ctypes.c_int, [_c_void_p, _c_void_p]),
+    "pa_slot_mapping": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p]),
+    "pa_reshape_and_cache": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32, _i32, _i32, _c_void_p],
+    ),
+    "pa_decode_workspace_size": (_size, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_paged_decode_attention": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+         _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _c_void_p, _size, _c_void_p],
+    ),
+    "pa_prefill_workspace_size": (_size, [_i32, _i64, _i32, _i32]),
+    "pa_paged_prefill_attention": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+         _i32, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _c_void_p, _size, _c_void_p],
+    ),
+}
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+_lib = None
+_lock = threading.Lock()
+
+
+class PagedAttnError(RuntimeError):
+    """A libpaged_attn call returned an error status."""
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpaged_attn.so (built by ``paged_kv_cache_48_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise PagedAttnError(
+                    f"{path} is missing: build it first (python -m paged_kv_cache_48_amd.build)"
+                )
+            lib = ctypes.CDLL(path)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        msg = lib.pa_last_error().decode() or lib.pa_status_string(status).decode()
+        if status in (-1, -2, -3):
+            raise ValueError(msg)
+        raise PagedAttnError(msg)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _req(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype=None, dim=None) -> None:
+    _req(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _req(t.is_cuda, f"{name} must be a device tensor")
+    _req(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _req(t.dtype == dtype, f"{name} must be {dtype} (got {t.dtype})")
+    if dim is not None:
+        _req(t.dim() == dim, f"{name} must have {dim} dimensions (got {t.dim()})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    _req(t.dtype in _DTYPES, f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    return _DTYPES[t.dtype]
+
+
+# one workspace per (device, stream): calls on one stream run in order, so
+# they can share it; calls on different streams must not.
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq) -> int:
+    return int(load_library().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size,
+                                                       max_blocks_per_seq))
+
+
+def prefill_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads) -> int:
+    return int(load_library().pa_prefill_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads))
+
+
+def slot_mapping(block_table: torch.Tensor, cu_seqlens: torch.Tensor, context_lens: torch.Tensor,
+                 block_size: int, num_tokens: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """int32 ``[num_tokens]`` slots of the new tokens (see ``pa_slot_mapping``).
+    ``num_tokens`` must equal ``cu_seqlens[-1]`` (passed explicitly so that no
+    device value is read on the host)."""
+    lib = load_library()
+    _dev_tensor(block_table, "block_table", torch.int32, 2)
+    _dev_tensor(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _dev_tensor(context_lens, "context_lens", torch.int32, 1)
+    B = context_lens.shape[0]
+    _req(cu_seqlens.shape[0] == B + 1, "cu_seqlens must have num_seqs + 1 entries")
+    _req(block_table.shape[0] == B, "block_table must have num_seqs rows")
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int32, device=block_table.device)
+    _dev_tensor(out, "out", torch.int32, 1)
+    _req(out.shape[0] == num_tokens, "out must have num_tokens entries")
+    _check(lib.pa_slot_mapping(block_table.data_ptr(), cu_seqlens.data_ptr(), context_lens.data_ptr(),
+                               out.data_ptr(), B, num_tokens, int(block_size), block_table.shape[1],
+                               _stream(block_table)))
+    return out
+
+
+def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                      k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Scatter ``k``, ``v`` ``[T, H_kv, D]`` into the pools ``[N, P, H_kv, D]`` in place."""
+    lib = load_library()
+    for name, t in (("k", k), ("v", v)):
+        _dev_tensor(t, name, dim=3)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name, dim=4)
+    _dev_tensor(slot_mapping, "slot_mapping", torch.int32, 1)
+    T, H, D = k.shape
+    N, P, H2, D2 = k_cache.shape
+    _req(v.shape == k.shape, "k and v must have the same shape")
+    _req(v_cache.shape == k_cache.shape, "k_cache and v_cache must have the same shape")
+    _req((H, D) == (H2, D2), "k rows and cache rows differ in [H_kv, D]")
+    _req(slot_mapping.shape[0] == T, "slot_mapping must have one entry per token")
+    _req(len({k.dtype, v.dtype, k_cache.dtype, v_cache.dtype}) == 1, "k, v and the caches must share a dtype")
+    _check(lib.pa_reshape_and_cache(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+                                    v_cache.data_ptr(), T, N, P, H, D, _dtype_code(k), _stream(k)))
+
+
+def _attn_common(q, k_cache, v_cache, block_table, context_lens, out):
+    _dev_tensor(q, "q", dim=3)
+    _dev_tensor(out, "out", dim=3)
+    _dev_tensor(k_cache, "k_cache", dim=4)
+    _dev_tensor(v_cache, "v_cache", dim=4)
+    _dev_tensor(block_table, "block_table", torch.int32, 2)
+    _dev_tensor(context_lens, "context_lens", torch.int32, 1)
+    _req(out.shape == q.shape and out.dtype == q.dtype, "out must match q in shape and dtype")
+    _req(out.data_ptr() != q.data_ptr(), "out must not alias q")
+    _req(k_cache.shape == v_cache.shape, "k_cache and v_cache must have the same shape")
+    _req(len({q.dtype, k_cache.dtype, v_cache.dtype}) == 1, "q and the caches must share a dtype")
+    _req(q.shape[2] == k_cache.shape[3], "head_dim of q and of the caches differ")
+    B = context_lens.shape[0]
+    _req(block_table.shape[0] == B, "block_table must have one row per sequence")
+    return B
+
+
+def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                           out: torch.Tensor) -> torch.Tensor:
+    """Decode attention: ``q``/``out`` ``[B, H_q, D]``; see ``pa_paged_decode_attention``."""
+    lib = load_library()
+    B = _attn_common(q, k_cache, v_cache, block_table, context_lens, out)
+    _req(q.shape[0] == B, "q must have one row per sequence")
+    N, P, Hkv, D = k_cache.shape
+    Hq = q.shape[1]
+    M = block_table.shape[1]
+    stream = _stream(q)
+    need = decode_workspace_size(B, Hq, D, P, M)
+    ws = _workspace(q.device, stream, need)
+    _check(lib.pa_paged_decode_attention(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                         block_table.data_ptr(), context_lens.data_ptr(), float(scale),
+                                         out.data_ptr(), B, Hq, Hkv, D, P, N, M, _dtype_code(q),
+                                         ws.data_ptr(), ws.numel(), stream))
+    return out
+
+
+def paged_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                            block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                            out: torch.Tensor) -> torch.Tensor:
+    """Varlen / chunked prefill: ``q``/``out`` ``[T_total, H_q, D]``; ``k``, ``v`` are the
+    paged pools; see ``pa_paged_prefill_attention``."""
+    lib = load_library()
+    B = _attn_common(q, k, v, block_table, context_lens, out)
+    _dev_tensor(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _req(cu_seqlens.shape[0] == B + 1, "cu_seqlens must have num_seqs + 1 entries")
+    N, P, Hkv, D = k.shape
+    T, Hq, _ = q.shape
+    M = block_table.shape[1]
+    stream = _stream(q)
+    need = prefill_workspace_size(B, T, Hq, Hkv)
+    ws = _workspace(q.device, stream, need)
+    _check(lib.pa_paged_prefill_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                                          block_table.data_ptr(), context_lens.data_ptr(), float(scale),
+                                          out.data_ptr(), B, T, Hq, Hkv, D, P, N, M, _dtype_code(q),
+                                          ws.data_ptr(), ws.numel(), stream))
+    return out
+
+
+@contextlib.contextmanager
+def kernel_timer(start: "torch.cuda.Event", stop: "torch.cuda.Event"):
+    """While active, each attention call records ``start``/``stop`` around its
+    main kernel on its stream (``pa_set_timing_events``).  The events must have
+    been created (recorded once) before."""
+    lib = load_library()
+    _req(start.cuda_event != 0 and stop.cuda_event != 0, "record the events once before use")
+    lib.pa_set_timing_events(start.cuda_event, stop.cuda_event)
+    try:
+        yield
+    finally:
+        lib.pa_set_timing_events(None, None)

@@ -1,0 +1,246 @@
+// C ABI of libpaged_attn.so: argument validation, status codes and dispatch to
+// the gfx950 launchers.  Every check below runs before the first HIP call, so
+// a malformed call fails without touching the device.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <climits>
+#include <string>
+
+#include "../../include/paged_attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int32_t dtype) { return dtype == PA_DTYPE_F32 || dtype == PA_DTYPE_BF16; }
+int elem_size(int32_t dtype) { return dtype == PA_DTYPE_BF16 ? 2 : 4; }
+
+#define PA_REQUIRE(cond, status, ...) \
+  do {                                \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+// Checks shared by decode and prefill.
+int check_attn(const char* fn, int32_t num_seqs, int32_t hq, int32_t hkv, int32_t head_dim,
+               int32_t block_size, int64_t num_blocks, int32_t max_blocks, int32_t dtype) {
+  PA_REQUIRE(num_seqs >= 0, PA_ERR_INVALID, "%s: num_seqs must be >= 0 (got %d)", fn, num_seqs);
+  PA_REQUIRE(hq >= 1 && hkv >= 1, PA_ERR_INVALID, "%s: head counts must be >= 1 (got %d, %d)", fn, hq, hkv);
+  PA_REQUIRE(hq % hkv == 0, PA_ERR_INVALID,
+             "%s: num_q_heads (%d) must be a multiple of num_kv_heads (%d)", fn, hq, hkv);
+  PA_REQUIRE(dtype_ok(dtype), PA_ERR_UNSUPPORTED, "%s: unsupported dtype %d", fn, dtype);
+  PA_REQUIRE(head_dim == 64 || head_dim == 128, PA_ERR_UNSUPPORTED,
+             "%s: head_dim must be 64 or 128 (got %d)", fn, head_dim);
+  PA_REQUIRE(block_size >= 1, PA_ERR_INVALID, "%s: block_size must be >= 1 (got %d)", fn, block_size);
+  PA_REQUIRE(num_blocks >= 1 && num_blocks <= INT_MAX, PA_ERR_INVALID,
+             "%s: num_blocks must be in [1, 2^31) (got %lld)", fn, (long long)num_blocks);
+  PA_REQUIRE(max_blocks >= 1, PA_ERR_INVALID, "%s: max_blocks_per_seq must be >= 1 (got %d)", fn,
+             max_blocks);
+  PA_REQUIRE((int64_t)max_blocks * block_size <= INT_MAX, PA_ERR_INVALID,
+             "%s: max_blocks_per_seq * block_size must fit in int32", fn);
+  PA_REQUIRE(num_blocks * (int64_t)block_size <= INT_MAX, PA_ERR_INVALID,
+             "%s: num_blocks * block_size must fit in int32 (slots are int32)", fn);
+  return PA_OK;
+}
+
+}  // namespace
+
+namespace pa {
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int pa_version(void) { return 100; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+int pa_set_timing_events(void* start_event, void* stop_event) {
+  g_ev_start = static_cast<hipEvent_t>(start_event);
+  g_ev_stop = static_cast<hipEvent_t>(stop_event);
+  return PA_OK;
+}
+
+int pa_slot_mapping(const int32_t* block_table, const int32_t* cu_seqlens, const int32_t* context_lens,
+                    int32_t* slot_mapping, int32_t num_seqs, int64_t num_tokens, int32_t block_size,
+                    int32_t max_blocks_per_seq, void* stream) {
+  g_err.clear();
+  const char* fn = "pa_slot_mapping";
+  PA_REQUIRE(num_seqs >= 0 && num_tokens >= 0, PA_ERR_INVALID, "%s: negative size", fn);
+  PA_REQUIRE(num_tokens <= INT_MAX, PA_ERR_INVALID, "%s: num_tokens must fit in int32", fn);
+  PA_REQUIRE(block_size >= 1 && max_blocks_per_seq >= 1, PA_ERR_INVALID,
+             "%s: block_size and max_blocks_per_seq must be >= 1", fn);
+  if (num_tokens == 0) return PA_OK;
+  PA_REQUIRE(num_seqs >= 1, PA_ERR_INVALID, "%s: %lld tokens but no sequence", fn, (long long)num_tokens);
+  PA_REQUIRE(block_table && cu_seqlens && context_lens && slot_mapping, PA_ERR_INVALID,
+             "%s: null pointer argument", fn);
+  return hip_status(pa::launch_slot_mapping(block_table, cu_seqlens, context_lens, slot_mapping, num_seqs,
+                                            num_tokens, block_size, max_blocks_per_seq,
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int pa_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mapping, void* k_cache,
+                         void* v_cache, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* stream) {
+  g_err.clear();
+  const char* fn = "pa_reshape_and_cache";
+  PA_REQUIRE(num_tokens >= 0, PA_ERR_INVALID, "%s: num_tokens must be >= 0", fn);
+  PA_REQUIRE(dtype_ok(dtype), PA_ERR_UNSUPPORTED, "%s: unsupported dtype %d", fn, dtype);
+  PA_REQUIRE(num_kv_heads >= 1 && head_dim >= 1, PA_ERR_INVALID, "%s: head sizes must be >= 1", fn);
+  PA_REQUIRE(block_size >= 1, PA_ERR_INVALID, "%s: block_size must be >= 1", fn);
+  PA_REQUIRE(num_blocks >= 1, PA_ERR_INVALID, "%s: num_blocks must be >= 1", fn);
+  PA_REQUIRE(num_blocks * (int64_t)block_size <= INT_MAX, PA_ERR_INVALID,
+             "%s: num_blocks * block_size must fit in int32 (slots are int32)", fn);
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_size(dtype);
+  PA_REQUIRE(row_bytes % 16 == 0 && row_bytes <= INT_MAX, PA_ERR_UNSUPPORTED,
+             "%s: a token row (H_kv * D * elem) must be a multiple of 16 bytes (got %lld)", fn,
+             (long long)row_bytes);
+  if (num_tokens == 0) return PA_OK;
+  PA_REQUIRE(k && v && slot_mapping && k_cache && v_cache, PA_ERR_INVALID, "%s: null pointer argument", fn);
+  return hip_status(pa::launch_reshape_and_cache(k, v, slot_mapping, k_cache, v_cache, num_tokens,
+                                                 num_blocks * block_size, (int)row_bytes,
+                                                 static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_blocks_per_seq) {
+  if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || block_size < 1 || max_blocks_per_seq < 1) return 0;
+  return pa::decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq);
+}
+
+int pa_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* context_lens, float scale,
+                              void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "pa_paged_decode_attention";
+  int st = check_attn(fn, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  PA_REQUIRE(q && k_cache && v_cache && block_table && context_lens && out, PA_ERR_INVALID,
+             "%s: null pointer argument", fn);
+  const size_t need = pa::decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq);
+  PA_REQUIRE(workspace && workspace_bytes >= need, PA_ERR_WORKSPACE,
+             "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
+  pa::AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.scale = scale;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.dtype = dtype;
+  a.workspace = workspace;
+  return hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream), g_ev_start, g_ev_stop), fn);
+}
+
+size_t pa_prefill_workspace_size(int32_t num_seqs, int64_t total_q_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads) {
+  if (num_seqs < 0 || total_q_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1) return 0;
+  return pa::prefill_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads);
+}
+
+int pa_paged_prefill_attention(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                               const int32_t* block_table, const int32_t* context_lens, float scale,
+                               void* out, int32_t num_seqs, int64_t total_q_tokens, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "pa_paged_prefill_attention";
+  int st = check_attn(fn, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, dtype);
+  if (st != PA_OK) return st;
+  PA_REQUIRE(total_q_tokens >= 0 && total_q_tokens <= INT_MAX, PA_ERR_INVALID,
+             "%s: total_q_tokens must be in [0, 2^31)", fn);
+  PA_REQUIRE(dtype == PA_DTYPE_BF16, PA_ERR_UNSUPPORTED, "%s: prefill is provided for bf16 only", fn);
+  PA_REQUIRE(num_q_heads / num_kv_heads <= 64, PA_ERR_UNSUPPORTED,
+             "%s: GQA group size above 64 is not provided", fn);
+  if (total_q_tokens == 0) return PA_OK;
+  PA_REQUIRE(num_seqs >= 1, PA_ERR_INVALID, "%s: %lld query tokens but no sequence", fn,
+             (long long)total_q_tokens);
+  PA_REQUIRE(q && k && v && cu_seqlens && block_table && context_lens && out, PA_ERR_INVALID,
+             "%s: null pointer argument", fn);
+  const size_t need = pa::prefill_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads);
+  PA_REQUIRE(workspace && workspace_bytes >= need, PA_ERR_WORKSPACE,
+             "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
+  pa::AttnArgs a{};
+  a.q = q;
+  a.k_cache = k;
+  a.v_cache = v;
+  a.cu_seqlens = cu_seqlens;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.scale = scale;
+  a.num_seqs = num_seqs;
+  a.num_q_tokens = total_q_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.dtype = dtype;
+  a.workspace = workspace;
+  return hip_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream), g_ev_start, g_ev_stop), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16
+// conversion, DPP row reductions and the internal launcher interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 values are stored as their 16-bit patterns.
+typedef uint16_t bf16_bits;
+
+// Widening a bfloat16 to float is a 16-bit shift: the bf16 is the upper half
+// of the binary32 encoding.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// DPP lane permutations inside a 16-lane row (gfx9 dpp_ctrl encodings).
+// ---------------------------------------------------------------------------
+enum : int {
+  kDppQuadXor1 = 0xB1,       // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,       // quad_perm [2,3,0,1]
+  kDppRowRor8 = 0x128,       // row_ror:8  (lane i <- lane (i+8) mod 16)
+  kDppRowMirror = 0x140,     // lane i <- lane 15-i
+  kDppRowHalfMirror = 0x141  // lane i <- lane 7-i within each half row
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Max / sum over the 16 lanes of a DPP row; every lane of the row gets the
+// result (pairs see each other's values, so the result is identical in all).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// exp2 on the hardware transcendental unit (v_exp_f32); exp(x) is evaluated
+// as exp2(x * log2(e)) with the constant folded into the score scale.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace pa

@@ -1,0 +1,61 @@
+// Host launchers of the gfx950 kernels.  Called from api.hip after argument
+// validation; every launcher only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+// Tokens per split-context partition of the decode kernel.  A request with
+// context L is cut into ceil(L / kPartTokens) partitions; this depends on L
+// only, never on the batch, so a request's result does not depend on its
+// neighbours.
+constexpr int kPartTokens = 256;
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_slot_mapping(const int32_t* block_table, const int32_t* cu_seqlens,
+                               const int32_t* context_lens, int32_t* slot_mapping, int num_seqs,
+                               int64_t num_tokens, int block_size, int max_blocks, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mapping,
+                                    void* k_cache, void* v_cache, int64_t num_tokens,
+                                    int64_t pool_rows, int row_bytes, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cu_seqlens;  // prefill only
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  void* out;
+  float scale;
+  int num_seqs;
+  int64_t num_q_tokens;  // prefill only
+  int num_q_heads;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int64_t num_blocks;
+  int max_blocks;
+  int dtype;
+  void* workspace;
+};
+
+size_t decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int block_size,
+                             int max_blocks);
+hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_start,
+                         hipEvent_t ev_stop);
+
+size_t prefill_workspace_size(int num_seqs, int64_t num_q_tokens, int num_q_heads,
+                              int num_kv_heads);
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_start,
+                          hipEvent_t ev_stop);
+
+}  // namespace pa

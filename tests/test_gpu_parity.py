@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path against the fp64 oracle on seeded inputs.
+
+Scatter and slot math must be bit-exact; attention must be within 1e-4 (fp32
+inputs) or 1e-2 + 2e-2 |ref| (bf16 inputs) element by element.  Every pool is
+NaN-filled before it is written, so a kernel that lets a masked slot reach the
+output fails.  All calls go through the C ABI (ctypes binding)."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_48_amd as pa
+from oracle import ref_decode, ref_prefill, ref_slot_mapping
+from workloads import config_case, make_case
+
+from gpu_util import DEV, DevCase, assert_close, idx, oracle_pool, to_dev, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def decode_ref(case, select=None, block_table=None):
+    kc, vc = oracle_pool(case, block_table)
+    bt = case.block_table if block_table is None else block_table
+    return ref_decode(case.q, kc, vc, bt, case.context_lens, case.scale, select=select)
+
+
+def small(dtype="bf16", P=16, Hq=32, Hkv=8, D=128, lens=(1, 16, 255, 256, 257, 511, 700), qlens=None, seed=0, **kw):
+    return make_case(dtype=dtype, block_size=P, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                     context_lens=list(lens), query_lens=qlens, seed=seed, **kw)
+
+
+# ----------------------------------------------------------------------------
+# slot mapping and scatter: bit-exact
+# ----------------------------------------------------------------------------
+
+def test_slot_mapping_worked_examples_on_gpu():
+    # ember "The core idea" (block table [2, 0, 5], P = 4) and tiny-vllm-py
+    # "Mental Model" (blocks 17, 4, 23): whole sequence as one prefill step
+    for table, n, want in (([2, 0, 5], 9, [8, 9, 10, 11, 0, 1, 2, 3, 20]),
+                           ([17, 4, 23], 10, [68, 69, 70, 71, 16, 17, 18, 19, 92, 93])):
+        got = pa.slot_mapping(idx([table]), idx([0, n]), idx([n]), 4, n)
+        assert got.cpu().tolist() == want
+
+
+@pytest.mark.parametrize("idx_cfg,P", [(0, None), (4, 1), (4, 16), (4, 64)])
+def test_slot_mapping_matches_oracle(idx_cfg, P):
+    c = config_case(idx_cfg, block_size=P, values=False)
+    got = pa.slot_mapping(idx(c.block_table), idx(c.cu_seqlens), idx(c.context_lens), c.block_size, c.T_total)
+    want = ref_slot_mapping(c.block_table, c.cu_seqlens, c.context_lens, c.block_size)
+    assert np.array_equal(got.cpu().numpy().astype(np.int64), want)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_reshape_and_cache_bit_exact_whole_pool(dtype):
+    c = small(dtype=dtype, P=7, Hq=4, Hkv=2, D=64, lens=(3, 40, 9, 64), qlens=(3, 5, 1, 64), seed=3)
+    # plant special values in the new tokens' K: +-0, +-inf, NaN payloads, denormals
+    specials = {"f32": np.array([0x0, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00123, 0xFFBADBAD, 0x1, 0x807FFFFF],
+                                dtype=np.uint32).view(np.float32),
+                "bf16": np.array([0x0, 0x8000, 0x7F80, 0xFF80, 0x7FC1, 0xFFAB, 0x1, 0x807F], dtype=np.uint16)}[dtype]
+    flat = c.k_tok.reshape(-1)
+    flat[-len(specials) * 50:] = np.tile(specials, 50)
+    d = DevCase(c)
+    kc, vc = oracle_pool(c)
+    bits = np.uint16 if dtype == "bf16" else np.uint32
+    assert np.array_equal(to_host_bits(d.kc).view(bits), kc.view(bits))
+    assert np.array_equal(to_host_bits(d.vc).view(bits), vc.view(bits))
+
+
+def test_reshape_and_cache_skips_negative_slots():
+    c = small(dtype="bf16", P=4, Hq=2, Hkv=2, D=64, lens=(6,), qlens=(6,), seed=4)
+    d = DevCase(c)
+    before = to_host_bits(d.kc).copy()
+    k = to_dev(c.k_tok[:3] ^ np.uint16(0x1234), "bf16")
+    pa.reshape_and_cache(k, k, idx([-1, -5, -1]), d.kc, d.vc)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(d.kc), before)
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+
+def test_decode_tiny_config():
+    c = config_case(0)
+    d = DevCase(c)
+    assert_close(d.decode(), decode_ref(c), "f32", "tiny")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_decode_config_shapes_reduced(cfg):
+    """The config's head shape and dtype with a hand-picked set of lengths that
+    covers L = 1, one tile, exactly one partition, one partition + 1 token,
+    several partitions and the longest context."""
+    base = config_case(cfg, values=False)
+    lens = [1, 15, 16, 17, 255, 256, 257, 769, int(base.context_lens.max())]
+    c = small(dtype=base.dtype, P=base.block_size, Hq=base.num_q_heads, Hkv=base.num_kv_heads, D=base.head_dim,
+              lens=lens, seed=10 + cfg)
+    d = DevCase(c)
+    assert_close(d.decode(), decode_ref(c), c.dtype, f"config {cfg} shape")
+
+
+def test_decode_llama3_8b_full_size_sampled():
+    """Full Llama-3-8B-shaped batch (B=256, log-normal lengths, 90% pool) in the
+    launch configuration the benchmark times; the oracle checks 12 requests."""
+    c = config_case(3)
+    d = DevCase(c)
+    out = d.decode()
+    order = np.argsort(c.context_lens)
+    rng = np.random.default_rng(123)
+    pick = sorted(set([int(order[0]), int(order[1]), int(order[-1]), int(order[-2])]
+                      + rng.choice(c.B, 8, replace=False).tolist()))
+    ref = decode_ref(c, select=pick)
+    assert_close(out, ref, "bf16", "llama3_8b", rows=pick)
+
+
+@pytest.mark.parametrize("G,Hkv,D,dtype", [(1, 12, 64, "f32"), (1, 4, 128, "bf16"), (3, 2, 64, "bf16"),
+                                           (4, 8, 128, "f32"), (8, 2, 128, "bf16"), (6, 1, 64, "bf16"),
+                                           (2, 3, 128, "bf16"), (16, 1, 64, "bf16")])
+def test_decode_head_layouts(G, Hkv, D, dtype):
+    c = small(dtype=dtype, P=16, Hq=G * Hkv, Hkv=Hkv, D=D, lens=(1, 33, 300, 520), seed=G * 7 + D)
+    d = DevCase(c)
+    assert_close(d.decode(), decode_ref(c), dtype, f"G={G} D={D} {dtype}")
+
+
+def test_decode_block_size_invariance():
+    """ember "Correctness": block_size in {1,2,3,7,16,64}.  Each matches the
+    oracle; the kernel tiles by token position only, so results are bitwise
+    identical across block sizes."""
+    outs = []
+    for P in (1, 2, 3, 7, 16, 64):
+        c = small(P=P, lens=(5, 130, 257, 600), seed=21)
+        d = DevCase(c)
+        o = d.decode()
+        assert_close(o, decode_ref(c), "bf16", f"P={P}")
+        outs.append(to_host_bits(o))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_decode_block_permutation_invariance_bitwise():
+    c = small(P=16, lens=(40, 300, 513), seed=22)
+    d = DevCase(c)
+    ref = to_host_bits(d.decode())
+    perm = np.random.default_rng(5).permutation(c.num_blocks).astype(np.int64)
+    kc2 = torch.empty_like(d.kc)
+    vc2 = torch.empty_like(d.vc)
+    p = torch.as_tensor(perm, device=DEV)
+    kc2[p] = d.kc
+    vc2[p] = d.vc
+    bt2 = idx(perm[c.block_table])
+    out = torch.empty_like(d.q)
+    pa.paged_decode_attention(d.q, kc2, vc2, bt2, d.lens, c.scale, out)
+    assert np.array_equal(to_host_bits(out), ref)
+
+
+def test_decode_batch_invariance_bitwise():
+    c = small(P=16, lens=(12, 700, 256, 33, 1025), seed=23)
+    d = DevCase(c)
+    full = to_host_bits(d.decode())
+    for b in range(c.B):
+        out = torch.empty_like(d.q[b:b + 1])
+        pa.paged_decode_attention(d.q[b:b + 1].contiguous(), d.kc, d.vc, d.bt[b:b + 1].contiguous(),
+                                  d.lens[b:b + 1].contiguous(), c.scale, out)
+        assert np.array_equal(to_host_bits(out)[0], full[b]), b
+
+
+def test_decode_empty_context_gives_zeros_and_repeat_is_deterministic():
+    c = small(P=16, Hq=8, Hkv=2, lens=(300, 5, 1), seed=24)
+    d = DevCase(c)
+    lens = d.lens.clone()
+    lens[1] = 0
+    out = torch.full_like(d.q, 7.0)
+    pa.paged_decode_attention(d.q, d.kc, d.vc, d.bt, lens, c.scale, out)
+    o = to_host_bits(out)
+    assert np.all(o[1] == 0)
+    ref = decode_ref(c)
+    assert_close(out, ref, "bf16", "len0 batch", rows=[0, 2])
+    out2 = torch.empty_like(d.q)
+    pa.paged_decode_attention(d.q, d.kc, d.vc, d.bt, lens, c.scale, out2)
+    assert np.array_equal(to_host_bits(out2), o)
+
+
+# ----------------------------------------------------------------------------
+# prefill
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,Hkv,D,P", [(4, 2, 128, 16), (1, 3, 64, 16), (2, 2, 128, 7), (8, 1, 64, 1),
+                                       (3, 2, 128, 64), (4, 8, 64, 16)])
+def test_prefill_matches_oracle(G, Hkv, D, P):
+    # chunks: whole prompt; chunk over a prefix; T not a multiple of the q tile;
+    # a single new token; a long chunk over a long prefix
+    lens = (70, 300, 45, 9, 620)
+    qlens = (70, 100, 33, 1, 300)
+    c = small(P=P, Hq=G * Hkv, Hkv=Hkv, D=D, lens=lens, qlens=qlens, seed=30 + G * D)
+    d = DevCase(c)
+    kc, vc = oracle_pool(c)
+    ref = ref_prefill(c.q, kc, vc, c.cu_seqlens, c.block_table, c.context_lens, c.scale)
+    assert_close(d.prefill(), ref, "bf16", f"prefill G={G} D={D} P={P}")
+
+
+def test_prefill_single_token_matches_decode():
+    c = small(P=16, lens=(77, 400, 1), seed=40)
+    d = DevCase(c)
+    dec = d.decode()
+    pre = d.prefill()
+    ref = decode_ref(c)
+    assert_close(pre, ref, "bf16", "prefill T=1")
+    assert_close(dec, ref, "bf16", "decode")
+
+
+def test_prefill_chunked_matches_one_shot():
+    """The same prompt prefilled in chunks (scatter each chunk, then attend)
+    gives the rows of a one-shot prefill, within tolerance of the oracle."""
+    one = small(P=16, Hq=8, Hkv=2, lens=(390,), qlens=(390,), seed=41)
+    d = DevCase(one)
+    whole = d.prefill()
+    kc, vc = oracle_pool(one)
+    ref = ref_prefill(one.q, kc, vc, one.cu_seqlens, one.block_table, one.context_lens, one.scale)
+    assert_close(whole, ref, "bf16", "one shot")
+    kpool = torch.full_like(d.kc, float("nan"))
+    vpool = torch.full_like(d.vc, float("nan"))
+    start = 0
+    pieces = []
+    k_all = to_dev(one.k_tok, "bf16")
+    v_all = to_dev(one.v_tok, "bf16")
+    for T in (100, 1, 130, 159):
+        L = start + T
+        slots = pa.slot_mapping(d.bt, idx([0, T]), idx([L]), 16, T)
+        pa.reshape_and_cache(k_all[start:L].contiguous(), v_all[start:L].contiguous(), slots, kpool, vpool)
+        out = torch.empty_like(d.q[start:L])
+        pa.paged_prefill_attention(d.q[start:L].contiguous(), kpool, vpool, idx([0, T]), d.bt, idx([L]),
+                                   one.scale, out)
+        pieces.append(out)
+        start = L
+    assert_close(torch.cat(pieces), ref, "bf16", "chunked")
+
+
+def mixed_step(c):
+    """One mixed step: scatter every new token, prefill the first 16 requests'
+    chunks, decode the other 48 (the workload's order)."""
+    d = DevCase(c)
+    npf = 16
+    cu = c.cu_seqlens
+    qp = d.q[: cu[npf]].contiguous()
+    outp = torch.empty_like(qp)
+    pa.paged_prefill_attention(qp, d.kc, d.vc, d.cu[: npf + 1].contiguous(), d.bt[:npf].contiguous(),
+                               d.lens[:npf].contiguous(), c.scale, outp)
+    qd = d.q[cu[npf]:].contiguous()
+    outd = torch.empty_like(qd)
+    pa.paged_decode_attention(qd, d.kc, d.vc, d.bt[npf:].contiguous(), d.lens[npf:].contiguous(), c.scale, outd)
+    return d, outp, outd
+
+
+@pytest.mark.parametrize("P", [1, 16, 64])
+def test_mixed_step_full_size_sampled(P):
+    """The mixed chunked-prefill + decode workload at full size, block sizes
+    1, 16, 64; the oracle checks sampled prefill rows and decode requests."""
+    c = config_case(4, block_size=P)
+    d, outp, outd = mixed_step(c)
+    kc, vc = oracle_pool(c)
+    cu = c.cu_seqlens
+    rng = np.random.default_rng(7)
+    rows = []
+    for b in range(16):  # first, last and two random rows of each chunk
+        s, e = int(cu[b]), int(cu[b + 1])
+        rows += [s, e - 1] + rng.integers(s, e, 2).tolist()
+    rows = sorted(set(rows))
+    refp = ref_prefill(c.q, kc, vc, cu, c.block_table, c.context_lens, c.scale, rows=rows)
+    assert_close(outp, refp[: cu[16]], "bf16", f"mixed prefill P={P}", rows=rows)
+    pick = sorted(set([0, 1, 47] + rng.integers(0, 48, 5).tolist()))
+    qdec = c.q[cu[16:64]]
+    refd = ref_decode(qdec, kc, vc, c.block_table[16:], c.context_lens[16:], c.scale, select=pick)
+    assert_close(outd, refd, "bf16", f"mixed decode P={P}", rows=pick)
