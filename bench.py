@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["llama3_8b", "mixed"], default="llama3_8b")
+    ap.add_argument("--workload", choices=["llama3_8b", "mixed", "copy"], default="llama3_8b")
+    ap.add_argument("--layers", type=int, default=None, help="profile runs only: fewer layers")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -132,7 +133,7 @@ def bench_decode(args):
     dev = torch.device("cuda:0")
     B, Hq, Hkv, D, P, N, M = (case.B, case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size,
                               case.num_blocks, case.max_blocks_per_seq)
-    L = case.num_layers
+    L = case.num_layers if args.layers is None else args.layers
     s = 2
     gen = torch.Generator(device=dev)
     bt = torch.as_tensor(case.block_table, device=dev)
@@ -323,6 +324,29 @@ def bench_mixed(args):
     return res, case
 
 
+def bench_copy(args):
+    """A plain device copy of 1 GiB, the calibration run for HBM byte counters
+    (FETCH_SIZE / WRITE_SIZE per dispatch divided by 1 GiB)."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    return {"metric": "device copy of 1 GiB (read + write)", "value": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "torch copy_ of 1 GiB", "bytes": n}, "cpu_baseline": None}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -335,7 +359,9 @@ def main():
     import paged_kv_cache_48_amd as pa
 
     pa.load_library()
-    if args.workload == "mixed":
+    if args.workload == "copy":
+        res = bench_copy(args)
+    elif args.workload == "mixed":
         res, case = bench_mixed(args)
         res["cpu_baseline"] = None
     else:

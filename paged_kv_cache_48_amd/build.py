@@ -17,6 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
 SOURCES = ["api.hip", "cache_ops.hip", "decode.hip", "prefill.hip"]
+# per-source extra flags: decode keeps its MFMA accumulators in VGPRs (its
+# softmax rescale multiplies them on the VALU, which would otherwise copy
+# them out of the accumulation registers on every tile)
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 FLAGS = [
@@ -64,7 +68,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *FLAGS, "-c", os.path.join(HERE, "csrc", src), "-o", obj])
+        cmds.append([cc, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(HERE, "csrc", src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"

@@ -11,6 +11,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // bf16 values are stored as their 16-bit patterns.
 typedef uint16_t bf16_bits;
@@ -27,8 +28,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two floats -> two packed bfloat16 (lo in bits 0..15), round to nearest even;
+// a single v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const f32x2_t x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
 }
 
 // ---------------------------------------------------------------------------

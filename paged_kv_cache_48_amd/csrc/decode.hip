@@ -13,24 +13,26 @@
 //   * Work queue.  A tiny plan kernel lists the (request, partition) items,
 //     full partitions first and short tail partitions last, and zeroes a queue
 //     counter; a persistent grid of waves pulls items with one atomic each.
-//   * Per 16-token tile the wave loads K and V straight from HBM, 16-byte
-//     vector loads, lane (n, g) holding token n's quarter g of the head
-//     (4 lanes read one 256-byte row).  QK^T is one MFMA chain
-//     (16x16x32 bf16 or 16x16x4 f32): the up-to-4 query heads are replicated
-//     over the 16 A rows, so every lane receives the scores of all heads for
-//     its own token without any cross-lane move.
-//   * Online softmax in base 2 (running max and sum); the max over the tile's
-//     16 tokens is a 4-step DPP reduction inside each 16-lane row.  P.V runs on
-//     the VALU (fp32 FMA): each lane accumulates its token's contribution to its
-//     quarter of the head; the 16 token lanes are merged once per item by a
-//     DPP reduce-scatter, which leaves each lane with D/16 outputs to store.
+//   * Coalesced gathers.  Per 16-token tile each quarter-wave reads whole
+//     contiguous row slices of one KV head (16-byte loads); the tile goes
+//     through a wave-private LDS region, K row-major and V transposed, which
+//     turns it into MFMA operands.  The next tile's loads are in flight while
+//     the current one computes.
+//   * S^T = K Q^T and O^T += V^T P^T run on MFMA (bf16: 16x16x32 and
+//     16x16x16; fp32: 16x16x4) with fp32 accumulation.  The group's query
+//     heads are the B-operand columns, so each lane holds one head's scores
+//     for four tokens, which is exactly the B operand of the P.V product: the
+//     probabilities never leave registers and the outputs need no cross-lane
+//     reduction.  Online softmax in base 2 (running max and sum).
 //   * Items of a request with one partition write the output directly; the
 //     others write (max, sum, unnormalised output) partials that the reduce
 //     kernel merges:  m = max_i m_i,  out = sum_i 2^(m_i-m) o_i / sum_i 2^(m_i-m) l_i.
-//   * Masked tokens never load: tail slots of a block may hold anything
-//     (even NaN), and block ids outside [0, N) mask their token instead of
-//     being dereferenced.
+//   * Tokens past the partition end never load: tail slots of a block may hold
+//     anything (even NaN).  Block ids outside [0, N) are never dereferenced
+//     (their rows read as zeros, so the result is unspecified but safe).
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -40,6 +42,9 @@ namespace pa {
 namespace {
 
 constexpr int kTile = 16;                        // tokens per MFMA tile
+// logical blocks one partition can touch: kPartTokens / P + 1 for P >= 1
+constexpr int kMaxPartBlocks = kPartTokens + 64;
+
 constexpr int kWavesPerBlock = 4;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -120,84 +125,155 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Element-type traits: K/V slices, MFMA QK step, widening V to fp32.
+// Tile geometry.  A tile is 16 consecutive tokens of one KV head.  Lane l
+// loads 16-byte piece l % CPR of the head's row slice for tokens
+// (l / CPR) * TPL + j, j < TPL, so each quarter-wave reads whole contiguous
+// row slices (at most two 128-byte lines per 16 lanes).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-struct Traits {
-  static constexpr int E = D / 4;                        // elements per lane per row
-  static constexpr int NV = E * (int)sizeof(T) / 16;     // 16-byte vectors per lane
+struct Geo {
+  static constexpr int ROWB = D * (int)sizeof(T);  // bytes of one head's row slice
+  static constexpr int CPR = ROWB / 16;            // 16-byte pieces per row slice
+  static constexpr int TPL = 16 * CPR / 64;        // tokens per lane per tile
+  static constexpr int KST = ROWB + 16;            // LDS row stride of K (and of V for fp32)
+  static constexpr int VTS = 40;                   // LDS row stride of transposed V (bf16): 16 tokens + pad
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int KBYTES = 16 * KST;
+  static constexpr int VBYTES = kBf16 ? D * VTS : 16 * KST;
+  static constexpr int IDS_BYTES = 4 * kMaxPartBlocks;  // block ids of one partition
+  static constexpr int LDS_PER_WAVE = KBYTES + VBYTES + IDS_BYTES;
+  static constexpr int NQ = kBf16 ? D / 32 : D / 4;  // QK MFMA steps over the head dimension
 };
 
-// QK^T for one tile: acc[m][n] = sum_k A[m][k] B[k][n], A = query rows, B = K^T.
-template <int D>
-__device__ __forceinline__ f32x4_t qk_mfma(const u32x4_t (&qv)[Traits<bf16_bits, D>::NV],
-                                           const u32x4_t (&kv)[Traits<bf16_bits, D>::NV]) {
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < Traits<bf16_bits, D>::NV; ++i)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qv[i]),
-                                                  __builtin_bit_cast(bf16x8_t, kv[i]), acc, 0, 0, 0);
-  return acc;
-}
-
-template <int D>
-__device__ __forceinline__ f32x4_t qk_mfma_f32(const u32x4_t (&qv)[Traits<float, D>::NV],
-                                               const u32x4_t (&kv)[Traits<float, D>::NV]) {
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < Traits<float, D>::NV; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(qv[i][j]), __uint_as_float(kv[i][j]),
-                                                 acc, 0, 0, 0);
-  return acc;
-}
+// Byte offsets into the pool: 32-bit when the pool is under 4 GiB (one VGPR
+// per address, added to a scalar base), 64-bit otherwise.
+template <bool kWide>
+struct Off {
+  typedef typename std::conditional<kWide, uint64_t, uint32_t>::type type;
+};
 
 template <typename T, int D>
-__device__ __forceinline__ void widen_slice(const u32x4_t (&v)[Traits<T, D>::NV],
-                                            float (&f)[Traits<T, D>::E]) {
-  if constexpr (sizeof(T) == 2) {
+struct TileRegs {
+  u32x4_t k[Geo<T, D>::TPL];
+  u32x4_t v[Geo<T, D>::TPL];
+  uint32_t ok;  // bit j: token j of this lane is inside the partition with a valid block id
+};
+
+struct PoolView {
+  const char* k;
+  const char* v;
+  uint32_t row_bytes;   // H_kv * D * elem: one token's row over all KV heads
+  uint32_t head_bytes;  // this item's KV head offset within the row, plus the lane's piece
+};
+
+// Issues the K/V loads of one tile.  Block ids come from the wave's LDS copy
+// of the partition's block-table slice (a global load here would make the
+// wait for it drain the K/V loads already in flight).  Invalid tokens load
+// row 0 (always in range, and cached) and are zeroed when staged.
+template <typename T, int D, bool kWide, bool kAligned>
+__device__ __forceinline__ void load_tile(const PoolView& pv, const int* __restrict__ ids, int blk0, int tile0,
+                                          int end, int P, int p_shift, int N, TileRegs<T, D>& r) {
+  using Gm = Geo<T, D>;
+  using O = typename Off<kWide>::type;
+  const int lane = lane_id();
+  const int q = lane / Gm::CPR;
+  const int first = tile0 + q * Gm::TPL;  // this lane's first token
+  r.ok = 0;
+  if constexpr (kAligned) {
+    // the tile lies inside one block: one (broadcast) id lookup, rows are consecutive
+    int lb, off;
+    if (p_shift >= 0) {
+      lb = tile0 >> p_shift;
+      off = tile0 & ((1 << p_shift) - 1);
+    } else {
+      lb = tile0 / P;
+      off = tile0 - lb * P;
+    }
+    const int blk = ids[lb - blk0];
+    const bool bok = blk >= 0 && blk < N;
+    const O base = bok ? ((O)blk * (O)P + (O)(off + q * Gm::TPL)) * (O)pv.row_bytes : (O)0;
 #pragma unroll
-    for (int i = 0; i < Traits<T, D>::NV; ++i)
+    for (int j = 0; j < Gm::TPL; ++j) {
+      const bool ok = bok && first + j < end;
+      r.ok |= (ok ? 1u : 0u) << j;
+      const O e = (ok ? base + (O)j * (O)pv.row_bytes : (O)0) + (O)pv.head_bytes;
+      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.k + e));
+      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.v + e));
+    }
+  } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f[8 * i + 2 * j] = bf16_lo(v[i][j]);
-        f[8 * i + 2 * j + 1] = bf16_hi(v[i][j]);
+    for (int j = 0; j < Gm::TPL; ++j) {
+      const int pos = first + j;
+      int lb, off;
+      if (p_shift >= 0) {
+        lb = pos >> p_shift;
+        off = pos & ((1 << p_shift) - 1);
+      } else {
+        lb = pos / P;
+        off = pos - lb * P;
       }
-  } else {
-#pragma unroll
-    for (int i = 0; i < Traits<T, D>::NV; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) f[4 * i + j] = __uint_as_float(v[i][j]);
+      const bool in = pos < end;
+      const int blk = ids[in ? lb - blk0 : 0];
+      const bool ok = in && blk >= 0 && blk < N;
+      r.ok |= (ok ? 1u : 0u) << j;
+      const O e = (ok ? ((O)blk * (O)P + (O)off) * (O)pv.row_bytes : (O)0) + (O)pv.head_bytes;
+      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.k + e));
+      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.v + e));
+    }
   }
 }
 
+// Registers -> this wave's LDS region: K row-major; V transposed (bf16, d-major
+// so a P.V operand is one 8-byte read) or row-major (fp32).
 template <typename T, int D>
-__device__ __forceinline__ void load_slice(const T* base, bool valid, u32x4_t (&v)[Traits<T, D>::NV]) {
-  const u32x4_t* p = reinterpret_cast<const u32x4_t*>(base);
+__device__ __forceinline__ void stage_tile(char* lds, TileRegs<T, D>& r, bool full) {
+  using Gm = Geo<T, D>;
+  const int lane = lane_id();
+  const int c = lane % Gm::CPR, q = lane / Gm::CPR;
+  if (!full) {
 #pragma unroll
-  for (int i = 0; i < Traits<T, D>::NV; ++i) {
-    if (valid) v[i] = __builtin_nontemporal_load(p + i);
-    else v[i] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int j = 0; j < Gm::TPL; ++j)
+      if (!((r.ok >> j) & 1u)) {
+        r.k[j] = u32x4_t{0u, 0u, 0u, 0u};
+        r.v[j] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < Gm::TPL; ++j)
+    *reinterpret_cast<u32x4_t*>(lds + (q * Gm::TPL + j) * Gm::KST + 16 * c) = r.k[j];
+  char* vl = lds + Gm::KBYTES;
+  if constexpr (Gm::kBf16) {
+    // piece c holds head elements 8c..8c+7; this lane owns tokens q*TPL .. q*TPL+TPL-1
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int d = 8 * c + 2 * w;
+      if constexpr (Gm::TPL == 4) {
+        const u32x2_t lo = {__builtin_amdgcn_perm(r.v[1][w], r.v[0][w], 0x05040100u),
+                            __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], 0x05040100u)};
+        const u32x2_t hi = {__builtin_amdgcn_perm(r.v[1][w], r.v[0][w], 0x07060302u),
+                            __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], 0x07060302u)};
+        *reinterpret_cast<u32x2_t*>(vl + d * Gm::VTS + 8 * q) = lo;
+        *reinterpret_cast<u32x2_t*>(vl + (d + 1) * Gm::VTS + 8 * q) = hi;
+      } else {
+        static_assert(Gm::TPL == 2, "bf16 tiles hold 2 or 4 tokens per lane");
+        *reinterpret_cast<uint32_t*>(vl + d * Gm::VTS + 4 * q) = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(vl + (d + 1) * Gm::VTS + 4 * q) =
+            __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], 0x07060302u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < Gm::TPL; ++j)
+      *reinterpret_cast<u32x4_t*>(vl + (q * Gm::TPL + j) * Gm::KST + 16 * c) = r.v[j];
   }
 }
 
-// Physical row (blk * P + pos % P) of logical position pos, or -1 if the
-// position is past the partition end or its block id is out of range.
-__device__ __forceinline__ int64_t token_row(const int32_t* __restrict__ bt_row, int pos, int end,
-                                             int P, int p_shift, int N) {
-  if (pos >= end) return -1;
-  int j, off;
-  if (p_shift >= 0) {
-    j = pos >> p_shift;
-    off = pos & ((1 << p_shift) - 1);
-  } else {
-    j = pos / P;
-    off = pos - j * P;
-  }
-  const int blk = bt_row[j];
-  if (blk < 0 || blk >= N) return -1;
-  return (int64_t)blk * P + off;
+// Orders this wave's LDS stores before its later LDS loads (the wave reads
+// what other lanes of the same wave wrote).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ---------------------------------------------------------------------------
@@ -219,27 +295,45 @@ struct DecodeParams {
   int Hq, Hkv, G, n_hg, P, p_shift, N, M, cap, max_parts;
 };
 
-template <typename T, int D>
+// Softmax reference max is moved only when a score exceeds it by more than
+// this (log2 units), so probabilities stay below 2^8 and the rescale of the
+// accumulators is rare; the result does not depend on the reference.
+constexpr float kRescaleSlack = 8.0f;
+
+// One wave = one work item (request, partition, KV head, group of up to 4
+// query heads).  Per 16-token tile:
+//   S^T = K Q^T   (A = K rows from LDS, B = Q^T with the group's heads as
+//                  columns 0..3), so lane (n, g) gets the scores of head n for
+//                  tokens 4g .. 4g+3;
+//   online softmax per head (max over the lane's 4 tokens, then across the
+//                  four 16-lane rows);
+//   O^T += V^T P^T (A = V^T from LDS, B = the lane's own probabilities), so
+//                  lane (n, g) accumulates head n's outputs d = 16db + 4g + j.
+template <typename T, int D, bool kWide, bool kAligned>
 __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm) {
-  using Tr = Traits<T, D>;
-  constexpr int E = Tr::E;
-  constexpr int NV = Tr::NV;
+  using Gm = Geo<T, D>;
+  constexpr int NDB = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* lds = smem + (threadIdx.x >> 6) * Gm::LDS_PER_WAVE;
+  int* ids = reinterpret_cast<int*>(lds + Gm::KBYTES + Gm::VBYTES);
   const int lane = lane_id();
-  const int n = lane & 15;  // token column / A row
-  const int g = lane >> 4;  // quarter of the head this lane holds
-  const bool b3 = n & 8, b2 = n & 4, b1 = n & 2, b0 = n & 1;
+  const int n = lane & 15;  // head column (S^T, O^T) / token row (K operand)
+  const int g = lane >> 4;
   const uint32_t per_item = (uint32_t)(prm.Hkv * prm.n_hg);
   const uint32_t total = prm.hdr[1] * per_item;
   const T* __restrict__ q = static_cast<const T*>(prm.q);
-  const T* __restrict__ kc = static_cast<const T*>(prm.kc);
-  const T* __restrict__ vc = static_cast<const T*>(prm.vc);
-  const int64_t row_elems = (int64_t)prm.Hkv * D;
+  PoolView pv;
+  pv.k = static_cast<const char*>(prm.kc);
+  pv.v = static_cast<const char*>(prm.vc);
+  pv.row_bytes = (uint32_t)(prm.Hkv * Gm::ROWB);
 
+  uint32_t fv = 0;
+  if (lane == 0) fv = atomicAdd(prm.counter, 1u);
   for (;;) {
-    uint32_t f = 0;
-    if (lane == 0) f = atomicAdd(prm.counter, 1u);
-    f = __builtin_amdgcn_readfirstlane(f);
+    const uint32_t f = __builtin_amdgcn_readfirstlane(fv);
     if (f >= total) break;
+    // claim the next item now; its index is only read when this one is done
+    if (lane == 0) fv = atomicAdd(prm.counter, 1u);
     const int2 it = prm.items[f / per_item];
     const int rem = (int)(f % per_item);
     const int b = it.x, part = it.y;
@@ -250,142 +344,150 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     const int tok0 = part * kPartTokens;
     const int tok_end = min(L, tok0 + kPartTokens);
     const int ntiles = (tok_end - tok0 + kTile - 1) / kTile;
-    const int nh = min(4, prm.G - hg * 4);  // valid heads of this group
+    const int nh = min(4, prm.G - hg * 4);  // valid heads of this group (columns 0..nh-1)
     const int32_t* __restrict__ bt_row = prm.bt + (int64_t)b * prm.M;
+    const bool col_ok = n < nh;
+    const int h = hkv * prm.G + hg * 4 + (col_ok ? n : 0);
+    pv.head_bytes = (uint32_t)(hkv * Gm::ROWB + 16 * (lane % Gm::CPR));
 
-    // Query operand: A row n carries local head n & 3 (replicated 4 times).
-    u32x4_t qv[NV];
+    // Q^T operand: column n = query head h; k = head dimension
+    u32x4_t qv[Gm::kBf16 ? Gm::NQ : Gm::NQ / 4];
     {
-      const int r = n & 3;
-      const bool qok = r < nh;
-      const int h = hkv * prm.G + hg * 4 + (qok ? r : 0);
-      load_slice<T, D>(q + ((int64_t)b * prm.Hq + h) * D + g * E, qok, qv);
-    }
-    const int64_t head_off = (int64_t)hkv * D + g * E;
-
-    float m[4], l[4], o[4][E];
+      const T* qrow = q + ((int64_t)b * prm.Hq + h) * D;
+      if constexpr (Gm::kBf16) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      m[r] = -INFINITY;
-      l[r] = 0.f;
+        for (int i = 0; i < Gm::NQ; ++i)
+          qv[i] = col_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * i + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
+      } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[r][e] = 0.f;
+        for (int i = 0; i < Gm::NQ / 4; ++i)
+          qv[i] = col_ok ? *reinterpret_cast<const u32x4_t*>(qrow + g * (D / 4) + 4 * i) : u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
 
-    // software pipeline: K/V of tile t+1 are in flight while tile t computes
-    u32x4_t kcur[NV], vcur[NV];
-    int64_t row = token_row(bt_row, tok0 + n, tok_end, prm.P, prm.p_shift, prm.N);
-    load_slice<T, D>(kc + row * row_elems + head_off, row >= 0, kcur);
-    load_slice<T, D>(vc + row * row_elems + head_off, row >= 0, vcur);
-    bool cur_ok = row >= 0;
+    // this partition's block ids -> the wave's LDS
+    int blk0, blk_last;
+    if (prm.p_shift >= 0) {
+      blk0 = tok0 >> prm.p_shift;
+      blk_last = (tok_end - 1) >> prm.p_shift;
+    } else {
+      blk0 = tok0 / prm.P;
+      blk_last = (tok_end - 1) / prm.P;
+    }
+    wave_lds_sync();  // the previous item is done with the LDS
+    for (int i = lane; i <= blk_last - blk0; i += 64) ids[i] = bt_row[blk0 + i];
+    wave_lds_sync();
 
+    float m = -INFINITY, l = 0.f;
+    f32x4_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // software pipeline: the next tile's K/V loads are in flight while one computes
+    TileRegs<T, D> regs;
+    load_tile<T, D, kWide, kAligned>(pv, ids, blk0, tok0, tok_end, prm.P, prm.p_shift, prm.N, regs);
     for (int t = 0; t < ntiles; ++t) {
-      u32x4_t knxt[NV], vnxt[NV];
-      const int64_t nrow = token_row(bt_row, tok0 + (t + 1) * kTile + n, tok_end, prm.P, prm.p_shift, prm.N);
-      load_slice<T, D>(kc + nrow * row_elems + head_off, nrow >= 0, knxt);
-      load_slice<T, D>(vc + nrow * row_elems + head_off, nrow >= 0, vnxt);
+      const int tile0 = tok0 + t * kTile;
+      // every token of the tile valid: no zeroing needed (the usual case)
+      bool full;
+      if constexpr (kAligned)
+        full = tile0 + kTile <= tok_end && __builtin_amdgcn_readfirstlane((int)regs.ok) == (1 << Gm::TPL) - 1;
+      else
+        full = __builtin_amdgcn_readfirstlane((int)(__ballot(regs.ok != (1u << Gm::TPL) - 1u) == 0));
+      wave_lds_sync();  // previous tile's LDS reads are done
+      stage_tile<T, D>(lds, regs, full);
+      wave_lds_sync();
+      if (t + 1 < ntiles)
+        load_tile<T, D, kWide, kAligned>(pv, ids, blk0, tile0 + kTile, tok_end, prm.P, prm.p_shift, prm.N, regs);
 
-      f32x4_t acc;
-      if constexpr (sizeof(T) == 2) acc = qk_mfma<D>(qv, kcur);
-      else acc = qk_mfma_f32<D>(qv, kcur);
-
-      float s[4], mnew[4];
-      bool grow = false;
+      // ---- S^T = K Q^T ----
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (Gm::kBf16) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[r] = cur_ok ? acc[r] * prm.scale_log2 : -INFINITY;
-        mnew[r] = fmaxf(m[r], row16_max(s[r]));
-        grow |= mnew[r] > m[r];
-      }
-      if (grow) {
+        for (int i = 0; i < Gm::NQ; ++i) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                      __builtin_bit_cast(bf16x8_t, qv[i]), s, 0, 0, 0);
+        }
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float alpha = fast_exp2(m[r] - mnew[r]);
-          m[r] = mnew[r];
-          l[r] *= alpha;
+        for (int i = 0; i < Gm::NQ / 4; ++i) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 4 * (g * (D / 4) + 4 * i));
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[r][e] *= alpha;
+          for (int j = 0; j < 4; ++j)
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(qv[i][j]), s, 0, 0, 0);
         }
       }
-      float vf[E];
-      widen_slice<T, D>(vcur, vf);
+      // ---- online softmax for head n over tokens tile0 + 4g + j ----
+      float sc[4];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (r < nh) {
-          const float p = fast_exp2(s[r] - m[r]);
-          l[r] += p;
+      for (int j = 0; j < 4; ++j) {
+        sc[j] = (tile0 + 4 * g + j < tok_end) ? s[j] * prm.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[j]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (mx > m + kRescaleSlack) {  // also true for the first tile (m = -inf)
+        if (m != -INFINITY) {
+          const float alpha = fast_exp2(m - mx);
+          l *= alpha;
 #pragma unroll
-          for (int e = 0; e < E; ++e) o[r][e] = fmaf(p, vf[e], o[r][e]);
+          for (int db = 0; db < NDB; ++db) o[db] *= alpha;
         }
+        m = mx;
       }
+      float p[4];
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        kcur[i] = knxt[i];
-        vcur[i] = vnxt[i];
+      for (int j = 0; j < 4; ++j) {
+        p[j] = fast_exp2(sc[j] - m);
+        l += p[j];
       }
-      cur_ok = nrow >= 0;
+      // ---- O^T += V^T P^T ----
+      const char* vl = lds + Gm::KBYTES;
+      if constexpr (Gm::kBf16) {
+        const u32x2_t pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vl + (16 * db + n) * Gm::VTS + 8 * g);
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                            __builtin_bit_cast(s16x4_t, pb), o[db], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float a = *reinterpret_cast<const float*>(vl + (4 * g + j) * Gm::KST + 4 * (16 * db + n));
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[j], o[db], 0, 0, 0);
+          }
+      }
     }
 
-    // ---- merge the 16 token lanes of each row: DPP reduce-scatter ----------
-    float a2[2][E];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float keep = b3 ? o[i + 2][e] : o[i][e];
-        const float send = b3 ? o[i][e] : o[i + 2][e];
-        a2[i][e] = keep + dpp<kDppRowRor8>(send);
-      }
-    float c1[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float keep = b2 ? a2[1][e] : a2[0][e];
-      const float send = b2 ? a2[0][e] : a2[1][e];
-      c1[e] = keep + dpp<kDppRowHalfMirror>(send);
-    }
-    float c2[E / 2];
-#pragma unroll
-    for (int e = 0; e < E / 2; ++e) {
-      const float keep = b1 ? c1[e + E / 2] : c1[e];
-      const float send = b1 ? c1[e] : c1[e + E / 2];
-      c2[e] = keep + dpp<kDppQuadXor2>(send);
-    }
-    float res[E / 4];
-#pragma unroll
-    for (int e = 0; e < E / 4; ++e) {
-      const float keep = b0 ? c2[e + E / 4] : c2[e];
-      const float send = b0 ? c2[e] : c2[e + E / 4];
-      res[e] = keep + dpp<kDppQuadXor1>(send);
-    }
-    float lsum[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lsum[r] = row16_sum(l[r]);
-
-    const int hl = (b3 ? 2 : 0) + (b2 ? 1 : 0);
-    const float my_l = hl == 0 ? lsum[0] : hl == 1 ? lsum[1] : hl == 2 ? lsum[2] : lsum[3];
-    const float my_m = hl == 0 ? m[0] : hl == 1 ? m[1] : hl == 2 ? m[2] : m[3];
-    if (hl < nh) {
-      const int h = hkv * prm.G + hg * 4 + hl;
-      const int d0 = g * E + (b1 ? E / 2 : 0) + (b0 ? E / 4 : 0);
+    // ---- finish: total of l over the four 16-lane rows; store head n ----
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (col_ok) {
       if (nparts == 1) {
-        const float inv = 1.0f / my_l;
-        T* dst = static_cast<T*>(prm.out) + ((int64_t)b * prm.Hq + h) * D + d0;
-        if constexpr (sizeof(T) == 2) {
+        const float inv = 1.0f / l;
+        T* dst = static_cast<T*>(prm.out) + ((int64_t)b * prm.Hq + h) * D + 4 * g;
 #pragma unroll
-          for (int e = 0; e < E / 4; e += 2)
-            *reinterpret_cast<uint32_t*>(dst + e) = pack_bf16(res[e] * inv, res[e + 1] * inv);
-        } else {
-#pragma unroll
-          for (int e = 0; e < E / 4; ++e) dst[e] = res[e] * inv;
+        for (int db = 0; db < NDB; ++db) {
+          if constexpr (Gm::kBf16) {
+            *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
+                u32x2_t{pack_bf16(o[db][0] * inv, o[db][1] * inv), pack_bf16(o[db][2] * inv, o[db][3] * inv)};
+          } else {
+            *reinterpret_cast<f32x4_t*>(dst + 16 * db) = o[db] * inv;
+          }
         }
       } else {
         const int64_t slot = ((int64_t)b * prm.Hq + h) * prm.max_parts + part;
-        float* dst = prm.o + slot * D + d0;
+        float* dst = prm.o + slot * D + 4 * g;
 #pragma unroll
-        for (int e = 0; e < E / 4; ++e) dst[e] = res[e];
-        if (g == 0 && !b1 && !b0) {
-          prm.ml[slot * 2 + 0] = my_m;
-          prm.ml[slot * 2 + 1] = my_l;
+        for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db) = o[db];
+        if (g == 0) {
+          prm.ml[slot * 2 + 0] = m;
+          prm.ml[slot * 2 + 1] = l;
         }
       }
     }
@@ -435,17 +537,20 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams prm) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kWide, bool kAligned>
 hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipStream_t stream,
                         hipEvent_t ev0, hipEvent_t ev1) {
-  const int64_t want = (max_items + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t cap = (int64_t)device_cu_count() * 8;
+  // waves are independent workers; a block holds as many as fit in 64 KiB of LDS (at most 4)
+  constexpr int wpb = Geo<T, D>::LDS_PER_WAVE * kWavesPerBlock <= 65536 ? kWavesPerBlock : 2;
+  const int64_t want = (max_items + wpb - 1) / wpb;
+  const int64_t cap = (int64_t)device_cu_count() * 16 / wpb;  // up to 16 waves per CU
   const unsigned blocks = (unsigned)(want < cap ? (want > 0 ? want : 1) : cap);
   if (ev0) {
     const hipError_t e = hipEventRecord(ev0, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_partition_kernel<T, D>), dim3(blocks), dim3(64 * kWavesPerBlock), 0,
+  constexpr unsigned lds_bytes = Geo<T, D>::LDS_PER_WAVE * wpb;
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, kWide, kAligned>), dim3(blocks), dim3(64 * wpb), lds_bytes,
                      stream, prm);
   if (ev1) {
     const hipError_t e = hipEventRecord(ev1, stream);
@@ -453,6 +558,19 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
   }
   hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(prm.Hq, B), dim3(64), 0, stream, prm);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_sized(const DecodeParams& prm, int B, int64_t max_items, int64_t pool_bytes,
+                        hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  // tiles of 16 tokens never straddle a block when P is a multiple of 16
+  const bool aligned = prm.P % kTile == 0;
+  if (pool_bytes < ((int64_t)1 << 32)) {
+    if (aligned) return launch_typed<T, D, false, true>(prm, B, max_items, stream, ev0, ev1);
+    return launch_typed<T, D, false, false>(prm, B, max_items, stream, ev0, ev1);
+  }
+  if (aligned) return launch_typed<T, D, true, true>(prm, B, max_items, stream, ev0, ev1);
+  return launch_typed<T, D, true, false>(prm, B, max_items, stream, ev0, ev1);
 }
 
 }  // namespace
@@ -493,12 +611,15 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
                      prm.cap, reinterpret_cast<uint32_t*>(ws + Lw.hdr),
                      reinterpret_cast<int2*>(ws + Lw.items));
   const int64_t max_items = (int64_t)a.num_seqs * Lw.max_parts * prm.Hkv * prm.n_hg;
+  const int64_t pool_bytes =
+      a.num_blocks * a.block_size * a.num_kv_heads * a.head_dim * (a.dtype == kBF16 ? 2 : 4);
   if (a.dtype == kBF16) {
-    if (a.head_dim == 128) return launch_typed<bf16_bits, 128>(prm, a.num_seqs, max_items, stream, ev0, ev1);
-    return launch_typed<bf16_bits, 64>(prm, a.num_seqs, max_items, stream, ev0, ev1);
+    if (a.head_dim == 128)
+      return launch_sized<bf16_bits, 128>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
+    return launch_sized<bf16_bits, 64>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
   }
-  if (a.head_dim == 128) return launch_typed<float, 128>(prm, a.num_seqs, max_items, stream, ev0, ev1);
-  return launch_typed<float, 64>(prm, a.num_seqs, max_items, stream, ev0, ev1);
+  if (a.head_dim == 128) return launch_sized<float, 128>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
+  return launch_sized<float, 64>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
 }
 
 }  // namespace pa
