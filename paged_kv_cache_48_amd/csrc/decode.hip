@@ -11,8 +11,10 @@
 //     (a count that depends on L_b only).  A (request, partition, KV head, group
 //     of up to 4 query heads) is one work item; a single wave64 computes it.
 //   * Work queue.  A tiny plan kernel lists the (request, partition) items,
-//     full partitions first and short tail partitions last, and zeroes a queue
-//     counter; a persistent grid of waves pulls items with one atomic each.
+//     full partitions first and short tail partitions last, and zeroes the
+//     queue counters; a persistent grid of exactly the resident waves takes
+//     one item each to start, then pulls items with one atomic each from
+//     per-XCD queues, stealing from the other queues at the end.
 //   * Coalesced gathers.  Per 16-token tile each quarter-wave reads whole
 //     contiguous row slices of one KV head (16-byte loads); the tile goes
 //     through a wave-private LDS region, K row-major and V transposed, which
@@ -49,6 +51,13 @@ constexpr int kWavesPerBlock = 4;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Work-queue header in the workspace: kQueues counters, each on its own
+// 128-byte line, and the item count in the last word.
+constexpr int kQueues = 8;  // one per XCD of the MI355X
+constexpr int kCounterStride = 32;  // uint32 words between counters
+constexpr int kHeaderBytes = 1024;
+constexpr int kItemCountWord = kHeaderBytes / 4 - 1;
+
 struct DecodeLayout {
   int64_t max_parts;
   size_t hdr, items, ml, o, total;
@@ -59,7 +68,7 @@ DecodeLayout decode_layout(int B, int Hq, int D, int P, int M) {
   L.max_parts = ((int64_t)M * P + kPartTokens - 1) / kPartTokens;
   size_t off = 0;
   L.hdr = off;
-  off += 256;
+  off += kHeaderBytes;
   L.items = off;
   off = align256(off + sizeof(int2) * (size_t)B * L.max_parts);
   L.ml = off;
@@ -118,10 +127,8 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __rest
     full_off += ftot;
     tail_off += ttot;
   }
-  if (tid == 0) {
-    hdr[0] = 0u;
-    hdr[1] = (uint32_t)(nfull + tail_off);
-  }
+  if (tid < kQueues) hdr[tid * kCounterStride] = 0u;
+  if (tid == 0) hdr[kItemCountWord] = (uint32_t)(nfull + tail_off);
 }
 
 // ---------------------------------------------------------------------------
@@ -320,20 +327,42 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
   const int n = lane & 15;  // head column (S^T, O^T) / token row (K operand)
   const int g = lane >> 4;
   const uint32_t per_item = (uint32_t)(prm.Hkv * prm.n_hg);
-  const uint32_t total = prm.hdr[1] * per_item;
+  const uint32_t total = prm.hdr[kItemCountWord] * per_item;
   const T* __restrict__ q = static_cast<const T*>(prm.q);
   PoolView pv;
   pv.k = static_cast<const char*>(prm.kc);
   pv.v = static_cast<const char*>(prm.vc);
   pv.row_bytes = (uint32_t)(prm.Hkv * Gm::ROWB);
 
-  uint32_t fv = 0;
-  if (lane == 0) fv = atomicAdd(prm.counter, 1u);
+  // Item f of the flat list (items x KV heads x head groups).  The first item
+  // of each wave is its global wave index.  The rest are split into kQueues
+  // interleaved queues, f = nwaves + kQueues * c + x for the c-th claim of
+  // queue x; a wave claims from the queue of its XCD (blocks are dealt to the
+  // XCDs round robin) and moves on to the next queue when that one is empty.
+  // Separate counters keep the claims from serialising on one address.
+  const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
+  const uint32_t home = blockIdx.x % kQueues;
+  uint32_t queue = 0;  // queues found empty so far
+  uint32_t f = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   for (;;) {
-    const uint32_t f = __builtin_amdgcn_readfirstlane(fv);
-    if (f >= total) break;
-    // claim the next item now; its index is only read when this one is done
-    if (lane == 0) fv = atomicAdd(prm.counter, 1u);
+    if (f >= total) {
+      if (f < nwaves) break;  // fewer items than waves: no queued items either
+      bool got = false;
+      while (queue < kQueues) {
+        const uint32_t x = (home + queue) % kQueues;
+        uint32_t c = 0;
+        if (lane == 0) c = atomicAdd(prm.counter + x * kCounterStride, 1u);
+        c = __builtin_amdgcn_readfirstlane(c);
+        const uint32_t fx = nwaves + kQueues * c + x;
+        if (fx < total) {
+          f = fx;
+          got = true;
+          break;
+        }
+        ++queue;
+      }
+      if (!got) break;
+    }
     const int2 it = prm.items[f / per_item];
     const int rem = (int)(f % per_item);
     const int b = it.x, part = it.y;
@@ -491,6 +520,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
         }
       }
     }
+    f = 0xffffffffu;  // this item is done: claim the next one
   }
 }
 
@@ -542,14 +572,24 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
                         hipEvent_t ev0, hipEvent_t ev1) {
   // waves are independent workers; a block holds as many as fit in 64 KiB of LDS (at most 4)
   constexpr int wpb = Geo<T, D>::LDS_PER_WAVE * kWavesPerBlock <= 65536 ? kWavesPerBlock : 2;
+  constexpr unsigned lds_bytes = Geo<T, D>::LDS_PER_WAVE * wpb;
+  // exactly the blocks that can be resident at once: every wave starts on its
+  // first item immediately, and none waits for a slot while holding one
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partition_kernel<T, D, kWide, kAligned>,
+                                                     64 * wpb, lds_bytes) != hipSuccess || nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
   const int64_t want = (max_items + wpb - 1) / wpb;
-  const int64_t cap = (int64_t)device_cu_count() * 16 / wpb;  // up to 16 waves per CU
+  const int64_t cap = (int64_t)device_cu_count() * per_cu;
   const unsigned blocks = (unsigned)(want < cap ? (want > 0 ? want : 1) : cap);
   if (ev0) {
     const hipError_t e = hipEventRecord(ev0, stream);
     if (e != hipSuccess) return e;
   }
-  constexpr unsigned lds_bytes = Geo<T, D>::LDS_PER_WAVE * wpb;
   hipLaunchKernelGGL((decode_partition_kernel<T, D, kWide, kAligned>), dim3(blocks), dim3(64 * wpb), lds_bytes,
                      stream, prm);
   if (ev1) {
