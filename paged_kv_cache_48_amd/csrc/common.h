@@ -12,6 +12,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 // bf16 values are stored as their 16-bit patterns.
 typedef uint16_t bf16_bits;
@@ -71,6 +72,26 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Max over the four 16-lane rows for each lane position (lanes l, l^16, l^32,
+// l^48), with gfx950's row-swap permutes: permlane32_swap(x, x) yields rows
+// (0,1,0,1) and (2,3,2,3); permlane16_swap(y, y) yields (0,0,2,2) and
+// (1,1,3,3).  Every lane of a column gets the same result.
+__device__ __forceinline__ float max_over_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Wave-uniform copy of a value (held in a scalar register).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // exp2 on the hardware transcendental unit (v_exp_f32); exp(x) is evaluated
 // as exp2(x * log2(e)) with the constant folded into the score scale.

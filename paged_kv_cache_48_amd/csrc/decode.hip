@@ -44,8 +44,6 @@ namespace pa {
 namespace {
 
 constexpr int kTile = 16;                        // tokens per MFMA tile
-// logical blocks one partition can touch: kPartTokens / P + 1 for P >= 1
-constexpr int kMaxPartBlocks = kPartTokens + 64;
 
 constexpr int kWavesPerBlock = 4;
 
@@ -57,6 +55,7 @@ constexpr int kQueues = 8;  // one per XCD of the MI355X
 constexpr int kCounterStride = 32;  // uint32 words between counters
 constexpr int kHeaderBytes = 1024;
 constexpr int kItemCountWord = kHeaderBytes / 4 - 1;
+constexpr int kFullCountWord = kHeaderBytes / 4 - 2;  // items that are full partitions
 
 struct DecodeLayout {
   int64_t max_parts;
@@ -70,7 +69,7 @@ DecodeLayout decode_layout(int B, int Hq, int D, int P, int M) {
   L.hdr = off;
   off += kHeaderBytes;
   L.items = off;
-  off = align256(off + sizeof(int2) * (size_t)B * L.max_parts);
+  off = align256(off + sizeof(i32x4_t) * (size_t)B * L.max_parts);
   L.ml = off;
   off = align256(off + sizeof(float) * 2 * (size_t)B * Hq * L.max_parts);
   L.o = off;
@@ -82,53 +81,83 @@ DecodeLayout decode_layout(int B, int Hq, int D, int P, int M) {
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
 // ---------------------------------------------------------------------------
-// Plan: list (request, partition) items, full partitions first.
+// Plan: one wave lists the (request, partition) items in decreasing size --
+// every full partition first, then the tail partitions sorted by their tile
+// count (16 .. 1) -- so the last items handed out are the smallest.  Each
+// item carries (request, partition, clamped length, partition count).  It
+// also zeroes the queue counters.  Lane i owns requests i, i+64, ...; item
+// offsets come from wave-wide exclusive scans of the per-lane counts.
 // ---------------------------------------------------------------------------
-__device__ int block_excl_scan(int v, int* buf, int* total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+constexpr int kTileBuckets = kPartTokens / 16;  // tail partitions hold 1 .. 16 tiles
+
+template <int NV>
+__device__ __forceinline__ void wave_excl_scan(int (&v)[NV], int (&total)[NV]) {
+  const int lane = threadIdx.x & 63;
+  int x[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) x[k] = v[k];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int y = __shfl_up(x[k], d);
+      if (lane >= d) x[k] += y;
+    }
   }
-  const int incl = buf[tid];
-  *total = buf[1023];
-  __syncthreads();
-  return incl - v;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    total[k] = __shfl(x[k], 63);
+    v[k] = x[k] - v[k];
+  }
 }
 
-__global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __restrict__ lens,
-                                                           int B, int cap, uint32_t* hdr,
-                                                           int2* __restrict__ items) {
-  __shared__ int buf[1024];
-  const int tid = threadIdx.x;
-  // total number of full partitions = offset of the first tail partition
-  int nfull = 0, tot = 0;
-  for (int base = 0; base < B; base += 1024) {
-    const int b = base + tid;
-    const int L = b < B ? clamp_len(lens[b], cap) : 0;
-    block_excl_scan(L / kPartTokens, buf, &tot);
-    nfull += tot;
+__global__ __launch_bounds__(64) void decode_plan_kernel(const int32_t* __restrict__ lens, int B, int cap,
+                                                         uint32_t* hdr, i32x4_t* __restrict__ items) {
+  const int lane = threadIdx.x;
+  // counts: [0] full partitions, [1 + k] tail partitions of k+1 tiles
+  int cnt[1 + kTileBuckets];
+#pragma unroll
+  for (int k = 0; k <= kTileBuckets; ++k) cnt[k] = 0;
+  for (int b = lane; b < B; b += 64) {
+    const int L = clamp_len(lens[b], cap);
+    cnt[0] += L / kPartTokens;
+    const int rest = L % kPartTokens;
+#pragma unroll
+    for (int k = 0; k < kTileBuckets; ++k) cnt[1 + k] += (rest > 0 && (rest + 15) / 16 == k + 1) ? 1 : 0;
   }
-  int full_off = 0, tail_off = 0;
-  for (int base = 0; base < B; base += 1024) {
-    const int b = base + tid;
-    const int L = b < B ? clamp_len(lens[b], cap) : 0;
+  int tot[1 + kTileBuckets];
+  wave_excl_scan<1 + kTileBuckets>(cnt, tot);
+  // bucket base offsets: full items, then tails of 16, 15, ..., 1 tiles
+  int base[1 + kTileBuckets];
+  base[0] = 0;
+  int run = tot[0];
+#pragma unroll
+  for (int k = kTileBuckets - 1; k >= 0; --k) {
+    base[1 + k] = run;
+    run += tot[1 + k];
+  }
+#pragma unroll
+  for (int k = 0; k <= kTileBuckets; ++k) cnt[k] += base[k];  // this lane's next write position
+  for (int b = lane; b < B; b += 64) {
+    const int L = clamp_len(lens[b], cap);
+    const int np = (L + kPartTokens - 1) / kPartTokens;
     const int f = L / kPartTokens;
-    const int t = (L % kPartTokens) != 0;
-    int ftot, ttot;
-    const int fo = block_excl_scan(f, buf, &ftot);
-    const int to = block_excl_scan(t, buf, &ttot);
-    for (int j = 0; j < f; ++j) items[full_off + fo + j] = make_int2(b, j);
-    if (t) items[nfull + tail_off + to] = make_int2(b, f);
-    full_off += ftot;
-    tail_off += ttot;
+    for (int j = 0; j < f; ++j) items[cnt[0]++] = i32x4_t{b, j, L, np};
+    const int rest = L % kPartTokens;
+    if (rest > 0) {
+      const int k = (rest + 15) / 16 - 1;
+      int at = 0;
+#pragma unroll
+      for (int kk = 0; kk < kTileBuckets; ++kk)
+        if (kk == k) at = cnt[1 + kk]++;
+      items[at] = i32x4_t{b, f, L, np};
+    }
   }
-  if (tid < kQueues) hdr[tid * kCounterStride] = 0u;
-  if (tid == 0) hdr[kItemCountWord] = (uint32_t)(nfull + tail_off);
+  if (lane < kQueues) hdr[lane * kCounterStride] = 0u;
+  if (lane == 0) {
+    hdr[kItemCountWord] = (uint32_t)run;
+    hdr[kFullCountWord] = (uint32_t)tot[0];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -147,9 +176,9 @@ struct Geo {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int KBYTES = 16 * KST;
   static constexpr int VBYTES = kBf16 ? D * VTS : 16 * KST;
-  static constexpr int IDS_BYTES = 4 * kMaxPartBlocks;  // block ids of one partition
-  static constexpr int LDS_PER_WAVE = KBYTES + VBYTES + IDS_BYTES;
+  static constexpr int LDS_PER_WAVE = KBYTES + VBYTES;
   static constexpr int NQ = kBf16 ? D / 32 : D / 4;  // QK MFMA steps over the head dimension
+  static constexpr int NQV = kBf16 ? NQ : NQ / 4;    // 16-byte Q pieces per lane
 };
 
 // Byte offsets into the pool: 32-bit when the pool is under 4 GiB (one VGPR
@@ -170,40 +199,127 @@ struct PoolView {
   const char* k;
   const char* v;
   uint32_t row_bytes;   // H_kv * D * elem: one token's row over all KV heads
-  uint32_t head_bytes;  // this item's KV head offset within the row, plus the lane's piece
 };
 
-// Issues the K/V loads of one tile.  Block ids come from the wave's LDS copy
-// of the partition's block-table slice (a global load here would make the
-// wait for it drain the K/V loads already in flight).  Invalid tokens load
-// row 0 (always in range, and cached) and are zeroed when staged.
-template <typename T, int D, bool kWide, bool kAligned>
-__device__ __forceinline__ void load_tile(const PoolView& pv, const int* __restrict__ ids, int blk0, int tile0,
-                                          int end, int P, int p_shift, int N, TileRegs<T, D>& r) {
+struct DecodeParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* bt;
+  const int32_t* lens;
+  void* out;
+  const uint32_t* hdr;
+  uint32_t* counter;
+  const i32x4_t* items;
+  float* ml;
+  float* o;
+  float scale_log2;
+  int Hq, Hkv, G, n_hg, P, p_shift, N, M, cap, max_parts;
+};
+
+// One work item, wave-uniform (scalar registers).
+struct Item {
+  int b, part, L, nparts;  // request, partition, visible tokens, partitions of the request
+  int hkv, hg, nh;         // KV head, group of query heads, valid heads in the group
+  int tok0, tok_end, ntiles, blk0, nblk;
+};
+
+__device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, uint32_t f, uint32_t per_item) {
+  Item it;
+  it.b = uniform(d[0]);
+  it.part = uniform(d[1]);
+  it.L = uniform(d[2]);
+  it.nparts = uniform(d[3]);
+  const int rem = (int)(f % per_item);
+  it.hkv = rem / prm.n_hg;
+  it.hg = rem - it.hkv * prm.n_hg;
+  it.nh = min(4, prm.G - it.hg * 4);
+  it.tok0 = it.part * kPartTokens;
+  it.tok_end = min(it.L, it.tok0 + kPartTokens);
+  it.ntiles = (it.tok_end - it.tok0 + kTile - 1) / kTile;
+  int last;
+  if (prm.p_shift >= 0) {
+    it.blk0 = it.tok0 >> prm.p_shift;
+    last = (it.tok_end - 1) >> prm.p_shift;
+  } else {
+    it.blk0 = it.tok0 / prm.P;
+    last = (it.tok_end - 1) / prm.P;
+  }
+  it.nblk = last - it.blk0 + 1;
+  return it;
+}
+
+// The item's block ids, lane i of register r holding entry blk0 + 64r + i.
+// The index is clamped so every lane loads (no divergent load to wait on).
+template <int NR>
+__device__ __forceinline__ void load_ids(const DecodeParams& prm, const Item& it, int (&ids)[NR]) {
+  const int lane = lane_id();
+  const int32_t* row = prm.bt + (int64_t)it.b * prm.M + it.blk0;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) ids[r] = row[min(64 * r + lane, it.nblk - 1)];
+}
+
+// Q^T operand: column n = query head of the group (heads past the group's
+// last read head 0's row; their columns are never stored).
+template <typename T, int D>
+__device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, u32x4_t (&qv)[Geo<T, D>::NQV]) {
+  using Gm = Geo<T, D>;
+  const int lane = lane_id();
+  const int n = lane & 15, g = lane >> 4;
+  const int h = it.hkv * prm.G + it.hg * 4 + (n < it.nh ? n : 0);
+  const T* qrow = static_cast<const T*>(prm.q) + ((int64_t)it.b * prm.Hq + h) * D;
+#pragma unroll
+  for (int i = 0; i < Gm::NQV; ++i) {
+    if constexpr (Gm::kBf16) qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * i + 8 * g);
+    else qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + g * (D / 4) + 4 * i);
+  }
+}
+
+// Block id of logical block `idx` (relative to the item's first block) for
+// a per-lane index: lane crossbar read from the id registers.
+template <int NR>
+__device__ __forceinline__ int lane_id_lookup(const int (&ids)[NR], int idx) {
+  int blk = __builtin_amdgcn_ds_bpermute((idx & 63) << 2, ids[0]);
+#pragma unroll
+  for (int r = 1; r < NR; ++r) {
+    const int v = __builtin_amdgcn_ds_bpermute((idx & 63) << 2, ids[r]);
+    if ((idx >> 6) == r) blk = v;
+  }
+  return blk;
+}
+
+// Issues the K/V loads of one tile.  Block ids come from registers, so no
+// global load is waited on here (a wait on one would drain the K/V loads
+// already in flight, since loads complete in order).  Invalid tokens load the
+// head's slice of row 0 (always in range, and cached) and are zeroed when
+// staged.  kAligned: the tile lies inside one block (P a multiple of 16).
+template <typename T, int D, bool kWide, bool kAligned, int NR>
+__device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams& prm, const Item& it,
+                                          const int (&ids)[NR], int tile0, TileRegs<T, D>& r) {
   using Gm = Geo<T, D>;
   using O = typename Off<kWide>::type;
   const int lane = lane_id();
   const int q = lane / Gm::CPR;
   const int first = tile0 + q * Gm::TPL;  // this lane's first token
+  const O lane_off = (O)(it.hkv * Gm::ROWB + 16 * (lane % Gm::CPR));
   r.ok = 0;
   if constexpr (kAligned) {
-    // the tile lies inside one block: one (broadcast) id lookup, rows are consecutive
     int lb, off;
-    if (p_shift >= 0) {
-      lb = tile0 >> p_shift;
-      off = tile0 & ((1 << p_shift) - 1);
+    if (prm.p_shift >= 0) {
+      lb = tile0 >> prm.p_shift;
+      off = tile0 & ((1 << prm.p_shift) - 1);
     } else {
-      lb = tile0 / P;
-      off = tile0 - lb * P;
+      lb = tile0 / prm.P;
+      off = tile0 - lb * prm.P;
     }
-    const int blk = ids[lb - blk0];
-    const bool bok = blk >= 0 && blk < N;
-    const O base = bok ? ((O)blk * (O)P + (O)(off + q * Gm::TPL)) * (O)pv.row_bytes : (O)0;
+    const int blk = __builtin_amdgcn_readlane(ids[0], lb - it.blk0);
+    const bool bok = blk >= 0 && blk < prm.N;
+    const O base = bok ? ((O)blk * (O)prm.P + (O)(off + q * Gm::TPL)) * (O)pv.row_bytes : (O)0;
 #pragma unroll
     for (int j = 0; j < Gm::TPL; ++j) {
-      const bool ok = bok && first + j < end;
+      const bool ok = bok && first + j < it.tok_end;
       r.ok |= (ok ? 1u : 0u) << j;
-      const O e = (ok ? base + (O)j * (O)pv.row_bytes : (O)0) + (O)pv.head_bytes;
+      const O e = (ok ? base + (O)j * (O)pv.row_bytes : (O)0) + lane_off;
       r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.k + e));
       r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.v + e));
     }
@@ -212,18 +328,18 @@ __device__ __forceinline__ void load_tile(const PoolView& pv, const int* __restr
     for (int j = 0; j < Gm::TPL; ++j) {
       const int pos = first + j;
       int lb, off;
-      if (p_shift >= 0) {
-        lb = pos >> p_shift;
-        off = pos & ((1 << p_shift) - 1);
+      if (prm.p_shift >= 0) {
+        lb = pos >> prm.p_shift;
+        off = pos & ((1 << prm.p_shift) - 1);
       } else {
-        lb = pos / P;
-        off = pos - lb * P;
+        lb = pos / prm.P;
+        off = pos - lb * prm.P;
       }
-      const bool in = pos < end;
-      const int blk = ids[in ? lb - blk0 : 0];
-      const bool ok = in && blk >= 0 && blk < N;
+      const bool in = pos < it.tok_end;
+      const int blk = lane_id_lookup<NR>(ids, in ? lb - it.blk0 : 0);
+      const bool ok = in && blk >= 0 && blk < prm.N;
       r.ok |= (ok ? 1u : 0u) << j;
-      const O e = (ok ? ((O)blk * (O)P + (O)off) * (O)pv.row_bytes : (O)0) + (O)pv.head_bytes;
+      const O e = (ok ? ((O)blk * (O)prm.P + (O)off) * (O)pv.row_bytes : (O)0) + lane_off;
       r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.k + e));
       r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.v + e));
     }
@@ -283,32 +399,43 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// ---------------------------------------------------------------------------
-// Partition kernel.
-// ---------------------------------------------------------------------------
-struct DecodeParams {
-  const void* q;
-  const void* kc;
-  const void* vc;
-  const int32_t* bt;
-  const int32_t* lens;
-  void* out;
-  const uint32_t* hdr;
-  uint32_t* counter;
-  const int2* items;
-  float* ml;
-  float* o;
-  float scale_log2;
-  int Hq, Hkv, G, n_hg, P, p_shift, N, M, cap, max_parts;
-};
-
 // Softmax reference max is moved only when a score exceeds it by more than
 // this (log2 units), so probabilities stay below 2^8 and the rescale of the
 // accumulators is rare; the result does not depend on the reference.
 constexpr float kRescaleSlack = 8.0f;
 
-// One wave = one work item (request, partition, KV head, group of up to 4
-// query heads).  Per 16-token tile:
+// Takes the next dynamically scheduled item: queue x holds flat items
+// f = first_dyn + kQueues * c + x; a wave starts at the queue of its XCD and
+// moves to the next queue when one is empty.  Returns 0xffffffff when all
+// queues are empty.
+__device__ __forceinline__ uint32_t claim(const DecodeParams& prm, uint32_t home, uint32_t& queue,
+                                          uint32_t first_dyn, uint32_t total) {
+  const int lane = lane_id();
+  while (queue < kQueues) {
+    const uint32_t x = (home + queue) % kQueues;
+    uint32_t c = 0;
+    if (lane == 0) c = atomicAdd(prm.counter + x * kCounterStride, 1u);
+    c = __builtin_amdgcn_readfirstlane(c);
+    const uint32_t f = first_dyn + kQueues * c + x;
+    if (f < total) return f;
+    ++queue;
+  }
+  return 0xffffffffu;
+}
+
+// ---------------------------------------------------------------------------
+// Partition kernel.  One wave = one work item (request, partition, KV head,
+// group of up to 4 query heads) at a time.
+//
+// Schedule: the flat item list (items x KV heads x head groups) starts with
+// the full partitions, all of the same size.  Whole rounds of those are dealt
+// statically (wave w takes w, w + nwaves, ...), which balances exactly and
+// tells each wave its next item in advance; the rest (the last full round and
+// all tail partitions, largest first) is claimed dynamically from per-XCD
+// queues.  While item i runs, item i+1's descriptor, block ids, first tile
+// and query are fetched, so consecutive items stream without a gap.
+//
+// Per 16-token tile:
 //   S^T = K Q^T   (A = K rows from LDS, B = Q^T with the group's heads as
 //                  columns 0..3), so lane (n, g) gets the scores of head n for
 //                  tokens 4g .. 4g+3;
@@ -316,118 +443,76 @@ constexpr float kRescaleSlack = 8.0f;
 //                  four 16-lane rows);
 //   O^T += V^T P^T (A = V^T from LDS, B = the lane's own probabilities), so
 //                  lane (n, g) accumulates head n's outputs d = 16db + 4g + j.
-template <typename T, int D, bool kWide, bool kAligned>
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool kWide, bool kAligned, int NR>
 __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm) {
   using Gm = Geo<T, D>;
   constexpr int NDB = D / 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* lds = smem + (threadIdx.x >> 6) * Gm::LDS_PER_WAVE;
-  int* ids = reinterpret_cast<int*>(lds + Gm::KBYTES + Gm::VBYTES);
   const int lane = lane_id();
   const int n = lane & 15;  // head column (S^T, O^T) / token row (K operand)
   const int g = lane >> 4;
   const uint32_t per_item = (uint32_t)(prm.Hkv * prm.n_hg);
   const uint32_t total = prm.hdr[kItemCountWord] * per_item;
-  const T* __restrict__ q = static_cast<const T*>(prm.q);
+  const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
+  // (threadIdx.x >> 6 is the same in every lane; readfirstlane tells the compiler)
+  const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (uint32_t)uniform((int)(threadIdx.x >> 6));
+  // static rounds: every full round of full partitions
+  const uint32_t first_dyn = (prm.hdr[kFullCountWord] * per_item) / nwaves * nwaves;
+  const uint32_t home = blockIdx.x % kQueues;
+  uint32_t queue = 0;
   PoolView pv;
   pv.k = static_cast<const char*>(prm.kc);
   pv.v = static_cast<const char*>(prm.vc);
   pv.row_bytes = (uint32_t)(prm.Hkv * Gm::ROWB);
 
-  // Item f of the flat list (items x KV heads x head groups).  The first item
-  // of each wave is its global wave index.  The rest are split into kQueues
-  // interleaved queues, f = nwaves + kQueues * c + x for the c-th claim of
-  // queue x; a wave claims from the queue of its XCD (blocks are dealt to the
-  // XCDs round robin) and moves on to the next queue when that one is empty.
-  // Separate counters keep the claims from serialising on one address.
-  const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
-  const uint32_t home = blockIdx.x % kQueues;
-  uint32_t queue = 0;  // queues found empty so far
-  uint32_t f = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  uint32_t f = wave < first_dyn ? wave : claim(prm, home, queue, first_dyn, total);
+  if (f >= total) return;
+  Item it = make_item(prm, prm.items[f / per_item], f, per_item);
+  int ids[NR];
+  load_ids<NR>(prm, it, ids);
+  u32x4_t qv[Gm::NQV];
+  load_q<T, D>(prm, it, qv);
+  TileRegs<T, D> regs;
+  load_tile<T, D, kWide, kAligned, NR>(pv, prm, it, ids, it.tok0, regs);
+
   for (;;) {
-    if (f >= total) {
-      if (f < nwaves) break;  // fewer items than waves: no queued items either
-      bool got = false;
-      while (queue < kQueues) {
-        const uint32_t x = (home + queue) % kQueues;
-        uint32_t c = 0;
-        if (lane == 0) c = atomicAdd(prm.counter + x * kCounterStride, 1u);
-        c = __builtin_amdgcn_readfirstlane(c);
-        const uint32_t fx = nwaves + kQueues * c + x;
-        if (fx < total) {
-          f = fx;
-          got = true;
-          break;
-        }
-        ++queue;
-      }
-      if (!got) break;
-    }
-    const int2 it = prm.items[f / per_item];
-    const int rem = (int)(f % per_item);
-    const int b = it.x, part = it.y;
-    const int hkv = rem / prm.n_hg;
-    const int hg = rem - hkv * prm.n_hg;
-    const int L = clamp_len(prm.lens[b], prm.cap);
-    const int nparts = (L + kPartTokens - 1) / kPartTokens;
-    const int tok0 = part * kPartTokens;
-    const int tok_end = min(L, tok0 + kPartTokens);
-    const int ntiles = (tok_end - tok0 + kTile - 1) / kTile;
-    const int nh = min(4, prm.G - hg * 4);  // valid heads of this group (columns 0..nh-1)
-    const int32_t* __restrict__ bt_row = prm.bt + (int64_t)b * prm.M;
-    const bool col_ok = n < nh;
-    const int h = hkv * prm.G + hg * 4 + (col_ok ? n : 0);
-    pv.head_bytes = (uint32_t)(hkv * Gm::ROWB + 16 * (lane % Gm::CPR));
-
-    // Q^T operand: column n = query head h; k = head dimension
-    u32x4_t qv[Gm::kBf16 ? Gm::NQ : Gm::NQ / 4];
-    {
-      const T* qrow = q + ((int64_t)b * prm.Hq + h) * D;
-      if constexpr (Gm::kBf16) {
+    const uint32_t fn = f + nwaves < first_dyn ? f + nwaves : 0xffffffffu;  // next static item
+    const bool have_next = fn != 0xffffffffu;
+    i32x4_t dn = {0, 0, 0, 0};
+    Item nx = it;
+    int idn[NR];
 #pragma unroll
-        for (int i = 0; i < Gm::NQ; ++i)
-          qv[i] = col_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * i + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
-      } else {
-#pragma unroll
-        for (int i = 0; i < Gm::NQ / 4; ++i)
-          qv[i] = col_ok ? *reinterpret_cast<const u32x4_t*>(qrow + g * (D / 4) + 4 * i) : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-
-    // this partition's block ids -> the wave's LDS
-    int blk0, blk_last;
-    if (prm.p_shift >= 0) {
-      blk0 = tok0 >> prm.p_shift;
-      blk_last = (tok_end - 1) >> prm.p_shift;
-    } else {
-      blk0 = tok0 / prm.P;
-      blk_last = (tok_end - 1) / prm.P;
-    }
-    wave_lds_sync();  // the previous item is done with the LDS
-    for (int i = lane; i <= blk_last - blk0; i += 64) ids[i] = bt_row[blk0 + i];
-    wave_lds_sync();
+    for (int r = 0; r < NR; ++r) idn[r] = 0;
 
     float m = -INFINITY, l = 0.f;
     f32x4_t o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // software pipeline: the next tile's K/V loads are in flight while one computes
-    TileRegs<T, D> regs;
-    load_tile<T, D, kWide, kAligned>(pv, ids, blk0, tok0, tok_end, prm.P, prm.p_shift, prm.N, regs);
-    for (int t = 0; t < ntiles; ++t) {
-      const int tile0 = tok0 + t * kTile;
+    for (int t = 0; t < it.ntiles; ++t) {
+      const int tile0 = it.tok0 + t * kTile;
+      const bool last = t + 1 == it.ntiles;
       // every token of the tile valid: no zeroing needed (the usual case)
       bool full;
       if constexpr (kAligned)
-        full = tile0 + kTile <= tok_end && __builtin_amdgcn_readfirstlane((int)regs.ok) == (1 << Gm::TPL) - 1;
+        full = tile0 + kTile <= it.tok_end && __builtin_amdgcn_readfirstlane((int)regs.ok) == (1 << Gm::TPL) - 1;
       else
         full = __builtin_amdgcn_readfirstlane((int)(__ballot(regs.ok != (1u << Gm::TPL) - 1u) == 0));
       wave_lds_sync();  // previous tile's LDS reads are done
       stage_tile<T, D>(lds, regs, full);
       wave_lds_sync();
-      if (t + 1 < ntiles)
-        load_tile<T, D, kWide, kAligned>(pv, ids, blk0, tile0 + kTile, tok_end, prm.P, prm.p_shift, prm.N, regs);
+      if (!last) load_tile<T, D, kWide, kAligned, NR>(pv, prm, it, ids, tile0 + kTile, regs);
+      // prefetch of the next static item, spread over this item's tiles
+      if (have_next) {
+        if (t == 0) dn = prm.items[fn / per_item];
+        if (t == min(1, it.ntiles - 1)) {
+          nx = make_item(prm, dn, fn, per_item);
+          load_ids<NR>(prm, nx, idn);
+        }
+        if (last) load_tile<T, D, kWide, kAligned, NR>(pv, prm, nx, idn, nx.tok0, regs);
+      }
 
       // ---- S^T = K Q^T ----
       f32x4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -447,24 +532,26 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
             s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(qv[i][j]), s, 0, 0, 0);
         }
       }
+      if (have_next && last) load_q<T, D>(prm, nx, qv);  // this item's query is no longer needed
+
       // ---- online softmax for head n over tokens tile0 + 4g + j ----
       float sc[4];
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sc[j] = (tile0 + 4 * g + j < tok_end) ? s[j] * prm.scale_log2 : -INFINITY;
+        sc[j] = (tile0 + 4 * g + j < it.tok_end) ? s[j] * prm.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sc[j]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (mx > m + kRescaleSlack) {  // also true for the first tile (m = -inf)
-        if (m != -INFINITY) {
-          const float alpha = fast_exp2(m - mx);
-          l *= alpha;
+      mx = max_over_rows(mx);
+      // move the reference max only when a score exceeds it by the slack
+      // (always on the first tile, m = -inf); uniform branch, rarely taken
+      const bool move = mx > m + kRescaleSlack;
+      if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
+        const float alpha = (move && m != -INFINITY) ? fast_exp2(m - mx) : 1.0f;
+        if (move) m = mx;
+        l *= alpha;
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-        }
-        m = mx;
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
       }
       float p[4];
 #pragma unroll
@@ -494,12 +581,12 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     }
 
     // ---- finish: total of l over the four 16-lane rows; store head n ----
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (col_ok) {
-      if (nparts == 1) {
+    l = sum_over_rows(l);
+    if (n < it.nh) {
+      const int h = it.hkv * prm.G + it.hg * 4 + n;
+      if (it.nparts == 1) {
         const float inv = 1.0f / l;
-        T* dst = static_cast<T*>(prm.out) + ((int64_t)b * prm.Hq + h) * D + 4 * g;
+        T* dst = static_cast<T*>(prm.out) + ((int64_t)it.b * prm.Hq + h) * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           if constexpr (Gm::kBf16) {
@@ -510,7 +597,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
           }
         }
       } else {
-        const int64_t slot = ((int64_t)b * prm.Hq + h) * prm.max_parts + part;
+        const int64_t slot = ((int64_t)it.b * prm.Hq + h) * prm.max_parts + it.part;
         float* dst = prm.o + slot * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db) = o[db];
@@ -520,44 +607,87 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
         }
       }
     }
-    f = 0xffffffffu;  // this item is done: claim the next one
+
+    if (have_next) {  // already fetched: descriptor, ids, first tile, query
+      f = fn;
+      it = nx;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) ids[r] = idn[r];
+      continue;
+    }
+    f = claim(prm, home, queue, first_dyn, total);
+    if (f >= total) break;
+    it = make_item(prm, prm.items[f / per_item], f, per_item);
+    load_ids<NR>(prm, it, ids);
+    load_q<T, D>(prm, it, qv);
+    load_tile<T, D, kWide, kAligned, NR>(pv, prm, it, ids, it.tok0, regs);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Reduce: merge the partitions of requests that have more than one; write
-// zeros for empty requests.  One wave per (query head, request).
+// zeros for empty requests.  One wave per (request, query head), four heads
+// per block.  Lane i first turns partition i's (max, sum) into its weight
+// 2^(m_i - m); the weighted sum over partitions then reads each weight with
+// a lane broadcast while the partial outputs stream in, four at a time.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams prm) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams prm) {
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6), b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  if (h >= prm.Hq) return;
   const int L = clamp_len(prm.lens[b], prm.cap);
   const int np = (L + kPartTokens - 1) / kPartTokens;
   if (np == 1) return;
+  constexpr int PER = D / 64;
   T* dst = static_cast<T*>(prm.out) + ((int64_t)b * prm.Hq + h) * D;
   if (np == 0) {
-    for (int d = lane; d < D; d += 64) {
-      if constexpr (sizeof(T) == 2) dst[d] = 0;
-      else dst[d] = 0.f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if constexpr (sizeof(T) == 2) dst[lane + 64 * j] = 0;
+      else dst[lane + 64 * j] = 0.f;
     }
     return;
   }
   const int64_t slot0 = ((int64_t)b * prm.Hq + h) * prm.max_parts;
-  float mx = -INFINITY;
-  for (int i = lane; i < np; i += 64) mx = fmaxf(mx, prm.ml[(slot0 + i) * 2]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  constexpr int PER = D / 64;
-  float acc[PER], den = 0.f;
+  const float2* ml = reinterpret_cast<const float2*>(prm.ml) + slot0;
+  float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-  for (int i = 0; i < np; ++i) {
-    const float w = fast_exp2(prm.ml[(slot0 + i) * 2] - mx);
-    den = fmaf(w, prm.ml[(slot0 + i) * 2 + 1], den);
-    const float* src = prm.o + (slot0 + i) * D;
+  float den = 0.f;
+  for (int c0 = 0; c0 < np; c0 += 64) {  // chunks of 64 partitions
+    const int nc = min(64, np - c0);
+    // global max over all partitions (first chunk computes it for every chunk)
+    float mx = -INFINITY;
+    for (int i = lane; i < np; i += 64) mx = fmaxf(mx, ml[i].x);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, src[lane + 64 * j], acc[j]);
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float2 mine = lane < nc ? ml[c0 + lane] : make_float2(-INFINITY, 0.f);
+    const float w = lane < nc ? fast_exp2(mine.x - mx) : 0.f;
+    float lw = w * mine.y;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
+    den += lw;
+    const float* src = prm.o + (slot0 + c0) * D + lane;
+    int i = 0;
+    for (; i + 4 <= nc; i += 4) {
+      float v[4][PER];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[u][j] = src[(i + u) * D + 64 * j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wu = __shfl(w, i + u);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] = fmaf(wu, v[u][j], acc[j]);
+      }
+    }
+    for (; i < nc; ++i) {
+      const float wu = __shfl(w, i);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) acc[j] = fmaf(wu, src[i * D + 64 * j], acc[j]);
+    }
   }
   const float inv = 1.0f / den;
 #pragma unroll
@@ -567,7 +697,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams prm) {
   }
 }
 
-template <typename T, int D, bool kWide, bool kAligned>
+template <typename T, int D, bool kWide, bool kAligned, int NR>
 hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipStream_t stream,
                         hipEvent_t ev0, hipEvent_t ev1) {
   // waves are independent workers; a block holds as many as fit in 64 KiB of LDS (at most 4)
@@ -578,7 +708,7 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partition_kernel<T, D, kWide, kAligned>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partition_kernel<T, D, kWide, kAligned, NR>,
                                                      64 * wpb, lds_bytes) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
@@ -590,27 +720,31 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
     const hipError_t e = hipEventRecord(ev0, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, kWide, kAligned>), dim3(blocks), dim3(64 * wpb), lds_bytes,
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, kWide, kAligned, NR>), dim3(blocks), dim3(64 * wpb), lds_bytes,
                      stream, prm);
   if (ev1) {
     const hipError_t e = hipEventRecord(ev1, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(prm.Hq, B), dim3(64), 0, stream, prm);
+  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3((prm.Hq + 3) / 4, B), dim3(256), 0, stream, prm);
   return hipGetLastError();
+}
+
+template <typename T, int D, bool kWide>
+hipError_t launch_mode(const DecodeParams& prm, int B, int64_t max_items, hipStream_t stream, hipEvent_t ev0,
+                       hipEvent_t ev1) {
+  // tiles of 16 tokens never straddle a block when P is a multiple of 16; a
+  // partition touches at most 256 / P + 1 blocks: one id register for P >= 5
+  if (prm.P % kTile == 0) return launch_typed<T, D, kWide, true, 1>(prm, B, max_items, stream, ev0, ev1);
+  if (prm.P >= 5) return launch_typed<T, D, kWide, false, 1>(prm, B, max_items, stream, ev0, ev1);
+  return launch_typed<T, D, kWide, false, 5>(prm, B, max_items, stream, ev0, ev1);
 }
 
 template <typename T, int D>
 hipError_t launch_sized(const DecodeParams& prm, int B, int64_t max_items, int64_t pool_bytes,
                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  // tiles of 16 tokens never straddle a block when P is a multiple of 16
-  const bool aligned = prm.P % kTile == 0;
-  if (pool_bytes < ((int64_t)1 << 32)) {
-    if (aligned) return launch_typed<T, D, false, true>(prm, B, max_items, stream, ev0, ev1);
-    return launch_typed<T, D, false, false>(prm, B, max_items, stream, ev0, ev1);
-  }
-  if (aligned) return launch_typed<T, D, true, true>(prm, B, max_items, stream, ev0, ev1);
-  return launch_typed<T, D, true, false>(prm, B, max_items, stream, ev0, ev1);
+  if (pool_bytes < ((int64_t)1 << 32)) return launch_mode<T, D, false>(prm, B, max_items, stream, ev0, ev1);
+  return launch_mode<T, D, true>(prm, B, max_items, stream, ev0, ev1);
 }
 
 }  // namespace
@@ -632,7 +766,7 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.out = a.out;
   prm.hdr = reinterpret_cast<const uint32_t*>(ws + Lw.hdr);
   prm.counter = reinterpret_cast<uint32_t*>(ws + Lw.hdr);
-  prm.items = reinterpret_cast<const int2*>(ws + Lw.items);
+  prm.items = reinterpret_cast<const i32x4_t*>(ws + Lw.items);
   prm.ml = reinterpret_cast<float*>(ws + Lw.ml);
   prm.o = reinterpret_cast<float*>(ws + Lw.o);
   prm.scale_log2 = a.scale * kLog2e;
@@ -647,9 +781,9 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.cap = (int)((int64_t)a.max_blocks * a.block_size);
   prm.max_parts = (int)Lw.max_parts;
 
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens, a.num_seqs,
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(64), 0, stream, a.context_lens, a.num_seqs,
                      prm.cap, reinterpret_cast<uint32_t*>(ws + Lw.hdr),
-                     reinterpret_cast<int2*>(ws + Lw.items));
+                     reinterpret_cast<i32x4_t*>(ws + Lw.items));
   const int64_t max_items = (int64_t)a.num_seqs * Lw.max_parts * prm.Hkv * prm.n_hg;
   const int64_t pool_bytes =
       a.num_blocks * a.block_size * a.num_kv_heads * a.head_dim * (a.dtype == kBF16 ? 2 : 4);
