@@ -46,6 +46,7 @@ namespace {
 constexpr int kTile = 16;                        // tokens per MFMA tile
 
 constexpr int kWavesPerBlock = 4;
+constexpr int kMaxStaticRounds = 64;  // static items per wave: one descriptor per lane
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -275,6 +276,12 @@ __device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, 
   }
 }
 
+// Descriptor held in lane `r` of a per-lane descriptor register (wave-uniform result).
+__device__ __forceinline__ i32x4_t lane_desc(const i32x4_t& d, int r) {
+  return i32x4_t{__builtin_amdgcn_readlane(d[0], r), __builtin_amdgcn_readlane(d[1], r),
+                 __builtin_amdgcn_readlane(d[2], r), __builtin_amdgcn_readlane(d[3], r)};
+}
+
 // Block id of logical block `idx` (relative to the item's first block) for
 // a per-lane index: lane crossbar read from the id registers.
 template <int NR>
@@ -429,11 +436,18 @@ __device__ __forceinline__ uint32_t claim(const DecodeParams& prm, uint32_t home
 //
 // Schedule: the flat item list (items x KV heads x head groups) starts with
 // the full partitions, all of the same size.  Whole rounds of those are dealt
-// statically (wave w takes w, w + nwaves, ...), which balances exactly and
-// tells each wave its next item in advance; the rest (the last full round and
-// all tail partitions, largest first) is claimed dynamically from per-XCD
-// queues.  While item i runs, item i+1's descriptor, block ids, first tile
-// and query are fetched, so consecutive items stream without a gap.
+// statically (wave w takes w, w + nwaves, ...), which balances exactly; lane
+// r of a register holds the wave's round-r descriptor, so the next static
+// item costs no memory access.  The rest (the last full round and all tail
+// partitions, largest first) is claimed dynamically from per-XCD queues, one
+// item ahead.
+//
+// The loop runs over the wave's stream of tiles, across item boundaries: each
+// iteration stages the tile that has landed, issues the loads of the next
+// tile of the stream (the next item's first tile after an item's last), and
+// computes.  The next item's block ids are fetched at its predecessor's
+// first tile and its query after the predecessor's last S^T product, so
+// items follow one another without draining the loads in flight.
 //
 // Per 16-token tile:
 //   S^T = K Q^T   (A = K rows from LDS, B = Q^T with the group's heads as
@@ -458,8 +472,9 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
   const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
   // (threadIdx.x >> 6 is the same in every lane; readfirstlane tells the compiler)
   const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (uint32_t)uniform((int)(threadIdx.x >> 6));
-  // static rounds: every full round of full partitions
-  const uint32_t first_dyn = (prm.hdr[kFullCountWord] * per_item) / nwaves * nwaves;
+  // static rounds: whole rounds of full partitions, at most one per lane
+  const uint32_t rounds = min((prm.hdr[kFullCountWord] * per_item) / nwaves, (uint32_t)kMaxStaticRounds);
+  const uint32_t first_dyn = rounds * nwaves;
   const uint32_t home = blockIdx.x % kQueues;
   uint32_t queue = 0;
   PoolView pv;
@@ -467,9 +482,22 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
   pv.v = static_cast<const char*>(prm.vc);
   pv.row_bytes = (uint32_t)(prm.Hkv * Gm::ROWB);
 
-  uint32_t f = wave < first_dyn ? wave : claim(prm, home, queue, first_dyn, total);
-  if (f >= total) return;
-  Item it = make_item(prm, prm.items[f / per_item], f, per_item);
+  // lane r: descriptor of this wave's item of static round r
+  i32x4_t sdesc = {0, 0, 0, 0};
+  if (rounds > 0) sdesc = prm.items[(wave + (uint32_t)min(lane, (int)rounds - 1) * nwaves) / per_item];
+
+  // the current item: round r < rounds is static item wave + r * nwaves
+  uint32_t r = 0;
+  uint32_t f = wave;
+  Item it;
+  if (rounds > 0) {
+    it = make_item(prm, lane_desc(sdesc, 0), f, per_item);
+  } else {
+    r = rounds;
+    f = claim(prm, home, queue, first_dyn, total);
+    if (f >= total) return;
+    it = make_item(prm, prm.items[f / per_item], f, per_item);
+  }
   int ids[NR];
   load_ids<NR>(prm, it, ids);
   u32x4_t qv[Gm::NQV];
@@ -477,110 +505,124 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
   TileRegs<T, D> regs;
   load_tile<T, D, kWide, kAligned, NR>(pv, prm, it, ids, it.tok0, regs);
 
-  for (;;) {
-    const uint32_t fn = f + nwaves < first_dyn ? f + nwaves : 0xffffffffu;  // next static item
-    const bool have_next = fn != 0xffffffffu;
-    i32x4_t dn = {0, 0, 0, 0};
-    Item nx = it;
-    int idn[NR];
+  Item nx = it;        // the item after the current one, once known
+  uint32_t fn = 0;     // its flat index
+  bool has_next = false;
+  int idn[NR];         // its block ids
 #pragma unroll
-    for (int r = 0; r < NR; ++r) idn[r] = 0;
+  for (int i = 0; i < NR; ++i) idn[i] = 0;
 
-    float m = -INFINITY, l = 0.f;
-    f32x4_t o[NDB];
+  float m = -INFINITY, l = 0.f;
+  f32x4_t o[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int t = 0; t < it.ntiles; ++t) {
-      const int tile0 = it.tok0 + t * kTile;
-      const bool last = t + 1 == it.ntiles;
-      // every token of the tile valid: no zeroing needed (the usual case)
-      bool full;
-      if constexpr (kAligned)
-        full = tile0 + kTile <= it.tok_end && __builtin_amdgcn_readfirstlane((int)regs.ok) == (1 << Gm::TPL) - 1;
-      else
-        full = __builtin_amdgcn_readfirstlane((int)(__ballot(regs.ok != (1u << Gm::TPL) - 1u) == 0));
-      wave_lds_sync();  // previous tile's LDS reads are done
-      stage_tile<T, D>(lds, regs, full);
-      wave_lds_sync();
-      if (!last) load_tile<T, D, kWide, kAligned, NR>(pv, prm, it, ids, tile0 + kTile, regs);
-      // prefetch of the next static item, spread over this item's tiles
-      if (have_next) {
-        if (t == 0) dn = prm.items[fn / per_item];
-        if (t == min(1, it.ntiles - 1)) {
-          nx = make_item(prm, dn, fn, per_item);
-          load_ids<NR>(prm, nx, idn);
-        }
-        if (last) load_tile<T, D, kWide, kAligned, NR>(pv, prm, nx, idn, nx.tok0, regs);
-      }
+  for (int t = 0;;) {
+    const int tile0 = it.tok0 + t * kTile;
+    const bool last = t + 1 == it.ntiles;
+    // every token of the tile valid: no zeroing needed (the usual case)
+    bool full;
+    if constexpr (kAligned)
+      full = tile0 + kTile <= it.tok_end && __builtin_amdgcn_readfirstlane((int)regs.ok) == (1 << Gm::TPL) - 1;
+    else
+      full = __builtin_amdgcn_readfirstlane((int)(__ballot(regs.ok != (1u << Gm::TPL) - 1u) == 0));
+    wave_lds_sync();  // previous tile's LDS reads are done
+    stage_tile<T, D>(lds, regs, full);
+    wave_lds_sync();
 
-      // ---- S^T = K Q^T ----
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (Gm::kBf16) {
-#pragma unroll
-        for (int i = 0; i < Gm::NQ; ++i) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                      __builtin_bit_cast(bf16x8_t, qv[i]), s, 0, 0, 0);
-        }
+    if (t == 0) {  // find the next item and fetch its block ids
+      if (r + 1 < rounds) {
+        fn = f + nwaves;
+        nx = make_item(prm, lane_desc(sdesc, (int)r + 1), fn, per_item);
+        has_next = true;
       } else {
-#pragma unroll
-        for (int i = 0; i < Gm::NQ / 4; ++i) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 4 * (g * (D / 4) + 4 * i));
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(qv[i][j]), s, 0, 0, 0);
-        }
+        fn = claim(prm, home, queue, first_dyn, total);
+        has_next = fn < total;
+        if (has_next) nx = make_item(prm, prm.items[fn / per_item], fn, per_item);
       }
-      if (have_next && last) load_q<T, D>(prm, nx, qv);  // this item's query is no longer needed
+      if (has_next) load_ids<NR>(prm, nx, idn);
+    }
+    // the next tile of the stream: this item's, or the next item's first
+    if (last && has_next) {
+      // a real branch, not a select: a select would read idn on every tile
+      // and so wait for its load right after it is issued
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < NR; ++i) ids[i] = idn[i];
+    }
+    if (!last || has_next)
+      load_tile<T, D, kWide, kAligned, NR>(pv, prm, last ? nx : it, ids, last ? nx.tok0 : tile0 + kTile, regs);
 
-      // ---- online softmax for head n over tokens tile0 + 4g + j ----
-      float sc[4];
-      float mx = -INFINITY;
+    // ---- S^T = K Q^T ----
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (Gm::kBf16) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sc[j] = (tile0 + 4 * g + j < it.tok_end) ? s[j] * prm.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sc[j]);
+      for (int i = 0; i < Gm::NQ; ++i) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, qv[i]), s, 0, 0, 0);
       }
-      mx = max_over_rows(mx);
-      // move the reference max only when a score exceeds it by the slack
-      // (always on the first tile, m = -inf); uniform branch, rarely taken
-      const bool move = mx > m + kRescaleSlack;
-      if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
-        const float alpha = (move && m != -INFINITY) ? fast_exp2(m - mx) : 1.0f;
-        if (move) m = mx;
-        l *= alpha;
+    } else {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      }
-      float p[4];
+      for (int i = 0; i < Gm::NQ / 4; ++i) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 4 * (g * (D / 4) + 4 * i));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = fast_exp2(sc[j] - m);
-        l += p[j];
-      }
-      // ---- O^T += V^T P^T ----
-      const char* vl = lds + Gm::KBYTES;
-      if constexpr (Gm::kBf16) {
-        const u32x2_t pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vl + (16 * db + n) * Gm::VTS + 8 * g);
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
-                                                            __builtin_bit_cast(s16x4_t, pb), o[db], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float a = *reinterpret_cast<const float*>(vl + (4 * g + j) * Gm::KST + 4 * (16 * db + n));
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[j], o[db], 0, 0, 0);
-          }
+        for (int j = 0; j < 4; ++j)
+          s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(qv[i][j]), s, 0, 0, 0);
       }
     }
+    if (last && has_next) load_q<T, D>(prm, nx, qv);  // this item's query is no longer needed
 
-    // ---- finish: total of l over the four 16-lane rows; store head n ----
+    // ---- online softmax for head n over tokens tile0 + 4g + j ----
+    float sc[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = (tile0 + 4 * g + j < it.tok_end) ? s[j] * prm.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sc[j]);
+    }
+    mx = max_over_rows(mx);
+    // move the reference max only when a score exceeds it by the slack
+    // (always on the first tile, m = -inf); uniform branch, rarely taken
+    const bool move = mx > m + kRescaleSlack;
+    if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
+      const float alpha = (move && m != -INFINITY) ? fast_exp2(m - mx) : 1.0f;
+      if (move) m = mx;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = fast_exp2(sc[j] - m);
+      l += p[j];
+    }
+    // ---- O^T += V^T P^T ----
+    const char* vl = lds + Gm::KBYTES;
+    if constexpr (Gm::kBf16) {
+      const u32x2_t pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vl + (16 * db + n) * Gm::VTS + 8 * g);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                          __builtin_bit_cast(s16x4_t, pb), o[db], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = *reinterpret_cast<const float*>(vl + (4 * g + j) * Gm::KST + 4 * (16 * db + n));
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[j], o[db], 0, 0, 0);
+        }
+    }
+    if (!last) {
+      ++t;
+      continue;
+    }
+
+    // ---- item done: total of l over the four 16-lane rows; store head n ----
     l = sum_over_rows(l);
     if (n < it.nh) {
       const int h = it.hkv * prm.G + it.hg * 4 + n;
@@ -607,20 +649,17 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
         }
       }
     }
-
-    if (have_next) {  // already fetched: descriptor, ids, first tile, query
-      f = fn;
-      it = nx;
+    if (!has_next) break;
+    // the next item's ids, first tile and query are already in flight
+    it = nx;
+    f = fn;
+    r = r + 1 < rounds ? r + 1 : rounds;
+    has_next = false;
+    t = 0;
+    m = -INFINITY;
+    l = 0.f;
 #pragma unroll
-      for (int r = 0; r < NR; ++r) ids[r] = idn[r];
-      continue;
-    }
-    f = claim(prm, home, queue, first_dyn, total);
-    if (f >= total) break;
-    it = make_item(prm, prm.items[f / per_item], f, per_item);
-    load_ids<NR>(prm, it, ids);
-    load_q<T, D>(prm, it, qv);
-    load_tile<T, D, kWide, kAligned, NR>(pv, prm, it, ids, it.tok0, regs);
+    for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 }
 
