@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="no GPU run: turn the rocprofv3 CSVs under DIR into the summaries in profiles/")
     return ap.parse_args()
 
 
@@ -347,8 +349,128 @@ def bench_copy(args):
             "config": {"workload": "torch copy_ of 1 GiB", "bytes": n}, "cpu_baseline": None}
 
 
+# ---------------------------------------------------------------------------
+# Profile summaries.  The GPU runs that feed them (each writes CSVs under DIR):
+PROFILE_RUNS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_decode -o decode -- "
+             "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+    "trace_mixed": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_mixed -o mixed -- "
+                   "python3 bench.py --workload mixed --steps 10 --warmup 2",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch -o fetch -- "
+             "python3 bench.py --layers 2 --steps 2 --warmup 1 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write -o write -- "
+             "python3 bench.py --layers 2 --steps 2 --warmup 1 --no-cpu-baseline",
+    "copyf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_copyf -o copyf -- "
+             "python3 bench.py --workload copy --steps 3 --warmup 1",
+    "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_copyw -o copyw -- "
+             "python3 bench.py --workload copy --steps 3 --warmup 1",
+}
+
+
+def _short_kernel(name):
+    name = name.replace("(anonymous namespace)::", "").replace("pa::", "")
+    return name if len(name) < 110 else name[:107] + "..."
+
+
+def _stats_table(path, top=8):
+    import csv
+
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"{'kernel':<110} {'calls':>6} {'avg us':>9} {'min us':>9} {'max us':>9} {'% time':>7}"]
+    for r in rows[:top]:
+        out.append(f"{_short_kernel(r['Name']):<110} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.2f} "
+                   f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} {float(r['Percentage']):>7.2f}")
+    return out, rows
+
+
+def _counter_mean(path, kernel_substr, counter):
+    """Mean over dispatches of one counter (KiB per dispatch) for the kernels
+    whose name contains kernel_substr."""
+    import csv
+
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def summarize_profiles(d):
+    import glob
+
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    src = os.path.join(ROOT, "paged_kv_cache_48_amd", "csrc", "decode.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    one = lambda pat: (glob.glob(os.path.join(d, pat)) or [None])[0]  # noqa: E731
+
+    stats = one("prof_decode/*kernel_stats.csv")
+    if stats:
+        table, _ = _stats_table(stats)
+        with open(os.path.join(prof, "decode_llama3_8b_kernel_stats.txt"), "w") as f:
+            f.write("Llama-3-8B-shaped decode step (32 layers x (reshape_and_cache + paged decode: plan, partition,\n"
+                    "reduce), B=256, H_q=32, H_kv=8, D=128, P=16, bf16), rocprofv3 kernel statistics.\n")
+            f.write("command (run from the repository root, DIR = an output folder):\n  "
+                    + PROFILE_RUNS["trace"] + "\n")
+            f.write(f"decode.hip sha256: {sha}\n\n")
+            f.write("\n".join(table) + "\n")
+    stats = one("prof_mixed/*kernel_stats.csv")
+    if stats:
+        table, _ = _stats_table(stats)
+        with open(os.path.join(prof, "prefill_mixed_kernel_stats.txt"), "w") as f:
+            f.write("Mixed chunked-prefill + decode step (16 prefill chunks over cached prefixes + 48 decodes,\n"
+                    "Llama-3-8B heads, P=16, bf16), rocprofv3 kernel statistics.\n")
+            f.write("command (run from the repository root, DIR = an output folder):\n  "
+                    + PROFILE_RUNS["trace_mixed"] + "\n\n")
+            f.write("\n".join(table) + "\n")
+
+    fetch_kib, nf = _counter_mean(one("pmc_fetch/*counter_collection.csv"), "decode_partition_kernel", "FETCH_SIZE") \
+        if one("pmc_fetch/*counter_collection.csv") else (None, 0)
+    write_kib, nw = _counter_mean(one("pmc_write/*counter_collection.csv"), "decode_partition_kernel", "WRITE_SIZE") \
+        if one("pmc_write/*counter_collection.csv") else (None, 0)
+    cf_kib, _ = _counter_mean(one("pmc_copyf/*counter_collection.csv"), "copyBuffer", "FETCH_SIZE") \
+        if one("pmc_copyf/*counter_collection.csv") else (None, 0)
+    cw_kib, _ = _counter_mean(one("pmc_copyw/*counter_collection.csv"), "copyBuffer", "WRITE_SIZE") \
+        if one("pmc_copyw/*counter_collection.csv") else (None, 0)
+    if None in (fetch_kib, write_kib, cf_kib, cw_kib):
+        log("counter CSVs incomplete; traffic summary not written")
+        return
+    gib = float(1 << 30)
+    kf, kw = gib / (cf_kib * 1024), gib / (cw_kib * 1024)  # true bytes per counted byte
+    fetch_b, write_b = fetch_kib * 1024 * kf, write_kib * 1024 * kw
+    from workloads import config_case
+
+    case = config_case(3, values=False)
+    alg = decode_bytes(case.context_lens, case.block_size, case.num_q_heads, case.num_kv_heads, case.head_dim, 2)
+    lines = [
+        "HBM traffic of decode_partition_kernel<bf16, 128> on the Llama-3-8B-shaped batch (one launch = one layer:",
+        "B=256, sum of context lengths " + f"{int(case.context_lens.sum())}, H_kv=8, D=128, P=16).",
+        "commands (run from the repository root, DIR = an output folder):",
+        "  " + PROFILE_RUNS["fetch"], "  " + PROFILE_RUNS["write"],
+        "  " + PROFILE_RUNS["copyf"], "  " + PROFILE_RUNS["copyw"],
+        f"decode.hip sha256: {sha}", "",
+        f"calibration: torch copy_ of 1 GiB reads FETCH_SIZE {cf_kib:.0f} KiB and WRITE_SIZE {cw_kib:.0f} KiB "
+        f"per dispatch -> scale {kf:.4f} (fetch), {kw:.4f} (write)",
+        f"partition kernel: FETCH_SIZE {fetch_kib:.0f} KiB, WRITE_SIZE {write_kib:.0f} KiB per dispatch "
+        f"(mean of {nf} and {nw} dispatches)",
+        f"  -> fetched {fetch_b / 1e9:.4f} GB + written {write_b / 1e9:.4f} GB = {(fetch_b + write_b) / 1e9:.4f} GB "
+        f"per launch",
+        f"algorithmic bytes per launch: {alg / 1e9:.4f} GB (KV rows + q/out + block table + lengths); "
+        f"measured / algorithmic = {(fetch_b + write_b) / alg:.3f}",
+    ]
+    with open(os.path.join(prof, "decode_llama3_8b_hbm_traffic.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(prof, "traffic.json"), "w") as f:
+        json.dump({"decode_partition_llama3_8b": {
+            "source_sha256": sha, "bytes_per_launch": int(fetch_b + write_b), "fetch_bytes": int(fetch_b),
+            "write_bytes": int(write_b), "fetch_scale": kf, "write_scale": kw}}, f, indent=1)
+    log("profiles written")
+
+
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path has no multi-GPU component)", file=sys.stderr)

@@ -47,6 +47,7 @@ constexpr int kTile = 16;                        // tokens per MFMA tile
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kMaxStaticRounds = 64;  // static items per wave: one descriptor per lane
+constexpr int kDynamicRounds = 1;     // whole rounds of full partitions handed out by the queues
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -57,6 +58,7 @@ constexpr int kCounterStride = 32;  // uint32 words between counters
 constexpr int kHeaderBytes = 1024;
 constexpr int kItemCountWord = kHeaderBytes / 4 - 1;
 constexpr int kFullCountWord = kHeaderBytes / 4 - 2;  // items that are full partitions
+constexpr int kQueueCountWord = kHeaderBytes / 4 - 3;  // queues in use
 
 struct DecodeLayout {
   int64_t max_parts;
@@ -82,82 +84,59 @@ DecodeLayout decode_layout(int B, int Hq, int D, int P, int M) {
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
 // ---------------------------------------------------------------------------
-// Plan: one wave lists the (request, partition) items in decreasing size --
-// every full partition first, then the tail partitions sorted by their tile
-// count (16 .. 1) -- so the last items handed out are the smallest.  Each
-// item carries (request, partition, clamped length, partition count).  It
-// also zeroes the queue counters.  Lane i owns requests i, i+64, ...; item
-// offsets come from wave-wide exclusive scans of the per-lane counts.
+// Plan: lists the (request, partition) items in decreasing size -- every full
+// partition first, then the tail partitions grouped by their tile count
+// (16 .. 1) -- so the last items handed out are the smallest.  Each item
+// carries (request, partition, clamped length, partition count).  One block:
+// the bucket sizes are counted with LDS atomics, turned into bucket offsets,
+// and each request then takes its positions with a second round of LDS
+// atomics (the order inside a bucket is arbitrary; results do not depend on
+// which wave computes an item).  It also zeroes the queue counters and picks
+// one queue when items are long enough for a single counter to keep up.
 // ---------------------------------------------------------------------------
-constexpr int kTileBuckets = kPartTokens / 16;  // tail partitions hold 1 .. 16 tiles
+constexpr int kTileBuckets = kPartTokens / 16;  // bucket k >= 1: tails of k tiles; bucket 0: full
+constexpr int kPlanThreads = 1024;
 
-template <int NV>
-__device__ __forceinline__ void wave_excl_scan(int (&v)[NV], int (&total)[NV]) {
-  const int lane = threadIdx.x & 63;
-  int x[NV];
-#pragma unroll
-  for (int k = 0; k < NV; ++k) x[k] = v[k];
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int y = __shfl_up(x[k], d);
-      if (lane >= d) x[k] += y;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    total[k] = __shfl(x[k], 63);
-    v[k] = x[k] - v[k];
-  }
-}
-
-__global__ __launch_bounds__(64) void decode_plan_kernel(const int32_t* __restrict__ lens, int B, int cap,
-                                                         uint32_t* hdr, i32x4_t* __restrict__ items) {
-  const int lane = threadIdx.x;
-  // counts: [0] full partitions, [1 + k] tail partitions of k+1 tiles
-  int cnt[1 + kTileBuckets];
-#pragma unroll
-  for (int k = 0; k <= kTileBuckets; ++k) cnt[k] = 0;
-  for (int b = lane; b < B; b += 64) {
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ lens, int B,
+                                                                   int cap, uint32_t* hdr,
+                                                                   i32x4_t* __restrict__ items) {
+  __shared__ int cnt[kTileBuckets + 1];
+  __shared__ int cur[kTileBuckets + 1];
+  __shared__ unsigned long long tiles;
+  const int tid = threadIdx.x;
+  if (tid <= kTileBuckets) cnt[tid] = 0;
+  if (tid == 0) tiles = 0;
+  __syncthreads();
+  for (int b = tid; b < B; b += kPlanThreads) {
     const int L = clamp_len(lens[b], cap);
-    cnt[0] += L / kPartTokens;
-    const int rest = L % kPartTokens;
-#pragma unroll
-    for (int k = 0; k < kTileBuckets; ++k) cnt[1 + k] += (rest > 0 && (rest + 15) / 16 == k + 1) ? 1 : 0;
+    const int full = L / kPartTokens, rest = L % kPartTokens;
+    if (full) atomicAdd(&cnt[0], full);
+    if (rest) atomicAdd(&cnt[(rest + 15) / 16], 1);
+    if (L) atomicAdd(&tiles, (unsigned long long)((L + 15) / 16));
   }
-  int tot[1 + kTileBuckets];
-  wave_excl_scan<1 + kTileBuckets>(cnt, tot);
-  // bucket base offsets: full items, then tails of 16, 15, ..., 1 tiles
-  int base[1 + kTileBuckets];
-  base[0] = 0;
-  int run = tot[0];
-#pragma unroll
-  for (int k = kTileBuckets - 1; k >= 0; --k) {
-    base[1 + k] = run;
-    run += tot[1 + k];
-  }
-#pragma unroll
-  for (int k = 0; k <= kTileBuckets; ++k) cnt[k] += base[k];  // this lane's next write position
-  for (int b = lane; b < B; b += 64) {
-    const int L = clamp_len(lens[b], cap);
-    const int np = (L + kPartTokens - 1) / kPartTokens;
-    const int f = L / kPartTokens;
-    for (int j = 0; j < f; ++j) items[cnt[0]++] = i32x4_t{b, j, L, np};
-    const int rest = L % kPartTokens;
-    if (rest > 0) {
-      const int k = (rest + 15) / 16 - 1;
-      int at = 0;
-#pragma unroll
-      for (int kk = 0; kk < kTileBuckets; ++kk)
-        if (kk == k) at = cnt[1 + kk]++;
-      items[at] = i32x4_t{b, f, L, np};
+  __syncthreads();
+  if (tid == 0) {
+    int run = cnt[0];
+    cur[0] = 0;
+    for (int k = kTileBuckets; k >= 1; --k) {
+      cur[k] = run;
+      run += cnt[k];
     }
-  }
-  if (lane < kQueues) hdr[lane * kCounterStride] = 0u;
-  if (lane == 0) {
     hdr[kItemCountWord] = (uint32_t)run;
-    hdr[kFullCountWord] = (uint32_t)tot[0];
+    hdr[kFullCountWord] = (uint32_t)cnt[0];
+    hdr[kQueueCountWord] = tiles >= 4ull * (unsigned long long)run ? 1u : (uint32_t)kQueues;
+  }
+  if (tid < kQueues) hdr[tid * kCounterStride] = 0u;
+  __syncthreads();
+  for (int b = tid; b < B; b += kPlanThreads) {
+    const int L = clamp_len(lens[b], cap);
+    const int full = L / kPartTokens, rest = L % kPartTokens;
+    const int np = full + (rest ? 1 : 0);
+    if (full) {
+      const int at = atomicAdd(&cur[0], full);
+      for (int j = 0; j < full; ++j) items[at + j] = i32x4_t{b, j, L, np};
+    }
+    if (rest) items[atomicAdd(&cur[(rest + 15) / 16], 1)] = i32x4_t{b, full, L, np};
   }
 }
 
@@ -216,6 +195,8 @@ struct DecodeParams {
   float* o;
   float scale_log2;
   int Hq, Hkv, G, n_hg, P, p_shift, N, M, cap, max_parts;
+  int dyn_rounds;  // full rounds of full partitions left to the queues
+  int nq;          // queues in use (at most kQueues); 0: as the plan chose
 };
 
 // One work item, wave-uniform (scalar registers).
@@ -411,19 +392,19 @@ __device__ __forceinline__ void wave_lds_sync() {
 // accumulators is rare; the result does not depend on the reference.
 constexpr float kRescaleSlack = 8.0f;
 
-// Takes the next dynamically scheduled item: queue x holds flat items
-// f = first_dyn + kQueues * c + x; a wave starts at the queue of its XCD and
-// moves to the next queue when one is empty.  Returns 0xffffffff when all
-// queues are empty.
-__device__ __forceinline__ uint32_t claim(const DecodeParams& prm, uint32_t home, uint32_t& queue,
+// Takes the next dynamically scheduled item: with nq queues, queue x holds
+// flat items f = first_dyn + nq * c + x; a wave starts at its home queue (its
+// XCD's, when there are eight) and moves to the next one when that is empty.
+// Returns 0xffffffff when all queues are empty.
+__device__ __forceinline__ uint32_t claim(const DecodeParams& prm, uint32_t nq, uint32_t home, uint32_t& queue,
                                           uint32_t first_dyn, uint32_t total) {
   const int lane = lane_id();
-  while (queue < kQueues) {
-    const uint32_t x = (home + queue) % kQueues;
+  while (queue < nq) {
+    const uint32_t x = (home + queue) % nq;
     uint32_t c = 0;
     if (lane == 0) c = atomicAdd(prm.counter + x * kCounterStride, 1u);
     c = __builtin_amdgcn_readfirstlane(c);
-    const uint32_t f = first_dyn + kQueues * c + x;
+    const uint32_t f = first_dyn + nq * c + x;
     if (f < total) return f;
     ++queue;
   }
@@ -472,10 +453,14 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
   const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
   // (threadIdx.x >> 6 is the same in every lane; readfirstlane tells the compiler)
   const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (uint32_t)uniform((int)(threadIdx.x >> 6));
-  // static rounds: whole rounds of full partitions, at most one per lane
-  const uint32_t rounds = min((prm.hdr[kFullCountWord] * per_item) / nwaves, (uint32_t)kMaxStaticRounds);
+  // static rounds: whole rounds of full partitions, at most one per lane;
+  // the last kDynamicRounds of them are left to the queues, which balance
+  // waves that run at different speeds
+  uint32_t rounds = min((prm.hdr[kFullCountWord] * per_item) / nwaves, (uint32_t)kMaxStaticRounds);
+  rounds = rounds > (uint32_t)prm.dyn_rounds ? rounds - (uint32_t)prm.dyn_rounds : min(rounds, 1u);
   const uint32_t first_dyn = rounds * nwaves;
-  const uint32_t home = blockIdx.x % kQueues;
+  const uint32_t nq = prm.nq > 0 ? (uint32_t)prm.nq : prm.hdr[kQueueCountWord];
+  const uint32_t home = blockIdx.x % nq;
   uint32_t queue = 0;
   PoolView pv;
   pv.k = static_cast<const char*>(prm.kc);
@@ -494,7 +479,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     it = make_item(prm, lane_desc(sdesc, 0), f, per_item);
   } else {
     r = rounds;
-    f = claim(prm, home, queue, first_dyn, total);
+    f = claim(prm, nq, home, queue, first_dyn, total);
     if (f >= total) return;
     it = make_item(prm, prm.items[f / per_item], f, per_item);
   }
@@ -508,6 +493,8 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
   Item nx = it;        // the item after the current one, once known
   uint32_t fn = 0;     // its flat index
   bool has_next = false;
+  int pend = 0;        // 1: next item claimed (fn), 2: its descriptor loaded (dn)
+  i32x4_t dn = {0, 0, 0, 0};
   int idn[NR];         // its block ids
 #pragma unroll
   for (int i = 0; i < NR; ++i) idn[i] = 0;
@@ -530,17 +517,37 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     stage_tile<T, D>(lds, regs, full);
     wave_lds_sync();
 
-    if (t == 0) {  // find the next item and fetch its block ids
-      if (r + 1 < rounds) {
+    // find the next item and fetch its block ids.  A static item is known at
+    // once.  A dynamic one is claimed with an atomic right after tile 1's
+    // loads are issued (its wait then only delays tile 0's arithmetic, not
+    // the memory stream), its descriptor is loaded at tile 1 and its ids at
+    // tile 2; items of one or two tiles claim everything up front.
+    const bool stat_next = r + 1 < rounds;
+    const bool early = it.ntiles >= 3;
+    if (t == 0) {
+      if (stat_next) {
         fn = f + nwaves;
         nx = make_item(prm, lane_desc(sdesc, (int)r + 1), fn, per_item);
         has_next = true;
-      } else {
-        fn = claim(prm, home, queue, first_dyn, total);
-        has_next = fn < total;
-        if (has_next) nx = make_item(prm, prm.items[fn / per_item], fn, per_item);
+        load_ids<NR>(prm, nx, idn);
+      } else if (!early) {
+        fn = claim(prm, nq, home, queue, first_dyn, total);
+        if (fn < total) {
+          nx = make_item(prm, prm.items[fn / per_item], fn, per_item);
+          has_next = true;
+          load_ids<NR>(prm, nx, idn);
+        }
       }
-      if (has_next) load_ids<NR>(prm, nx, idn);
+    }
+    if (pend == 1 && t == 1) {
+      dn = prm.items[fn / per_item];
+      pend = 2;
+    }
+    if (pend == 2 && t == 2) {
+      nx = make_item(prm, dn, fn, per_item);
+      has_next = true;
+      load_ids<NR>(prm, nx, idn);
+      pend = 0;
     }
     // the next tile of the stream: this item's, or the next item's first
     if (last && has_next) {
@@ -552,6 +559,10 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     }
     if (!last || has_next)
       load_tile<T, D, kWide, kAligned, NR>(pv, prm, last ? nx : it, ids, last ? nx.tok0 : tile0 + kTile, regs);
+    if (t == 0 && early && !stat_next) {
+      fn = claim(prm, nq, home, queue, first_dyn, total);
+      if (fn < total) pend = 1;
+    }
 
     // ---- S^T = K Q^T ----
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -668,71 +679,85 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
 // zeros for empty requests.  One wave per (request, query head), four heads
 // per block.  Lane i first turns partition i's (max, sum) into its weight
 // 2^(m_i - m); the weighted sum over partitions then reads each weight with
-// a lane broadcast while the partial outputs stream in, four at a time.
+// a lane broadcast while the partial outputs stream in, sixteen partitions
+// per round so that many loads are in flight.  Lane l owns output elements
+// D/64 * l .. D/64 * l + D/64 - 1 (one vector load per partition).
 // ---------------------------------------------------------------------------
+template <int PER>
+struct RowPiece;
+template <>
+struct RowPiece<1> {
+  typedef float type;
+  static __device__ __forceinline__ float get(const type& v, int) { return v; }
+};
+template <>
+struct RowPiece<2> {
+  typedef f32x2_t type;
+  static __device__ __forceinline__ float get(const type& v, int j) { return v[j]; }
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams prm) {
+  constexpr int PER = D / 64;
+  constexpr int U = 16;  // partitions per round
+  typedef RowPiece<PER> RP;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6), b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   if (h >= prm.Hq) return;
+  const int64_t slot0 = ((int64_t)b * prm.Hq + h) * prm.max_parts;
+  const f32x2_t* ml = reinterpret_cast<const f32x2_t*>(prm.ml) + slot0;
+  // the (max, sum) pairs are read before the length is known (slots past the
+  // request's partition count exist in the workspace and are masked below),
+  // so the two loads overlap
+  const f32x2_t ml0 = ml[min(lane, prm.max_parts - 1)];
   const int L = clamp_len(prm.lens[b], prm.cap);
   const int np = (L + kPartTokens - 1) / kPartTokens;
   if (np == 1) return;
-  constexpr int PER = D / 64;
-  T* dst = static_cast<T*>(prm.out) + ((int64_t)b * prm.Hq + h) * D;
+  T* dst = static_cast<T*>(prm.out) + ((int64_t)b * prm.Hq + h) * D + PER * lane;
   if (np == 0) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      if constexpr (sizeof(T) == 2) dst[lane + 64 * j] = 0;
-      else dst[lane + 64 * j] = 0.f;
+      if constexpr (sizeof(T) == 2) dst[j] = 0;
+      else dst[j] = 0.f;
     }
     return;
   }
-  const int64_t slot0 = ((int64_t)b * prm.Hq + h) * prm.max_parts;
-  const float2* ml = reinterpret_cast<const float2*>(prm.ml) + slot0;
+  // global max over all partitions
+  float mx = lane < np ? ml0[0] : -INFINITY;
+  for (int i = lane + 64; i < np; i += 64) mx = fmaxf(mx, ml[i][0]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   float den = 0.f;
   for (int c0 = 0; c0 < np; c0 += 64) {  // chunks of 64 partitions
     const int nc = min(64, np - c0);
-    // global max over all partitions (first chunk computes it for every chunk)
-    float mx = -INFINITY;
-    for (int i = lane; i < np; i += 64) mx = fmaxf(mx, ml[i].x);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const float2 mine = lane < nc ? ml[c0 + lane] : make_float2(-INFINITY, 0.f);
-    const float w = lane < nc ? fast_exp2(mine.x - mx) : 0.f;
-    float lw = w * mine.y;
+    const f32x2_t mine = c0 == 0 ? ml0 : ml[c0 + min(lane, nc - 1)];
+    const float w = lane < nc ? fast_exp2(mine[0] - mx) : 0.f;
+    float lw = w * mine[1];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
     den += lw;
-    const float* src = prm.o + (slot0 + c0) * D + lane;
-    int i = 0;
-    for (; i + 4 <= nc; i += 4) {
-      float v[4][PER];
+    const typename RP::type* src =
+        reinterpret_cast<const typename RP::type*>(prm.o + (slot0 + c0) * D) + lane;
+    for (int i = 0; i < nc; i += U) {
+      typename RP::type v[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < U; ++u) v[u] = src[(size_t)min(i + u, nc - 1) * (D / PER)];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) v[u][j] = src[(i + u) * D + 64 * j];
+      for (int u = 0; u < U; ++u) {
+        const float wu = i + u < nc ? __shfl(w, i + u) : 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wu = __shfl(w, i + u);
-#pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] = fmaf(wu, v[u][j], acc[j]);
+        for (int j = 0; j < PER; ++j) acc[j] = fmaf(wu, RP::get(v[u], j), acc[j]);
       }
-    }
-    for (; i < nc; ++i) {
-      const float wu = __shfl(w, i);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) acc[j] = fmaf(wu, src[i * D + 64 * j], acc[j]);
     }
   }
   const float inv = 1.0f / den;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    if constexpr (sizeof(T) == 2) dst[lane + 64 * j] = (bf16_bits)f32_to_bf16(acc[j] * inv);
-    else dst[lane + 64 * j] = acc[j] * inv;
+    if constexpr (sizeof(T) == 2) dst[j] = (bf16_bits)f32_to_bf16(acc[j] * inv);
+    else dst[j] = acc[j] * inv;
   }
 }
 
@@ -819,8 +844,10 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.M = a.max_blocks;
   prm.cap = (int)((int64_t)a.max_blocks * a.block_size);
   prm.max_parts = (int)Lw.max_parts;
+  prm.dyn_rounds = kDynamicRounds;
+  prm.nq = 0;
 
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(64), 0, stream, a.context_lens, a.num_seqs,
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.context_lens, a.num_seqs,
                      prm.cap, reinterpret_cast<uint32_t*>(ws + Lw.hdr),
                      reinterpret_cast<i32x4_t*>(ws + Lw.items));
   const int64_t max_items = (int64_t)a.num_seqs * Lw.max_parts * prm.Hkv * prm.n_hg;
