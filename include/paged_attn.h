@@ -144,7 +144,9 @@ size_t pa_prefill_workspace_size(int32_t num_seqs, int64_t total_q_tokens,
  *   block_table   int32 [num_seqs, max_blocks_per_seq]
  *   context_lens  int32 [num_seqs]
  *   workspace     at least pa_prefill_workspace_size() bytes
- * dtype must be PA_DTYPE_BF16 (bf16 MFMA); fp32 returns PA_ERR_UNSUPPORTED.
+ * dtype must be PA_DTYPE_BF16 (bf16 MFMA); fp32 returns PA_ERR_UNSUPPORTED, as
+ * does max_blocks_per_seq above 16384 (a request's block ids are staged on
+ * chip).  scale must be positive and finite (PA_ERR_INVALID otherwise).
  */
 int pa_paged_prefill_attention(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens, const int32_t* block_table,

@@ -213,6 +213,10 @@ int pa_paged_prefill_attention(const void* q, const void* k, const void* v, cons
   PA_REQUIRE(dtype == PA_DTYPE_BF16, PA_ERR_UNSUPPORTED, "%s: prefill is provided for bf16 only", fn);
   PA_REQUIRE(num_q_heads / num_kv_heads <= 64, PA_ERR_UNSUPPORTED,
              "%s: GQA group size above 64 is not provided", fn);
+  PA_REQUIRE(max_blocks_per_seq <= pa::kPrefillMaxBlocks, PA_ERR_UNSUPPORTED,
+             "%s: max_blocks_per_seq above %d is not provided (a request's block ids are held in LDS)", fn,
+             pa::kPrefillMaxBlocks);
+  PA_REQUIRE(scale > 0.0f && scale < INFINITY, PA_ERR_INVALID, "%s: scale must be positive and finite", fn);
   if (total_q_tokens == 0) return PA_OK;
   PA_REQUIRE(num_seqs >= 1, PA_ERR_INVALID, "%s: %lld query tokens but no sequence", fn,
              (long long)total_q_tokens);

@@ -16,6 +16,10 @@ enum DType : int { kF32 = 0, kBF16 = 1 };
 // neighbours.
 constexpr int kPartTokens = 256;
 
+// Largest max_blocks_per_seq the prefill kernel takes: an item's block ids
+// are staged in LDS (64 KiB of them).
+constexpr int kPrefillMaxBlocks = 16384;
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

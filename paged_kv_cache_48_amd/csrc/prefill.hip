@@ -11,20 +11,28 @@
 //   * Work item = (request, tile of TQ = 128 / G chunk tokens, KV head).  The
 //     G query heads that share a KV head are packed into the item's 128 rows
 //     (head-major), so each K/V tile fetched from the pool serves all of them.
-//   * A persistent grid pulls items from a queue that a plan kernel sorts by
-//     decreasing key count (largest causal extents first).
-//   * Per 64-key tile the 256 threads gather K and V rows through the block
-//     table (16-byte loads), K stored as is in LDS and V stored transposed
-//     (d-major) so that both MFMA operands are contiguous LDS reads.  The next
-//     tile's loads are in flight while the current tile computes.
+//   * A persistent grid of one 4-wave workgroup per CU pulls items from a
+//     queue that a plan kernel sorts by decreasing key count (largest causal
+//     extents first).
+//   * The item's block ids are copied to LDS first, so no gather address
+//     waits on a global load (a wait on one would drain the loads in flight,
+//     which complete in order).
+//   * Per 64-key tile, the 256 threads gather K and V rows through the block
+//     table (16-byte loads); K is stored as is in LDS and V
+//     transposed (d-major) so that both MFMA operands are contiguous LDS
+//     reads.  Two register sets and two LDS buffers keep the loads of the next
+//     two tiles in flight while one tile computes; one barrier per tile.
 //   * Each wave owns 32 rows.  S^T = K Q^T and O^T += V^T P^T run as
 //     16x16x32 bf16 MFMAs with fp32 accumulation.  Computing the transposed
 //     scores leaves each lane holding one query row's scores for a run of keys,
 //     which is exactly the B-operand layout the P.V product needs, so P never
-//     leaves registers.  Online softmax in base 2, fp32.
+//     leaves registers.  Online softmax in base 2, fp32, with a lazily moved
+//     reference max; tiles past every row of a wave are skipped.
 //   * Keys past the causal limit, tail slots and out-of-range block ids are
 //     masked and never multiply a value: masked K/V tile rows are zero-filled.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -33,9 +41,10 @@ namespace pa {
 
 namespace {
 
-constexpr int kRows = 128;   // rows (chunk token x query head) per work item
-constexpr int kTK = 64;      // keys per tile
-constexpr int kThreads = 256;
+constexpr int kRows = 128;     // rows (chunk token x query head) per work item
+constexpr int kTK = 64;        // keys per tile
+constexpr int kThreads = 256;  // 4 waves, 32 rows each
+constexpr int kIdCap = kPrefillMaxBlocks;  // block ids an item keeps in LDS
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -49,73 +58,97 @@ int64_t max_prefill_items(int num_seqs, int64_t num_q_tokens, int G) {
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
 // ---------------------------------------------------------------------------
-// Plan: list (request, q tile) items sorted by decreasing number of key tiles
-// (counting sort; ties in any order -- each item is computed independently,
-// so the order never changes a result).
+// Plan: the (request, q tile) items, requests ordered by their total number of
+// key tiles (largest first; counting sort, ties in any order -- each item is
+// computed independently, so the order never changes a result), and each
+// request's q tiles from the last (largest causal extent) to the first, so
+// that the items sharing a request's keys run at the same time.
 // ---------------------------------------------------------------------------
 constexpr int kBuckets = 1024;
+constexpr int kPlanThreads = 1024;
+constexpr int kXcds = 8;            // queues: one per XCD of the MI355X
+constexpr int kHeaderBytes = 1024;
+constexpr int kCounterStride = 32;  // uint32 words between queue counters (128-byte lines)
+constexpr int kEntryCountWord = kHeaderBytes / 4 - 1;
 
 __device__ __forceinline__ bool chunk_ok(const int32_t* __restrict__ cu, int b, int T, int L,
                                          int num_q_tokens) {
   return T > 0 && T <= L && cu[b] >= 0 && cu[b + 1] <= num_q_tokens;
 }
 
-__global__ __launch_bounds__(1024) void prefill_plan_kernel(const int32_t* __restrict__ cu,
-                                                            const int32_t* __restrict__ lens, int B,
-                                                            int cap, int TQ, int num_q_tokens,
-                                                            int item_cap, uint32_t* hdr,
-                                                            int2* __restrict__ items) {
+// Key tiles of all q tiles of a chunk of T tokens over a prefix of L - T.
+__device__ __forceinline__ int chunk_work(int T, int L, int TQ) {
+  int w = 0;
+  for (int t0 = 0; t0 < T; t0 += TQ) w += (L - T + min(T, t0 + TQ) + kTK - 1) / kTK;
+  return w;
+}
+
+// Exclusive scan of one value per thread over a kPlanThreads block.
+__device__ __forceinline__ int block_excl_scan(int v, int* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wave_tot[wv] = x;
+  __syncthreads();
+  if (wv == 0) {
+    int t = lane < kPlanThreads / 64 ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(t, d);
+      if (lane >= d) t += y;
+    }
+    if (lane < kPlanThreads / 64) wave_tot[lane] = t;  // inclusive totals
+  }
+  __syncthreads();
+  return x - v + (wv > 0 ? wave_tot[wv - 1] : 0);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const int32_t* __restrict__ cu,
+                                                                    const int32_t* __restrict__ lens, int B,
+                                                                    int cap, int TQ, int num_q_tokens,
+                                                                    int item_cap, uint32_t* hdr,
+                                                                    int2* __restrict__ items) {
   __shared__ int hist[kBuckets];
-  __shared__ int total;
+  __shared__ int wave_tot[kPlanThreads / 64];
   const int tid = threadIdx.x;
-  for (int i = tid; i < kBuckets; i += 1024) hist[i] = 0;
-  if (tid == 0) total = 0;
+  for (int i = tid; i < kBuckets; i += kPlanThreads) hist[i] = 0;
   __syncthreads();
-  for (int b = tid; b < B; b += 1024) {
+  for (int b = tid; b < B; b += kPlanThreads) {
+    const int T = cu[b + 1] - cu[b];
+    const int L = clamp_len(lens[b], cap);
+    if (!chunk_ok(cu, b, T, L, num_q_tokens)) continue;
+    const int bucket = min(chunk_work(T, L, TQ) / 4, kBuckets - 1);
+    atomicAdd(&hist[bucket], (T + TQ - 1) / TQ);
+  }
+  __syncthreads();
+  // descending bucket order: thread t owns bucket kBuckets - 1 - t
+  static_assert(kBuckets == kPlanThreads, "one bucket per thread");
+  const int mine = hist[kBuckets - 1 - tid];
+  const int off = block_excl_scan(mine, wave_tot);
+  hist[kBuckets - 1 - tid] = off;
+  if (tid == kPlanThreads - 1) hdr[kEntryCountWord] = (uint32_t)min(off + mine, item_cap);
+  if (tid < kXcds) hdr[tid * kCounterStride] = 0u;
+  __syncthreads();
+  for (int b = tid; b < B; b += kPlanThreads) {
     const int T = cu[b + 1] - cu[b];
     const int L = clamp_len(lens[b], cap);
     if (!chunk_ok(cu, b, T, L, num_q_tokens)) continue;
     const int nq = (T + TQ - 1) / TQ;
-    for (int j = 0; j < nq; ++j) {
-      const int kmax = L - T + min(T, (j + 1) * TQ);
-      const int bucket = min((kmax + kTK - 1) / kTK, kBuckets - 1);
-      atomicAdd(&hist[bucket], 1);
-    }
-    atomicAdd(&total, nq);
-  }
-  __syncthreads();
-  // descending exclusive scan over buckets (serial, 1024 entries)
-  if (tid == 0) {
-    int run = 0;
-    for (int i = kBuckets - 1; i >= 0; --i) {
-      const int c = hist[i];
-      hist[i] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  for (int b = tid; b < B; b += 1024) {
-    const int T = cu[b + 1] - cu[b];
-    const int L = clamp_len(lens[b], cap);
-    if (!chunk_ok(cu, b, T, L, num_q_tokens)) continue;
-    const int nq = (T + TQ - 1) / TQ;
-    for (int j = 0; j < nq; ++j) {
-      const int kmax = L - T + min(T, (j + 1) * TQ);
-      const int bucket = min((kmax + kTK - 1) / kTK, kBuckets - 1);
-      const int at = atomicAdd(&hist[bucket], 1);
-      if (at < item_cap) items[at] = make_int2(b, j);
-    }
-  }
-  if (tid == 0) {
-    hdr[0] = 0u;
-    hdr[1] = (uint32_t)min(total, item_cap);
+    const int bucket = min(chunk_work(T, L, TQ) / 4, kBuckets - 1);
+    const int at = atomicAdd(&hist[bucket], nq);
+    for (int j = 0; j < nq; ++j)
+      if (at + j < item_cap) items[at + j] = make_int2(b, nq - 1 - j);
   }
 }
 
 struct PrefillParams {
   const bf16_bits* q;
-  const bf16_bits* kc;
-  const bf16_bits* vc;
+  const char* kc;
+  const char* vc;
   const int32_t* cu;
   const int32_t* bt;
   const int32_t* lens;
@@ -124,118 +157,286 @@ struct PrefillParams {
   uint32_t* counter;
   const int2* items;
   float scale_log2;
-  int Hq, Hkv, G, TQ, P, p_shift, N, M, cap;
+  int Hq, Hkv, G, TQ, P, N, M, cap;
+  uint32_t div_m, div_l;  // pos / P = (mulhi(pos, div_m) + pos) >> div_l for 0 <= pos < 2^31
+  uint32_t row_bytes;     // H_kv * D * 2: one token's row of the pool
 };
 
+// Exact unsigned division by the block size with a precomputed multiplier
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): l = ceil(log2 P), m = ceil(2^(32+l) / P) - 2^32.
+__device__ __forceinline__ int div_block(const PrefillParams& p, int pos) {
+  return (int)((__umulhi((uint32_t)pos, p.div_m) + (uint32_t)pos) >> p.div_l);
+}
+
+// LDS of one workgroup: two K / V^T tile buffers and the item's block ids.
 template <int D>
 struct __attribute__((aligned(16))) PrefillLds {
-  static constexpr int KST = D + 8;     // K row stride (elements)
-  static constexpr int VST = kTK + 4;   // V^T row stride (elements)
-  bf16_bits k[kTK * KST];
-  bf16_bits vt[D * VST];
+  static constexpr int KST = D + 8;    // K row stride (elements)
+  static constexpr int VST = kTK + 4;  // V^T row stride (elements)
+  bf16_bits k[2][kTK * KST];
+  bf16_bits vt[2][D * VST];
+  int32_t ids[kIdCap];
 };
 
-// Gathers of one 64-key tile, held in registers between the global loads
-// and the LDS stores.
-template <int D>
-struct TileRegs {
-  static constexpr int KV = D / 4 * 2 / 16;  // 16-byte pieces of K per thread
-  u32x4_t k[KV];
+// One tile's gathers in flight, held in registers between the global loads
+// and the LDS stores: D/32 16-byte pieces of K rows, and 4 keys x one 16-byte
+// piece of V rows, per thread.  ok: bit i (K piece i) / bit 4 + j (V key j)
+// set when that key is visible and its block id valid.
+struct TileSet {
+  u32x4_t k[4];
   u32x4_t v[4];
+  uint32_t ok;
 };
 
-__device__ __forceinline__ int64_t key_row(const int32_t* __restrict__ bt_row, int pos, int kmax, int P,
-                                           int p_shift, int N) {
-  if (pos >= kmax) return -1;
-  int j, off;
-  if (p_shift >= 0) {
-    j = pos >> p_shift;
-    off = pos & ((1 << p_shift) - 1);
-  } else {
-    j = pos / P;
-    off = pos - j * P;
+// Gathers of one tile.  Every load is issued unconditionally: a key past kmax
+// or with an out-of-range block id reads the head's slice of row 0 instead --
+// always in bounds -- and is zeroed when the tile is stored.  The block ids of
+// the thread's 8 keys are read from LDS first, all together, so the LDS round
+// trip is paid once per tile.
+template <int D, bool kWide>
+__device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillLds<D>& s, int hkv, int k0,
+                                          int kmax, TileSet& r) {
+  typedef typename std::conditional<kWide, uint64_t, uint32_t>::type O;
+  constexpr int CPR = D / 8;  // 16-byte pieces per head row
+  constexpr int NK = D / 32;  // K pieces per thread
+  const int tid = threadIdx.x;
+  const int kq = tid / CPR, dc = tid % CPR;  // V: keys 4 kq .. 4 kq + 3, elements 8 dc .. 8 dc + 7
+  // threads with kq >= 16 exist only for D = 64: whole waves 2 and 3
+  const bool v_wave = uniform(tid >> 6) < 16 * CPR / 64;
+  int pos[NK + 4], off[NK + 4], blk[NK + 4];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) pos[i] = k0 + (tid + kThreads * i) / CPR;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pos[NK + j] = k0 + 4 * kq + j;
+#pragma unroll
+  for (int x = 0; x < NK + 4; ++x) {
+    const int jb = div_block(p, pos[x] < kmax ? pos[x] : 0);
+    off[x] = pos[x] - jb * p.P;
+    blk[x] = s.ids[jb];
   }
-  const int blk = bt_row[j];
-  if (blk < 0 || blk >= N) return -1;
-  return (int64_t)blk * P + off;
+  const O head = (O)(hkv * D * 2);
+  r.ok = 0;
+#pragma unroll
+  for (int x = 0; x < NK + 4; ++x) {
+    const bool ok = pos[x] < kmax && blk[x] >= 0 && blk[x] < p.N;
+    const O o = (ok ? ((O)blk[x] * (O)p.P + (O)off[x]) * (O)p.row_bytes : (O)0) + head +
+                (O)(16 * (x < NK ? (tid + kThreads * x) % CPR : dc));
+    r.ok |= (ok ? 1u : 0u) << (x < NK ? x : 4 + x - NK);
+    if (x < NK) r.k[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.kc + o));
+    else if (v_wave) r.v[x - NK] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.vc + o));
+  }
 }
 
 template <int D>
-__device__ __forceinline__ void load_tile(const PrefillParams& p, const int32_t* __restrict__ bt_row,
-                                          int hkv, int k0, int kmax, TileRegs<D>& r) {
+__device__ __forceinline__ void store_tile(PrefillLds<D>& s, int buf, TileSet& r) {
+  constexpr int CPR = D / 8;
   const int tid = threadIdx.x;
-  const int64_t row_elems = (int64_t)p.Hkv * D;
-  // K: thread -> key tid/4, quarter tid%4 of the head
-  {
-    const int kk = tid >> 2, c = tid & 3;
-    const int64_t row = key_row(bt_row, k0 + kk, kmax, p.P, p.p_shift, p.N);
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.kc + row * row_elems + (int64_t)hkv * D + c * (D / 4));
+  const bool v_wave = uniform(tid >> 6) < 16 * CPR / 64;
+  const uint32_t all = (1u << (D / 32)) - 1u | (v_wave ? 0xf0u : 0u);
+  if (__builtin_amdgcn_readfirstlane((int)(__ballot(r.ok != all) != 0))) {  // rare: zero the keys that are not ok
 #pragma unroll
-    for (int i = 0; i < TileRegs<D>::KV; ++i) r.k[i] = row >= 0 ? src[i] : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < D / 32; ++i)
+      if (!((r.ok >> i) & 1u)) r.k[i] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (!((r.ok >> (4 + j)) & 1u)) r.v[j] = u32x4_t{0u, 0u, 0u, 0u};
   }
-  // V: thread -> keys 4*kq .. 4*kq+3, head elements 8*dc .. 8*dc+7
-  {
-    constexpr int DC = D / 8;
-    const int kq = tid / DC, dc = tid % DC;
-    if (kq < 16) {
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int e = tid + kThreads * i, key = e / CPR, c = e % CPR;
+    *reinterpret_cast<u32x4_t*>(&s.k[buf][key * PrefillLds<D>::KST + 8 * c]) = r.k[i];
+  }
+  if (v_wave) {
+    const int kq = tid / CPR, dc = tid % CPR;
+    // transpose the 4 keys x 8 elements block into 8 rows of 4 keys
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w0 = r.v[0][i], w1 = r.v[1][i], w2 = r.v[2][i], w3 = r.v[3][i];
+      const u32x2_t lo = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
+      const u32x2_t hi = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
+      const int d = dc * 8 + 2 * i;
+      *reinterpret_cast<u32x2_t*>(&s.vt[buf][d * PrefillLds<D>::VST + 4 * kq]) = lo;
+      *reinterpret_cast<u32x2_t*>(&s.vt[buf][(d + 1) * PrefillLds<D>::VST + 4 * kq]) = hi;
+    }
+  }
+}
+
+// Softmax reference max moves only when a score exceeds it by more than this
+// (log2 units): probabilities stay below 2^8, and rescaling is rare.
+constexpr float kRescaleSlack = 8.0f;
+
+// Per-wave state of one item: 32 rows (two blocks of 16), one per lane column.
+template <int D>
+struct RowState {
+  static constexpr int NI = D / 32;
+  static constexpr int NDB = D / 16;
+  u32x4_t q[2][NI];  // Q^T operand of each row block
+  int pos[2];        // absolute position of the lane's row (-1: no row)
+  float m[2], l[2];
+  f32x4_t o[NDB][2];  // O^T: lane (n, g) holds d = 16 db + 4 g + j of row n
+};
+
+// One 64-key tile for this wave's 32 rows: S^T = K Q^T, online softmax, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int k0, float scale_log2,
+                                            RowState<D>& st) {
+  constexpr int NI = RowState<D>::NI, NDB = RowState<D>::NDB;
+  const int lane = lane_id();
+  const int n = lane & 15, g = lane >> 4;
+  // all K operands of the tile are read before the products start, so the
+  // LDS latency is paid once
+  u32x4_t ka[4][NI];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      ka[kb][i] = *reinterpret_cast<const u32x4_t*>(&s.k[buf][(kb * 16 + n) * PrefillLds<D>::KST + 32 * i + 8 * g]);
+  f32x4_t sc[4][2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    sc[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    sc[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, ka[kb][i]);
+      sc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, st.q[0][i]), sc[kb][0], 0,
+                                                          0, 0);
+      sc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, st.q[1][i]), sc[kb][1], 0,
+                                                          0, 0);
+    }
+  }
+  // scheduling: every K operand read first, then the products
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 * NI, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 8 * NI, 0);
+  u32x4_t pop[2][2];  // [rb][k-step]: P^T operand, 8 bf16
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    // causal mask, only where this row block's last key position is inside
+    // the tile (keys past a row's position get -inf)
+    // (the lane's keys are kb*16 + 4g + j, kb, j < 4: all visible when lim >= 51)
+    const int lim = st.pos[rb] - k0 - 4 * g;  // key kb*16 + 4g + j is visible when kb*16 + j <= lim
+    if (__builtin_amdgcn_readfirstlane((int)(__ballot(lim < 3 * 16 + 3) != 0))) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[kb][rb][j] = kb * 16 + j <= lim ? sc[kb][rb][j] : -INFINITY;
+    }
+    // max of the raw scores (scale_log2 > 0), in log2 units after scaling
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sc[kb][rb][j]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax *= scale_log2;
+    const bool move = tmax > st.m[rb] + kRescaleSlack;
+    if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
+      const float alpha = (move && st.m[rb] != -INFINITY) ? fast_exp2(st.m[rb] - tmax) : 1.0f;
+      if (move) st.m[rb] = tmax;
+      st.l[rb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) st.o[db][rb] *= alpha;
+    }
+    const float nm = st.m[rb] == -INFINITY ? 0.f : -st.m[rb];
+    float pv[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t row = key_row(bt_row, k0 + 4 * kq + j, kmax, p.P, p.p_shift, p.N);
-        const u32x4_t* src =
-            reinterpret_cast<const u32x4_t*>(p.vc + row * row_elems + (int64_t)hkv * D + dc * 8);
-        r.v[j] = row >= 0 ? *src : u32x4_t{0u, 0u, 0u, 0u};
+        pv[kb][j] = fast_exp2(fmaf(sc[kb][rb][j], scale_log2, nm));
+        st.l[rb] += pv[kb][j];
       }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      pop[rb][ks] = u32x4_t{pack_bf16(pv[2 * ks][0], pv[2 * ks][1]), pack_bf16(pv[2 * ks][2], pv[2 * ks][3]),
+                            pack_bf16(pv[2 * ks + 1][0], pv[2 * ks + 1][1]),
+                            pack_bf16(pv[2 * ks + 1][2], pv[2 * ks + 1][3])};
+  }
+  // k-slots 0..3 of step ks are keys 32 ks + 4 g + j, slots 4..7 keys 32 ks + 16 + 4 g + j
+  u32x4_t va[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16_bits* vrow = &s.vt[buf][(db * 16 + n) * PrefillLds<D>::VST + 32 * ks + 4 * g];
+      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
+      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+      va[db][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, va[db][ks]);
+      st.o[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, pop[0][ks]), st.o[db][0],
+                                                            0, 0, 0);
+      st.o[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, pop[1][ks]), st.o[db][1],
+                                                            0, 0, 0);
     }
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDB, 1);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4 * NDB, 1);
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(PrefillLds<D>& s, const TileRegs<D>& r) {
-  const int tid = threadIdx.x;
-  {
-    const int kk = tid >> 2, c = tid & 3;
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s.k[kk * PrefillLds<D>::KST + c * (D / 4)]);
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::KV; ++i) dst[i] = r.k[i];
-  }
-  {
-    constexpr int DC = D / 8;
-    const int kq = tid / DC, dc = tid % DC;
-    if (kq < 16) {
-      // transpose the 4 keys x 8 elements block into 8 rows of 4 keys
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w0 = r.v[0][i], w1 = r.v[1][i], w2 = r.v[2][i], w3 = r.v[3][i];
-        const u32x2_t lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-        const u32x2_t hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-        const int d = dc * 8 + 2 * i;
-        *reinterpret_cast<u32x2_t*>(&s.vt[d * PrefillLds<D>::VST + 4 * kq]) = lo;
-        *reinterpret_cast<u32x2_t*>(&s.vt[(d + 1) * PrefillLds<D>::VST + 4 * kq]) = hi;
-      }
-    }
-  }
+__device__ __forceinline__ void attend(const PrefillLds<D>& s, int buf, int k0, float scale_log2, int wave_max,
+                                       RowState<D>& st) {
+  if (k0 > wave_max) return;  // every row of this wave is causally done
+  attend_tile<D>(s, buf, k0, scale_log2, st);
 }
 
-template <int D>
+// ---------------------------------------------------------------------------
+// Prefill kernel: one persistent workgroup of 4 waves per CU pulls items.
+// An item is (request, tile of TQ chunk tokens, KV head) with 128 rows
+// (TQ tokens x G query heads, head-major); wave w owns rows 32w .. 32w+31.
+// Key tiles of 64 go through two LDS buffers; the loads of the next two tiles
+// are in flight while one tile computes, and the item's block ids sit in LDS
+// so no gather address waits on a global load.
+// ---------------------------------------------------------------------------
+template <int D, bool kWide>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
-  constexpr int NI = D / 32;  // MFMA k-steps over the head dimension
-  constexpr int NDB = D / 16; // 16-row blocks of O^T
   __shared__ PrefillLds<D> lds;
-  __shared__ uint32_t s_item;
+  __shared__ uint32_t s_item, s_head;
+  constexpr int NI = RowState<D>::NI, NDB = RowState<D>::NDB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = uniform(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const uint32_t total = p.hdr[1] * (uint32_t)p.Hkv;
+  const uint32_t entries = p.hdr[kEntryCountWord];
+  // With H_kv a multiple of 8, KV head h is worked on by the workgroups of
+  // XCD h % 8 (blocks are dealt to the XCDs in turn), so the q tiles that
+  // share a request's keys meet in one L2; a workgroup whose queue is empty
+  // helps the other queues.  Otherwise one queue serves all.
+  const bool affine = p.Hkv % kXcds == 0;
+  const uint32_t nqueues = affine ? kXcds : 1;
+  const uint32_t per_entry = affine ? (uint32_t)(p.Hkv / kXcds) : (uint32_t)p.Hkv;
+  const uint32_t home = blockIdx.x % nqueues;
+  uint32_t queue = 0;  // queues found empty so far (thread 0)
 
   for (;;) {
+    __syncthreads();  // the previous item's LDS reads are done
+    if (tid == 0) {
+      uint32_t e = 0xffffffffu, h = 0;
+      while (queue < nqueues) {
+        const uint32_t x = (home + queue) % nqueues;
+        const uint32_t c = atomicAdd(p.counter + x * kCounterStride, 1u);
+        if (c / per_entry < entries) {
+          e = c / per_entry;
+          h = affine ? x + kXcds * (c % per_entry) : c % per_entry;
+          break;
+        }
+        ++queue;
+      }
+      s_item = e;
+      s_head = h;
+    }
     __syncthreads();
-    if (tid == 0) s_item = atomicAdd(p.counter, 1u);
-    __syncthreads();
-    const uint32_t f = s_item;
-    if (f >= total) break;
-    const int2 it = p.items[f / p.Hkv];
-    const int hkv = (int)(f % p.Hkv);
+    const uint32_t e = s_item;
+    if (e == 0xffffffffu) break;
+    const int2 it = p.items[e];
+    const int hkv = (int)s_head;
     const int b = it.x, qt = it.y;
     const int cu0 = p.cu[b];
     const int T = p.cu[b + 1] - cu0;
@@ -246,135 +447,70 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const int kmax = start + t0 + nt;  // keys 0 .. kmax-1 are visible to some row
     const int nkt = (kmax + kTK - 1) / kTK;
     const int32_t* __restrict__ bt_row = p.bt + (int64_t)b * p.M;
+    const int nblk = div_block(p, kmax - 1) + 1;  // kmax <= cap = M * P, so nblk <= M <= kIdCap
+    for (int i = tid; i < nblk; i += kThreads) lds.ids[i] = bt_row[i];
 
-    // rows of this wave: r = 32w + 16rb + n -> (head r / TQ, chunk token r % TQ)
-    int pos[2];
-    u32x4_t qop[2][NI];
+    RowState<D> st;
     int wave_max = -1;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int r = 32 * w + 16 * rb + n;
       const int hl = r / p.TQ, tl = r - hl * p.TQ;
       const bool ok = hl < p.G && tl < nt;
-      pos[rb] = ok ? start + t0 + tl : -1;
+      st.pos[rb] = ok ? start + t0 + tl : -1;
       const int64_t qrow = ((int64_t)(cu0 + t0 + tl) * p.Hq + hkv * p.G + hl) * D;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        qop[rb][i] = ok ? *reinterpret_cast<const u32x4_t*>(p.q + qrow + 32 * i + 8 * g)
-                        : u32x4_t{0u, 0u, 0u, 0u};
-      wave_max = max(wave_max, pos[rb]);
+        st.q[rb][i] = ok ? *reinterpret_cast<const u32x4_t*>(p.q + qrow + 32 * i + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
+      if (ok) wave_max = max(wave_max, st.pos[rb]);
+      st.m[rb] = -INFINITY;
+      st.l[rb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) st.o[db][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    // largest position of any row in the wave (uniform)
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) wave_max = max(wave_max, __shfl_xor(wave_max, off));
+    wave_max = uniform(wave_max);
+    __syncthreads();  // block ids visible
 
-    float m[2], l[2];
-    f32x4_t o[NDB][2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      m[rb] = -INFINITY;
-      l[rb] = 0.f;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-
-    TileRegs<D> regs;
-    load_tile<D>(p, bt_row, hkv, 0, kmax, regs);
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int k0 = kt * kTK;
+    // pipeline: tile j travels in register set j & 1 and LDS buffer j & 1
+    TileSet ra, rb;
+    load_tile<D, kWide>(p, lds, hkv, 0, kmax, ra);
+    if (nkt > 1) load_tile<D, kWide>(p, lds, hkv, kTK, kmax, rb);
+    store_tile<D>(lds, 0, ra);
+    if (nkt > 2) load_tile<D, kWide>(p, lds, hkv, 2 * kTK, kmax, ra);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt += 2) {
+      attend<D>(lds, 0, kt * kTK, p.scale_log2, wave_max, st);
+      if (kt + 1 < nkt) {
+        store_tile<D>(lds, 1, rb);
+        if (kt + 3 < nkt) load_tile<D, kWide>(p, lds, hkv, (kt + 3) * kTK, kmax, rb);
+      }
       __syncthreads();
-      store_tile<D>(lds, regs);
+      if (kt + 1 >= nkt) break;
+      attend<D>(lds, 1, (kt + 1) * kTK, p.scale_log2, wave_max, st);
+      if (kt + 2 < nkt) {
+        store_tile<D>(lds, 0, ra);
+        if (kt + 4 < nkt) load_tile<D, kWide>(p, lds, hkv, (kt + 4) * kTK, kmax, ra);
+      }
       __syncthreads();
-      if (kt + 1 < nkt) load_tile<D>(p, bt_row, hkv, k0 + kTK, kmax, regs);
-      if (k0 > wave_max) continue;  // every row of this wave is causally done
-
-      // ---- S^T = K Q^T : 4 key blocks x 2 row blocks ----
-      f32x4_t s[4][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        s[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-              &lds.k[(kb * 16 + n) * PrefillLds<D>::KST + 32 * i + 8 * g]);
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
-          s[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, qop[0][i]),
-                                                             s[kb][0], 0, 0, 0);
-          s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, qop[1][i]),
-                                                             s[kb][1], 0, 0, 0);
-        }
-      }
-      // ---- mask, online softmax (per row = per lane column n) ----
-      u32x4_t pop[2][2];  // [rb][k-step]: P^T operand, 8 bf16
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int kp = k0 + kb * 16 + 4 * g + j;
-            const float v = kp <= pos[rb] ? s[kb][rb][j] * p.scale_log2 : -INFINITY;
-            s[kb][rb][j] = v;
-            tmax = fmaxf(tmax, v);
-          }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mnew = fmaxf(m[rb], tmax);
-        const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = fast_exp2(m[rb] - muse);
-        m[rb] = mnew;
-        l[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db][rb] *= alpha;
-        float pv[4][4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            pv[kb][j] = fast_exp2(s[kb][rb][j] - muse);
-            l[rb] += pv[kb][j];
-          }
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          pop[rb][st] = u32x4_t{pack_bf16(pv[2 * st][0], pv[2 * st][1]), pack_bf16(pv[2 * st][2], pv[2 * st][3]),
-                                pack_bf16(pv[2 * st + 1][0], pv[2 * st + 1][1]),
-                                pack_bf16(pv[2 * st + 1][2], pv[2 * st + 1][3])};
-        }
-      }
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16_bits* vrow = &lds.vt[(db * 16 + n) * PrefillLds<D>::VST + 32 * st + 4 * g];
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-          o[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, pop[0][st]),
-                                                             o[db][0], 0, 0, 0);
-          o[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, pop[1][st]),
-                                                             o[db][1], 0, 0, 0);
-        }
-      }
     }
 
     // ---- normalise and store: lane holds O^T[d = 16db + 4g + j][row n] ----
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float lt = l[rb];
+      float lt = st.l[rb];
       lt += __shfl_xor(lt, 16);
       lt += __shfl_xor(lt, 32);
-      if (pos[rb] < 0) continue;
+      if (st.pos[rb] < 0) continue;
       const int r = 32 * w + 16 * rb + n;
       const int hl = r / p.TQ, tl = r - hl * p.TQ;
       const float inv = 1.0f / lt;
       bf16_bits* dst = p.out + ((int64_t)(cu0 + t0 + tl) * p.Hq + hkv * p.G + hl) * D + 4 * g;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const u32x2_t v = {pack_bf16(o[db][rb][0] * inv, o[db][rb][1] * inv),
-                           pack_bf16(o[db][rb][2] * inv, o[db][rb][3] * inv)};
+        const u32x2_t v = {pack_bf16(st.o[db][rb][0] * inv, st.o[db][rb][1] * inv),
+                           pack_bf16(st.o[db][rb][2] * inv, st.o[db][rb][3] * inv)};
         *reinterpret_cast<u32x2_t*>(dst + 16 * db) = v;
       }
     }
@@ -385,48 +521,60 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 
 size_t prefill_workspace_size(int num_seqs, int64_t num_q_tokens, int num_q_heads, int num_kv_heads) {
   const int G = num_q_heads / num_kv_heads;
-  return 256 + align256(sizeof(int2) * (size_t)max_prefill_items(num_seqs, num_q_tokens, G));
+  return kHeaderBytes + align256(sizeof(int2) * (size_t)max_prefill_items(num_seqs, num_q_tokens, G));
 }
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   char* ws = static_cast<char*>(a.workspace);
   PrefillParams p;
   p.q = static_cast<const bf16_bits*>(a.q);
-  p.kc = static_cast<const bf16_bits*>(a.k_cache);
-  p.vc = static_cast<const bf16_bits*>(a.v_cache);
+  p.kc = static_cast<const char*>(a.k_cache);
+  p.vc = static_cast<const char*>(a.v_cache);
   p.cu = a.cu_seqlens;
   p.bt = a.block_table;
   p.lens = a.context_lens;
   p.out = static_cast<bf16_bits*>(a.out);
   p.hdr = reinterpret_cast<const uint32_t*>(ws);
   p.counter = reinterpret_cast<uint32_t*>(ws);
-  p.items = reinterpret_cast<const int2*>(ws + 256);
+  p.items = reinterpret_cast<const int2*>(ws + kHeaderBytes);
   p.scale_log2 = a.scale * kLog2e;
   p.Hq = a.num_q_heads;
   p.Hkv = a.num_kv_heads;
   p.G = a.num_q_heads / a.num_kv_heads;
   p.TQ = tokens_per_tile(p.G);
   p.P = a.block_size;
-  p.p_shift = (a.block_size & (a.block_size - 1)) == 0 ? __builtin_ctz((unsigned)a.block_size) : -1;
+  {
+    uint32_t l = 0;
+    while ((1ull << l) < (uint64_t)a.block_size) ++l;
+    p.div_l = l;
+    p.div_m = (uint32_t)((((uint64_t)1 << (32 + l)) + (uint64_t)a.block_size - 1) / (uint64_t)a.block_size -
+                         ((uint64_t)1 << 32));
+  }
+  p.row_bytes = (uint32_t)(a.num_kv_heads * a.head_dim * 2);
   p.N = (int)a.num_blocks;
   p.M = a.max_blocks;
   p.cap = (int)((int64_t)a.max_blocks * a.block_size);
 
   const int64_t item_cap = max_prefill_items(a.num_seqs, a.num_q_tokens, p.G);
-  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.context_lens,
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.cu_seqlens, a.context_lens,
                      a.num_seqs, p.cap, p.TQ, (int)a.num_q_tokens, (int)item_cap,
-                     reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int2*>(ws + 256));
+                     reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int2*>(ws + kHeaderBytes));
   const int64_t max_items = item_cap * p.Hkv;
-  const int64_t cap = (int64_t)device_cu_count() * 2;
+  const int64_t cap = (int64_t)device_cu_count();  // one workgroup (4 waves, 135 KB of LDS) per CU
   const unsigned blocks = (unsigned)(max_items < cap ? max_items : cap);
+  // 32-bit pool offsets when one pool is under 4 GiB
+  const bool wide = a.num_blocks * a.block_size * (int64_t)p.row_bytes >= ((int64_t)1 << 32);
   if (ev0) {
     const hipError_t e = hipEventRecord(ev0, stream);
     if (e != hipSuccess) return e;
   }
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3(blocks), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3(blocks), dim3(kThreads), 0, stream, p);
+  if (a.head_dim == 128) {
+    if (wide) hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((prefill_kernel<128, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  } else {
+    if (wide) hipLaunchKernelGGL((prefill_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    else hipLaunchKernelGGL((prefill_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  }
   if (ev1) {
     const hipError_t e = hipEventRecord(ev1, stream);
     if (e != hipSuccess) return e;

@@ -109,6 +109,9 @@ def prefill(lib, **kw):
     (dict(cu=NUL), INVALID),
     (dict(wsb=8), WORKSPACE),
     (dict(D=32), UNSUPPORTED),
+    (dict(M=16385), UNSUPPORTED),          # block ids of a request must fit in LDS
+    (dict(scale=0.0), INVALID),
+    (dict(scale=-0.5), INVALID),
 ])
 def test_prefill_validation(lib, kw, status):
     assert prefill(lib, **kw) == status
