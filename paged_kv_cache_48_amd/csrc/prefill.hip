@@ -8,17 +8,18 @@
 //     out[row, h] = sum_{j <= pos} softmax_j(scale * q[row, h] . k_j) v_j.
 //
 // Design (MI355X):
-//   * Work item = (request, tile of TQ = 128 / G chunk tokens, KV head).  The
-//     G query heads that share a KV head are packed into the item's 128 rows
+//   * Work item = (request, tile of TQ = 256 / G chunk tokens, KV head).  The
+//     G query heads that share a KV head are packed into the item's 256 rows
 //     (head-major), so each K/V tile fetched from the pool serves all of them.
-//   * A persistent grid of one 4-wave workgroup per CU pulls items from a
+//   * A persistent grid of one 8-wave workgroup per CU (two waves per SIMD,
+//     so one's softmax overlaps the other's matrix products) pulls items from a
 //     queue that a plan kernel sorts by decreasing key count (largest causal
 //     extents first).
 //   * The item's block ids are copied to LDS first, so no gather address
 //     waits on a global load (a wait on one would drain the loads in flight,
 //     which complete in order).
-//   * Per 64-key tile, the 256 threads gather K and V rows through the block
-//     table (16-byte loads); K is stored as is in LDS and V
+//   * Per 64-key tile, four waves gather K rows and four gather V rows through
+//     the block table (16-byte loads); K is stored as is in LDS and V
 //     transposed (d-major) so that both MFMA operands are contiguous LDS
 //     reads.  Two register sets and two LDS buffers keep the loads of the next
 //     two tiles in flight while one tile computes; one barrier per tile.
@@ -41,9 +42,9 @@ namespace pa {
 
 namespace {
 
-constexpr int kRows = 128;     // rows (chunk token x query head) per work item
+constexpr int kRows = 256;     // rows (chunk token x query head) per work item
 constexpr int kTK = 64;        // keys per tile
-constexpr int kThreads = 256;  // 4 waves, 32 rows each
+constexpr int kThreads = 512;  // 8 waves, 32 rows each
 constexpr int kIdCap = kPrefillMaxBlocks;  // block ids an item keeps in LDS
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -180,79 +181,79 @@ struct __attribute__((aligned(16))) PrefillLds {
 };
 
 // One tile's gathers in flight, held in registers between the global loads
-// and the LDS stores: D/32 16-byte pieces of K rows, and 4 keys x one 16-byte
-// piece of V rows, per thread.  ok: bit i (K piece i) / bit 4 + j (V key j)
-// set when that key is visible and its block id valid.
+// and the LDS stores.  Waves 0-3 gather K (D/32 16-byte pieces per thread),
+// waves 4-7 gather V (4 keys x one 16-byte piece per thread).  ok: bit x set
+// when the key of load x is visible and its block id valid.
 struct TileSet {
   u32x4_t k[4];
-  u32x4_t v[4];
   uint32_t ok;
 };
 
 // Gathers of one tile.  Every load is issued unconditionally: a key past kmax
 // or with an out-of-range block id reads the head's slice of row 0 instead --
 // always in bounds -- and is zeroed when the tile is stored.  The block ids of
-// the thread's 8 keys are read from LDS first, all together, so the LDS round
+// the thread's 4 keys are read from LDS first, all together, so the LDS round
 // trip is paid once per tile.
 template <int D, bool kWide>
 __device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillLds<D>& s, int hkv, int k0,
                                           int kmax, TileSet& r) {
   typedef typename std::conditional<kWide, uint64_t, uint32_t>::type O;
-  constexpr int CPR = D / 8;  // 16-byte pieces per head row
-  constexpr int NK = D / 32;  // K pieces per thread
+  constexpr int CPR = D / 8;
+  constexpr int NK = D / 32;
   const int tid = threadIdx.x;
-  const int kq = tid / CPR, dc = tid % CPR;  // V: keys 4 kq .. 4 kq + 3, elements 8 dc .. 8 dc + 7
-  // threads with kq >= 16 exist only for D = 64: whole waves 2 and 3
-  const bool v_wave = uniform(tid >> 6) < 16 * CPR / 64;
-  int pos[NK + 4], off[NK + 4], blk[NK + 4];
+  const bool kw = uniform(tid >> 8) == 0;  // waves 0-3: K, waves 4-7: V
+  const int u = tid & 255;
+  const int kq = u / CPR, dc = u % CPR;    // V: keys 4 kq .. 4 kq + 3, elements 8 dc .. 8 dc + 7
+  // V threads with kq >= 16 exist only for D = 64: whole waves 6 and 7
+  const bool v_wave = !kw && uniform((tid & 255) >> 6) < 16 * CPR / 64;
+  int pos[4], off[4], blk[4];
 #pragma unroll
-  for (int i = 0; i < NK; ++i) pos[i] = k0 + (tid + kThreads * i) / CPR;
+  for (int x = 0; x < 4; ++x) pos[x] = kw ? k0 + (u + 256 * x) / CPR : k0 + 4 * kq + x;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pos[NK + j] = k0 + 4 * kq + j;
-#pragma unroll
-  for (int x = 0; x < NK + 4; ++x) {
+  for (int x = 0; x < 4; ++x) {
     const int jb = div_block(p, pos[x] < kmax ? pos[x] : 0);
     off[x] = pos[x] - jb * p.P;
     blk[x] = s.ids[jb];
   }
   const O head = (O)(hkv * D * 2);
   r.ok = 0;
+  const char* base = kw ? p.kc : p.vc;
 #pragma unroll
-  for (int x = 0; x < NK + 4; ++x) {
+  for (int x = 0; x < 4; ++x) {
+    if (kw && x >= NK) break;
     const bool ok = pos[x] < kmax && blk[x] >= 0 && blk[x] < p.N;
     const O o = (ok ? ((O)blk[x] * (O)p.P + (O)off[x]) * (O)p.row_bytes : (O)0) + head +
-                (O)(16 * (x < NK ? (tid + kThreads * x) % CPR : dc));
-    r.ok |= (ok ? 1u : 0u) << (x < NK ? x : 4 + x - NK);
-    if (x < NK) r.k[x] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.kc + o));
-    else if (v_wave) r.v[x - NK] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.vc + o));
+                (O)(16 * (kw ? (u + 256 * x) % CPR : dc));
+    r.ok |= (ok ? 1u : 0u) << x;
+    if (kw || v_wave) r.k[x] = *reinterpret_cast<const u32x4_t*>(base + o);
   }
 }
 
 template <int D>
 __device__ __forceinline__ void store_tile(PrefillLds<D>& s, int buf, TileSet& r) {
   constexpr int CPR = D / 8;
+  constexpr int NK = D / 32;
   const int tid = threadIdx.x;
-  const bool v_wave = uniform(tid >> 6) < 16 * CPR / 64;
-  const uint32_t all = (1u << (D / 32)) - 1u | (v_wave ? 0xf0u : 0u);
-  if (__builtin_amdgcn_readfirstlane((int)(__ballot(r.ok != all) != 0))) {  // rare: zero the keys that are not ok
+  const bool kw = uniform(tid >> 8) == 0;
+  const int u = tid & 255;
+  const bool v_wave = !kw && uniform((tid & 255) >> 6) < 16 * CPR / 64;
+  const uint32_t all = kw ? (1u << NK) - 1u : (v_wave ? 0xfu : 0u);
+  if (__builtin_amdgcn_readfirstlane((int)(__ballot(r.ok != all) != 0))) {
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-      if (!((r.ok >> i) & 1u)) r.k[i] = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (!((r.ok >> (4 + j)) & 1u)) r.v[j] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int x = 0; x < 4; ++x)
+      if (!((r.ok >> x) & 1u)) r.k[x] = u32x4_t{0u, 0u, 0u, 0u};
   }
+  if (kw) {
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int e = tid + kThreads * i, key = e / CPR, c = e % CPR;
-    *reinterpret_cast<u32x4_t*>(&s.k[buf][key * PrefillLds<D>::KST + 8 * c]) = r.k[i];
-  }
-  if (v_wave) {
-    const int kq = tid / CPR, dc = tid % CPR;
-    // transpose the 4 keys x 8 elements block into 8 rows of 4 keys
+    for (int i = 0; i < NK; ++i) {
+      const int e = u + 256 * i, key = e / CPR, c = e % CPR;
+      *reinterpret_cast<u32x4_t*>(&s.k[buf][key * PrefillLds<D>::KST + 8 * c]) = r.k[i];
+    }
+  } else if (v_wave) {
+    const int kq = u / CPR, dc = u % CPR;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t w0 = r.v[0][i], w1 = r.v[1][i], w2 = r.v[2][i], w3 = r.v[3][i];
+      const uint32_t w0 = r.k[0][i], w1 = r.k[1][i], w2 = r.k[2][i], w3 = r.k[3][i];
       const u32x2_t lo = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
       const u32x2_t hi = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
       const int d = dc * 8 + 2 * i;
@@ -284,14 +285,6 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
   constexpr int NI = RowState<D>::NI, NDB = RowState<D>::NDB;
   const int lane = lane_id();
   const int n = lane & 15, g = lane >> 4;
-  // all K operands of the tile are read before the products start, so the
-  // LDS latency is paid once
-  u32x4_t ka[4][NI];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      ka[kb][i] = *reinterpret_cast<const u32x4_t*>(&s.k[buf][(kb * 16 + n) * PrefillLds<D>::KST + 32 * i + 8 * g]);
   f32x4_t sc[4][2];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -299,7 +292,7 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
     sc[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, ka[kb][i]);
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&s.k[buf][(kb * 16 + n) * PrefillLds<D>::KST + 32 * i + 8 * g]));
       sc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, st.q[0][i]), sc[kb][0], 0,
                                                           0, 0);
       sc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, st.q[1][i]), sc[kb][1], 0,
@@ -307,8 +300,7 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
     }
   }
   // scheduling: every K operand read first, then the products
-  __builtin_amdgcn_sched_group_barrier(0x100, 4 * NI, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 8 * NI, 0);
+
   u32x4_t pop[2][2];  // [rb][k-step]: P^T operand, 8 bf16
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -376,8 +368,7 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
                                                             0, 0, 0);
     }
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 4 * NDB, 1);
-  __builtin_amdgcn_sched_group_barrier(0x008, 4 * NDB, 1);
+
 }
 
 template <int D>
@@ -388,8 +379,8 @@ __device__ __forceinline__ void attend(const PrefillLds<D>& s, int buf, int k0, 
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel: one persistent workgroup of 4 waves per CU pulls items.
-// An item is (request, tile of TQ chunk tokens, KV head) with 128 rows
+// Prefill kernel: one persistent workgroup of 8 waves per CU pulls items.
+// An item is (request, tile of TQ chunk tokens, KV head) with 256 rows
 // (TQ tokens x G query heads, head-major); wave w owns rows 32w .. 32w+31.
 // Key tiles of 64 go through two LDS buffers; the loads of the next two tiles
 // are in flight while one tile computes, and the item's block ids sit in LDS
@@ -560,7 +551,7 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0,
                      a.num_seqs, p.cap, p.TQ, (int)a.num_q_tokens, (int)item_cap,
                      reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int2*>(ws + kHeaderBytes));
   const int64_t max_items = item_cap * p.Hkv;
-  const int64_t cap = (int64_t)device_cu_count();  // one workgroup (4 waves, 135 KB of LDS) per CU
+  const int64_t cap = (int64_t)device_cu_count();  // one workgroup (8 waves, 135 KB of LDS) per CU
   const unsigned blocks = (unsigned)(max_items < cap ? max_items : cap);
   // 32-bit pool offsets when one pool is under 4 GiB
   const bool wide = a.num_blocks * a.block_size * (int64_t)p.row_bytes >= ((int64_t)1 << 32);
