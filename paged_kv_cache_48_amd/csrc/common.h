@@ -38,6 +38,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// Two floats -> two packed IEEE half floats (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const f32x2_t x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2_t));
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
 // ---------------------------------------------------------------------------
 // DPP lane permutations inside a 16-lane row (gfx9 dpp_ctrl encodings).
 // ---------------------------------------------------------------------------

@@ -27,8 +27,11 @@
 //     probabilities never leave registers and the outputs need no cross-lane
 //     reduction.  Online softmax in base 2 (running max and sum).
 //   * Items of a request with one partition write the output directly; the
-//     others write (max, sum, unnormalised output) partials that the reduce
-//     kernel merges:  m = max_i m_i,  out = sum_i 2^(m_i-m) o_i / sum_i 2^(m_i-m) l_i.
+//     others write (max, sum, output) partials that the reduce kernel merges:
+//     m = max_i m_i,  out = sum_i 2^(m_i-m) o_i / sum_i 2^(m_i-m) l_i, where o_i
+//     is unnormalised (fp32 requests) or stored as l_i * (o_i / l_i) with
+//     o_i / l_i in fp16 (bf16 requests: half the partial bytes, whose writes
+//     interleaved with the KV reads are costly).
 //   * Tokens past the partition end never load: tail slots of a block may hold
 //     anything (even NaN).  Block ids outside [0, N) are never dereferenced
 //     (their rows read as zeros, so the result is unspecified but safe).
@@ -651,9 +654,20 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
         }
       } else {
         const int64_t slot = ((int64_t)it.b * prm.Hq + h) * prm.max_parts + it.part;
-        float* dst = prm.o + slot * D + 4 * g;
+        if constexpr (Gm::kBf16) {
+          // bf16 requests: the partial output normalised by its sum, as fp16
+          // (half the bytes of fp32; its rounding is far below bf16's)
+          const float inv = 1.0f / l;
+          uint16_t* dst = reinterpret_cast<uint16_t*>(prm.o) + slot * D + 4 * g;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db) = o[db];
+          for (int db = 0; db < NDB; ++db)
+            *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
+                u32x2_t{pack_f16(o[db][0] * inv, o[db][1] * inv), pack_f16(o[db][2] * inv, o[db][3] * inv)};
+        } else {
+          float* dst = prm.o + slot * D + 4 * g;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db) = o[db];
+        }
         if (g == 0) {
           prm.ml[slot * 2 + 0] = m;
           prm.ml[slot * 2 + 1] = l;
@@ -683,24 +697,38 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
 // per round so that many loads are in flight.  Lane l owns output elements
 // D/64 * l .. D/64 * l + D/64 - 1 (one vector load per partition).
 // ---------------------------------------------------------------------------
-template <int PER>
+// Partial outputs: fp32, unnormalised, for fp32 requests; fp16 normalised by
+// the partition's sum for bf16 requests.  Lane l reads elements PER*l ..
+// PER*l + PER-1 of a partition's row with one load.
+template <bool kHalf, int PER>
 struct RowPiece;
 template <>
-struct RowPiece<1> {
+struct RowPiece<false, 1> {
   typedef float type;
   static __device__ __forceinline__ float get(const type& v, int) { return v; }
 };
 template <>
-struct RowPiece<2> {
+struct RowPiece<false, 2> {
   typedef f32x2_t type;
   static __device__ __forceinline__ float get(const type& v, int j) { return v[j]; }
+};
+template <>
+struct RowPiece<true, 1> {
+  typedef uint16_t type;
+  static __device__ __forceinline__ float get(const type& v, int) { return f16_lo(v); }
+};
+template <>
+struct RowPiece<true, 2> {
+  typedef uint32_t type;
+  static __device__ __forceinline__ float get(const type& v, int j) { return j ? f16_hi(v) : f16_lo(v); }
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams prm) {
   constexpr int PER = D / 64;
   constexpr int U = 16;  // partitions per round
-  typedef RowPiece<PER> RP;
+  constexpr bool kHalf = sizeof(T) == 2;
+  typedef RowPiece<kHalf, PER> RP;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6), b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   if (h >= prm.Hq) return;
@@ -731,23 +759,27 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams prm) {
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
   float den = 0.f;
+  const typename RP::type* rows =
+      kHalf ? reinterpret_cast<const typename RP::type*>(reinterpret_cast<const uint16_t*>(prm.o) + slot0 * D)
+            : reinterpret_cast<const typename RP::type*>(prm.o + slot0 * D);
   for (int c0 = 0; c0 < np; c0 += 64) {  // chunks of 64 partitions
     const int nc = min(64, np - c0);
     const f32x2_t mine = c0 == 0 ? ml0 : ml[c0 + min(lane, nc - 1)];
     const float w = lane < nc ? fast_exp2(mine[0] - mx) : 0.f;
     float lw = w * mine[1];
+    // weight of a partial row: 2^(m_i - m) for unnormalised rows, times l_i for normalised ones
+    const float wr = kHalf ? lw : w;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
     den += lw;
-    const typename RP::type* src =
-        reinterpret_cast<const typename RP::type*>(prm.o + (slot0 + c0) * D) + lane;
+    const typename RP::type* src = rows + (size_t)c0 * (D / PER) + lane;
     for (int i = 0; i < nc; i += U) {
       typename RP::type v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) v[u] = src[(size_t)min(i + u, nc - 1) * (D / PER)];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float wu = i + u < nc ? __shfl(w, i + u) : 0.f;
+        const float wu = i + u < nc ? __shfl(wr, i + u) : 0.f;
 #pragma unroll
         for (int j = 0; j < PER; ++j) acc[j] = fmaf(wu, RP::get(v[u], j), acc[j]);
       }

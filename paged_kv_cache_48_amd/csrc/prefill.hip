@@ -180,6 +180,12 @@ struct __attribute__((aligned(16))) PrefillLds {
   int32_t ids[kIdCap];
 };
 
+// Column (element) of the 4-key group kq in row d of V^T.  The group index is
+// XORed with 2 * ((d / 32) % 4): the transposing stores (rows 8 apart across
+// a wave's lanes) then fall in distinct banks, and a P.V operand read (16
+// rows of one 32-row block) keeps its conflict-free pattern, only permuted.
+__device__ __forceinline__ int vt_col(int d, int kq) { return 4 * (kq ^ (2 * ((d >> 5) & 3))); }
+
 // One tile's gathers in flight, held in registers between the global loads
 // and the LDS stores.  Waves 0-3 gather K (D/32 16-byte pieces per thread),
 // waves 4-7 gather V (4 keys x one 16-byte piece per thread).  ok: bit x set
@@ -220,7 +226,7 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillL
   const char* base = kw ? p.kc : p.vc;
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    if (kw && x >= NK) break;
+    if (kw && x >= NK) continue;  // D = 64: two K pieces per thread
     const bool ok = pos[x] < kmax && blk[x] >= 0 && blk[x] < p.N;
     const O o = (ok ? ((O)blk[x] * (O)p.P + (O)off[x]) * (O)p.row_bytes : (O)0) + head +
                 (O)(16 * (kw ? (u + 256 * x) % CPR : dc));
@@ -257,8 +263,8 @@ __device__ __forceinline__ void store_tile(PrefillLds<D>& s, int buf, TileSet& r
       const u32x2_t lo = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
       const u32x2_t hi = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
       const int d = dc * 8 + 2 * i;
-      *reinterpret_cast<u32x2_t*>(&s.vt[buf][d * PrefillLds<D>::VST + 4 * kq]) = lo;
-      *reinterpret_cast<u32x2_t*>(&s.vt[buf][(d + 1) * PrefillLds<D>::VST + 4 * kq]) = hi;
+      *reinterpret_cast<u32x2_t*>(&s.vt[buf][d * PrefillLds<D>::VST + vt_col(d, kq)]) = lo;
+      *reinterpret_cast<u32x2_t*>(&s.vt[buf][(d + 1) * PrefillLds<D>::VST + vt_col(d + 1, kq)]) = hi;
     }
   }
 }
@@ -352,9 +358,10 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16_bits* vrow = &s.vt[buf][(db * 16 + n) * PrefillLds<D>::VST + 32 * ks + 4 * g];
-      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+      const int d = db * 16 + n;
+      const bf16_bits* vrow = &s.vt[buf][d * PrefillLds<D>::VST];
+      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + vt_col(d, 8 * ks + g));
+      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + vt_col(d, 8 * ks + 4 + g));
       va[db][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     }
 #pragma unroll
