@@ -174,17 +174,21 @@ __device__ __forceinline__ int div_block(const PrefillParams& p, int pos) {
 template <int D>
 struct __attribute__((aligned(16))) PrefillLds {
   static constexpr int KST = D + 8;    // K row stride (elements)
-  static constexpr int VST = kTK + 4;  // V^T row stride (elements)
+  static constexpr int VST = kTK + 8;  // V^T row stride (elements; rows 16-byte aligned)
   bf16_bits k[2][kTK * KST];
   bf16_bits vt[2][D * VST];
   int32_t ids[kIdCap];
 };
 
-// Column (element) of the 4-key group kq in row d of V^T.  The group index is
-// XORed with 2 * ((d / 32) % 4): the transposing stores (rows 8 apart across
-// a wave's lanes) then fall in distinct banks, and a P.V operand read (16
-// rows of one 32-row block) keeps its conflict-free pattern, only permuted.
-__device__ __forceinline__ int vt_col(int d, int kq) { return 4 * (kq ^ (2 * ((d >> 5) & 3))); }
+// V^T row d holds the tile's 64 keys in 8-byte units of 4 keys.  The P.V
+// operand of lane (n, g) for k-step ks is keys 32 ks + 4 g + (0..3) followed by
+// 32 ks + 16 + 4 g + (0..3), so those two units are placed side by side (unit
+// index u = 2 (4 ks + g) + half) and the operand is one 16-byte read.  The
+// unit index is XORed with an even function of d, so that the transposing
+// stores (rows 8 apart across a wave's lanes) spread over the banks and the
+// operand reads stay conflict-free.
+__device__ __forceinline__ int vt_unit(int kq) { return 2 * (4 * (kq >> 3) + (kq & 3)) + ((kq >> 2) & 1); }
+__device__ __forceinline__ int vt_col(int d, int u) { return 4 * (u ^ (2 * ((d >> 4) & 7))); }
 
 // One tile's gathers in flight, held in registers between the global loads
 // and the LDS stores.  Waves 0-3 gather K (D/32 16-byte pieces per thread),
@@ -263,8 +267,8 @@ __device__ __forceinline__ void store_tile(PrefillLds<D>& s, int buf, TileSet& r
       const u32x2_t lo = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
       const u32x2_t hi = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
       const int d = dc * 8 + 2 * i;
-      *reinterpret_cast<u32x2_t*>(&s.vt[buf][d * PrefillLds<D>::VST + vt_col(d, kq)]) = lo;
-      *reinterpret_cast<u32x2_t*>(&s.vt[buf][(d + 1) * PrefillLds<D>::VST + vt_col(d + 1, kq)]) = hi;
+      *reinterpret_cast<u32x2_t*>(&s.vt[buf][d * PrefillLds<D>::VST + vt_col(d, vt_unit(kq))]) = lo;
+      *reinterpret_cast<u32x2_t*>(&s.vt[buf][(d + 1) * PrefillLds<D>::VST + vt_col(d + 1, vt_unit(kq))]) = hi;
     }
   }
 }
@@ -359,10 +363,7 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int d = db * 16 + n;
-      const bf16_bits* vrow = &s.vt[buf][d * PrefillLds<D>::VST];
-      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + vt_col(d, 8 * ks + g));
-      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + vt_col(d, 8 * ks + 4 + g));
-      va[db][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      va[db][ks] = *reinterpret_cast<const u32x4_t*>(&s.vt[buf][d * PrefillLds<D>::VST + vt_col(d, 2 * (4 * ks + g))]);
     }
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
