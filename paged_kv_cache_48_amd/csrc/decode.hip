@@ -29,9 +29,10 @@
 //   * Items of a request with one partition write the output directly; the
 //     others write (max, sum, output) partials that the reduce kernel merges:
 //     m = max_i m_i,  out = sum_i 2^(m_i-m) o_i / sum_i 2^(m_i-m) l_i, where o_i
-//     is unnormalised (fp32 requests) or stored as l_i * (o_i / l_i) with
-//     o_i / l_i in fp16 (bf16 requests: half the partial bytes, whose writes
-//     interleaved with the KV reads are costly).
+//     is unnormalised (fp32 requests) or stored as l_i * r_i * (o_i / l_i / r_i)
+//     with the last factor in fp16 and r_i a power of two that keeps it in
+//     range (bf16 requests: half the partial bytes, whose writes interleaved
+//     with the KV reads are costly).
 //   * Tokens past the partition end never load: tail slots of a block may hold
 //     anything (even NaN).  Block ids outside [0, N) are never dereferenced
 //     (their rows read as zeros, so the result is unspecified but safe).
@@ -77,7 +78,7 @@ DecodeLayout decode_layout(int B, int Hq, int D, int P, int M) {
   L.items = off;
   off = align256(off + sizeof(i32x4_t) * (size_t)B * L.max_parts);
   L.ml = off;
-  off = align256(off + sizeof(float) * 2 * (size_t)B * Hq * L.max_parts);
+  off = align256(off + sizeof(float) * 4 * (size_t)B * Hq * L.max_parts);  // (max, sum, scale, -)
   L.o = off;
   off = align256(off + sizeof(float) * (size_t)B * Hq * L.max_parts * D);
   L.total = off;
@@ -654,24 +655,37 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
         }
       } else {
         const int64_t slot = ((int64_t)it.b * prm.Hq + h) * prm.max_parts + it.part;
+        float rs = 1.0f;  // the stored row is o / l / rs (bf16) or o (fp32)
         if constexpr (Gm::kBf16) {
           // bf16 requests: the partial output normalised by its sum, as fp16
-          // (half the bytes of fp32; its rounding is far below bf16's)
+          // (half the bytes of fp32; its rounding is far below bf16's).  A
+          // normalised row is a weighted mean of value rows, so it can exceed
+          // the fp16 range only if the values do; then it is scaled down by a
+          // power of two, kept beside (max, sum), so it stays below 2^15.
           const float inv = 1.0f / l;
+          float amax = 0.f;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(o[db][j]));
+          amax = max_over_rows(amax * inv);  // the head's whole row (lanes n, n+16, n+32, n+48)
+          if (amax >= 32768.0f) {
+            int ex;
+            frexpf(amax, &ex);  // amax < 2^ex
+            rs = ldexpf(1.0f, ex - 15);
+          }
+          const float sc = inv / rs;
           uint16_t* dst = reinterpret_cast<uint16_t*>(prm.o) + slot * D + 4 * g;
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
             *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
-                u32x2_t{pack_f16(o[db][0] * inv, o[db][1] * inv), pack_f16(o[db][2] * inv, o[db][3] * inv)};
+                u32x2_t{pack_f16(o[db][0] * sc, o[db][1] * sc), pack_f16(o[db][2] * sc, o[db][3] * sc)};
         } else {
           float* dst = prm.o + slot * D + 4 * g;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db) = o[db];
         }
-        if (g == 0) {
-          prm.ml[slot * 2 + 0] = m;
-          prm.ml[slot * 2 + 1] = l;
-        }
+        if (g == 0) *reinterpret_cast<f32x4_t*>(prm.ml + slot * 4) = f32x4_t{m, l, rs, 0.f};
       }
     }
     if (!has_next) break;
@@ -733,11 +747,11 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams prm) {
   const int lane = threadIdx.x & 63;
   if (h >= prm.Hq) return;
   const int64_t slot0 = ((int64_t)b * prm.Hq + h) * prm.max_parts;
-  const f32x2_t* ml = reinterpret_cast<const f32x2_t*>(prm.ml) + slot0;
-  // the (max, sum) pairs are read before the length is known (slots past the
-  // request's partition count exist in the workspace and are masked below),
-  // so the two loads overlap
-  const f32x2_t ml0 = ml[min(lane, prm.max_parts - 1)];
+  const f32x4_t* ml = reinterpret_cast<const f32x4_t*>(prm.ml) + slot0;
+  // the (max, sum, scale) entries are read before the length is known (slots
+  // past the request's partition count exist in the workspace and are masked
+  // below), so the two loads overlap
+  const f32x4_t ml0 = ml[min(lane, prm.max_parts - 1)];
   const int L = clamp_len(prm.lens[b], prm.cap);
   const int np = (L + kPartTokens - 1) / kPartTokens;
   if (np == 1) return;
@@ -764,11 +778,12 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams prm) {
             : reinterpret_cast<const typename RP::type*>(prm.o + slot0 * D);
   for (int c0 = 0; c0 < np; c0 += 64) {  // chunks of 64 partitions
     const int nc = min(64, np - c0);
-    const f32x2_t mine = c0 == 0 ? ml0 : ml[c0 + min(lane, nc - 1)];
+    const f32x4_t mine = c0 == 0 ? ml0 : ml[c0 + min(lane, nc - 1)];
     const float w = lane < nc ? fast_exp2(mine[0] - mx) : 0.f;
     float lw = w * mine[1];
-    // weight of a partial row: 2^(m_i - m) for unnormalised rows, times l_i for normalised ones
-    const float wr = kHalf ? lw : w;
+    // weight of a partial row: 2^(m_i - m) for unnormalised rows, times l_i and
+    // the row's scale for normalised ones
+    const float wr = kHalf ? lw * mine[2] : w;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
     den += lw;

@@ -180,6 +180,36 @@ def test_decode_empty_context_gives_zeros_and_repeat_is_deterministic():
     assert np.array_equal(to_host_bits(out2), o)
 
 
+def _scale_bf16(bits: np.ndarray, pow2: int) -> np.ndarray:
+    """bf16 bits times 2**pow2 (exact while in range)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** pow2)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_decode_values_beyond_fp16_range():
+    """bf16 values far above 65504 (up to ~2^24 here), with the magnitude
+    changing from partition to partition inside a request: the partial results
+    of several-partition requests must neither overflow nor be weighted wrongly.
+    Attention is homogeneous in V, so each request is compared at the usual bf16
+    tolerance after dividing both sides by its largest power-of-two factor."""
+    lens = (300, 1025, 700, 40, 512)
+    pow2 = ([22, 22], [20, 17, 20, 0, 16], [0, 0, 0], [24], [17, 16])  # per 256-token partition
+    c = small(P=16, Hq=8, Hkv=2, lens=lens, seed=25)
+    row = 0
+    for L, ps in zip(lens, pow2):
+        for j, e in enumerate(ps):
+            lo, hi = row + 256 * j, row + min(L, 256 * (j + 1))
+            c.v_tok[lo:hi] = _scale_bf16(c.v_tok[lo:hi], e)
+        row += L
+    d = DevCase(c)
+    out = d.decode()
+    ref = decode_ref(c)
+    assert np.all(np.isfinite(ref)) and np.abs(ref).max() > 1e5
+    S = np.array([2.0 ** max(ps) for ps in pow2])
+    got = out.float() / torch.as_tensor(S, dtype=torch.float32, device=DEV)[:, None, None]
+    assert_close(got, ref / S[:, None, None], "bf16", "large values")
+
+
 # ----------------------------------------------------------------------------
 # prefill
 # ----------------------------------------------------------------------------
