@@ -10,11 +10,13 @@
 //   * Split context.  Each request is cut into partitions of kPartTokens tokens
 //     (a count that depends on L_b only).  A (request, partition, KV head, group
 //     of up to 4 query heads) is one work item; a single wave64 computes it.
-//   * Work queue.  A tiny plan kernel lists the (request, partition) items,
-//     full partitions first and short tail partitions last, and zeroes the
-//     queue counters; a persistent grid of exactly the resident waves takes
-//     one item each to start, then pulls items with one atomic each from
-//     per-XCD queues, stealing from the other queues at the end.
+//   * Work queue.  The (request, partition) items are listed full partitions
+//     first and short tail partitions last: for batches of up to
+//     kSelfPlanMax requests every workgroup derives the list itself in LDS
+//     from the lengths, otherwise a tiny plan kernel writes it.  A persistent
+//     grid of exactly the resident waves takes one item each to start, then
+//     pulls items with one atomic each from per-XCD queues, stealing from the
+//     other queues at the end.
 //   * Coalesced gathers.  Per 16-token tile each quarter-wave reads whole
 //     contiguous row slices of one KV head (16-byte loads); the tile goes
 //     through a wave-private LDS region, K row-major and V transposed, which
@@ -37,7 +39,10 @@
 //     anything (even NaN).  Block ids outside [0, N) are never dereferenced
 //     (their rows read as zeros, so the result is unspecified but safe).
 #include <math.h>
+#include <unistd.h>
 
+#include <atomic>
+#include <chrono>
 #include <type_traits>
 
 #include "common.h"
@@ -55,14 +60,21 @@ constexpr int kDynamicRounds = 1;     // whole rounds of full partitions handed 
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Work-queue header in the workspace: kQueues counters, each on its own
-// 128-byte line, and the item count in the last word.
+// Work-queue header in the workspace: kQueues 64-bit counters, each on its
+// own 128-byte line, and the plan kernel's counts in the last words.  A
+// counter holds a tag in bits 24..63 and the count in bits 0..23: the tag
+// names the launch that reset it (zero when the plan kernel did), so a claim
+// that lands on a counter left by an earlier call, or on whatever else the
+// workspace held, is recognised as such and retried.
 constexpr int kQueues = 8;  // one per XCD of the MI355X
-constexpr int kCounterStride = 32;  // uint32 words between counters
+constexpr int kCounterStride = 16;  // uint64 words between counters
 constexpr int kHeaderBytes = 1024;
 constexpr int kItemCountWord = kHeaderBytes / 4 - 1;
 constexpr int kFullCountWord = kHeaderBytes / 4 - 2;  // items that are full partitions
 constexpr int kQueueCountWord = kHeaderBytes / 4 - 3;  // queues in use
+constexpr int kCountBits = 24;
+constexpr int64_t kMaxQueueItems = (int64_t)1 << kCountBits;  // claims per counter
+constexpr int64_t kMaxWaves = 256 * 32;  // resident waves of a launch, at most
 
 struct DecodeLayout {
   int64_t max_parts;
@@ -130,7 +142,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
     hdr[kFullCountWord] = (uint32_t)cnt[0];
     hdr[kQueueCountWord] = tiles >= 4ull * (unsigned long long)run ? 1u : (uint32_t)kQueues;
   }
-  if (tid < kQueues) hdr[tid * kCounterStride] = 0u;
+  if (tid < kQueues) reinterpret_cast<unsigned long long*>(hdr)[tid * kCounterStride] = 0ull;
   __syncthreads();
   for (int b = tid; b < B; b += kPlanThreads) {
     const int L = clamp_len(lens[b], cap);
@@ -193,7 +205,7 @@ struct DecodeParams {
   const int32_t* lens;
   void* out;
   const uint32_t* hdr;
-  uint32_t* counter;
+  unsigned long long* counter;
   const i32x4_t* items;
   float* ml;
   float* o;
@@ -201,6 +213,9 @@ struct DecodeParams {
   int Hq, Hkv, G, n_hg, P, p_shift, N, M, cap, max_parts;
   int dyn_rounds;  // full rounds of full partitions left to the queues
   int nq;          // queues in use (at most kQueues); 0: as the plan chose
+  int B;
+  int self_plan;   // 1: the workgroups plan (B <= kSelfPlanMax); 0: the plan kernel did
+  unsigned long long salt;  // per call; mixed into the counters' tag
 };
 
 // One work item, wave-uniform (scalar registers).
@@ -396,23 +411,215 @@ __device__ __forceinline__ void wave_lds_sync() {
 // accumulators is rare; the result does not depend on the reference.
 constexpr float kRescaleSlack = 8.0f;
 
+__device__ __forceinline__ unsigned long long uniform64(unsigned long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// The launch's dispatch id: the packet's index on its hardware queue (every
+// launch, graph replays included, gets a new one).
+extern "C" __device__ unsigned long long llvm_amdgcn_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+// Tag of this launch's queue counters: dispatch id, queue address and the
+// host's per-call salt, mixed with the splitmix64 finaliser and cut to the
+// tag's 40 bits; never zero (zero marks counters the plan kernel reset).
+__device__ __forceinline__ unsigned long long launch_tag(unsigned long long salt) {
+  unsigned long long x = llvm_amdgcn_dispatch_id() * 0x9E3779B97F4A7C15ull;
+  x ^= (unsigned long long)(uintptr_t)__builtin_amdgcn_queue_ptr() ^ salt;
+  x ^= x >> 30;
+  x *= 0xBF58476D1CE4E5B9ull;
+  x ^= x >> 27;
+  x *= 0x94D049BB133111EBull;
+  x ^= x >> 31;
+  x &= (1ull << (64 - kCountBits)) - 1ull;
+  return x ? x : 1ull;
+}
+
+// Sleeps a claim may wait for workgroup 0 to reset the counters (a few
+// atomics of a resident workgroup, so a handful in practice; the bound only
+// guarantees that every wave exits).
+constexpr int kMaxSpins = 1 << 20;
+
 // Takes the next dynamically scheduled item: with nq queues, queue x holds
 // flat items f = first_dyn + nq * c + x; a wave starts at its home queue (its
 // XCD's, when there are eight) and moves to the next one when that is empty.
-// Returns 0xffffffff when all queues are empty.
-__device__ __forceinline__ uint32_t claim(const DecodeParams& prm, uint32_t nq, uint32_t home, uint32_t& queue,
-                                          uint32_t first_dyn, uint32_t total) {
+// A self-planned launch checks the counter's tag: a counter not yet reset
+// for this launch is tried again after a short sleep.  Returns 0xffffffff
+// when all queues are empty.
+__device__ __forceinline__ uint32_t claim(const DecodeParams& prm, unsigned long long tag, uint32_t nq, uint32_t home,
+                                          uint32_t& queue, uint32_t first_dyn, uint32_t total) {
   const int lane = lane_id();
+  int spins = 0;
   while (queue < nq) {
     const uint32_t x = (home + queue) % nq;
-    uint32_t c = 0;
-    if (lane == 0) c = atomicAdd(prm.counter + x * kCounterStride, 1u);
-    c = __builtin_amdgcn_readfirstlane(c);
-    const uint32_t f = first_dyn + nq * c + x;
-    if (f < total) return f;
+    unsigned long long old = 0;
+    if (lane == 0) old = atomicAdd(prm.counter + x * kCounterStride, 1ull);
+    old = uniform64(old);
+    if (prm.self_plan && (old >> kCountBits) != tag) {
+      if (++spins < kMaxSpins) __builtin_amdgcn_s_sleep(8);
+      else ++queue;
+      continue;
+    }
+    const unsigned long long c = prm.self_plan ? old & (kMaxQueueItems - 1) : old;
+    const unsigned long long f = first_dyn + nq * c + x;
+    if (f < total) return (uint32_t)f;
     ++queue;
   }
   return 0xffffffffu;
+}
+
+// ---------------------------------------------------------------------------
+// In-kernel plan (batches of at most kSelfPlanMax requests).  Each workgroup
+// derives the item list from the lengths, in LDS: full partitions first,
+// request by request, then the tail partitions by tile count (16 .. 1),
+// requests in increasing order within a count.  The list is a function of
+// the lengths alone, so all workgroups agree on it without communicating.
+// List entry i < F (the full-partition count) is full partition i - pf[b]
+// of the request b with pf[b] <= i < pf[b + 1]; entry F + j is the tail of
+// request tail_b[j].
+// ---------------------------------------------------------------------------
+constexpr int kSelfPlanMax = 1024;
+constexpr int kPlanChunks = kSelfPlanMax / 64;
+
+struct PlanLds {
+  int pf[kSelfPlanMax + 1];                // first list entry of request b's full partitions; pf[B] = F
+  int len[kSelfPlanMax];                   // clamped lengths
+  uint16_t tail_b[kSelfPlanMax];           // requests with a tail partition, in list order
+  uint16_t rk[kSelfPlanMax];               // tile count of the tail | rank among equal counts of its chunk << 5
+  int pre[kPlanChunks][kTileBuckets + 1];  // per 64-request chunk: counts, then exclusive prefixes
+  int bstart[kTileBuckets + 1];            // first tail position of each tile count
+  int nfull, nitems, nq;
+};
+
+// Inclusive prefix sums with DPP row shifts (lanes shifted in from outside
+// the 16-lane row read zero): inside each row, then across the wave.
+template <int CTRL>
+__device__ __forceinline__ int dpp_zero(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+__device__ __forceinline__ int row16_incl_scan(int v) {
+  v += dpp_zero<0x111>(v);  // row_shr:1
+  v += dpp_zero<0x112>(v);  // row_shr:2
+  v += dpp_zero<0x114>(v);  // row_shr:4
+  v += dpp_zero<0x118>(v);  // row_shr:8
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v = row16_incl_scan(v);
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane_id() >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// Every thread of the workgroup takes part (three barriers).
+__device__ void self_plan(const DecodeParams& prm, PlanLds* pl) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int B = prm.B;
+  const int nc = (B + 63) >> 6;
+  // 1: per chunk of 64 requests: lengths, the full-partition prefix inside
+  // the chunk, each tail's rank among the chunk's tails of equal tile count,
+  // and the chunk's counts
+  for (int c = wave; c < nc; c += nw) {
+    const int b = 64 * c + lane;
+    const int L = b < B ? clamp_len(prm.lens[b], prm.cap) : 0;
+    const int full = L / kPartTokens, rest = L - full * kPartTokens;
+    const int bk = rest ? (rest + kTile - 1) / kTile : 0;
+    const int incl = wave_incl_scan(full);
+    // tails of k tiles counted in 8-bit field (k - 1) % 4 of word (k - 1) / 4
+    // (at most 64 per field): one prefix sum per word gives every lane the
+    // number of lower lanes with its tile count, and lane 63 the totals
+    const int kb = bk - 1;
+    int sc[4], tw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      sc[w] = wave_incl_scan(bk != 0 && (kb >> 2) == w ? 1 << (8 * (kb & 3)) : 0);
+      tw[w] = __builtin_amdgcn_readlane(sc[w], 63);
+    }
+    const int mine = kb < 4 ? sc[0] : kb < 8 ? sc[1] : kb < 12 ? sc[2] : sc[3];
+    const int rank = bk ? ((mine >> (8 * (kb & 3))) & 255) - 1 : 0;
+    // lane k (1..16) takes the chunk's count of tails of k tiles, lane 0 its full partitions
+    const int lk = lane - 1;
+    const int word = lk < 4 ? tw[0] : lk < 8 ? tw[1] : lk < 12 ? tw[2] : tw[3];
+    int cnt = (word >> (8 * (lk & 3))) & 255;
+    if (lane == 0) cnt = __builtin_amdgcn_readlane(incl, 63);
+    if (b < B) {
+      pl->len[b] = L;
+      pl->pf[b] = incl - full;
+      pl->rk[b] = (uint16_t)(bk | rank << 5);
+    }
+    if (lane <= kTileBuckets) pl->pre[c][lane] = cnt;
+  }
+  __syncthreads();
+  // 2: exclusive prefixes over the chunks (lane c < 16: chunk c), totals,
+  // the first tail position of each tile count, and the queue count (one
+  // queue when items average at least 4 tiles: 16 per full partition, k
+  // per tail of k tiles)
+  if (wave == 0) {
+    int tot[kTileBuckets + 1], v[kTileBuckets + 1];
+#pragma unroll
+    for (int k = 0; k <= kTileBuckets; ++k) v[k] = lane < nc ? pl->pre[lane][k] : 0;
+#pragma unroll
+    for (int k = 0; k <= kTileBuckets; ++k) {
+      const int incl = row16_incl_scan(v[k]);
+      if (lane < nc) pl->pre[lane][k] = incl - v[k];
+      tot[k] = __builtin_amdgcn_readlane(incl, kPlanChunks - 1);
+    }
+    if (lane == 0) {
+      int run = 0;
+      long long tiles = (long long)kTileBuckets * tot[0];
+#pragma unroll
+      for (int k = kTileBuckets; k >= 1; --k) {
+        pl->bstart[k] = run;
+        run += tot[k];
+        tiles += (long long)k * tot[k];
+      }
+      pl->nfull = tot[0];
+      pl->nitems = tot[0] + run;
+      pl->nq = tiles >= 4ll * (tot[0] + run) ? 1 : kQueues;
+      pl->pf[B] = tot[0];
+    }
+  }
+  __syncthreads();
+  // 3: global full-partition offsets and the tail order
+  for (int c = wave; c < nc; c += nw) {
+    const int b = 64 * c + lane;
+    if (b < B) {
+      const int rk = pl->rk[b];
+      const int bk = rk & 31;
+      pl->pf[b] += pl->pre[c][0];
+      if (bk) pl->tail_b[pl->bstart[bk] + pl->pre[c][bk] + (rk >> 5)] = (uint16_t)b;
+    }
+  }
+  __syncthreads();
+}
+
+// Descriptor {request, partition, length, partitions} of list entry i.
+__device__ __forceinline__ i32x4_t plan_desc(const PlanLds* pl, int B, int nfull, int i) {
+  int b, part;
+  if (i < nfull) {
+    int lo = 0, hi = B;  // pf[lo] <= i < pf[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pl->pf[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    b = lo;
+    part = i - pl->pf[lo];
+  } else {
+    b = pl->tail_b[i - nfull];
+    part = pl->len[b] / kPartTokens;
+  }
+  const int L = pl->len[b];
+  return i32x4_t{b, part, L, (L + kPartTokens - 1) / kPartTokens};
+}
+
+__device__ __forceinline__ i32x4_t item_desc(const DecodeParams& prm, const PlanLds* pl, uint32_t nfull, uint32_t i) {
+  if (prm.self_plan) return plan_desc(pl, prm.B, (int)nfull, (int)i);
+  return prm.items[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -452,18 +659,35 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
   const int lane = lane_id();
   const int n = lane & 15;  // head column (S^T, O^T) / token row (K operand)
   const int g = lane >> 4;
+  PlanLds* pl = reinterpret_cast<PlanLds*>(smem + (blockDim.x >> 6) * Gm::LDS_PER_WAVE);
+  unsigned long long tag = 0;
+  uint32_t n_items, n_full, nq_plan;
+  if (prm.self_plan) {
+    tag = launch_tag(prm.salt);
+    // workgroup 0 resets the queue counters for this launch
+    if (blockIdx.x == 0 && threadIdx.x < kQueues)
+      atomicExch(prm.counter + threadIdx.x * kCounterStride, tag << kCountBits);
+    self_plan(prm, pl);
+    n_items = (uint32_t)uniform(pl->nitems);
+    n_full = (uint32_t)uniform(pl->nfull);
+    nq_plan = (uint32_t)uniform(pl->nq);
+  } else {
+    n_items = prm.hdr[kItemCountWord];
+    n_full = prm.hdr[kFullCountWord];
+    nq_plan = prm.hdr[kQueueCountWord];
+  }
   const uint32_t per_item = (uint32_t)(prm.Hkv * prm.n_hg);
-  const uint32_t total = prm.hdr[kItemCountWord] * per_item;
+  const uint32_t total = n_items * per_item;
   const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
   // (threadIdx.x >> 6 is the same in every lane; readfirstlane tells the compiler)
   const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (uint32_t)uniform((int)(threadIdx.x >> 6));
   // static rounds: whole rounds of full partitions, at most one per lane;
   // the last kDynamicRounds of them are left to the queues, which balance
   // waves that run at different speeds
-  uint32_t rounds = min((prm.hdr[kFullCountWord] * per_item) / nwaves, (uint32_t)kMaxStaticRounds);
+  uint32_t rounds = min((n_full * per_item) / nwaves, (uint32_t)kMaxStaticRounds);
   rounds = rounds > (uint32_t)prm.dyn_rounds ? rounds - (uint32_t)prm.dyn_rounds : min(rounds, 1u);
   const uint32_t first_dyn = rounds * nwaves;
-  const uint32_t nq = prm.nq > 0 ? (uint32_t)prm.nq : prm.hdr[kQueueCountWord];
+  const uint32_t nq = prm.nq > 0 ? (uint32_t)prm.nq : nq_plan;
   const uint32_t home = blockIdx.x % nq;
   uint32_t queue = 0;
   PoolView pv;
@@ -473,7 +697,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
 
   // lane r: descriptor of this wave's item of static round r
   i32x4_t sdesc = {0, 0, 0, 0};
-  if (rounds > 0) sdesc = prm.items[(wave + (uint32_t)min(lane, (int)rounds - 1) * nwaves) / per_item];
+  if (rounds > 0) sdesc = item_desc(prm, pl, n_full, (wave + (uint32_t)min(lane, (int)rounds - 1) * nwaves) / per_item);
 
   // the current item: round r < rounds is static item wave + r * nwaves
   uint32_t r = 0;
@@ -483,9 +707,9 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     it = make_item(prm, lane_desc(sdesc, 0), f, per_item);
   } else {
     r = rounds;
-    f = claim(prm, nq, home, queue, first_dyn, total);
+    f = claim(prm, tag, nq, home, queue, first_dyn, total);
     if (f >= total) return;
-    it = make_item(prm, prm.items[f / per_item], f, per_item);
+    it = make_item(prm, item_desc(prm, pl, n_full, f / per_item), f, per_item);
   }
   int ids[NR];
   load_ids<NR>(prm, it, ids);
@@ -535,16 +759,16 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
         has_next = true;
         load_ids<NR>(prm, nx, idn);
       } else if (!early) {
-        fn = claim(prm, nq, home, queue, first_dyn, total);
+        fn = claim(prm, tag, nq, home, queue, first_dyn, total);
         if (fn < total) {
-          nx = make_item(prm, prm.items[fn / per_item], fn, per_item);
+          nx = make_item(prm, item_desc(prm, pl, n_full, fn / per_item), fn, per_item);
           has_next = true;
           load_ids<NR>(prm, nx, idn);
         }
       }
     }
     if (pend == 1 && t == 1) {
-      dn = prm.items[fn / per_item];
+      dn = item_desc(prm, pl, n_full, fn / per_item);
       pend = 2;
     }
     if (pend == 2 && t == 2) {
@@ -564,7 +788,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     if (!last || has_next)
       load_tile<T, D, kWide, kAligned, NR>(pv, prm, last ? nx : it, ids, last ? nx.tok0 : tile0 + kTile, regs);
     if (t == 0 && early && !stat_next) {
-      fn = claim(prm, nq, home, queue, first_dyn, total);
+      fn = claim(prm, tag, nq, home, queue, first_dyn, total);
       if (fn < total) pend = 1;
     }
 
@@ -779,11 +1003,14 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams prm) {
   for (int c0 = 0; c0 < np; c0 += 64) {  // chunks of 64 partitions
     const int nc = min(64, np - c0);
     const f32x4_t mine = c0 == 0 ? ml0 : ml[c0 + min(lane, nc - 1)];
-    const float w = lane < nc ? fast_exp2(mine[0] - mx) : 0.f;
-    float lw = w * mine[1];
+    // lanes past the chunk hold whatever the workspace held: select, never
+    // multiply, their values away
+    const bool in = lane < nc;
+    const float w = in ? fast_exp2(mine[0] - mx) : 0.f;
+    float lw = in ? w * mine[1] : 0.f;
     // weight of a partial row: 2^(m_i - m) for unnormalised rows, times l_i and
     // the row's scale for normalised ones
-    const float wr = kHalf ? lw * mine[2] : w;
+    const float wr = kHalf ? (in ? lw * mine[2] : 0.f) : w;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
     den += lw;
@@ -813,7 +1040,8 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
                         hipEvent_t ev0, hipEvent_t ev1) {
   // waves are independent workers; a block holds as many as fit in 64 KiB of LDS (at most 4)
   constexpr int wpb = Geo<T, D>::LDS_PER_WAVE * kWavesPerBlock <= 65536 ? kWavesPerBlock : 2;
-  constexpr unsigned lds_bytes = Geo<T, D>::LDS_PER_WAVE * wpb;
+  // per-wave tile buffers, then the in-kernel plan
+  constexpr unsigned lds_bytes = Geo<T, D>::LDS_PER_WAVE * wpb + (unsigned)sizeof(PlanLds);
   // exactly the blocks that can be resident at once: every wave starts on its
   // first item immediately, and none waits for a slot while holding one
   static int per_cu = 0;
@@ -858,6 +1086,15 @@ hipError_t launch_sized(const DecodeParams& prm, int B, int64_t max_items, int64
   return launch_mode<T, D, true>(prm, B, max_items, stream, ev0, ev1);
 }
 
+// Per-call salt of the counters' tag: a process-wide sequence from a start
+// taken from the clock and the process id.
+unsigned long long next_salt() {
+  static std::atomic<unsigned long long> seq{
+      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
+      ((unsigned long long)getpid() << 40)};
+  return seq.fetch_add(0x9E3779B97F4A7C15ull, std::memory_order_relaxed);
+}
+
 }  // namespace
 
 size_t decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int block_size,
@@ -876,7 +1113,7 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.lens = a.context_lens;
   prm.out = a.out;
   prm.hdr = reinterpret_cast<const uint32_t*>(ws + Lw.hdr);
-  prm.counter = reinterpret_cast<uint32_t*>(ws + Lw.hdr);
+  prm.counter = reinterpret_cast<unsigned long long*>(ws + Lw.hdr);
   prm.items = reinterpret_cast<const i32x4_t*>(ws + Lw.items);
   prm.ml = reinterpret_cast<float*>(ws + Lw.ml);
   prm.o = reinterpret_cast<float*>(ws + Lw.o);
@@ -893,11 +1130,17 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.max_parts = (int)Lw.max_parts;
   prm.dyn_rounds = kDynamicRounds;
   prm.nq = 0;
+  prm.B = a.num_seqs;
+  prm.salt = next_salt();
 
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.context_lens, a.num_seqs,
-                     prm.cap, reinterpret_cast<uint32_t*>(ws + Lw.hdr),
-                     reinterpret_cast<i32x4_t*>(ws + Lw.items));
   const int64_t max_items = (int64_t)a.num_seqs * Lw.max_parts * prm.Hkv * prm.n_hg;
+  // the workgroups plan small batches themselves (their counters then carry
+  // a tag and a 24-bit count: items plus one failed claim per wave must fit)
+  prm.self_plan = a.num_seqs <= kSelfPlanMax && max_items + kMaxWaves < kMaxQueueItems;
+  if (!prm.self_plan)
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.context_lens, a.num_seqs,
+                       prm.cap, reinterpret_cast<uint32_t*>(ws + Lw.hdr),
+                       reinterpret_cast<i32x4_t*>(ws + Lw.items));
   const int64_t pool_bytes =
       a.num_blocks * a.block_size * a.num_kv_heads * a.head_dim * (a.dtype == kBF16 ? 2 : 4);
   if (a.dtype == kBF16) {

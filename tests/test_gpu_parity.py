@@ -180,6 +180,87 @@ def test_decode_empty_context_gives_zeros_and_repeat_is_deterministic():
     assert np.array_equal(to_host_bits(out2), o)
 
 
+def _decode_with_workspace(d, ws):
+    """pa_paged_decode_attention through the C ABI with a caller-supplied workspace."""
+    c = d.case
+    lib = pa.load_library()
+    out = torch.empty_like(d.q)
+    N, P, Hkv, D = d.kc.shape
+    code = 1 if c.dtype == "bf16" else 0
+    st = lib.pa_paged_decode_attention(d.q.data_ptr(), d.kc.data_ptr(), d.vc.data_ptr(), d.bt.data_ptr(),
+                                       d.lens.data_ptr(), float(c.scale), out.data_ptr(), c.B, d.q.shape[1], Hkv,
+                                       D, P, N, d.bt.shape[1], code, ws.data_ptr(), ws.numel(),
+                                       torch.cuda.current_stream().cuda_stream)
+    assert st == 0, st
+    return out
+
+
+def test_decode_any_workspace_contents():
+    """The work queues reset themselves in every launch: a workspace holding
+    random bytes, all ones, or another call's state gives the same bits."""
+    c = small(P=16, lens=(1, 40, 256, 257, 700, 1500, 3000, 90), seed=26)
+    d = DevCase(c)
+    ref = to_host_bits(d.decode())
+    assert_close(d.decode(), decode_ref(c), "bf16", "workspace")
+    need = pa.decode_workspace_size(c.B, c.num_q_heads, c.head_dim, c.block_size, c.max_blocks_per_seq)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    for fill in ("random", "ones", "reuse", "reuse"):
+        if fill == "random":
+            ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=DEV, generator=gen)
+        elif fill == "ones":
+            ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+        out = _decode_with_workspace(d, ws)
+        assert np.array_equal(to_host_bits(out), ref), fill
+
+
+def test_decode_large_batch_plan_kernel_path_bitwise():
+    """Above 1024 requests a plan kernel lists the items; below, the
+    workgroups do.  Both must give each request the same bits (the split
+    depends on its length only), and match the oracle."""
+    rng = np.random.default_rng(27)
+    lens = rng.integers(1, 800, size=1100)
+    lens[:6] = [1, 16, 255, 256, 257, 799]
+    c = small(P=16, Hq=8, Hkv=2, D=64, lens=tuple(int(x) for x in lens), seed=27)
+    d = DevCase(c)
+    full = to_host_bits(d.decode())
+    pick = [0, 1, 2, 3, 4, 5, 517, 1023, 1024, 1099]
+    assert_close(d.decode(), decode_ref(c, select=pick), "bf16", "B=1100", rows=pick)
+    for lo, hi in ((0, 300), (1000, 1100)):
+        out = torch.empty_like(d.q[lo:hi])
+        pa.paged_decode_attention(d.q[lo:hi].contiguous(), d.kc, d.vc, d.bt[lo:hi].contiguous(),
+                                  d.lens[lo:hi].contiguous(), c.scale, out)
+        assert np.array_equal(to_host_bits(out), full[lo:hi]), (lo, hi)
+
+
+def test_decode_graph_replays_match_eager():
+    """Captured in a HIP graph, every replay gets a new dispatch id and so
+    resets the queues again: each replay equals the eager result, with other
+    eager decode calls and synchronisations in between."""
+    c = small(P=16, lens=(5, 300, 1025, 4000, 77, 512), seed=28)
+    d = DevCase(c)
+    c2 = small(P=16, lens=(900, 3, 2048), seed=29)
+    d2 = DevCase(c2)
+    ref = to_host_bits(d.decode())
+    ref2 = to_host_bits(d2.decode())
+    out = torch.empty_like(d.q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pa.paged_decode_attention(d.q, d.kc, d.vc, d.bt, d.lens, c.scale, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.paged_decode_attention(d.q, d.kc, d.vc, d.bt, d.lens, c.scale, out)
+    for rep in range(4):
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(out), ref), rep
+        assert np.array_equal(to_host_bits(d2.decode()), ref2), rep
+
+
 def _scale_bf16(bits: np.ndarray, pow2: int) -> np.ndarray:
     """bf16 bits times 2**pow2 (exact while in range)."""
     f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** pow2)
