@@ -176,19 +176,36 @@ def bench_decode(args):
         a.record()
         b.record()
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the timed region is bracketed by
+    # the first and the last, and each step's own time is the gap between two
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t_start.record()
+    marks[0].record()
     for k in range(args.steps):
         step(evs[k], k % L)
-    t_stop.record()
+        marks[k + 1].record()
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_stop)
+    ms_total = marks[0].elapsed_time(marks[-1])
     ms_step = ms_total / args.steps
+    step_ms = np.array([marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps)])
     kern_ms = [a.elapsed_time(b) for a, b in evs]
     kern_avg_ms = float(np.mean(kern_ms))
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, decode kernel {kern_avg_ms * 1e3:.1f} us avg")
+
+    # attention only: the same sweep without the slot mapping and the scatters
+    def attn_only():
+        for kc, vc, q, kn, vn, out in layers:
+            pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out)
+
+    attn_only()
+    amarks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    amarks[0].record()
+    for k in range(args.steps):
+        attn_only()
+        amarks[k + 1].record()
+    torch.cuda.synchronize()
+    attn_ms = np.array([amarks[k].elapsed_time(amarks[k + 1]) for k in range(args.steps)])
 
     dec_b = decode_bytes(case.context_lens, P, Hq, Hkv, D, s)
     sc_b = scatter_bytes(B, Hkv, D, s)
@@ -220,6 +237,9 @@ def bench_decode(args):
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "us_per_layer_step": round(1e3 * ms_step / L, 2),
+        "us_per_layer_step_p10_p50_p90": [round(float(x), 2) for x in np.percentile(1e3 * step_ms / L, [10, 50, 90])],
+        "attention_only_us_per_layer_step_p10_p50_p90": [round(float(x), 2)
+                                                         for x in np.percentile(1e3 * attn_ms / L, [10, 50, 90])],
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "roofline_tokens_per_s": round(B / (step_bytes / (HBM_PEAK_GBS * 1e9)), 1),
         "roofline": {

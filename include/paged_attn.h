@@ -116,7 +116,12 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *                      ceil(context_lens[b] / block_size) entries are read
  *   context_lens       int32 [num_seqs]
  *   workspace          device scratch of at least pa_decode_workspace_size()
- *                      bytes, not shared with a concurrently running call
+ *                      bytes, not shared with a concurrently running call.
+ *                      Its contents on entry do not matter (no clearing is
+ *                      needed, also between calls or HIP graph replays); on
+ *                      return it holds scratch values only.
+ * The call enqueues two kernels (three for batches above 1024 requests, where
+ * a separate kernel lists the work items).
  */
 int pa_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_table, const int32_t* context_lens,
