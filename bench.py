@@ -427,8 +427,8 @@ def summarize_profiles(d):
     if stats:
         table, _ = _stats_table(stats)
         with open(os.path.join(prof, "decode_llama3_8b_kernel_stats.txt"), "w") as f:
-            f.write("Llama-3-8B-shaped decode step (32 layers x (reshape_and_cache + paged decode: plan, partition,\n"
-                    "reduce), B=256, H_q=32, H_kv=8, D=128, P=16, bf16), rocprofv3 kernel statistics.\n")
+            f.write("Llama-3-8B-shaped decode step (32 layers x (reshape_and_cache + paged decode: partition with\n"
+                    "in-kernel plan, reduce), B=256, H_q=32, H_kv=8, D=128, P=16, bf16), rocprofv3 kernel statistics.\n")
             f.write("command (run from the repository root, DIR = an output folder):\n  "
                     + PROFILE_RUNS["trace"] + "\n")
             f.write(f"decode.hip sha256: {sha}\n\n")
