@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["llama3_8b", "mixed", "copy"], default="llama3_8b")
+    ap.add_argument("--workload", choices=["llama3_8b", "mixed", "cow", "copy"], default="llama3_8b")
     ap.add_argument("--layers", type=int, default=None, help="profile runs only: fewer layers")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -346,6 +346,54 @@ def bench_mixed(args):
     return res, case
 
 
+def bench_cow(args):
+    """Copy-on-write block copies (pa_copy_blocks) in a Llama-3-8B layer pool:
+    4096 (src, dst) pairs of 32 KiB blocks (P=16, H_kv=8, D=128, bf16) per pool,
+    K and V.  Roofline: HBM, each byte read once and written once."""
+    import paged_kv_cache_48_amd as pa
+
+    dev = torch.device("cuda:0")
+    N, P, Hkv, D, pairs_n = 30438, 16, 8, 128, 4096
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    kc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    vc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    perm = np.random.default_rng(6).permutation(N)
+    pairs = torch.as_tensor(np.stack([perm[:pairs_n], perm[pairs_n:2 * pairs_n]], axis=1).astype(np.int32),
+                            device=dev)
+    for _ in range(args.warmup):
+        pa.copy_blocks(kc, vc, pairs)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for k in range(args.steps):
+        evs[k][0].record()
+        pa.copy_blocks(kc, vc, pairs)
+        evs[k][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    moved = 2 * 2 * pairs_n * P * Hkv * D * 2  # K and V, read and written
+    achieved = moved / (kern_ms * 1e-3) / 1e9
+    return {"metric": "copy-on-write block copies GB/s (read + write)", "value": round(moved / (ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": f"pa_copy_blocks: {pairs_n} random (src, dst) pairs of 32 KiB blocks per pool "
+                                   f"(P={P}, H_kv={Hkv}, D={D}, bf16), K and V, pool of {N} blocks"},
+            "roofline": {"kernel": "copy_blocks_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": None, "algorithmic_bytes_per_launch": moved,
+                         "avg_launch_us": round(kern_ms * 1e3, 2)},
+            "cpu_baseline": None}
+
+
 def bench_copy(args):
     """A plain device copy of 1 GiB, the calibration run for HBM byte counters
     (FETCH_SIZE / WRITE_SIZE per dispatch divided by 1 GiB)."""
@@ -376,6 +424,8 @@ PROFILE_RUNS = {
              "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
     "trace_mixed": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_mixed -o mixed -- "
                    "python3 bench.py --workload mixed --steps 10 --warmup 2",
+    "trace_cow": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_cow -o cow -- "
+                 "python3 bench.py --workload cow --steps 20 --warmup 3",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch -o fetch -- "
              "python3 bench.py --layers 2 --steps 2 --warmup 1 --no-cpu-baseline",
     "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write -o write -- "
@@ -443,6 +493,16 @@ def summarize_profiles(d):
                     + PROFILE_RUNS["trace_mixed"] + "\n\n")
             f.write("\n".join(table) + "\n")
 
+    stats = one("prof_cow/*kernel_stats.csv")
+    if stats:
+        table, _ = _stats_table(stats)
+        with open(os.path.join(prof, "copy_blocks_cow_kernel_stats.txt"), "w") as f:
+            f.write("Copy-on-write block copies: pa_copy_blocks with 4096 (src, dst) pairs of 32 KiB blocks per pool\n"
+                    "(P=16, H_kv=8, D=128, bf16), K and V: 512 MiB moved per launch, rocprofv3 kernel statistics.\n")
+            f.write("command (run from the repository root, DIR = an output folder):\n  "
+                    + PROFILE_RUNS["trace_cow"] + "\n\n")
+            f.write("\n".join(table) + "\n")
+
     fetch_kib, nf = _counter_mean(one("pmc_fetch/*counter_collection.csv"), "decode_partition_kernel", "FETCH_SIZE") \
         if one("pmc_fetch/*counter_collection.csv") else (None, 0)
     write_kib, nw = _counter_mean(one("pmc_write/*counter_collection.csv"), "decode_partition_kernel", "WRITE_SIZE") \
@@ -503,6 +563,8 @@ def main():
     pa.load_library()
     if args.workload == "copy":
         res = bench_copy(args)
+    elif args.workload == "cow":
+        res = bench_cow(args)
     elif args.workload == "mixed":
         res, case = bench_mixed(args)
         res["cpu_baseline"] = None

@@ -98,6 +98,25 @@ int pa_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mappi
                          int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                          int32_t head_dim, int32_t dtype, void* stream);
 
+/*
+ * pa_copy_blocks -- copy-on-write support for prefix sharing (tiny-vllm-py,
+ * "Prefix Sharing": requests with a common prefix point their block tables at
+ * the same physical blocks; a shared, partly filled block must be copied
+ * before one request appends to it; ember, "Deliberately out of scope":
+ * copy-on-write block tables).  For each pair, block dst of k_cache and of
+ * v_cache becomes a bit-for-bit copy of block src.  Reads need nothing else:
+ * attention through a table that shares blocks equals attention through one
+ * that points at copies.
+ *   k_cache, v_cache   [num_blocks, block_size, num_kv_heads, head_dim], in place
+ *   block_mapping      int32 [num_pairs, 2]: (src, dst) per pair
+ * Destinations must be distinct and must not be sources (the pairs run
+ * concurrently); a pair with an entry outside [0, num_blocks) is skipped.
+ * Same dtype and row-size rules as pa_reshape_and_cache.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int64_t num_pairs,
+                   int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t dtype, void* stream);
+
 /* Bytes of workspace pa_paged_decode_attention needs for these shapes. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t block_size, int32_t max_blocks_per_seq);

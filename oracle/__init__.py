@@ -14,6 +14,7 @@ from .paged_attention import (  # noqa: F401
     widen,
     ref_slot_mapping,
     ref_reshape_and_cache,
+    ref_copy_blocks,
     ref_gather,
     ref_decode,
     ref_prefill,

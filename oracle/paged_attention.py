@@ -50,6 +50,7 @@ __all__ = [
     "widen",
     "ref_slot_mapping",
     "ref_reshape_and_cache",
+    "ref_copy_blocks",
     "ref_gather",
     "ref_decode",
     "ref_prefill",
@@ -126,6 +127,32 @@ def ref_reshape_and_cache(k, v, slot_mapping, k_cache, v_cache):
     vflat = _bits(vc).reshape(N * P, H, D)
     kflat[used] = _bits(np.asarray(k, dtype=kc.dtype))[keep]
     vflat[used] = _bits(np.asarray(v, dtype=vc.dtype))[keep]
+    return kc, vc
+
+
+def ref_copy_blocks(k_cache, v_cache, block_mapping):
+    """Copy whole blocks for copy-on-write (tiny-vllm-py, "Prefix Sharing": requests
+    with a common prefix point their block tables at the same physical blocks,
+    and a shared partial tail block is copied before a request appends to it;
+    ember, "Deliberately out of scope": copy-on-write block tables).  For each
+    pair ``(src, dst)`` of ``block_mapping`` (``[n, 2]``), block ``dst`` of both
+    pools becomes a bit-for-bit copy of block ``src``.  Pairs with a negative
+    entry are skipped.  Destinations must be distinct and no destination may be
+    a source (so the order of the pairs does not matter).  Returns
+    ``(new_k_cache, new_v_cache)``; the inputs are not modified.
+    """
+    pairs = np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2)
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    N = kc.shape[0]
+    keep = (pairs[:, 0] >= 0) & (pairs[:, 1] >= 0)
+    src, dst = pairs[keep, 0], pairs[keep, 1]
+    assert np.all(src < N) and np.all(dst < N), "oracle: block outside the pool"
+    assert len(np.unique(dst)) == len(dst), "oracle: a block is copied into twice"
+    assert not np.any(np.isin(dst, src)), "oracle: a destination is also a source"
+    kb, vb = _bits(kc), _bits(vc)
+    kb[dst] = _bits(np.asarray(k_cache))[src]
+    vb[dst] = _bits(np.asarray(v_cache))[src]
     return kc, vc
 
 

@@ -29,6 +29,7 @@ __all__ = [
     "load_library",
     "slot_mapping",
     "reshape_and_cache",
+    "copy_blocks",
     "paged_decode_attention",
     "paged_prefill_attention",
     "decode_workspace_size",
@@ -55,6 +56,7 @@ SIGNATURES = {
         ctypes.c_int,
         [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32, _i32, _i32, _c_void_p],
     ),
+    "pa_copy_blocks": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32, _i32, _i32, _c_void_p]),
     "pa_decode_workspace_size": (_size, [_i32, _i32, _i32, _i32, _i32]),
     "pa_paged_decode_attention": (
         ctypes.c_int,
@@ -192,6 +194,21 @@ def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tens
     _req(len({k.dtype, v.dtype, k_cache.dtype, v_cache.dtype}) == 1, "k, v and the caches must share a dtype")
     _check(lib.pa_reshape_and_cache(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
                                     v_cache.data_ptr(), T, N, P, H, D, _dtype_code(k), _stream(k)))
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: torch.Tensor) -> None:
+    """Copy-on-write block copy: for each row ``(src, dst)`` of the int32
+    ``[n, 2]`` ``block_mapping``, block ``dst`` of both pools becomes a copy of
+    block ``src`` (see ``pa_copy_blocks``)."""
+    lib = load_library()
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name, dim=4)
+    _dev_tensor(block_mapping, "block_mapping", torch.int32, 2)
+    _req(block_mapping.shape[1] == 2, "block_mapping must be [num_pairs, 2]")
+    _req(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype, "k_cache and v_cache must match")
+    N, P, H, D = k_cache.shape
+    _check(lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_mapping.data_ptr(),
+                              block_mapping.shape[0], N, P, H, D, _dtype_code(k_cache), _stream(k_cache)))
 
 
 def _attn_common(q, k_cache, v_cache, block_table, context_lens, out):

@@ -148,6 +148,27 @@ int pa_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mappi
                     fn);
 }
 
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int64_t num_pairs,
+                   int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                   void* stream) {
+  g_err.clear();
+  const char* fn = "pa_copy_blocks";
+  PA_REQUIRE(num_pairs >= 0 && num_pairs <= INT_MAX / 2, PA_ERR_INVALID, "%s: num_pairs must be in [0, 2^30)", fn);
+  PA_REQUIRE(dtype_ok(dtype), PA_ERR_UNSUPPORTED, "%s: unsupported dtype %d", fn, dtype);
+  PA_REQUIRE(num_kv_heads >= 1 && head_dim >= 1, PA_ERR_INVALID, "%s: head sizes must be >= 1", fn);
+  PA_REQUIRE(block_size >= 1, PA_ERR_INVALID, "%s: block_size must be >= 1", fn);
+  PA_REQUIRE(num_blocks >= 1, PA_ERR_INVALID, "%s: num_blocks must be >= 1", fn);
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_size(dtype);
+  PA_REQUIRE(row_bytes % 16 == 0 && row_bytes <= INT_MAX, PA_ERR_UNSUPPORTED,
+             "%s: a token row (H_kv * D * elem) must be a multiple of 16 bytes (got %lld)", fn,
+             (long long)row_bytes);
+  if (num_pairs == 0) return PA_OK;
+  PA_REQUIRE(k_cache && v_cache && block_mapping, PA_ERR_INVALID, "%s: null pointer argument", fn);
+  return hip_status(pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, num_blocks,
+                                           row_bytes * block_size, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t block_size, int32_t max_blocks_per_seq) {
   if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || block_size < 1 || max_blocks_per_seq < 1) return 0;

@@ -61,6 +61,39 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// Copy-on-write: block dst of a pool becomes a bit copy of block src
+// (tiny-vllm-py, "Prefix Sharing": a shared partly filled block is copied
+// before one of its requests appends to it).  One workgroup per (pair, pool);
+// its threads move the block's 16-byte pieces, four loads in flight each.
+// Pairs with an entry outside [0, num_blocks) are skipped.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4_t* __restrict__ kc, u32x4_t* __restrict__ vc,
+                                                          const int32_t* __restrict__ mapping,
+                                                          int64_t num_blocks, int64_t pieces_per_block) {
+  const int64_t pair = blockIdx.x >> 1;
+  u32x4_t* pool = (blockIdx.x & 1) ? vc : kc;
+  const int64_t src = mapping[2 * pair], dst = mapping[2 * pair + 1];
+  if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks) return;
+  const u32x4_t* from = pool + src * pieces_per_block;
+  u32x4_t* to = pool + dst * pieces_per_block;
+  constexpr int U = 4;
+  for (int64_t i0 = threadIdx.x; i0 < pieces_per_block; i0 += U * 256) {
+    u32x4_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + 256 * u < pieces_per_block) x[u] = __builtin_nontemporal_load(from + i0 + 256 * u);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + 256 * u < pieces_per_block) to[i0 + 256 * u] = x[u];
+  }
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int64_t num_pairs,
+                              int64_t num_blocks, int64_t block_bytes, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)(2 * num_pairs)), dim3(256), 0, stream,
+                     (u32x4_t*)k_cache, (u32x4_t*)v_cache, block_mapping, num_blocks, block_bytes / 16);
+  return hipGetLastError();
+}
+
 hipError_t launch_slot_mapping(const int32_t* block_table, const int32_t* cu_seqlens,
                                const int32_t* context_lens, int32_t* slot_mapping, int num_seqs,
                                int64_t num_tokens, int block_size, int max_blocks,

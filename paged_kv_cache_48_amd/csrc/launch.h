@@ -31,6 +31,9 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, const int32_t*
                                     void* k_cache, void* v_cache, int64_t num_tokens,
                                     int64_t pool_rows, int row_bytes, hipStream_t stream);
 
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int64_t num_pairs,
+                              int64_t num_blocks, int64_t block_bytes, hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   const void* k_cache;

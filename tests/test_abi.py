@@ -148,3 +148,14 @@ def test_workspace_sizes(lib):
     assert big >= 256 * 32 * 32 * 130 * 4
     assert lib.pa_decode_workspace_size(-1, 12, 64, 16, 13) == 0
     assert lib.pa_prefill_workspace_size(16, 17000, 32, 8) > lib.pa_prefill_workspace_size(16, 100, 32, 8)
+
+
+def test_copy_blocks_validation(lib):
+    f = lib.pa_copy_blocks
+    assert f(1, 1, 1, -1, 100, 16, 8, 128, BF16, NUL) == INVALID
+    assert f(1, 1, 1, 4, 0, 16, 8, 128, BF16, NUL) == INVALID
+    assert f(1, 1, 1, 4, 100, 0, 8, 128, BF16, NUL) == INVALID
+    assert f(1, 1, 1, 4, 100, 16, 8, 128, 9, NUL) == UNSUPPORTED
+    assert f(1, 1, 1, 4, 100, 16, 1, 4, BF16, NUL) == UNSUPPORTED   # 8-byte rows
+    assert f(NUL, 1, 1, 4, 100, 16, 8, 128, BF16, NUL) == INVALID
+    assert f(NUL, NUL, NUL, 0, 100, 16, 8, 128, BF16, NUL) == OK    # no pairs: no-op

@@ -376,3 +376,89 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(pa, "_attend", lambda q, K, V, s: orig(q, K[:-1], V[:-1], s))
     bad = pa.ref_prefill(pcase.q, kc, vc, pcase.cu_seqlens, pcase.block_table, pcase.context_lens, pcase.scale)
     assert not np.allclose(bad[1:], bfp[1:])
+
+
+# ----------------------------------------------------------------------------
+# prefix sharing and copy-on-write (tiny-vllm-py, "Prefix Sharing")
+# ----------------------------------------------------------------------------
+
+from oracle import ref_copy_blocks  # noqa: E402
+from workloads import shared_prefix_case  # noqa: E402
+
+
+def prefix_pools(c, table, pairs, per_request=False):
+    """Oracle pools of a shared-prefix case: the prefix written once through
+    request 0's table, then the block copies, then every request's tail through
+    ``table`` (one call, or one call per request)."""
+    P, S = c.block_size, c.prefix_len
+    kc = nan_pool(c.num_blocks, P, c.num_kv_heads, c.head_dim, c.dtype)
+    vc = kc.copy()
+    slots = ref_slot_mapping(table[:1], [0, S], [S], P)
+    kc, vc = ref_reshape_and_cache(c.k_tok[:S], c.v_tok[:S], slots, kc, vc)
+    if len(pairs):
+        kc, vc = ref_copy_blocks(kc, vc, pairs)
+    rows = [np.arange(c.cu_ctx[b] + S, c.cu_ctx[b + 1]) for b in range(c.B)]
+    groups = [[b] for b in range(c.B)] if per_request else [list(range(c.B))]
+    for grp in groups:
+        idx = np.concatenate([rows[b] for b in grp]).astype(np.int64)
+        cu = np.concatenate([[0], np.cumsum([len(rows[b]) for b in grp])])
+        slots = ref_slot_mapping(table[grp], cu, c.context_lens[grp], P)
+        kc, vc = ref_reshape_and_cache(c.k_tok[idx], c.v_tok[idx], slots, kc, vc)
+    return kc, vc
+
+
+def cow_pairs(c):
+    return [(int(c.shared_blocks[-1]), int(c.cow_blocks[b])) for b in range(c.B) if c.cow_blocks[b] >= 0]
+
+
+def dup_pairs(c):
+    return [(int(c.shared_blocks[i]), int(c.dup_blocks[b, i])) for b in range(1, c.B)
+            for i in range(len(c.shared_blocks))]
+
+
+def test_copy_blocks_is_a_bit_copy_and_skips_negative_pairs():
+    kc = np.arange(6 * 2 * 1 * 4, dtype=np.uint16).reshape(6, 2, 1, 4)
+    kc[1, 0, 0, 0] = 0x7FC1  # a NaN payload survives
+    vc = kc + np.uint16(1000)
+    nk, nv = ref_copy_blocks(kc, vc, [[1, 4], [-1, 5], [2, -1], [0, 3]])
+    assert np.array_equal(nk[4], kc[1]) and np.array_equal(nv[4], vc[1])
+    assert np.array_equal(nk[3], kc[0]) and np.array_equal(nv[3], vc[0])
+    for blk in (0, 1, 2, 5):
+        assert np.array_equal(nk[blk], kc[blk]) and np.array_equal(nv[blk], vc[blk])
+    assert np.array_equal(kc[4], np.arange(32, 40).reshape(2, 1, 4))  # input untouched
+    with pytest.raises(AssertionError):
+        ref_copy_blocks(kc, vc, [[1, 2], [2, 3]])  # a destination that is also a source
+    with pytest.raises(AssertionError):
+        ref_copy_blocks(kc, vc, [[1, 2], [0, 2]])  # two copies into one block
+
+
+@pytest.mark.parametrize("S,P,tails", [(10, 4, (3, 0, 9)), (8, 4, (5, 1)), (13, 1, (2, 7, 4)), (21, 7, (6, 30))])
+def test_prefix_sharing_with_copy_on_write_matches_brute_force(S, P, tails):
+    c = shared_prefix_case(dtype="f32", block_size=P, num_q_heads=4, num_kv_heads=2, head_dim=8, prefix_len=S,
+                           tail_lens=tails, seed=S + P)
+    kc, vc = prefix_pools(c, c.block_table, cow_pairs(c))
+    out = ref_decode(c.q, kc, vc, c.block_table, c.context_lens, c.scale)
+    bf = np.array(brute_decode(c.q, c.k_tok, c.v_tok, c.cu_ctx, c.num_kv_heads, c.scale))
+    np.testing.assert_allclose(out, bf, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("S,P,tails", [(10, 4, (3, 0, 9)), (16, 4, (5, 1, 2)), (13, 1, (2, 7, 4))])
+def test_shared_blocks_equal_duplicated_blocks_bitwise(S, P, tails):
+    c = shared_prefix_case(dtype="bf16", block_size=P, num_q_heads=8, num_kv_heads=2, head_dim=16, prefix_len=S,
+                           tail_lens=tails, seed=3 * S + P)
+    kc, vc = prefix_pools(c, c.block_table, cow_pairs(c))
+    shared = ref_decode(c.q, kc, vc, c.block_table, c.context_lens, c.scale)
+    kd, vd = prefix_pools(c, c.dup_table, dup_pairs(c))
+    dup = ref_decode(c.q, kd, vd, c.dup_table, c.context_lens, c.scale)
+    assert np.array_equal(shared, dup)
+
+
+def test_appending_into_a_shared_partial_block_without_copy_corrupts_the_other_request():
+    # planted mistake: no copy-on-write; request 0 then reads request 2's tail
+    c = shared_prefix_case(dtype="f32", block_size=4, num_q_heads=4, num_kv_heads=2, head_dim=8, prefix_len=10,
+                           tail_lens=(3, 0, 9), seed=14)
+    kc, vc = prefix_pools(c, c.naive_table, [], per_request=True)
+    out = ref_decode(c.q, kc, vc, c.naive_table, c.context_lens, c.scale)
+    bf = np.array(brute_decode(c.q, c.k_tok, c.v_tok, c.cu_ctx, c.num_kv_heads, c.scale))
+    assert not np.allclose(out[0], bf[0], atol=1e-6)
+    np.testing.assert_allclose(out[2], bf[2], rtol=0, atol=1e-12)  # the last writer sees its own tail

@@ -1,3 +1,13 @@
 """Seeded synthetic workloads for paged attention (no attention arithmetic here)."""
 
-from .synth import CONFIGS, Case, config_case, draw_values, make_case, nan_pool, to_bf16_bits  # noqa: F401
+from .synth import (  # noqa: F401
+    CONFIGS,
+    Case,
+    SharedPrefixCase,
+    config_case,
+    draw_values,
+    make_case,
+    nan_pool,
+    shared_prefix_case,
+    to_bf16_bits,
+)

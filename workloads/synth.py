@@ -50,6 +50,8 @@ __all__ = [
     "make_case",
     "config_case",
     "nan_pool",
+    "SharedPrefixCase",
+    "shared_prefix_case",
 ]
 
 NAN_BITS = {"bf16": 0x7FC0, "f32": 0x7FC00000}
@@ -296,3 +298,106 @@ def config_case(idx: int, seed: Optional[int] = None, block_size: Optional[int] 
         layer=layer,
         values=values,
     )
+
+
+# ---------------------------------------------------------------------------
+# Prefix sharing: several requests whose streams start with the same tokens.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class SharedPrefixCase:
+    """Requests ``b < B`` share their first ``prefix_len`` tokens (identical K/V
+    rows) and then continue with ``tail_lens[b]`` tokens of their own.
+
+    ``shared_blocks`` hold the prefix once: ``ceil(prefix_len / P)`` physical
+    blocks, the last one partly used when ``prefix_len % P != 0``.
+    ``cow_blocks[b]`` (``-1`` for request 0, and for every request when the
+    prefix fills whole blocks) is a free block that receives a copy of that
+    partly used block before request ``b`` appends to it.  ``block_table`` is
+    the table after copy-on-write (request 0 keeps the shared partial block);
+    ``naive_table`` points every request at the shared partial block instead.
+    ``dup_table`` gives every request private copies of all prefix blocks
+    (``dup_blocks[b]``, one per prefix block; request 0 keeps the originals).
+    ``k_tok``/``v_tok`` are ``[sum L, H_kv, D]`` streams in request order
+    (request ``b`` at rows ``cu_ctx[b] .. cu_ctx[b+1]-1``), ``q`` is
+    ``[B, H_q, D]`` (one decode query per request)."""
+
+    dtype: str
+    block_size: int
+    num_blocks: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    scale: float
+    prefix_len: int
+    tail_lens: np.ndarray
+    context_lens: np.ndarray
+    cu_ctx: np.ndarray
+    shared_blocks: np.ndarray
+    cow_blocks: np.ndarray
+    dup_blocks: np.ndarray
+    block_table: np.ndarray
+    naive_table: np.ndarray
+    dup_table: np.ndarray
+    k_tok: np.ndarray
+    v_tok: np.ndarray
+    q: np.ndarray
+
+    @property
+    def B(self) -> int:
+        return len(self.tail_lens)
+
+
+def shared_prefix_case(*, dtype: str, block_size: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                       prefix_len: int, tail_lens, seed: int = 0) -> SharedPrefixCase:
+    P = int(block_size)
+    tails = np.asarray(tail_lens, dtype=np.int32)
+    B = len(tails)
+    S = int(prefix_len)
+    lens = (S + tails).astype(np.int32)
+    ns = (S + P - 1) // P              # prefix blocks
+    partial = S % P != 0
+    own = [(int(L) + P - 1) // P - ns for L in lens]  # blocks after the prefix blocks
+    need = ns + sum(own) + (B - 1 if partial else 0) + ns * (B - 1) + 1
+    N = need + 3
+    rng = np.random.default_rng([seed, 4, P])
+    perm = rng.permutation(N).astype(np.int32)
+    it = iter(perm.tolist())
+    shared = np.array([next(it) for _ in range(ns)], dtype=np.int32)
+    cow = np.full(B, -1, dtype=np.int32)
+    if partial:
+        for b in range(1, B):
+            cow[b] = next(it)
+    dup = np.full((B, max(ns, 1)), -1, dtype=np.int32)
+    for b in range(1, B):
+        for i in range(ns):
+            dup[b, i] = next(it)
+    M = max(int(ns + o) for o in own)
+    filler = None
+    own_blocks = [[next(it) for _ in range(o)] for o in own]
+    filler = next(it)
+    table = np.full((B, M), filler, dtype=np.int32)
+    naive = np.full((B, M), filler, dtype=np.int32)
+    dupt = np.full((B, M), filler, dtype=np.int32)
+    for b in range(B):
+        row = list(shared) + own_blocks[b]
+        naive[b, : len(row)] = row
+        if partial and b > 0:
+            row = list(shared[:-1]) + [int(cow[b])] + own_blocks[b]
+        table[b, : len(row)] = row
+        drow = (list(shared) if b == 0 else list(dup[b, :ns])) + own_blocks[b]
+        dupt[b, : len(drow)] = drow
+    vr = np.random.default_rng([seed, 5])
+    pre_k = draw_values(vr, (S, num_kv_heads, head_dim), dtype)
+    pre_v = draw_values(vr, (S, num_kv_heads, head_dim), dtype)
+    ks, vs = [], []
+    for b in range(B):
+        ks += [pre_k, draw_values(vr, (int(tails[b]), num_kv_heads, head_dim), dtype)]
+        vs += [pre_v, draw_values(vr, (int(tails[b]), num_kv_heads, head_dim), dtype)]
+    q = draw_values(vr, (B, num_q_heads, head_dim), dtype)
+    cu = np.concatenate([[0], np.cumsum(lens, dtype=np.int64)]).astype(np.int64)
+    return SharedPrefixCase(dtype=dtype, block_size=P, num_blocks=N, num_q_heads=num_q_heads,
+                            num_kv_heads=num_kv_heads, head_dim=head_dim, scale=1.0 / math.sqrt(head_dim),
+                            prefix_len=S, tail_lens=tails, context_lens=lens, cu_ctx=cu, shared_blocks=shared,
+                            cow_blocks=cow, dup_blocks=dup, block_table=table, naive_table=naive, dup_table=dupt,
+                            k_tok=np.concatenate(ks), v_tok=np.concatenate(vs), q=q)
