@@ -20,3 +20,11 @@ from .paged_attention import (  # noqa: F401
     ref_prefill,
 )
 from .brute_force import brute_decode, brute_prefill, contiguous_cache  # noqa: F401
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_decode,
+    e4m3_encode,
+    ref_dequantize,
+    ref_quantize,
+    ref_reshape_and_cache_fp8,
+)

@@ -17,7 +17,7 @@ from oracle import (
     ref_slot_mapping,
     widen,
 )
-from workloads import make_case, nan_pool
+from workloads import draw_values, make_case, nan_pool
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "slot_examples.json")
 
@@ -462,3 +462,103 @@ def test_appending_into_a_shared_partial_block_without_copy_corrupts_the_other_r
     bf = np.array(brute_decode(c.q, c.k_tok, c.v_tok, c.cu_ctx, c.num_kv_heads, c.scale))
     assert not np.allclose(out[0], bf[0], atol=1e-6)
     np.testing.assert_allclose(out[2], bf[2], rtol=0, atol=1e-12)  # the last writer sees its own tail
+
+
+# ----------------------------------------------------------------------------
+# fp8 (OCP E4M3) KV: encode / decode against the format's definition and
+# torch's float8_e4m3fn conversion (a library routine), then attention over
+# the dequantised pool against the brute force
+# ----------------------------------------------------------------------------
+
+import torch  # noqa: E402
+
+from oracle import (  # noqa: E402
+    e4m3_decode,
+    e4m3_encode,
+    ref_dequantize,
+    ref_quantize,
+    ref_reshape_and_cache_fp8,
+)
+
+
+def _torch_e4m3(x32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def test_e4m3_decode_table():
+    codes = np.arange(256, dtype=np.uint8)
+    d = e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(d), np.isnan(ref))
+    assert np.array_equal(d[~np.isnan(d)], ref[~np.isnan(ref)])
+    assert d[0x7E] == 448.0 and d[0xFE] == -448.0 and d[0x38] == 1.0
+    assert d[0x01] == 2.0 ** -9 and d[0x08] == 2.0 ** -6 and d[0x07] == 7 * 2.0 ** -9
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF]) and d[0x80] == 0 and np.signbit(d[0x80])
+    assert np.all(np.diff(d[:0x7F]) > 0)  # monotone over the finite positive codes
+
+
+def test_e4m3_encode_round_trip_ties_and_saturation():
+    codes = np.arange(256, dtype=np.uint8)
+    d = e4m3_decode(codes)
+    fin = ~np.isnan(d)
+    assert np.array_equal(e4m3_encode(d[fin]), codes[fin])
+    # exact midpoints between neighbouring positive codes go to the even code
+    mids = (d[0:0x7E] + d[1:0x7F]) / 2.0
+    want = np.where(np.arange(0x7E) % 2 == 0, np.arange(0x7E), np.arange(1, 0x7F)).astype(np.uint8)
+    assert np.array_equal(e4m3_encode(mids), want)
+    assert np.array_equal(e4m3_encode(-mids), want | 0x80)
+    assert np.array_equal(_torch_e4m3(mids.astype(np.float32)), want)
+    # saturation (torch turns these into NaN; this reading clamps to 448)
+    big = np.array([448.5, 464.0, 479.0, 480.0, 1e4, np.inf])
+    assert np.all(e4m3_encode(big) == 0x7E) and np.all(e4m3_encode(-big) == 0xFE)
+    assert e4m3_encode(np.array([np.nan]))[0] == 0x7F
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(8)
+    x = np.concatenate([rng.uniform(-463.9, 463.9, 200000), rng.uniform(-0.03, 0.03, 100000),
+                        rng.standard_normal(100000) * 4]).astype(np.float32)
+    assert np.array_equal(e4m3_encode(x.astype(np.float64)), _torch_e4m3(x))
+
+
+def test_quantize_is_scaled_rne_with_bounded_error():
+    rng = np.random.default_rng(9)
+    H, D = 4, 32
+    x = draw_values(rng, (500, H, D), "bf16")
+    s = np.array([0.01, 0.05, 0.3, 1.7], dtype=np.float32)
+    codes = ref_quantize(x, s)
+    # the quotient is fp32 division of the fp32 values (torch's CPU division is IEEE)
+    xf = torch.from_numpy(widen(x).astype(np.float32))
+    q = (xf / torch.from_numpy(s)[:, None]).numpy()
+    assert np.all(np.abs(q) < 463)
+    assert np.array_equal(codes, _torch_e4m3(q))
+    back = ref_dequantize(codes, s)
+    err = np.abs(back - widen(x))
+    # half a step of the code grid, plus the fp32 rounding of the quotient
+    # (which can land exactly on a tie, as 0.02490234375 / 1.7 does)
+    bound = np.maximum(np.abs(widen(x)) * 2.0 ** -4, 2.0 ** -10 * s[:, None].astype(np.float64))
+    assert np.all(err <= bound * (1 + 2.0 ** -16))
+
+
+@pytest.mark.parametrize("G,H_kv,P", [(2, 2, 4), (4, 1, 3), (1, 3, 16)])
+def test_fp8_decode_is_attention_over_dequantised_values(G, H_kv, P):
+    case = tiny_case(G=G, H_kv=H_kv, D=16, P=P, lens=(5, 1, 30, 17), seed=40 + P, dtype="bf16")
+    ks = np.linspace(0.005, 0.02, H_kv).astype(np.float32)
+    vs = np.linspace(0.01, 0.03, H_kv).astype(np.float32)
+    # pool: prefix and new tokens written through the fp8 scatter
+    kc = np.zeros((case.num_blocks, P, H_kv, 16), dtype=np.uint8)
+    vc = kc.copy()
+    kp, vp, cu_pre, lens_pre = case.prefix()
+    kc, vc = ref_reshape_and_cache_fp8(kp, vp, ref_slot_mapping(case.block_table, cu_pre, lens_pre, P), kc, vc,
+                                       ks, vs)
+    kn, vn = case.new_kv()
+    kc, vc = ref_reshape_and_cache_fp8(
+        kn, vn, ref_slot_mapping(case.block_table, case.cu_seqlens, case.context_lens, P), kc, vc, ks, vs)
+    out = ref_decode(case.q, ref_dequantize(kc, ks), ref_dequantize(vc, vs), case.block_table, case.context_lens,
+                     case.scale)
+    # brute force on the dequantised token streams (contiguous layout, no pool)
+    kq = ref_dequantize(ref_quantize(case.k_tok, ks), ks)
+    vq = ref_dequantize(ref_quantize(case.v_tok, vs), vs)
+    bf = np.array(brute_decode(case.q, kq, vq, case.cu_ctx, H_kv, case.scale))
+    np.testing.assert_allclose(out, bf, rtol=0, atol=1e-12)
