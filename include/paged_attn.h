@@ -43,7 +43,9 @@
 extern "C" {
 #endif
 
-typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+/* Element types.  PA_DTYPE_FP8_E4M3 (uint8 codes, see pa_reshape_and_cache_fp8)
+ * is accepted by pa_copy_blocks only; the fp8 calls take it implicitly. */
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1, PA_DTYPE_FP8_E4M3 = 2 } pa_dtype;
 
 typedef enum {
   PA_OK = 0,
@@ -97,6 +99,43 @@ int pa_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mappi
                          void* k_cache, void* v_cache, int64_t num_tokens,
                          int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                          int32_t head_dim, int32_t dtype, void* stream);
+
+/*
+ * fp8 paged KV (ember, "Deliberately out of scope (for now)": paged KV
+ * quantisation is a next step; the pages fix no format, so this library's
+ * reading is): pools of uint8 OCP FP8 E4M3 codes (1 sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits, no infinities, largest magnitude 448), with
+ * one fp32 scale per KV head for K and one for V.  Element x of KV head h is
+ * stored as encode(x / scale[h]) -- the quotient correctly rounded to fp32,
+ * then rounded to the nearest code with ties to even, magnitudes above 448
+ * saturated to +-448 and NaN stored as 0x7F -- and read as decode(code) *
+ * scale[h].  Attention over an fp8 pool is attention over those values.
+ *
+ * pa_reshape_and_cache_fp8 -- pa_reshape_and_cache into fp8 pools.
+ *   k, v               [num_tokens, num_kv_heads, head_dim], dtype (F32 or BF16)
+ *   k_cache, v_cache   uint8 [num_blocks, block_size, num_kv_heads, head_dim]
+ *   k_scale, v_scale   float [num_kv_heads], device pointers, positive
+ * head_dim must be a multiple of 16.  Slot rules as pa_reshape_and_cache.
+ */
+int pa_reshape_and_cache_fp8(const void* k, const void* v, const int32_t* slot_mapping, void* k_cache,
+                             void* v_cache, const float* k_scale, const float* v_scale, int64_t num_tokens,
+                             int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t dtype, void* stream);
+
+/*
+ * pa_paged_decode_attention_fp8 -- pa_paged_decode_attention over fp8 pools
+ * (format and scales as above).  q and out are bfloat16; q's elements must lie
+ * inside the fp16 range (the products run on fp16 matrix cores: the codes
+ * widen exactly to fp16, and bf16 q converts exactly within that range).
+ * Other arguments, the workspace and the errors are those of
+ * pa_paged_decode_attention.
+ */
+int pa_paged_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                  const float* v_scale, const int32_t* block_table, const int32_t* context_lens,
+                                  float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                  int32_t max_blocks_per_seq, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /*
  * pa_copy_blocks -- copy-on-write support for prefix sharing (tiny-vllm-py,

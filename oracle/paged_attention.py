@@ -74,7 +74,7 @@ def widen(x) -> np.ndarray:
 
 def _bits(x: np.ndarray) -> np.ndarray:
     """Raw-bit view so copies never touch floating-point values (NaN payloads survive)."""
-    if x.dtype == np.uint16:
+    if x.dtype == np.uint16 or x.dtype == np.uint8:
         return x
     if x.dtype == np.float32:
         return x.view(np.uint32)

@@ -56,6 +56,16 @@ SIGNATURES = {
         ctypes.c_int,
         [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32, _i32, _i32, _c_void_p],
     ),
+    "pa_reshape_and_cache_fp8": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32, _i32,
+         _i32, _c_void_p],
+    ),
+    "pa_paged_decode_attention_fp8": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+         _i32, _i32, _i32, _i32, _i32, _i64, _i32, _c_void_p, _size, _c_void_p],
+    ),
     "pa_copy_blocks": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32, _i32, _i32, _c_void_p]),
     "pa_decode_workspace_size": (_size, [_i32, _i32, _i32, _i32, _i32]),
     "pa_paged_decode_attention": (
@@ -176,9 +186,20 @@ def slot_mapping(block_table: torch.Tensor, cu_seqlens: torch.Tensor, context_le
     return out
 
 
+def _scales(k_scale, v_scale, H: int, device):
+    _req(k_scale is not None and v_scale is not None, "fp8 (uint8) pools need k_scale and v_scale")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _dev_tensor(t, name, torch.float32, 1)
+        _req(t.shape[0] == H and t.device == device, f"{name} must be float32 [num_kv_heads] on the pools' device")
+
+
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
-                      k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
-    """Scatter ``k``, ``v`` ``[T, H_kv, D]`` into the pools ``[N, P, H_kv, D]`` in place."""
+                      k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor | None = None,
+                      v_scale: torch.Tensor | None = None) -> None:
+    """Scatter ``k``, ``v`` ``[T, H_kv, D]`` into the pools ``[N, P, H_kv, D]`` in place.
+    uint8 pools hold fp8 (OCP E4M3) codes: the values are divided by the
+    per-KV-head ``k_scale``/``v_scale`` (float32 ``[H_kv]``) and quantised
+    (see ``pa_reshape_and_cache_fp8``)."""
     lib = load_library()
     for name, t in (("k", k), ("v", v)):
         _dev_tensor(t, name, dim=3)
@@ -191,6 +212,14 @@ def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tens
     _req(v_cache.shape == k_cache.shape, "k_cache and v_cache must have the same shape")
     _req((H, D) == (H2, D2), "k rows and cache rows differ in [H_kv, D]")
     _req(slot_mapping.shape[0] == T, "slot_mapping must have one entry per token")
+    if k_cache.dtype == torch.uint8:
+        _req(v_cache.dtype == torch.uint8, "k_cache and v_cache must share a dtype")
+        _req(k.dtype == v.dtype, "k and v must share a dtype")
+        _scales(k_scale, v_scale, H, k_cache.device)
+        _check(lib.pa_reshape_and_cache_fp8(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+                                            v_cache.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), T, N, P, H, D,
+                                            _dtype_code(k), _stream(k)))
+        return
     _req(len({k.dtype, v.dtype, k_cache.dtype, v_cache.dtype}) == 1, "k, v and the caches must share a dtype")
     _check(lib.pa_reshape_and_cache(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
                                     v_cache.data_ptr(), T, N, P, H, D, _dtype_code(k), _stream(k)))
@@ -207,8 +236,9 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: tor
     _req(block_mapping.shape[1] == 2, "block_mapping must be [num_pairs, 2]")
     _req(v_cache.shape == k_cache.shape and v_cache.dtype == k_cache.dtype, "k_cache and v_cache must match")
     N, P, H, D = k_cache.shape
+    code = 2 if k_cache.dtype == torch.uint8 else _dtype_code(k_cache)  # uint8: fp8 codes
     _check(lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_mapping.data_ptr(),
-                              block_mapping.shape[0], N, P, H, D, _dtype_code(k_cache), _stream(k_cache)))
+                              block_mapping.shape[0], N, P, H, D, code, _stream(k_cache)))
 
 
 def _attn_common(q, k_cache, v_cache, block_table, context_lens, out):
@@ -221,7 +251,10 @@ def _attn_common(q, k_cache, v_cache, block_table, context_lens, out):
     _req(out.shape == q.shape and out.dtype == q.dtype, "out must match q in shape and dtype")
     _req(out.data_ptr() != q.data_ptr(), "out must not alias q")
     _req(k_cache.shape == v_cache.shape, "k_cache and v_cache must have the same shape")
-    _req(len({q.dtype, k_cache.dtype, v_cache.dtype}) == 1, "q and the caches must share a dtype")
+    if k_cache.dtype == torch.uint8:
+        _req(v_cache.dtype == torch.uint8 and q.dtype == torch.bfloat16, "fp8 (uint8) pools take a bfloat16 q")
+    else:
+        _req(len({q.dtype, k_cache.dtype, v_cache.dtype}) == 1, "q and the caches must share a dtype")
     _req(q.shape[2] == k_cache.shape[3], "head_dim of q and of the caches differ")
     B = context_lens.shape[0]
     _req(block_table.shape[0] == B, "block_table must have one row per sequence")
@@ -230,8 +263,11 @@ def _attn_common(q, k_cache, v_cache, block_table, context_lens, out):
 
 def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                           out: torch.Tensor) -> torch.Tensor:
-    """Decode attention: ``q``/``out`` ``[B, H_q, D]``; see ``pa_paged_decode_attention``."""
+                           out: torch.Tensor, k_scale: torch.Tensor | None = None,
+                           v_scale: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention: ``q``/``out`` ``[B, H_q, D]``; see ``pa_paged_decode_attention``.
+    uint8 pools hold fp8 (OCP E4M3) codes with per-KV-head scales
+    (``pa_paged_decode_attention_fp8``; q and out bfloat16)."""
     lib = load_library()
     B = _attn_common(q, k_cache, v_cache, block_table, context_lens, out)
     _req(q.shape[0] == B, "q must have one row per sequence")
@@ -241,6 +277,13 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     stream = _stream(q)
     need = decode_workspace_size(B, Hq, D, P, M)
     ws = _workspace(q.device, stream, need)
+    if k_cache.dtype == torch.uint8:
+        _scales(k_scale, v_scale, Hkv, k_cache.device)
+        _check(lib.pa_paged_decode_attention_fp8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                                 k_scale.data_ptr(), v_scale.data_ptr(), block_table.data_ptr(),
+                                                 context_lens.data_ptr(), float(scale), out.data_ptr(), B, Hq, Hkv,
+                                                 D, P, N, M, ws.data_ptr(), ws.numel(), stream))
+        return out
     _check(lib.pa_paged_decode_attention(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                          block_table.data_ptr(), context_lens.data_ptr(), float(scale),
                                          out.data_ptr(), B, Hq, Hkv, D, P, N, M, _dtype_code(q),

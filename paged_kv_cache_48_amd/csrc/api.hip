@@ -34,7 +34,7 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 bool dtype_ok(int32_t dtype) { return dtype == PA_DTYPE_F32 || dtype == PA_DTYPE_BF16; }
-int elem_size(int32_t dtype) { return dtype == PA_DTYPE_BF16 ? 2 : 4; }
+int elem_size(int32_t dtype) { return dtype == PA_DTYPE_BF16 ? 2 : (dtype == PA_DTYPE_FP8_E4M3 ? 1 : 4); }
 
 #define PA_REQUIRE(cond, status, ...) \
   do {                                \
@@ -148,13 +148,40 @@ int pa_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mappi
                     fn);
 }
 
+int pa_reshape_and_cache_fp8(const void* k, const void* v, const int32_t* slot_mapping, void* k_cache,
+                             void* v_cache, const float* k_scale, const float* v_scale, int64_t num_tokens,
+                             int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t dtype, void* stream) {
+  g_err.clear();
+  const char* fn = "pa_reshape_and_cache_fp8";
+  PA_REQUIRE(num_tokens >= 0, PA_ERR_INVALID, "%s: num_tokens must be >= 0", fn);
+  PA_REQUIRE(dtype_ok(dtype), PA_ERR_UNSUPPORTED, "%s: unsupported source dtype %d", fn, dtype);
+  PA_REQUIRE(num_kv_heads >= 1 && head_dim >= 1, PA_ERR_INVALID, "%s: head sizes must be >= 1", fn);
+  PA_REQUIRE(head_dim % 16 == 0, PA_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 16 (got %d)", fn,
+             head_dim);
+  PA_REQUIRE(block_size >= 1, PA_ERR_INVALID, "%s: block_size must be >= 1", fn);
+  PA_REQUIRE(num_blocks >= 1, PA_ERR_INVALID, "%s: num_blocks must be >= 1", fn);
+  PA_REQUIRE(num_blocks * (int64_t)block_size <= INT_MAX, PA_ERR_INVALID,
+             "%s: num_blocks * block_size must fit in int32 (slots are int32)", fn);
+  const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+  PA_REQUIRE(row_elems <= INT_MAX / 4, PA_ERR_UNSUPPORTED, "%s: token row too large", fn);
+  if (num_tokens == 0) return PA_OK;
+  PA_REQUIRE(k && v && slot_mapping && k_cache && v_cache && k_scale && v_scale, PA_ERR_INVALID,
+             "%s: null pointer argument", fn);
+  return hip_status(pa::launch_reshape_and_cache_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                                                     num_tokens, num_blocks * block_size, (int)row_elems, head_dim,
+                                                     dtype, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int64_t num_pairs,
                    int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                    void* stream) {
   g_err.clear();
   const char* fn = "pa_copy_blocks";
   PA_REQUIRE(num_pairs >= 0 && num_pairs <= INT_MAX / 2, PA_ERR_INVALID, "%s: num_pairs must be in [0, 2^30)", fn);
-  PA_REQUIRE(dtype_ok(dtype), PA_ERR_UNSUPPORTED, "%s: unsupported dtype %d", fn, dtype);
+  PA_REQUIRE(dtype_ok(dtype) || dtype == PA_DTYPE_FP8_E4M3, PA_ERR_UNSUPPORTED, "%s: unsupported dtype %d", fn,
+             dtype);
   PA_REQUIRE(num_kv_heads >= 1 && head_dim >= 1, PA_ERR_INVALID, "%s: head sizes must be >= 1", fn);
   PA_REQUIRE(block_size >= 1, PA_ERR_INVALID, "%s: block_size must be >= 1", fn);
   PA_REQUIRE(num_blocks >= 1, PA_ERR_INVALID, "%s: num_blocks must be >= 1", fn);
@@ -175,20 +202,22 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
   return pa::decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq);
 }
 
-int pa_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* block_table, const int32_t* context_lens, float scale,
-                              void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                              int32_t max_blocks_per_seq, int32_t dtype, void* workspace,
-                              size_t workspace_bytes, void* stream) {
-  g_err.clear();
-  const char* fn = "pa_paged_decode_attention";
+}  // extern "C"
+
+namespace {
+
+int decode_call(const char* fn, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                const float* v_scale, const int32_t* block_table, const int32_t* context_lens, float scale, void* out,
+                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype, int32_t kv_dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
   int st = check_attn(fn, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                       max_blocks_per_seq, dtype);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return PA_OK;
   PA_REQUIRE(q && k_cache && v_cache && block_table && context_lens && out, PA_ERR_INVALID,
              "%s: null pointer argument", fn);
+  PA_REQUIRE(kv_dtype != pa::kFP8E4M3 || (k_scale && v_scale), PA_ERR_INVALID, "%s: null scale pointer", fn);
   const size_t need = pa::decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq);
   PA_REQUIRE(workspace && workspace_bytes >= need, PA_ERR_WORKSPACE,
              "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
@@ -208,8 +237,39 @@ int pa_paged_decode_attention(const void* q, const void* k_cache, const void* v_
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.dtype = dtype;
+  a.kv_dtype = kv_dtype;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.workspace = workspace;
   return hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream), g_ev_start, g_ev_stop), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* context_lens, float scale,
+                              void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  return decode_call("pa_paged_decode_attention", q, k_cache, v_cache, nullptr, nullptr, block_table, context_lens,
+                     scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, dtype, dtype, workspace, workspace_bytes, stream);
+}
+
+int pa_paged_decode_attention_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                  const float* v_scale, const int32_t* block_table, const int32_t* context_lens,
+                                  float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                  int32_t max_blocks_per_seq, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  g_err.clear();
+  return decode_call("pa_paged_decode_attention_fp8", q, k_cache, v_cache, k_scale, v_scale, block_table,
+                     context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, PA_DTYPE_BF16, pa::kFP8E4M3, workspace, workspace_bytes, stream);
 }
 
 size_t pa_prefill_workspace_size(int32_t num_seqs, int64_t total_q_tokens, int32_t num_q_heads,
@@ -264,6 +324,7 @@ int pa_paged_prefill_attention(const void* q, const void* k, const void* v, cons
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.dtype = dtype;
+  a.kv_dtype = dtype;
   a.workspace = workspace;
   return hip_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream), g_ev_start, g_ev_stop), fn);
 }

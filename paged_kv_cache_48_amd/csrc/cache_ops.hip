@@ -87,6 +87,98 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4_t* __restrict__ 
   }
 }
 
+// fp32 -> OCP FP8 E4M3 code (1 sign bit, 4 exponent bits with bias 7, 3
+// mantissa bits, subnormals m/8 * 2^-6, no infinities, S.1111.111 = NaN):
+// nearest, ties to even; magnitudes above 448 saturate to +-448; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a == a)) return 0x7Fu;
+  if (a > 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // subnormal grid of 2^-9 (8 = smallest normal)
+  const uint32_t ua = __float_as_uint(a);
+  int e = (int)(ua >> 23) - 127;
+  const uint32_t mant = ua & 0x7FFFFFu;
+  uint32_t r = mant >> 20;
+  const uint32_t rem = mant & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+  if (r == 8u) {
+    r = 0u;
+    ++e;
+  }
+  const uint32_t code = ((uint32_t)(e + 7) << 3) | r;
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+template <typename S>
+__device__ __forceinline__ float src_elem(const S* p, int i);
+template <>
+__device__ __forceinline__ float src_elem<bf16_bits>(const bf16_bits* p, int i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+template <>
+__device__ __forceinline__ float src_elem<float>(const float* p, int i) {
+  return p[i];
+}
+
+// fp8 scatter: one wave per token (grid-stride); lane i quantises 16-element
+// pieces i, i+64, ... of the token's K and V rows (each piece lies in one KV
+// head, as D is a multiple of 16) -- x / scale[h], correctly rounded in fp32,
+// then encoded -- and stores 16 codes with one 16-byte store.
+template <typename S>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const S* __restrict__ k, const S* __restrict__ v, const int32_t* __restrict__ slots,
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, int64_t num_tokens, int row_elems, int head_dim, int64_t pool_rows) {
+  const int lane = lane_id();
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int pieces = row_elems / 16;
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < num_tokens; t += waves) {
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= pool_rows) continue;
+    for (int c = lane; c < pieces; c += 64) {
+      const int e0 = 16 * c;
+      const int h = e0 / head_dim;
+      const float sk = k_scale[h], sv = v_scale[h];
+      const S* ks = k + t * row_elems + e0;
+      const S* vs = v + t * row_elems + e0;
+      u32x4_t kw, vw;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t a = 0u, b = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a |= e4m3_from_f32(src_elem<S>(ks, 4 * w + j) / sk) << (8 * j);
+          b |= e4m3_from_f32(src_elem<S>(vs, 4 * w + j) / sv) << (8 * j);
+        }
+        kw[w] = a;
+        vw[w] = b;
+      }
+      *reinterpret_cast<u32x4_t*>(kc + slot * row_elems + e0) = kw;
+      *reinterpret_cast<u32x4_t*>(vc + slot * row_elems + e0) = vw;
+    }
+  }
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, const int32_t* slot_mapping, void* k_cache,
+                                        void* v_cache, const float* k_scale, const float* v_scale,
+                                        int64_t num_tokens, int64_t pool_rows, int row_elems, int head_dim,
+                                        int src_dtype, hipStream_t stream) {
+  int64_t blocks = (num_tokens + 3) / 4;
+  const int64_t cap = (int64_t)device_cu_count() * 16;
+  if (blocks > cap) blocks = cap;
+  if (src_dtype == kBF16)
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<bf16_bits>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const bf16_bits*)k, (const bf16_bits*)v, slot_mapping, (uint8_t*)k_cache, (uint8_t*)v_cache,
+                       k_scale, v_scale, num_tokens, row_elems, head_dim, pool_rows);
+  else
+    hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const float*)k, (const float*)v, slot_mapping, (uint8_t*)k_cache, (uint8_t*)v_cache,
+                       k_scale, v_scale, num_tokens, row_elems, head_dim, pool_rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int64_t num_pairs,
                               int64_t num_blocks, int64_t block_bytes, hipStream_t stream) {
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)(2 * num_pairs)), dim3(256), 0, stream,

@@ -39,6 +39,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 // Two floats -> two packed IEEE half floats (lo in bits 0..15), round to nearest even.
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   const f32x2_t x = {lo, hi};

@@ -157,6 +157,40 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
 }
 
 // ---------------------------------------------------------------------------
+// fp8 pools: OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+// bits), one fp32 scale per KV head for K and for V.
+struct fp8_e4m3 {
+  uint8_t bits;
+};
+
+// Element type of q and out: the pool's, except bf16 for fp8 pools.
+template <typename T>
+struct QType {
+  typedef T type;
+};
+template <>
+struct QType<fp8_e4m3> {
+  typedef bf16_bits type;
+};
+
+// Eight E4M3 codes -> eight fp16 values equal to code * 2^-8, exactly: the
+// sign goes to bit 15 and the 7 exponent-and-mantissa bits to bits 7..13, so
+// the e4m3 exponent (bias 7) reads as an fp16 exponent (bias 15) 8 lower, and
+// e4m3 subnormals land on fp16 subnormals.  (The NaN code reads as 480.)
+__device__ __forceinline__ u32x4_t e4m3x8_to_f16(u32x2_t w) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    // bytes b0 b1 b2 b3 -> [0, b0, 0, b1] and [0, b2, 0, b3]
+    const uint32_t x01 = __builtin_amdgcn_perm(w[i], w[i], 0x010C000Cu);
+    const uint32_t x23 = __builtin_amdgcn_perm(w[i], w[i], 0x030C020Cu);
+    r[2 * i] = (x01 & 0x80008000u) | ((x01 >> 1) & 0x3F803F80u);
+    r[2 * i + 1] = (x23 & 0x80008000u) | ((x23 >> 1) & 0x3F803F80u);
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
 // Tile geometry.  A tile is 16 consecutive tokens of one KV head.  Lane l
 // loads 16-byte piece l % CPR of the head's row slice for tokens
 // (l / CPR) * TPL + j, j < TPL, so each quarter-wave reads whole contiguous
@@ -164,12 +198,17 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct Geo {
-  static constexpr int ROWB = D * (int)sizeof(T);  // bytes of one head's row slice
-  static constexpr int CPR = ROWB / 16;            // 16-byte pieces per row slice
+  // fp8 pools are staged as 16-bit values (fp16 holding e4m3 * 2^-8)
+  static constexpr bool kFp8 = std::is_same<T, fp8_e4m3>::value;
+  static constexpr int ESZ = kFp8 ? 2 : (int)sizeof(T);  // bytes of a staged element
+  static constexpr int ROWB = D * ESZ;             // staged bytes of one head's row slice
+  static constexpr int GROWB = D * (int)sizeof(T);  // pool bytes of one head's row slice
+  static constexpr int CPR = ROWB / 16;            // 16-byte staged pieces per row slice
+  static constexpr int LOADB = GROWB / CPR;        // pool bytes a lane loads per token (16; 8 for fp8)
   static constexpr int TPL = 16 * CPR / 64;        // tokens per lane per tile
   static constexpr int KST = ROWB + 16;            // LDS row stride of K (and of V for fp32)
-  static constexpr int VTS = 40;                   // LDS row stride of transposed V (bf16): 16 tokens + pad
-  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int VTS = 40;                   // LDS row stride of transposed V (16-bit): 16 tokens + pad
+  static constexpr bool kBf16 = ESZ == 2;          // 16-bit path (bf16, or fp8 via fp16)
   static constexpr int KBYTES = 16 * KST;
   static constexpr int VBYTES = kBf16 ? D * VTS : 16 * KST;
   static constexpr int LDS_PER_WAVE = KBYTES + VBYTES;
@@ -186,8 +225,9 @@ struct Off {
 
 template <typename T, int D>
 struct TileRegs {
-  u32x4_t k[Geo<T, D>::TPL];
-  u32x4_t v[Geo<T, D>::TPL];
+  typedef typename std::conditional<Geo<T, D>::kFp8, u32x2_t, u32x4_t>::type LT;  // one lane's load per token
+  LT k[Geo<T, D>::TPL];
+  LT v[Geo<T, D>::TPL];
   uint32_t ok;  // bit j: token j of this lane is inside the partition with a valid block id
 };
 
@@ -214,6 +254,8 @@ struct DecodeParams {
   int dyn_rounds;  // full rounds of full partitions left to the queues
   int nq;          // queues in use (at most kQueues); 0: as the plan chose
   int B;
+  const float* k_scale;  // fp8 pools: per-KV-head scales (null otherwise)
+  const float* v_scale;
   int self_plan;   // 1: the workgroups plan (B <= kSelfPlanMax); 0: the plan kernel did
   unsigned long long salt;  // per call; mixed into the counters' tag
 };
@@ -223,6 +265,7 @@ struct Item {
   int b, part, L, nparts;  // request, partition, visible tokens, partitions of the request
   int hkv, hg, nh;         // KV head, group of query heads, valid heads in the group
   int tok0, tok_end, ntiles, blk0, nblk;
+  float sl2, vmul;         // score factor (log2 units) and output factor (fp8 scales folded in)
 };
 
 __device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, uint32_t f, uint32_t per_item) {
@@ -247,6 +290,9 @@ __device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, ui
     last = (it.tok_end - 1) / prm.P;
   }
   it.nblk = last - it.blk0 + 1;
+  // fp8 pools hold code * scale; the staged fp16 values are code * 2^-8
+  it.sl2 = prm.k_scale ? prm.scale_log2 * 256.0f * prm.k_scale[it.hkv] : prm.scale_log2;
+  it.vmul = prm.v_scale ? 256.0f * prm.v_scale[it.hkv] : 1.0f;
   return it;
 }
 
@@ -265,13 +311,19 @@ __device__ __forceinline__ void load_ids(const DecodeParams& prm, const Item& it
 template <typename T, int D>
 __device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, u32x4_t (&qv)[Geo<T, D>::NQV]) {
   using Gm = Geo<T, D>;
+  typedef typename QType<T>::type QT;
   const int lane = lane_id();
   const int n = lane & 15, g = lane >> 4;
   const int h = it.hkv * prm.G + it.hg * 4 + (n < it.nh ? n : 0);
-  const T* qrow = static_cast<const T*>(prm.q) + ((int64_t)it.b * prm.Hq + h) * D;
+  const QT* qrow = static_cast<const QT*>(prm.q) + ((int64_t)it.b * prm.Hq + h) * D;
 #pragma unroll
   for (int i = 0; i < Gm::NQV; ++i) {
-    if constexpr (Gm::kBf16) qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * i + 8 * g);
+    if constexpr (Gm::kFp8) {
+      // bf16 query -> fp16 operand (exact inside the fp16 range)
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + 32 * i + 8 * g);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) qv[i][w] = pack_f16(bf16_lo(x[w]), bf16_hi(x[w]));
+    } else if constexpr (Gm::kBf16) qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * i + 8 * g);
     else qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + g * (D / 4) + 4 * i);
   }
 }
@@ -308,7 +360,8 @@ __device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams
   const int lane = lane_id();
   const int q = lane / Gm::CPR;
   const int first = tile0 + q * Gm::TPL;  // this lane's first token
-  const O lane_off = (O)(it.hkv * Gm::ROWB + 16 * (lane % Gm::CPR));
+  const O lane_off = (O)(it.hkv * Gm::GROWB + Gm::LOADB * (lane % Gm::CPR));
+  typedef typename TileRegs<T, D>::LT LT;
   r.ok = 0;
   if constexpr (kAligned) {
     int lb, off;
@@ -327,8 +380,8 @@ __device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams
       const bool ok = bok && first + j < it.tok_end;
       r.ok |= (ok ? 1u : 0u) << j;
       const O e = (ok ? base + (O)j * (O)pv.row_bytes : (O)0) + lane_off;
-      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.k + e));
-      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.v + e));
+      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.k + e));
+      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.v + e));
     }
   } else {
 #pragma unroll
@@ -347,8 +400,8 @@ __device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams
       const bool ok = in && blk >= 0 && blk < prm.N;
       r.ok |= (ok ? 1u : 0u) << j;
       const O e = (ok ? ((O)blk * (O)prm.P + (O)off) * (O)pv.row_bytes : (O)0) + lane_off;
-      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.k + e));
-      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pv.v + e));
+      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.k + e));
+      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.v + e));
     }
   }
 }
@@ -356,17 +409,31 @@ __device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams
 // Registers -> this wave's LDS region: K row-major; V transposed (bf16, d-major
 // so a P.V operand is one 8-byte read) or row-major (fp32).
 template <typename T, int D>
-__device__ __forceinline__ void stage_tile(char* lds, TileRegs<T, D>& r, bool full) {
+__device__ __forceinline__ void stage_tile(char* lds, TileRegs<T, D>& r_in, bool full) {
   using Gm = Geo<T, D>;
+  typedef typename TileRegs<T, D>::LT LT;
   const int lane = lane_id();
   const int c = lane % Gm::CPR, q = lane / Gm::CPR;
   if (!full) {
 #pragma unroll
     for (int j = 0; j < Gm::TPL; ++j)
-      if (!((r.ok >> j) & 1u)) {
-        r.k[j] = u32x4_t{0u, 0u, 0u, 0u};
-        r.v[j] = u32x4_t{0u, 0u, 0u, 0u};
+      if (!((r_in.ok >> j) & 1u)) {
+        r_in.k[j] = LT{};
+        r_in.v[j] = LT{};
       }
+  }
+  struct {
+    u32x4_t k[Gm::TPL], v[Gm::TPL];
+  } r;
+#pragma unroll
+  for (int j = 0; j < Gm::TPL; ++j) {
+    if constexpr (Gm::kFp8) {
+      r.k[j] = e4m3x8_to_f16(r_in.k[j]);
+      r.v[j] = e4m3x8_to_f16(r_in.v[j]);
+    } else {
+      r.k[j] = r_in.k[j];
+      r.v[j] = r_in.v[j];
+    }
   }
 #pragma unroll
   for (int j = 0; j < Gm::TPL; ++j)
@@ -653,6 +720,7 @@ __device__ __forceinline__ i32x4_t item_desc(const DecodeParams& prm, const Plan
 template <typename T, int D, bool kWide, bool kAligned, int NR>
 __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm) {
   using Gm = Geo<T, D>;
+  typedef typename QType<T>::type QT;
   constexpr int NDB = D / 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* lds = smem + (threadIdx.x >> 6) * Gm::LDS_PER_WAVE;
@@ -695,7 +763,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
   PoolView pv;
   pv.k = static_cast<const char*>(prm.kc);
   pv.v = static_cast<const char*>(prm.vc);
-  pv.row_bytes = (uint32_t)(prm.Hkv * Gm::ROWB);
+  pv.row_bytes = (uint32_t)(prm.Hkv * Gm::GROWB);
 
   // lane r: descriptor of this wave's item of static round r
   i32x4_t sdesc = {0, 0, 0, 0};
@@ -796,7 +864,14 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
 
     // ---- S^T = K Q^T ----
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (Gm::kBf16) {
+    if constexpr (Gm::kFp8) {
+#pragma unroll
+      for (int i = 0; i < Gm::NQ; ++i) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                   __builtin_bit_cast(f16x8_t, qv[i]), s, 0, 0, 0);
+      }
+    } else if constexpr (Gm::kBf16) {
 #pragma unroll
       for (int i = 0; i < Gm::NQ; ++i) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
@@ -819,7 +894,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sc[j] = (tile0 + 4 * g + j < it.tok_end) ? s[j] * prm.scale_log2 : -INFINITY;
+      sc[j] = (tile0 + 4 * g + j < it.tok_end) ? s[j] * it.sl2 : -INFINITY;
       mx = fmaxf(mx, sc[j]);
     }
     mx = max_over_rows(mx);
@@ -841,7 +916,15 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     }
     // ---- O^T += V^T P^T ----
     const char* vl = lds + Gm::KBYTES;
-    if constexpr (Gm::kBf16) {
+    if constexpr (Gm::kFp8) {
+      const u32x2_t pb = {pack_f16(p[0], p[1]), pack_f16(p[2], p[3])};
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vl + (16 * db + n) * Gm::VTS + 8 * g);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                      __builtin_bit_cast(f16x4_t, pb), o[db], 0, 0, 0);
+      }
+    } else if constexpr (Gm::kBf16) {
       const u32x2_t pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -868,8 +951,8 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     if (n < it.nh) {
       const int h = it.hkv * prm.G + it.hg * 4 + n;
       if (it.nparts == 1) {
-        const float inv = 1.0f / l;
-        T* dst = static_cast<T*>(prm.out) + ((int64_t)it.b * prm.Hq + h) * D + 4 * g;
+        const float inv = it.vmul / l;
+        QT* dst = static_cast<QT*>(prm.out) + ((int64_t)it.b * prm.Hq + h) * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           if constexpr (Gm::kBf16) {
@@ -888,7 +971,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
           // normalised row is a weighted mean of value rows, so it can exceed
           // the fp16 range only if the values do; then it is scaled down by a
           // power of two, kept beside (max, sum), so it stays below 2^15.
-          const float inv = 1.0f / l;
+          const float inv = it.vmul / l;
           float amax = 0.f;
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
@@ -1067,7 +1150,8 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
     const hipError_t e = hipEventRecord(ev1, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3((prm.Hq + 3) / 4, B), dim3(256), 0, stream, prm);
+  hipLaunchKernelGGL((decode_reduce_kernel<typename QType<T>::type, D>), dim3((prm.Hq + 3) / 4, B), dim3(256), 0,
+                     stream, prm);
   return hipGetLastError();
 }
 
@@ -1134,6 +1218,9 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.nq = 0;
   prm.B = a.num_seqs;
   prm.salt = next_salt();
+  const bool fp8 = a.kv_dtype == kFP8E4M3;
+  prm.k_scale = fp8 ? a.k_scale : nullptr;
+  prm.v_scale = fp8 ? a.v_scale : nullptr;
 
   const int64_t max_items = (int64_t)a.num_seqs * Lw.max_parts * prm.Hkv * prm.n_hg;
   // the workgroups plan small batches themselves (their counters then carry
@@ -1144,7 +1231,12 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
                        prm.cap, reinterpret_cast<uint32_t*>(ws + Lw.hdr),
                        reinterpret_cast<i32x4_t*>(ws + Lw.items));
   const int64_t pool_bytes =
-      a.num_blocks * a.block_size * a.num_kv_heads * a.head_dim * (a.dtype == kBF16 ? 2 : 4);
+      a.num_blocks * a.block_size * a.num_kv_heads * a.head_dim * (fp8 ? 1 : (a.dtype == kBF16 ? 2 : 4));
+  if (fp8) {  // bf16 q and out
+    if (a.head_dim == 128)
+      return launch_sized<fp8_e4m3, 128>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
+    return launch_sized<fp8_e4m3, 64>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
+  }
   if (a.dtype == kBF16) {
     if (a.head_dim == 128)
       return launch_sized<bf16_bits, 128>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);

@@ -8,7 +8,7 @@
 
 namespace pa {
 
-enum DType : int { kF32 = 0, kBF16 = 1 };
+enum DType : int { kF32 = 0, kBF16 = 1, kFP8E4M3 = 2 };
 
 // Tokens per split-context partition of the decode kernel.  A request with
 // context L is cut into ceil(L / kPartTokens) partitions; this depends on L
@@ -31,6 +31,11 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, const int32_t*
                                     void* k_cache, void* v_cache, int64_t num_tokens,
                                     int64_t pool_rows, int row_bytes, hipStream_t stream);
 
+hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, const int32_t* slot_mapping, void* k_cache,
+                                        void* v_cache, const float* k_scale, const float* v_scale,
+                                        int64_t num_tokens, int64_t pool_rows, int row_elems, int head_dim,
+                                        int src_dtype, hipStream_t stream);
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int64_t num_pairs,
                               int64_t num_blocks, int64_t block_bytes, hipStream_t stream);
 
@@ -51,7 +56,10 @@ struct AttnArgs {
   int block_size;
   int64_t num_blocks;
   int max_blocks;
-  int dtype;
+  int dtype;     // q and out (and the pools, unless kv_dtype is kFP8E4M3)
+  int kv_dtype;  // the pools' element type
+  const float* k_scale;  // kFP8E4M3 pools: per-KV-head scales
+  const float* v_scale;
   void* workspace;
 };
 

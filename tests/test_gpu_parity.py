@@ -469,3 +469,119 @@ def test_mixed_step_full_size_sampled(P):
     qdec = c.q[cu[16:64]]
     refd = ref_decode(qdec, kc, vc, c.block_table[16:], c.context_lens[16:], c.scale, select=pick)
     assert_close(outd, refd, "bf16", f"mixed decode P={P}", rows=pick)
+
+
+# ----------------------------------------------------------------------------
+# fp8 (OCP E4M3) pools
+# ----------------------------------------------------------------------------
+
+from oracle import ref_dequantize, ref_reshape_and_cache_fp8  # noqa: E402
+
+
+def _scales(H, seed, lo=0.004, hi=0.03):
+    return np.random.default_rng(seed).uniform(lo, hi, H).astype(np.float32)
+
+
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_reshape_and_cache_fp8_bit_exact(src):
+    N, P, H, D = 40, 7, 4, 64
+    rng = np.random.default_rng(50)
+    T = 150
+    x = rng.standard_normal((T, H, D)).astype(np.float32) * np.float32(3.0) ** rng.integers(-9, 9, (T, H, D))
+    x[0, 0, :8] = [0.0, -0.0, np.inf, -np.inf, np.nan, 1e30, -1e30, 2.0 ** -20]
+    if src == "bf16":
+        from workloads import to_bf16_bits
+        xb = to_bf16_bits(np.nan_to_num(x, nan=0.0, posinf=3e38, neginf=-3e38))
+        xb[0, 0, :8] = [0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC1, 0x7149, 0xF149, 0x3580]
+        k = xb
+        v = xb[::-1].copy()
+    else:
+        k, v = x, x[::-1].copy()
+    ks, vs = _scales(H, 51, 0.01, 2.0), _scales(H, 52, 0.01, 2.0)
+    slots = rng.permutation(N * P)[:T].astype(np.int32)
+    slots[5] = -1
+    kc0 = rng.integers(0, 256, (N, P, H, D), dtype=np.uint8)
+    vc0 = rng.integers(0, 256, (N, P, H, D), dtype=np.uint8)
+    want_k, want_v = ref_reshape_and_cache_fp8(k, v, slots, kc0, vc0, ks, vs)
+    dk = torch.from_numpy(kc0).to(DEV)
+    dv = torch.from_numpy(vc0).to(DEV)
+    pa.reshape_and_cache(to_dev(k, src), to_dev(v, src), idx(slots), dk, dv, torch.from_numpy(ks).to(DEV),
+                         torch.from_numpy(vs).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.cpu().numpy(), want_k)
+    assert np.array_equal(dv.cpu().numpy(), want_v)
+
+
+class Fp8Case:
+    """A case's pools written as fp8 through the HIP path (prefix, then new tokens)."""
+
+    def __init__(self, c, ks, vs):
+        self.case, self.ks, self.vs = c, ks, vs
+        shape = (c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim)
+        # unwritten slots hold the largest code (448): a masking mistake would show
+        self.kc = torch.full(shape, 0x7E, dtype=torch.uint8, device=DEV)
+        self.vc = torch.full(shape, 0x7E, dtype=torch.uint8, device=DEV)
+        self.dks, self.dvs = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+        self.bt, self.lens = idx(c.block_table), idx(c.context_lens)
+        kp, vp, cu_pre, lens_pre = c.prefix()
+        if len(kp):
+            sl = pa.slot_mapping(self.bt, idx(cu_pre), idx(lens_pre), c.block_size, len(kp))
+            pa.reshape_and_cache(to_dev(kp, c.dtype), to_dev(vp, c.dtype), sl, self.kc, self.vc, self.dks, self.dvs)
+        kn, vn = c.new_kv()
+        sl = pa.slot_mapping(self.bt, idx(c.cu_seqlens), self.lens, c.block_size, c.T_total)
+        pa.reshape_and_cache(to_dev(kn, c.dtype), to_dev(vn, c.dtype), sl, self.kc, self.vc, self.dks, self.dvs)
+        self.q = to_dev(c.q, c.dtype)
+
+    def decode(self, q=None, bt=None, lens=None):
+        q = self.q if q is None else q
+        out = torch.empty_like(q)
+        pa.paged_decode_attention(q, self.kc, self.vc, self.bt if bt is None else bt,
+                                  self.lens if lens is None else lens, self.case.scale, out, self.dks, self.dvs)
+        return out
+
+    def reference(self, select=None):
+        c = self.case
+        kc, vc = self.kc.cpu().numpy(), self.vc.cpu().numpy()
+        return ref_decode(c.q, ref_dequantize(kc, self.ks), ref_dequantize(vc, self.vs), c.block_table,
+                          c.context_lens, c.scale, select=select)
+
+
+@pytest.mark.parametrize("G,Hkv,D,P", [(4, 8, 128, 16), (1, 4, 64, 16), (8, 2, 128, 7), (3, 2, 64, 1),
+                                       (16, 1, 128, 64)])
+def test_decode_fp8_matches_oracle(G, Hkv, D, P):
+    c = small(P=P, Hq=G * Hkv, Hkv=Hkv, D=D, lens=(1, 16, 255, 256, 257, 700, 1500), seed=60 + G * D + P)
+    f = Fp8Case(c, _scales(Hkv, 61), _scales(Hkv, 62))
+    # the pools hold exactly the oracle's codes
+    kc0 = np.full((c.num_blocks, P, Hkv, D), 0x7E, dtype=np.uint8)
+    kp, vp, cu_pre, lens_pre = c.prefix()
+    ok, ov = ref_reshape_and_cache_fp8(kp, vp, ref_slot_mapping(c.block_table, cu_pre, lens_pre, P), kc0, kc0,
+                                       f.ks, f.vs)
+    kn, vn = c.new_kv()
+    ok, ov = ref_reshape_and_cache_fp8(kn, vn, ref_slot_mapping(c.block_table, c.cu_seqlens, c.context_lens, P),
+                                       ok, ov, f.ks, f.vs)
+    assert np.array_equal(f.kc.cpu().numpy(), ok) and np.array_equal(f.vc.cpu().numpy(), ov)
+    assert_close(f.decode(), f.reference(), "bf16", f"fp8 G={G} D={D} P={P}")
+
+
+def test_decode_fp8_long_contexts_and_batch_invariance_bitwise():
+    c = small(P=16, Hq=32, Hkv=8, D=128, lens=(8192, 3000, 17, 4097, 256), seed=63)
+    f = Fp8Case(c, _scales(8, 64), _scales(8, 65))
+    full = f.decode()
+    assert_close(full, f.reference(), "bf16", "fp8 long contexts")
+    fb = to_host_bits(full)
+    for b in range(c.B):
+        one = f.decode(f.q[b:b + 1].contiguous(), f.bt[b:b + 1].contiguous(), f.lens[b:b + 1].contiguous())
+        assert np.array_equal(to_host_bits(one)[0], fb[b]), b
+
+
+def test_copy_blocks_fp8_pools():
+    N, P, H, D = 50, 16, 8, 128
+    rng = np.random.default_rng(66)
+    kc = rng.integers(0, 256, (N, P, H, D), dtype=np.uint8)
+    vc = rng.integers(0, 256, (N, P, H, D), dtype=np.uint8)
+    pairs = np.array([[3, 40], [7, 41], [-1, 42]], dtype=np.int32)
+    wk, wv = ref_copy_blocks(kc, vc, pairs)
+    dk, dv = torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV)
+    pa.copy_blocks(dk, dv, idx(pairs))
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.cpu().numpy(), wk) and np.array_equal(dv.cpu().numpy(), wv)
