@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["llama3_8b", "mixed", "cow", "copy"], default="llama3_8b")
+    ap.add_argument("--workload", choices=["llama3_8b", "llama3_8b_fp8", "mixed", "cow", "copy"], default="llama3_8b")
     ap.add_argument("--layers", type=int, default=None, help="profile runs only: fewer layers")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -57,16 +57,20 @@ def parse():
     return ap.parse_args()
 
 
-def decode_bytes(lens, P, Hq, Hkv, D, s):
+def decode_bytes(lens, P, Hq, Hkv, D, s, s_kv=None):
     """Algorithmic bytes one decode launch must move: every cached K and V row
-    of every request, q and out, the used block-table entries and the lengths."""
+    of every request (``s_kv`` bytes per element; 1 for fp8 pools), q and out
+    (``s``), the used block-table entries and the lengths."""
     lens = np.asarray(lens, dtype=np.int64)
-    return int(lens.sum() * Hkv * D * 2 * s + 2 * len(lens) * Hq * D * s
+    s_kv = s if s_kv is None else s_kv
+    return int(lens.sum() * Hkv * D * 2 * s_kv + 2 * len(lens) * Hq * D * s
                + 4 * ((lens + P - 1) // P).sum() + 4 * len(lens))
 
 
-def scatter_bytes(T, Hkv, D, s):
-    return int(4 * T * Hkv * D * s + 4 * T)
+def scatter_bytes(T, Hkv, D, s, s_kv=None):
+    """New K and V rows read (``s``) and written (``s_kv``), plus the slots."""
+    s_kv = s if s_kv is None else s_kv
+    return int(2 * T * Hkv * D * (s + s_kv) + 4 * T)
 
 
 def traffic_from_profiles(kernel_file: str, key: str):
@@ -137,6 +141,8 @@ def bench_decode(args):
                               case.num_blocks, case.max_blocks_per_seq)
     L = case.num_layers if args.layers is None else args.layers
     s = 2
+    fp8 = args.workload == "llama3_8b_fp8"
+    s_kv = 1 if fp8 else 2
     gen = torch.Generator(device=dev)
     bt = torch.as_tensor(case.block_table, device=dev)
     lens = torch.as_tensor(case.context_lens, device=dev)
@@ -144,25 +150,34 @@ def bench_decode(args):
     layers = []
     for layer in range(L):
         gen.manual_seed(1000 + layer)
-        kc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
-        vc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+        if fp8:  # random finite E4M3 codes (the two NaN codes replaced by +-448)
+            kc = torch.randint(0, 256, (N, P, Hkv, D), generator=gen, device=dev, dtype=torch.uint8)
+            vc = torch.randint(0, 256, (N, P, Hkv, D), generator=gen, device=dev, dtype=torch.uint8)
+            for t in (kc, vc):
+                t[(t & 0x7F) == 0x7F] -= 1
+        else:
+            kc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+            vc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
         q = torch.randn((B, Hq, D), generator=gen, device=dev, dtype=torch.bfloat16)
         kn = torch.randn((B, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
         vn = torch.randn((B, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
         layers.append((kc, vc, q, kn, vn, torch.empty_like(q)))
     slots = torch.empty(B, dtype=torch.int32, device=dev)
     scale = case.scale
-    log(f"llama3_8b: {L} layer pools of {N} blocks ready")
+    # fp8 pools: per-KV-head scales (values of this size keep N(0,1) data in range)
+    ks = torch.full((Hkv,), 0.02, dtype=torch.float32, device=dev) if fp8 else None
+    vs = torch.full((Hkv,), 0.02, dtype=torch.float32, device=dev) if fp8 else None
+    log(f"llama3_8b: {L} layer pools of {N} blocks ready ({'fp8 e4m3' if fp8 else 'bf16'})")
 
     def step(ev=None, timed_layer=-1):
         pa.slot_mapping(bt, cu, lens, P, B, out=slots)
         for i, (kc, vc, q, kn, vn, out) in enumerate(layers):
-            pa.reshape_and_cache(kn, vn, slots, kc, vc)
+            pa.reshape_and_cache(kn, vn, slots, kc, vc, ks, vs)
             if i != timed_layer:
-                pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out)
+                pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out, ks, vs)
             else:
                 with pa.kernel_timer(*ev):
-                    pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out)
+                    pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out, ks, vs)
 
     for _ in range(args.warmup):
         step()
@@ -195,7 +210,7 @@ def bench_decode(args):
     # attention only: the same sweep without the slot mapping and the scatters
     def attn_only():
         for kc, vc, q, kn, vn, out in layers:
-            pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out)
+            pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out, ks, vs)
 
     attn_only()
     amarks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -207,14 +222,15 @@ def bench_decode(args):
     torch.cuda.synchronize()
     attn_ms = np.array([amarks[k].elapsed_time(amarks[k + 1]) for k in range(args.steps)])
 
-    dec_b = decode_bytes(case.context_lens, P, Hq, Hkv, D, s)
-    sc_b = scatter_bytes(B, Hkv, D, s)
+    dec_b = decode_bytes(case.context_lens, P, Hq, Hkv, D, s, s_kv)
+    sc_b = scatter_bytes(B, Hkv, D, s, s_kv)
     step_bytes = L * (dec_b + sc_b) + 4 * B  # + the slot-mapping output
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dec_b / (kern_avg_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles("decode.hip", "decode_partition_llama3_8b")
+    traffic = None if fp8 else traffic_from_profiles("decode.hip", "decode_partition_llama3_8b")
     res = {
-        "metric": "paged decode attn KV GB/s (% HBM peak) + us/layer-step, Llama-3-8B shape",
+        "metric": ("paged decode attn (fp8 e4m3 KV) KV GB/s (% HBM peak) + us/layer-step + tokens/s, Llama-3-8B shape"
+                   if fp8 else "paged decode attn KV GB/s (% HBM peak) + us/layer-step, Llama-3-8B shape"),
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -224,10 +240,10 @@ def bench_decode(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3 KV, bf16 q/out" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"llama3_8b decode step: {L} layers x (reshape_and_cache + paged decode), B={B}, "
+            "workload": f"llama3_8b{'_fp8' if fp8 else ''} decode step: {L} layers x (reshape_and_cache + paged decode), B={B}, "
                         f"H_q={Hq}, H_kv={Hkv}, D={D}, P={P}, N={N} blocks/layer, context log-normal "
                         f"(median 1024, sigma 1) clipped to [16, 8192], sum L = {int(case.context_lens.sum())}",
             "global_batch": B,
@@ -243,7 +259,7 @@ def bench_decode(args):
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "roofline_tokens_per_s": round(B / (step_bytes / (HBM_PEAK_GBS * 1e9)), 1),
         "roofline": {
-            "kernel": "decode_partition_kernel<bf16,128>",
+            "kernel": "decode_partition_kernel<fp8_e4m3,128>" if fp8 else "decode_partition_kernel<bf16,128>",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -570,7 +586,7 @@ def main():
         res["cpu_baseline"] = None
     else:
         res, case = bench_decode(args)
-        if args.no_cpu_baseline:
+        if args.no_cpu_baseline or args.workload != "llama3_8b":
             res["cpu_baseline"] = None
         else:
             log("timing the oracle on the host")
