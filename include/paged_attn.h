@@ -220,6 +220,21 @@ int pa_paged_prefill_attention(const void* q, const void* k, const void* v,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_paged_prefill_attention_fp8 -- pa_paged_prefill_attention over fp8 pools
+ * (uint8 E4M3 codes with per-KV-head scales, as for
+ * pa_paged_decode_attention_fp8; q and out bfloat16, q inside the fp16 range).
+ * Other arguments, the workspace and the errors are those of
+ * pa_paged_prefill_attention.
+ */
+int pa_paged_prefill_attention_fp8(const void* q, const void* k, const void* v, const float* k_scale,
+                                   const float* v_scale, const int32_t* cu_seqlens, const int32_t* block_table,
+                                   const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                                   int64_t total_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                   int32_t max_blocks_per_seq, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * pa_set_timing_events -- measurement hook.  While both events are non-NULL
  * (hipEvent_t handles), each attention call on this thread records `start`
  * just before and `stop` just after its main kernel (the decode partition

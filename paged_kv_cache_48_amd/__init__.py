@@ -66,6 +66,11 @@ SIGNATURES = {
         [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
          _i32, _i32, _i32, _i32, _i32, _i64, _i32, _c_void_p, _size, _c_void_p],
     ),
+    "pa_paged_prefill_attention_fp8": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+         _i32, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _c_void_p, _size, _c_void_p],
+    ),
     "pa_copy_blocks": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32, _i32, _i32, _c_void_p]),
     "pa_decode_workspace_size": (_size, [_i32, _i32, _i32, _i32, _i32]),
     "pa_paged_decode_attention": (
@@ -293,9 +298,11 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
 
 def paged_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                             block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                            out: torch.Tensor) -> torch.Tensor:
+                            out: torch.Tensor, k_scale: torch.Tensor | None = None,
+                            v_scale: torch.Tensor | None = None) -> torch.Tensor:
     """Varlen / chunked prefill: ``q``/``out`` ``[T_total, H_q, D]``; ``k``, ``v`` are the
-    paged pools; see ``pa_paged_prefill_attention``."""
+    paged pools; see ``pa_paged_prefill_attention``.  uint8 pools hold fp8
+    (OCP E4M3) codes with per-KV-head scales (``pa_paged_prefill_attention_fp8``)."""
     lib = load_library()
     B = _attn_common(q, k, v, block_table, context_lens, out)
     _dev_tensor(cu_seqlens, "cu_seqlens", torch.int32, 1)
@@ -306,6 +313,13 @@ def paged_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, c
     stream = _stream(q)
     need = prefill_workspace_size(B, T, Hq, Hkv)
     ws = _workspace(q.device, stream, need)
+    if k.dtype == torch.uint8:
+        _scales(k_scale, v_scale, Hkv, k.device)
+        _check(lib.pa_paged_prefill_attention_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_scale.data_ptr(),
+                                                  v_scale.data_ptr(), cu_seqlens.data_ptr(), block_table.data_ptr(),
+                                                  context_lens.data_ptr(), float(scale), out.data_ptr(), B, T, Hq,
+                                                  Hkv, D, P, N, M, ws.data_ptr(), ws.numel(), stream))
+        return out
     _check(lib.pa_paged_prefill_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
                                           block_table.data_ptr(), context_lens.data_ptr(), float(scale),
                                           out.data_ptr(), B, T, Hq, Hkv, D, P, N, M, _dtype_code(q),

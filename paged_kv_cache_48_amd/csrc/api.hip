@@ -278,14 +278,16 @@ size_t pa_prefill_workspace_size(int32_t num_seqs, int64_t total_q_tokens, int32
   return pa::prefill_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads);
 }
 
-int pa_paged_prefill_attention(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
-                               const int32_t* block_table, const int32_t* context_lens, float scale,
-                               void* out, int32_t num_seqs, int64_t total_q_tokens, int32_t num_q_heads,
-                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
-                               void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
-  const char* fn = "pa_paged_prefill_attention";
+}  // extern "C"
+
+namespace {
+
+int prefill_call(const char* fn, const void* q, const void* k, const void* v, const float* k_scale,
+                 const float* v_scale, const int32_t* cu_seqlens, const int32_t* block_table,
+                 const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int64_t total_q_tokens,
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                 int32_t max_blocks_per_seq, int32_t dtype, int32_t kv_dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
   int st = check_attn(fn, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                       max_blocks_per_seq, dtype);
   if (st != PA_OK) return st;
@@ -303,6 +305,7 @@ int pa_paged_prefill_attention(const void* q, const void* k, const void* v, cons
              (long long)total_q_tokens);
   PA_REQUIRE(q && k && v && cu_seqlens && block_table && context_lens && out, PA_ERR_INVALID,
              "%s: null pointer argument", fn);
+  PA_REQUIRE(kv_dtype != pa::kFP8E4M3 || (k_scale && v_scale), PA_ERR_INVALID, "%s: null scale pointer", fn);
   const size_t need = pa::prefill_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads);
   PA_REQUIRE(workspace && workspace_bytes >= need, PA_ERR_WORKSPACE,
              "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
@@ -324,9 +327,41 @@ int pa_paged_prefill_attention(const void* q, const void* k, const void* v, cons
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.dtype = dtype;
-  a.kv_dtype = dtype;
+  a.kv_dtype = kv_dtype;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.workspace = workspace;
   return hip_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream), g_ev_start, g_ev_stop), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_paged_prefill_attention(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                               const int32_t* block_table, const int32_t* context_lens, float scale,
+                               void* out, int32_t num_seqs, int64_t total_q_tokens, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  return prefill_call("pa_paged_prefill_attention", q, k, v, nullptr, nullptr, cu_seqlens, block_table,
+                      context_lens, scale, out, num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                      block_size, num_blocks, max_blocks_per_seq, dtype, dtype, workspace, workspace_bytes, stream);
+}
+
+int pa_paged_prefill_attention_fp8(const void* q, const void* k, const void* v, const float* k_scale,
+                                   const float* v_scale, const int32_t* cu_seqlens, const int32_t* block_table,
+                                   const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                                   int64_t total_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                   int32_t max_blocks_per_seq, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  g_err.clear();
+  return prefill_call("pa_paged_prefill_attention_fp8", q, k, v, k_scale, v_scale, cu_seqlens, block_table,
+                      context_lens, scale, out, num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                      block_size, num_blocks, max_blocks_per_seq, PA_DTYPE_BF16, pa::kFP8E4M3, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"

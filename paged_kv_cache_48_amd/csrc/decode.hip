@@ -173,23 +173,6 @@ struct QType<fp8_e4m3> {
   typedef bf16_bits type;
 };
 
-// Eight E4M3 codes -> eight fp16 values equal to code * 2^-8, exactly: the
-// sign goes to bit 15 and the 7 exponent-and-mantissa bits to bits 7..13, so
-// the e4m3 exponent (bias 7) reads as an fp16 exponent (bias 15) 8 lower, and
-// e4m3 subnormals land on fp16 subnormals.  (The NaN code reads as 480.)
-__device__ __forceinline__ u32x4_t e4m3x8_to_f16(u32x2_t w) {
-  u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    // bytes b0 b1 b2 b3 -> [0, b0, 0, b1] and [0, b2, 0, b3]
-    const uint32_t x01 = __builtin_amdgcn_perm(w[i], w[i], 0x010C000Cu);
-    const uint32_t x23 = __builtin_amdgcn_perm(w[i], w[i], 0x030C020Cu);
-    r[2 * i] = (x01 & 0x80008000u) | ((x01 >> 1) & 0x3F803F80u);
-    r[2 * i + 1] = (x23 & 0x80008000u) | ((x23 >> 1) & 0x3F803F80u);
-  }
-  return r;
-}
-
 // ---------------------------------------------------------------------------
 // Tile geometry.  A tile is 16 consecutive tokens of one KV head.  Lane l
 // loads 16-byte piece l % CPR of the head's row slice for tokens

@@ -160,7 +160,9 @@ struct PrefillParams {
   float scale_log2;
   int Hq, Hkv, G, TQ, P, N, M, cap;
   uint32_t div_m, div_l;  // pos / P = (mulhi(pos, div_m) + pos) >> div_l for 0 <= pos < 2^31
-  uint32_t row_bytes;     // H_kv * D * 2: one token's row of the pool
+  uint32_t row_bytes;     // H_kv * D * element bytes: one token's row of the pool
+  const float* k_scale;   // fp8 pools: per-KV-head scales
+  const float* v_scale;
 };
 
 // Exact unsigned division by the block size with a precomputed multiplier
@@ -194,8 +196,12 @@ __device__ __forceinline__ int vt_col(int d, int u) { return 4 * (u ^ (2 * ((d >
 // and the LDS stores.  Waves 0-3 gather K (D/32 16-byte pieces per thread),
 // waves 4-7 gather V (4 keys x one 16-byte piece per thread).  ok: bit x set
 // when the key of load x is visible and its block id valid.
+// fp8 pools: the same pieces as 8-byte loads of E4M3 codes, widened to fp16
+// (code * 2^-8) when stored.
+template <bool kF8>
 struct TileSet {
-  u32x4_t k[4];
+  typedef typename std::conditional<kF8, u32x2_t, u32x4_t>::type LT;
+  LT k[4];
   uint32_t ok;
 };
 
@@ -204,9 +210,11 @@ struct TileSet {
 // always in bounds -- and is zeroed when the tile is stored.  The block ids of
 // the thread's 4 keys are read from LDS first, all together, so the LDS round
 // trip is paid once per tile.
-template <int D, bool kWide>
+template <int D, bool kWide, bool kF8>
 __device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillLds<D>& s, int hkv, int k0,
-                                          int kmax, TileSet& r) {
+                                          int kmax, TileSet<kF8>& r) {
+  typedef typename TileSet<kF8>::LT LT;
+  constexpr int EB = kF8 ? 1 : 2;  // pool bytes per element
   typedef typename std::conditional<kWide, uint64_t, uint32_t>::type O;
   constexpr int CPR = D / 8;
   constexpr int NK = D / 32;
@@ -225,7 +233,7 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillL
     off[x] = pos[x] - jb * p.P;
     blk[x] = s.ids[jb];
   }
-  const O head = (O)(hkv * D * 2);
+  const O head = (O)(hkv * D * EB);
   r.ok = 0;
   const char* base = kw ? p.kc : p.vc;
 #pragma unroll
@@ -233,14 +241,14 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillL
     if (kw && x >= NK) continue;  // D = 64: two K pieces per thread
     const bool ok = pos[x] < kmax && blk[x] >= 0 && blk[x] < p.N;
     const O o = (ok ? ((O)blk[x] * (O)p.P + (O)off[x]) * (O)p.row_bytes : (O)0) + head +
-                (O)(16 * (kw ? (u + 256 * x) % CPR : dc));
+                (O)(8 * EB * (kw ? (u + 256 * x) % CPR : dc));
     r.ok |= (ok ? 1u : 0u) << x;
-    if (kw || v_wave) r.k[x] = *reinterpret_cast<const u32x4_t*>(base + o);
+    if (kw || v_wave) r.k[x] = *reinterpret_cast<const LT*>(base + o);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(PrefillLds<D>& s, int buf, TileSet& r) {
+template <int D, bool kF8>
+__device__ __forceinline__ void store_tile(PrefillLds<D>& s, int buf, TileSet<kF8>& r_in) {
   constexpr int CPR = D / 8;
   constexpr int NK = D / 32;
   const int tid = threadIdx.x;
@@ -248,10 +256,18 @@ __device__ __forceinline__ void store_tile(PrefillLds<D>& s, int buf, TileSet& r
   const int u = tid & 255;
   const bool v_wave = !kw && uniform((tid & 255) >> 6) < 16 * CPR / 64;
   const uint32_t all = kw ? (1u << NK) - 1u : (v_wave ? 0xfu : 0u);
-  if (__builtin_amdgcn_readfirstlane((int)(__ballot(r.ok != all) != 0))) {
+  if (__builtin_amdgcn_readfirstlane((int)(__ballot(r_in.ok != all) != 0))) {
 #pragma unroll
     for (int x = 0; x < 4; ++x)
-      if (!((r.ok >> x) & 1u)) r.k[x] = u32x4_t{0u, 0u, 0u, 0u};
+      if (!((r_in.ok >> x) & 1u)) r_in.k[x] = typename TileSet<kF8>::LT{};
+  }
+  struct {
+    u32x4_t k[4];
+  } r;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    if constexpr (kF8) r.k[x] = e4m3x8_to_f16(r_in.k[x]);
+    else r.k[x] = r_in.k[x];
   }
   if (kw) {
 #pragma unroll
@@ -289,7 +305,24 @@ struct RowState {
 };
 
 // One 64-key tile for this wave's 32 rows: S^T = K Q^T, online softmax, O^T += V^T P^T.
-template <int D>
+// 16x16x32 products on bf16 operands, or on fp16 ones for fp8 pools.
+template <bool kF8>
+__device__ __forceinline__ f32x4_t mma32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  if constexpr (kF8)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
+template <bool kF8>
+__device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
+  if constexpr (kF8) return pack_f16(lo, hi);
+  else return pack_bf16(lo, hi);
+}
+
+template <int D, bool kF8>
 __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int k0, float scale_log2,
                                             RowState<D>& st) {
   constexpr int NI = RowState<D>::NI, NDB = RowState<D>::NDB;
@@ -302,11 +335,9 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
     sc[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&s.k[buf][(kb * 16 + n) * PrefillLds<D>::KST + 32 * i + 8 * g]));
-      sc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, st.q[0][i]), sc[kb][0], 0,
-                                                          0, 0);
-      sc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, st.q[1][i]), sc[kb][1], 0,
-                                                          0, 0);
+      const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&s.k[buf][(kb * 16 + n) * PrefillLds<D>::KST + 32 * i + 8 * g]);
+      sc[kb][0] = mma32<kF8>(av, st.q[0][i], sc[kb][0]);
+      sc[kb][1] = mma32<kF8>(av, st.q[1][i], sc[kb][1]);
     }
   }
   // scheduling: every K operand read first, then the products
@@ -352,9 +383,9 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
       }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      pop[rb][ks] = u32x4_t{pack_bf16(pv[2 * ks][0], pv[2 * ks][1]), pack_bf16(pv[2 * ks][2], pv[2 * ks][3]),
-                            pack_bf16(pv[2 * ks + 1][0], pv[2 * ks + 1][1]),
-                            pack_bf16(pv[2 * ks + 1][2], pv[2 * ks + 1][3])};
+      pop[rb][ks] = u32x4_t{pack_p<kF8>(pv[2 * ks][0], pv[2 * ks][1]), pack_p<kF8>(pv[2 * ks][2], pv[2 * ks][3]),
+                            pack_p<kF8>(pv[2 * ks + 1][0], pv[2 * ks + 1][1]),
+                            pack_p<kF8>(pv[2 * ks + 1][2], pv[2 * ks + 1][3])};
   }
   // k-slots 0..3 of step ks are keys 32 ks + 4 g + j, slots 4..7 keys 32 ks + 16 + 4 g + j
   u32x4_t va[NDB][2];
@@ -369,21 +400,18 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
   for (int db = 0; db < NDB; ++db) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, va[db][ks]);
-      st.o[db][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, pop[0][ks]), st.o[db][0],
-                                                            0, 0, 0);
-      st.o[db][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, pop[1][ks]), st.o[db][1],
-                                                            0, 0, 0);
+      st.o[db][0] = mma32<kF8>(va[db][ks], pop[0][ks], st.o[db][0]);
+      st.o[db][1] = mma32<kF8>(va[db][ks], pop[1][ks], st.o[db][1]);
     }
   }
 
 }
 
-template <int D>
+template <int D, bool kF8>
 __device__ __forceinline__ void attend(const PrefillLds<D>& s, int buf, int k0, float scale_log2, int wave_max,
                                        RowState<D>& st) {
   if (k0 > wave_max) return;  // every row of this wave is causally done
-  attend_tile<D>(s, buf, k0, scale_log2, st);
+  attend_tile<D, kF8>(s, buf, k0, scale_log2, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -394,7 +422,7 @@ __device__ __forceinline__ void attend(const PrefillLds<D>& s, int buf, int k0, 
 // are in flight while one tile computes, and the item's block ids sit in LDS
 // so no gather address waits on a global load.
 // ---------------------------------------------------------------------------
-template <int D, bool kWide>
+template <int D, bool kWide, bool kF8>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   __shared__ PrefillLds<D> lds;
   __shared__ uint32_t s_item, s_head;
@@ -459,8 +487,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       st.pos[rb] = ok ? start + t0 + tl : -1;
       const int64_t qrow = ((int64_t)(cu0 + t0 + tl) * p.Hq + hkv * p.G + hl) * D;
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < NI; ++i) {
         st.q[rb][i] = ok ? *reinterpret_cast<const u32x4_t*>(p.q + qrow + 32 * i + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
+        if constexpr (kF8) {  // bf16 query -> fp16 operand (exact inside the fp16 range)
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) st.q[rb][i][w2] = pack_f16(bf16_lo(st.q[rb][i][w2]), bf16_hi(st.q[rb][i][w2]));
+        }
+      }
       if (ok) wave_max = max(wave_max, st.pos[rb]);
       st.m[rb] = -INFINITY;
       st.l[rb] = 0.f;
@@ -472,25 +505,29 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     wave_max = uniform(wave_max);
     __syncthreads();  // block ids visible
 
+    // fp8 pools: codes * scale, staged as code * 2^-8
+    const float sl2 = kF8 ? p.scale_log2 * 256.0f * p.k_scale[hkv] : p.scale_log2;
+    const float vmul = kF8 ? 256.0f * p.v_scale[hkv] : 1.0f;
+
     // pipeline: tile j travels in register set j & 1 and LDS buffer j & 1
-    TileSet ra, rb;
-    load_tile<D, kWide>(p, lds, hkv, 0, kmax, ra);
-    if (nkt > 1) load_tile<D, kWide>(p, lds, hkv, kTK, kmax, rb);
-    store_tile<D>(lds, 0, ra);
-    if (nkt > 2) load_tile<D, kWide>(p, lds, hkv, 2 * kTK, kmax, ra);
+    TileSet<kF8> ra, rb;
+    load_tile<D, kWide, kF8>(p, lds, hkv, 0, kmax, ra);
+    if (nkt > 1) load_tile<D, kWide, kF8>(p, lds, hkv, kTK, kmax, rb);
+    store_tile<D, kF8>(lds, 0, ra);
+    if (nkt > 2) load_tile<D, kWide, kF8>(p, lds, hkv, 2 * kTK, kmax, ra);
     __syncthreads();
     for (int kt = 0; kt < nkt; kt += 2) {
-      attend<D>(lds, 0, kt * kTK, p.scale_log2, wave_max, st);
+      attend<D, kF8>(lds, 0, kt * kTK, sl2, wave_max, st);
       if (kt + 1 < nkt) {
-        store_tile<D>(lds, 1, rb);
-        if (kt + 3 < nkt) load_tile<D, kWide>(p, lds, hkv, (kt + 3) * kTK, kmax, rb);
+        store_tile<D, kF8>(lds, 1, rb);
+        if (kt + 3 < nkt) load_tile<D, kWide, kF8>(p, lds, hkv, (kt + 3) * kTK, kmax, rb);
       }
       __syncthreads();
       if (kt + 1 >= nkt) break;
-      attend<D>(lds, 1, (kt + 1) * kTK, p.scale_log2, wave_max, st);
+      attend<D, kF8>(lds, 1, (kt + 1) * kTK, sl2, wave_max, st);
       if (kt + 2 < nkt) {
-        store_tile<D>(lds, 0, ra);
-        if (kt + 4 < nkt) load_tile<D, kWide>(p, lds, hkv, (kt + 4) * kTK, kmax, ra);
+        store_tile<D, kF8>(lds, 0, ra);
+        if (kt + 4 < nkt) load_tile<D, kWide, kF8>(p, lds, hkv, (kt + 4) * kTK, kmax, ra);
       }
       __syncthreads();
     }
@@ -504,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       if (st.pos[rb] < 0) continue;
       const int r = 32 * w + 16 * rb + n;
       const int hl = r / p.TQ, tl = r - hl * p.TQ;
-      const float inv = 1.0f / lt;
+      const float inv = vmul / lt;
       bf16_bits* dst = p.out + ((int64_t)(cu0 + t0 + tl) * p.Hq + hkv * p.G + hl) * D + 4 * g;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -549,7 +586,10 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0,
     p.div_m = (uint32_t)((((uint64_t)1 << (32 + l)) + (uint64_t)a.block_size - 1) / (uint64_t)a.block_size -
                          ((uint64_t)1 << 32));
   }
-  p.row_bytes = (uint32_t)(a.num_kv_heads * a.head_dim * 2);
+  const bool f8 = a.kv_dtype == kFP8E4M3;
+  p.row_bytes = (uint32_t)(a.num_kv_heads * a.head_dim * (f8 ? 1 : 2));
+  p.k_scale = a.k_scale;
+  p.v_scale = a.v_scale;
   p.N = (int)a.num_blocks;
   p.M = a.max_blocks;
   p.cap = (int)((int64_t)a.max_blocks * a.block_size);
@@ -567,13 +607,26 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0,
     const hipError_t e = hipEventRecord(ev0, stream);
     if (e != hipSuccess) return e;
   }
+#define PA_PREFILL_LAUNCH(DD, W, F) \
+  hipLaunchKernelGGL((prefill_kernel<DD, W, F>), dim3(blocks), dim3(kThreads), 0, stream, p)
   if (a.head_dim == 128) {
-    if (wide) hipLaunchKernelGGL((prefill_kernel<128, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((prefill_kernel<128, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    if (f8) {
+      if (wide) PA_PREFILL_LAUNCH(128, true, true);
+      else PA_PREFILL_LAUNCH(128, false, true);
+    } else {
+      if (wide) PA_PREFILL_LAUNCH(128, true, false);
+      else PA_PREFILL_LAUNCH(128, false, false);
+    }
   } else {
-    if (wide) hipLaunchKernelGGL((prefill_kernel<64, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
-    else hipLaunchKernelGGL((prefill_kernel<64, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    if (f8) {
+      if (wide) PA_PREFILL_LAUNCH(64, true, true);
+      else PA_PREFILL_LAUNCH(64, false, true);
+    } else {
+      if (wide) PA_PREFILL_LAUNCH(64, true, false);
+      else PA_PREFILL_LAUNCH(64, false, false);
+    }
   }
+#undef PA_PREFILL_LAUNCH
   if (ev1) {
     const hipError_t e = hipEventRecord(ev1, stream);
     if (e != hipSuccess) return e;

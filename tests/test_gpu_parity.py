@@ -585,3 +585,17 @@ def test_copy_blocks_fp8_pools():
     pa.copy_blocks(dk, dv, idx(pairs))
     torch.cuda.synchronize()
     assert np.array_equal(dk.cpu().numpy(), wk) and np.array_equal(dv.cpu().numpy(), wv)
+
+
+@pytest.mark.parametrize("G,Hkv,D,P", [(4, 2, 128, 16), (1, 3, 64, 16), (2, 2, 128, 7), (8, 1, 64, 1)])
+def test_prefill_fp8_matches_oracle(G, Hkv, D, P):
+    lens = (70, 300, 45, 9, 620)
+    qlens = (70, 100, 33, 1, 300)
+    c = small(P=P, Hq=G * Hkv, Hkv=Hkv, D=D, lens=lens, qlens=qlens, seed=70 + G * D + P)
+    f = Fp8Case(c, _scales(Hkv, 71), _scales(Hkv, 72))
+    out = torch.empty_like(f.q)
+    pa.paged_prefill_attention(f.q, f.kc, f.vc, idx(c.cu_seqlens), f.bt, f.lens, c.scale, out, f.dks, f.dvs)
+    kc, vc = f.kc.cpu().numpy(), f.vc.cpu().numpy()
+    ref = ref_prefill(c.q, ref_dequantize(kc, f.ks), ref_dequantize(vc, f.vs), c.cu_seqlens, c.block_table,
+                      c.context_lens, c.scale)
+    assert_close(out, ref, "bf16", f"fp8 prefill G={G} D={D} P={P}")
