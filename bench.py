@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["llama3_8b", "llama3_8b_fp8", "mixed", "cow", "copy"], default="llama3_8b")
+    ap.add_argument("--workload", choices=["llama3_8b", "llama3_8b_fp8", "mixed", "mixed_fp8", "cow", "copy"],
+                    default="llama3_8b")
     ap.add_argument("--layers", type=int, default=None, help="profile runs only: fewer layers")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -286,8 +287,18 @@ def bench_mixed(args):
     T = case.T_total
     gen = torch.Generator(device=dev)
     gen.manual_seed(77)
-    kc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
-    vc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+    fp8 = args.workload == "mixed_fp8"
+    if fp8:  # random finite E4M3 codes; per-KV-head scales
+        kc = torch.randint(0, 256, (N, P, Hkv, D), generator=gen, device=dev, dtype=torch.uint8)
+        vc = torch.randint(0, 256, (N, P, Hkv, D), generator=gen, device=dev, dtype=torch.uint8)
+        for t in (kc, vc):
+            t[(t & 0x7F) == 0x7F] -= 1
+        ks = torch.full((Hkv,), 0.02, dtype=torch.float32, device=dev)
+        vs = torch.full((Hkv,), 0.02, dtype=torch.float32, device=dev)
+    else:
+        kc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+        vc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+        ks = vs = None
     q = torch.randn((T, Hq, D), generator=gen, device=dev, dtype=torch.bfloat16)
     kn = torch.randn((T, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
     vn = torch.randn((T, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
@@ -304,13 +315,13 @@ def bench_mixed(args):
 
     def step(ev=None):
         pa.slot_mapping(bt, cu, lens, P, T, out=slots)
-        pa.reshape_and_cache(kn, vn, slots, kc, vc)
+        pa.reshape_and_cache(kn, vn, slots, kc, vc, ks, vs)
         if ev is None:
-            pa.paged_prefill_attention(qp, kc, vc, cup, btp, lp, case.scale, outp)
+            pa.paged_prefill_attention(qp, kc, vc, cup, btp, lp, case.scale, outp, ks, vs)
         else:
             with pa.kernel_timer(*ev):
-                pa.paged_prefill_attention(qp, kc, vc, cup, btp, lp, case.scale, outp)
-        pa.paged_decode_attention(qd, kc, vc, btd, ld, case.scale, outd)
+                pa.paged_prefill_attention(qp, kc, vc, cup, btp, lp, case.scale, outp, ks, vs)
+        pa.paged_decode_attention(qd, kc, vc, btd, ld, case.scale, outd, ks, vs)
 
     for _ in range(args.warmup):
         step()
@@ -333,7 +344,8 @@ def bench_mixed(args):
     flops = int(np.sum(4 * D * Hq * (Tb * (Lb - Tb) + Tb * (Tb + 1) // 2)))
     tflops = flops / (kern_ms * 1e-3) / 1e12
     res = {
-        "metric": "mixed chunked-prefill + decode step time (prefill MFMA utilisation)",
+        "metric": "mixed chunked-prefill + decode step time (prefill MFMA utilisation)"
+                  + (", fp8 e4m3 KV" if fp8 else ""),
         "value": round(ms_step, 4),
         "unit": "ms/step",
         "n_gpus": 1,
@@ -343,12 +355,12 @@ def bench_mixed(args):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3 KV, bf16 q/out" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"mixed step: 16 prefill chunks (sum T = {int(Tb.sum())}) + 48 decodes, "
+        "config": {"workload": f"mixed{'_fp8' if fp8 else ''} step: 16 prefill chunks (sum T = {int(Tb.sum())}) + 48 decodes, "
                                f"H_q={Hq}, H_kv={Hkv}, D={D}, P={P}", "global_batch": B, "block_size": P},
         "roofline": {
-            "kernel": "prefill_kernel<128>",
+            "kernel": "prefill_kernel<128, fp8>" if fp8 else "prefill_kernel<128>",
             "bound": "mfma",
             "achieved": round(tflops, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -581,7 +593,7 @@ def main():
         res = bench_copy(args)
     elif args.workload == "cow":
         res = bench_cow(args)
-    elif args.workload == "mixed":
+    elif args.workload in ("mixed", "mixed_fp8"):
         res, case = bench_mixed(args)
         res["cpu_baseline"] = None
     else:
