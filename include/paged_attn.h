@@ -156,6 +156,31 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, i
                    int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                    int32_t dtype, void* stream);
 
+/*
+ * pa_check_metadata -- checks device metadata against the rules the other
+ * calls assume (they never read out of bounds when a rule is broken, but their
+ * output is then unspecified).  Rules, as bits of result[0]:
+ *   PA_CHECK_LENGTH        0 <= context_lens[b] <= max_blocks_per_seq * block_size
+ *   PA_CHECK_BLOCK_ID      the first ceil(context_lens[b] / block_size) entries
+ *                          of block_table row b lie in [0, num_blocks)
+ *   PA_CHECK_CU_SEQLENS    cu_seqlens starts at 0, never decreases and ends at
+ *                          num_tokens (only when cu_seqlens is given)
+ *   PA_CHECK_CHUNK_LENGTH  cu_seqlens[b+1] - cu_seqlens[b] <= context_lens[b]
+ *   PA_CHECK_SLOT          slot_mapping[t] < num_blocks * block_size (negative
+ *                          slots are padding; only when slot_mapping is given)
+ * result[1] counts the offending entries.  result is a device int32[2] that the
+ * call overwrites; read it after the stream reaches the call.  cu_seqlens and
+ * slot_mapping may be NULL.  Duplicate slots are not detected.
+ */
+#define PA_CHECK_LENGTH 1
+#define PA_CHECK_BLOCK_ID 2
+#define PA_CHECK_CU_SEQLENS 4
+#define PA_CHECK_CHUNK_LENGTH 8
+#define PA_CHECK_SLOT 16
+int pa_check_metadata(const int32_t* block_table, const int32_t* context_lens, const int32_t* cu_seqlens,
+                      const int32_t* slot_mapping, int32_t num_seqs, int64_t num_tokens, int64_t num_blocks,
+                      int32_t block_size, int32_t max_blocks_per_seq, int32_t* result, void* stream);
+
 /* Bytes of workspace pa_paged_decode_attention needs for these shapes. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t block_size, int32_t max_blocks_per_seq);

@@ -30,6 +30,7 @@ __all__ = [
     "slot_mapping",
     "reshape_and_cache",
     "copy_blocks",
+    "check_metadata",
     "paged_decode_attention",
     "paged_prefill_attention",
     "decode_workspace_size",
@@ -70,6 +71,10 @@ SIGNATURES = {
         ctypes.c_int,
         [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
          _i32, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _c_void_p, _size, _c_void_p],
+    ),
+    "pa_check_metadata": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p],
     ),
     "pa_copy_blocks": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i32, _i32, _i32, _i32, _c_void_p]),
     "pa_decode_workspace_size": (_size, [_i32, _i32, _i32, _i32, _i32]),
@@ -244,6 +249,38 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: tor
     code = 2 if k_cache.dtype == torch.uint8 else _dtype_code(k_cache)  # uint8: fp8 codes
     _check(lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_mapping.data_ptr(),
                               block_mapping.shape[0], N, P, H, D, code, _stream(k_cache)))
+
+
+CHECK_RULES = {1: "context_lens out of range", 2: "block id out of range", 4: "cu_seqlens malformed",
+               8: "chunk longer than its context", 16: "slot out of range"}
+
+
+def check_metadata(block_table: torch.Tensor, context_lens: torch.Tensor, num_blocks: int, block_size: int,
+                   cu_seqlens: torch.Tensor | None = None, slot_mapping: torch.Tensor | None = None,
+                   num_tokens: int | None = None) -> tuple[int, int]:
+    """Checks device metadata (see ``pa_check_metadata``); synchronises and
+    returns ``(mask of violated rules, offending entries)``; ``(0, 0)`` when valid."""
+    lib = load_library()
+    _dev_tensor(block_table, "block_table", torch.int32, 2)
+    _dev_tensor(context_lens, "context_lens", torch.int32, 1)
+    B = context_lens.shape[0]
+    _req(block_table.shape[0] == B, "block_table must have one row per sequence")
+    if cu_seqlens is not None:
+        _dev_tensor(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        _req(cu_seqlens.shape[0] == B + 1, "cu_seqlens must have num_seqs + 1 entries")
+    if slot_mapping is not None:
+        _dev_tensor(slot_mapping, "slot_mapping", torch.int32, 1)
+    if num_tokens is None:
+        _req(cu_seqlens is None or slot_mapping is not None, "pass num_tokens (cu_seqlens[-1]) with cu_seqlens")
+        num_tokens = slot_mapping.shape[0] if slot_mapping is not None else 0
+    result = torch.empty(2, dtype=torch.int32, device=block_table.device)
+    _check(lib.pa_check_metadata(block_table.data_ptr(), context_lens.data_ptr(),
+                                 cu_seqlens.data_ptr() if cu_seqlens is not None else None,
+                                 slot_mapping.data_ptr() if slot_mapping is not None else None, B, num_tokens,
+                                 int(num_blocks), int(block_size), block_table.shape[1], result.data_ptr(),
+                                 _stream(block_table)))
+    mask, count = result.cpu().tolist()
+    return int(mask), int(count)
 
 
 def _attn_common(q, k_cache, v_cache, block_table, context_lens, out):

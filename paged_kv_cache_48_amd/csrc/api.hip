@@ -174,6 +174,22 @@ int pa_reshape_and_cache_fp8(const void* k, const void* v, const int32_t* slot_m
                     fn);
 }
 
+int pa_check_metadata(const int32_t* block_table, const int32_t* context_lens, const int32_t* cu_seqlens,
+                      const int32_t* slot_mapping, int32_t num_seqs, int64_t num_tokens, int64_t num_blocks,
+                      int32_t block_size, int32_t max_blocks_per_seq, int32_t* result, void* stream) {
+  g_err.clear();
+  const char* fn = "pa_check_metadata";
+  PA_REQUIRE(num_seqs >= 0 && num_tokens >= 0 && num_tokens <= INT_MAX, PA_ERR_INVALID, "%s: negative sizes", fn);
+  PA_REQUIRE(block_size >= 1 && max_blocks_per_seq >= 1 && num_blocks >= 1, PA_ERR_INVALID,
+             "%s: block_size, max_blocks_per_seq and num_blocks must be >= 1", fn);
+  PA_REQUIRE(result, PA_ERR_INVALID, "%s: null result pointer", fn);
+  PA_REQUIRE(num_seqs == 0 || (block_table && context_lens), PA_ERR_INVALID, "%s: null pointer argument", fn);
+  return hip_status(pa::launch_check_metadata(block_table, context_lens, cu_seqlens, slot_mapping, num_seqs,
+                                              num_tokens, num_blocks, block_size, max_blocks_per_seq, result,
+                                              static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int64_t num_pairs,
                    int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                    void* stream) {

@@ -8,6 +8,7 @@
 // row copy: it moves raw bits and does no floating-point work.
 #include "common.h"
 #include "launch.h"
+#include "paged_attn.h"
 
 namespace pa {
 
@@ -176,6 +177,74 @@ hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, const int3
     hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const float*)k, (const float*)v, slot_mapping, (uint8_t*)k_cache, (uint8_t*)v_cache,
                        k_scale, v_scale, num_tokens, row_elems, head_dim, pool_rows);
+  return hipGetLastError();
+}
+
+// Metadata check.  result[0] collects a bitmask of the violated rules,
+// result[1] the number of offending entries (both cleared by the first
+// kernel).  One thread per request for lengths, tables and chunks, one per
+// token for slots.
+__global__ __launch_bounds__(64) void check_metadata_clear_kernel(int32_t* result) {
+  if (threadIdx.x < 2) result[threadIdx.x] = 0;
+}
+
+__global__ __launch_bounds__(256) void check_metadata_kernel(const int32_t* __restrict__ block_table,
+                                                             const int32_t* __restrict__ lens,
+                                                             const int32_t* __restrict__ cu,
+                                                             const int32_t* __restrict__ slots, int num_seqs,
+                                                             int64_t num_tokens, int64_t num_blocks, int block_size,
+                                                             int max_blocks, int32_t* result) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t bad = 0;
+  int count = 0;
+  if (i < num_seqs) {
+    const int b = (int)i;
+    const int64_t L = lens[b];
+    if (L < 0 || L > (int64_t)max_blocks * block_size) {
+      bad |= PA_CHECK_LENGTH;
+      ++count;
+    }
+    const int64_t nb = L <= 0 ? 0 : min((L + block_size - 1) / block_size, (int64_t)max_blocks);
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t id = block_table[(int64_t)b * max_blocks + j];
+      if (id < 0 || id >= num_blocks) {
+        bad |= PA_CHECK_BLOCK_ID;
+        ++count;
+      }
+    }
+    if (cu) {
+      const int64_t c0 = cu[b], c1 = cu[b + 1];
+      if ((b == 0 && c0 != 0) || c1 < c0 || (b == num_seqs - 1 && c1 != num_tokens)) {
+        bad |= PA_CHECK_CU_SEQLENS;
+        ++count;
+      } else if (c1 - c0 > L) {
+        bad |= PA_CHECK_CHUNK_LENGTH;
+        ++count;
+      }
+    }
+  }
+  if (slots && i < num_tokens) {
+    const int64_t sl = slots[i];
+    if (sl >= num_blocks * block_size) {
+      bad |= PA_CHECK_SLOT;
+      ++count;
+    }
+  }
+  if (bad) {
+    atomicOr(reinterpret_cast<uint32_t*>(result), bad);
+    atomicAdd(result + 1, count);
+  }
+}
+
+hipError_t launch_check_metadata(const int32_t* block_table, const int32_t* context_lens, const int32_t* cu_seqlens,
+                                 const int32_t* slot_mapping, int num_seqs, int64_t num_tokens, int64_t num_blocks,
+                                 int block_size, int max_blocks, int32_t* result, hipStream_t stream) {
+  hipLaunchKernelGGL(check_metadata_clear_kernel, dim3(1), dim3(64), 0, stream, result);
+  const int64_t n = max((int64_t)num_seqs, slot_mapping ? num_tokens : (int64_t)0);
+  if (n > 0)
+    hipLaunchKernelGGL(check_metadata_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, block_table,
+                       context_lens, cu_seqlens, slot_mapping, num_seqs, num_tokens, num_blocks, block_size, max_blocks,
+                       result);
   return hipGetLastError();
 }
 

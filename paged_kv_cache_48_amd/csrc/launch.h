@@ -36,6 +36,10 @@ hipError_t launch_reshape_and_cache_fp8(const void* k, const void* v, const int3
                                         int64_t num_tokens, int64_t pool_rows, int row_elems, int head_dim,
                                         int src_dtype, hipStream_t stream);
 
+hipError_t launch_check_metadata(const int32_t* block_table, const int32_t* context_lens, const int32_t* cu_seqlens,
+                                 const int32_t* slot_mapping, int num_seqs, int64_t num_tokens, int64_t num_blocks,
+                                 int block_size, int max_blocks, int32_t* result, hipStream_t stream);
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int64_t num_pairs,
                               int64_t num_blocks, int64_t block_bytes, hipStream_t stream);
 

@@ -159,3 +159,11 @@ def test_copy_blocks_validation(lib):
     assert f(1, 1, 1, 4, 100, 16, 1, 4, BF16, NUL) == UNSUPPORTED   # 8-byte rows
     assert f(NUL, 1, 1, 4, 100, 16, 8, 128, BF16, NUL) == INVALID
     assert f(NUL, NUL, NUL, 0, 100, 16, 8, 128, BF16, NUL) == OK    # no pairs: no-op
+
+
+def test_check_metadata_validation(lib):
+    f = lib.pa_check_metadata
+    assert f(1, 1, NUL, NUL, -1, 0, 10, 16, 4, 1, NUL) == INVALID
+    assert f(1, 1, NUL, NUL, 2, 0, 10, 0, 4, 1, NUL) == INVALID
+    assert f(1, 1, NUL, NUL, 2, 0, 10, 16, 4, NUL, NUL) == INVALID   # no result buffer
+    assert f(NUL, 1, NUL, NUL, 2, 0, 10, 16, 4, 1, NUL) == INVALID

@@ -599,3 +599,31 @@ def test_prefill_fp8_matches_oracle(G, Hkv, D, P):
     ref = ref_prefill(c.q, ref_dequantize(kc, f.ks), ref_dequantize(vc, f.vs), c.cu_seqlens, c.block_table,
                       c.context_lens, c.scale)
     assert_close(out, ref, "bf16", f"fp8 prefill G={G} D={D} P={P}")
+
+
+def test_check_metadata_flags_each_rule():
+    c = small(P=16, Hq=8, Hkv=2, lens=(40, 300, 17), qlens=(5, 300, 1), seed=80)
+    bt, lens, cu = idx(c.block_table), idx(c.context_lens), idx(c.cu_seqlens)
+    N, P, T = c.num_blocks, c.block_size, c.T_total
+    slots = pa.slot_mapping(bt, cu, lens, P, T)
+    assert pa.check_metadata(bt, lens, N, P, cu, slots) == (0, 0)
+    bad = lens.clone()
+    bad[1] = c.max_blocks_per_seq * P + 1
+    assert pa.check_metadata(bt, bad, N, P)[0] == 1
+    bt2 = bt.clone()
+    bt2[0, 1] = N
+    bt2[2, 0] = -3
+    assert pa.check_metadata(bt2, lens, N, P) == (2, 2)
+    bt3 = bt.clone()
+    bt3[0, c.max_blocks_per_seq - 1] = -1  # past the request's blocks: never read, not an error
+    assert pa.check_metadata(bt3, lens, N, P) == (0, 0)
+    cu2 = cu.clone()
+    cu2[2] = cu2[1] - 1
+    assert pa.check_metadata(bt, lens, N, P, cu2, slots)[0] & 4
+    long_chunk = lens.clone()
+    long_chunk[0] = 3  # 5 new tokens over a context of 3
+    assert pa.check_metadata(bt, long_chunk, N, P, cu, slots)[0] & 8
+    s2 = slots.clone()
+    s2[3] = N * P
+    s2[4] = -1  # padding is fine
+    assert pa.check_metadata(bt, lens, N, P, cu, s2) == (16, 1)
