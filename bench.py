@@ -21,6 +21,7 @@ region).  ``cpu_baseline`` times the fp64 oracle on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import hashlib
 import json
 import math
@@ -47,7 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["llama3_8b", "llama3_8b_fp8", "mixed", "mixed_fp8", "cow", "copy"],
+    ap.add_argument("--workload", choices=["llama3_8b", "llama3_8b_fp8", "mixed", "mixed_fp8", "mixed_single",
+                                           "mixed_single_fp8", "cow", "copy"],
                     default="llama3_8b")
     ap.add_argument("--layers", type=int, default=None, help="profile runs only: fewer layers")
     ap.add_argument("--block-size", type=int, default=None)
@@ -74,9 +76,21 @@ def scatter_bytes(T, Hkv, D, s, s_kv=None):
     return int(2 * T * Hkv * D * (s + s_kv) + 4 * T)
 
 
-def traffic_from_profiles(kernel_file: str, key: str):
+# sources the decode partition kernel is compiled from
+DECODE_SOURCES = ("decode.hip", "decode_dev.h", "common.h")
+
+
+def sources_sha(files) -> str:
+    h = hashlib.sha256()
+    for name in files:
+        with open(os.path.join(ROOT, "paged_kv_cache_48_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profiles(files, key: str):
     """Measured HBM bytes per launch from profiles/traffic.json, if it was taken
-    for the current source of the kernel."""
+    for the current sources of the kernel."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -84,9 +98,7 @@ def traffic_from_profiles(kernel_file: str, key: str):
         rec = json.load(f).get(key)
     if not rec:
         return None
-    src = os.path.join(ROOT, "paged_kv_cache_48_amd", "csrc", kernel_file)
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != sources_sha(files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -228,7 +240,7 @@ def bench_decode(args):
     step_bytes = L * (dec_b + sc_b) + 4 * B  # + the slot-mapping output
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dec_b / (kern_avg_ms * 1e-3) / 1e9
-    traffic = None if fp8 else traffic_from_profiles("decode.hip", "decode_partition_llama3_8b")
+    traffic = None if fp8 else traffic_from_profiles(DECODE_SOURCES, "decode_partition_llama3_8b")
     res = {
         "metric": ("paged decode attn (fp8 e4m3 KV) KV GB/s (% HBM peak) + us/layer-step + tokens/s, Llama-3-8B shape"
                    if fp8 else "paged decode attn KV GB/s (% HBM peak) + us/layer-step, Llama-3-8B shape"),
@@ -275,8 +287,11 @@ def bench_decode(args):
 
 
 def bench_mixed(args):
-    """Mixed chunked-prefill + decode step (one layer): scatter, prefill of 16
-    chunks, decode of 48 requests.  Roofline: the prefill kernel vs bf16 MFMA."""
+    """Mixed chunked-prefill + decode step (one layer): scatter, then prefill of
+    16 chunks and decode of 48 requests, as two calls (``mixed``) or as one
+    single-launch mixed call over the whole ragged batch (``mixed_single``).
+    Roofline: the prefill (or mixed) kernel vs bf16 MFMA, counting the prefill
+    flops only."""
     import paged_kv_cache_48_amd as pa
     from workloads import config_case
 
@@ -287,7 +302,8 @@ def bench_mixed(args):
     T = case.T_total
     gen = torch.Generator(device=dev)
     gen.manual_seed(77)
-    fp8 = args.workload == "mixed_fp8"
+    fp8 = args.workload.endswith("_fp8")
+    single = args.workload.startswith("mixed_single")
     if fp8:  # random finite E4M3 codes; per-KV-head scales
         kc = torch.randint(0, 256, (N, P, Hkv, D), generator=gen, device=dev, dtype=torch.uint8)
         vc = torch.randint(0, 256, (N, P, Hkv, D), generator=gen, device=dev, dtype=torch.uint8)
@@ -312,10 +328,15 @@ def bench_mixed(args):
     cup, btp, lp = cu[: npf + 1].contiguous(), bt[:npf].contiguous(), lens[:npf].contiguous()
     btd, ld = bt[npf:].contiguous(), lens[npf:].contiguous()
     slots = torch.empty(T, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
 
     def step(ev=None):
         pa.slot_mapping(bt, cu, lens, P, T, out=slots)
         pa.reshape_and_cache(kn, vn, slots, kc, vc, ks, vs)
+        if single:
+            with pa.kernel_timer(*ev) if ev is not None else contextlib.nullcontext():
+                pa.paged_mixed_attention(q, kc, vc, cu, bt, lens, case.scale, out, ks, vs)
+            return
         if ev is None:
             pa.paged_prefill_attention(qp, kc, vc, cup, btp, lp, case.scale, outp, ks, vs)
         else:
@@ -343,9 +364,12 @@ def bench_mixed(args):
     Lb = case.context_lens[:npf].astype(np.int64)
     flops = int(np.sum(4 * D * Hq * (Tb * (Lb - Tb) + Tb * (Tb + 1) // 2)))
     tflops = flops / (kern_ms * 1e-3) / 1e12
+    Ld = case.context_lens[npf:].astype(np.int64)
+    dec_bytes = decode_bytes(Ld, P, Hq, Hkv, D, 2, 1 if fp8 else 2)
+    kname = ("mixed_kernel" if single else "prefill_kernel") + ("<128, fp8>" if fp8 else "<128>")
     res = {
-        "metric": "mixed chunked-prefill + decode step time (prefill MFMA utilisation)"
-                  + (", fp8 e4m3 KV" if fp8 else ""),
+        "metric": ("single-launch " if single else "") + "mixed chunked-prefill + decode step time "
+                  "(prefill MFMA utilisation)" + (", fp8 e4m3 KV" if fp8 else ""),
         "value": round(ms_step, 4),
         "unit": "ms/step",
         "n_gpus": 1,
@@ -357,10 +381,12 @@ def bench_mixed(args):
         "vs_baseline": None,
         "dtype": "fp8_e4m3 KV, bf16 q/out" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"mixed{'_fp8' if fp8 else ''} step: 16 prefill chunks (sum T = {int(Tb.sum())}) + 48 decodes, "
-                               f"H_q={Hq}, H_kv={Hkv}, D={D}, P={P}", "global_batch": B, "block_size": P},
+        "config": {"workload": f"{args.workload} step: 16 prefill chunks (sum T = {int(Tb.sum())}) + 48 decodes, "
+                               f"H_q={Hq}, H_kv={Hkv}, D={D}, P={P}"
+                               + (", one mixed call" if single else ", prefill and decode calls"),
+                   "global_batch": B, "block_size": P},
         "roofline": {
-            "kernel": "prefill_kernel<128, fp8>" if fp8 else "prefill_kernel<128>",
+            "kernel": kname,
             "bound": "mfma",
             "achieved": round(tflops, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -371,6 +397,12 @@ def bench_mixed(args):
             "avg_launch_us": round(kern_ms * 1e3, 2),
         },
     }
+    if single:
+        # the mixed kernel also reads the decodes' KV: its lower bound is the
+        # larger of the two roofline times (the resources could overlap fully)
+        roof_us = max(flops / (MFMA_BF16_PEAK_TFLOPS * 1e12), dec_bytes / (HBM_PEAK_GBS * 1e9)) * 1e6
+        res["roofline"].update({"decode_bytes_per_launch": int(dec_bytes), "roofline_time_us": round(roof_us, 1),
+                                "time_frac": round(roof_us / (kern_ms * 1e3), 4)})
     return res, case
 
 
@@ -452,6 +484,8 @@ PROFILE_RUNS = {
              "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
     "trace_mixed": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_mixed -o mixed -- "
                    "python3 bench.py --workload mixed --steps 10 --warmup 2",
+    "trace_mixsingle": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_mixsingle -o mixsingle -- "
+                       "python3 bench.py --workload mixed_single --steps 10 --warmup 2",
     "trace_cow": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_cow -o cow -- "
                  "python3 bench.py --workload cow --steps 20 --warmup 3",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch -o fetch -- "
@@ -497,8 +531,8 @@ def summarize_profiles(d):
 
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
-    src = os.path.join(ROOT, "paged_kv_cache_48_amd", "csrc", "decode.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = sources_sha(DECODE_SOURCES)
+    sha_line = f"decode kernel sources ({', '.join(DECODE_SOURCES)}) sha256: {sha}"
     one = lambda pat: (glob.glob(os.path.join(d, pat)) or [None])[0]  # noqa: E731
 
     stats = one("prof_decode/*kernel_stats.csv")
@@ -509,7 +543,7 @@ def summarize_profiles(d):
                     "in-kernel plan, reduce), B=256, H_q=32, H_kv=8, D=128, P=16, bf16), rocprofv3 kernel statistics.\n")
             f.write("command (run from the repository root, DIR = an output folder):\n  "
                     + PROFILE_RUNS["trace"] + "\n")
-            f.write(f"decode.hip sha256: {sha}\n\n")
+            f.write(sha_line + "\n\n")
             f.write("\n".join(table) + "\n")
     stats = one("prof_mixed/*kernel_stats.csv")
     if stats:
@@ -519,6 +553,17 @@ def summarize_profiles(d):
                     "Llama-3-8B heads, P=16, bf16), rocprofv3 kernel statistics.\n")
             f.write("command (run from the repository root, DIR = an output folder):\n  "
                     + PROFILE_RUNS["trace_mixed"] + "\n\n")
+            f.write("\n".join(table) + "\n")
+
+    stats = one("prof_mixsingle/*kernel_stats.csv")
+    if stats:
+        table, _ = _stats_table(stats)
+        with open(os.path.join(prof, "mixed_single_launch_kernel_stats.txt"), "w") as f:
+            f.write("The same mixed step as one single-launch mixed call over the whole ragged batch (64 requests:\n"
+                    "16 prefill chunks + 48 one-token decodes, Llama-3-8B heads, P=16, bf16), then the merge of the\n"
+                    "decodes' partitions, rocprofv3 kernel statistics.\n")
+            f.write("command (run from the repository root, DIR = an output folder):\n  "
+                    + PROFILE_RUNS["trace_mixsingle"] + "\n\n")
             f.write("\n".join(table) + "\n")
 
     stats = one("prof_cow/*kernel_stats.csv")
@@ -555,7 +600,7 @@ def summarize_profiles(d):
         "commands (run from the repository root, DIR = an output folder):",
         "  " + PROFILE_RUNS["fetch"], "  " + PROFILE_RUNS["write"],
         "  " + PROFILE_RUNS["copyf"], "  " + PROFILE_RUNS["copyw"],
-        f"decode.hip sha256: {sha}", "",
+        sha_line, "",
         f"calibration: torch copy_ of 1 GiB reads FETCH_SIZE {cf_kib:.0f} KiB and WRITE_SIZE {cw_kib:.0f} KiB "
         f"per dispatch -> scale {kf:.4f} (fetch), {kw:.4f} (write)",
         f"partition kernel: FETCH_SIZE {fetch_kib:.0f} KiB, WRITE_SIZE {write_kib:.0f} KiB per dispatch "
@@ -593,7 +638,7 @@ def main():
         res = bench_copy(args)
     elif args.workload == "cow":
         res = bench_cow(args)
-    elif args.workload in ("mixed", "mixed_fp8"):
+    elif args.workload.startswith("mixed"):
         res, case = bench_mixed(args)
         res["cpu_baseline"] = None
     else:

@@ -259,11 +259,60 @@ int pa_paged_prefill_attention_fp8(const void* q, const void* k, const void* v, 
                                    int32_t max_blocks_per_seq, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* Bytes of workspace pa_paged_mixed_attention needs for these shapes. */
+size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq);
+
+/*
+ * pa_paged_mixed_attention -- one step's ragged mix of decode requests and
+ * prefill chunks in a single persistent launch (tiny-vllm-py "KV Cache": a
+ * step may mix prefill and decode, which wants ragged batches and a kernel
+ * that takes both; ember "Deliberately out of scope": a prefill/decode mix
+ * per step).  It computes exactly what pa_paged_prefill_attention computes on
+ * the same arguments: request b's chunk of T_b = cu_seqlens[b+1] -
+ * cu_seqlens[b] tokens, row i at absolute position L_b - T_b + i, attending
+ * causally to keys 0 .. L_b - T_b + i; a chunk of one token is a decode step
+ * over all L_b keys.  One-token chunks are computed as the decode call's
+ * split-context partitions (merged by a second, small kernel), longer chunks
+ * as the prefill call's items; requests with T_b > L_b (or T_b = 0) leave
+ * their rows untouched.
+ *   q, out        [total_q_tokens, num_q_heads, head_dim], packed by request
+ *   k, v          [num_blocks, block_size, num_kv_heads, head_dim]
+ *   cu_seqlens    int32 [num_seqs + 1]
+ *   block_table   int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens  int32 [num_seqs]
+ *   workspace     at least pa_mixed_workspace_size() bytes, not shared with a
+ *                 concurrently running call; its contents on entry do not
+ *                 matter (as for pa_paged_decode_attention)
+ * Restrictions and errors are those of pa_paged_prefill_attention, plus:
+ * num_seqs above 1024 returns PA_ERR_UNSUPPORTED (the work lists are derived
+ * on chip), as do batches whose work lists exceed 2^24 - 8192 items.
+ */
+int pa_paged_mixed_attention(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                             const int32_t* block_table, const int32_t* context_lens, float scale, void* out,
+                             int32_t num_seqs, int64_t total_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_paged_mixed_attention_fp8 -- pa_paged_mixed_attention over fp8 pools
+ * (uint8 E4M3 codes with per-KV-head scales, as for
+ * pa_paged_decode_attention_fp8; q and out bfloat16, q inside the fp16 range).
+ * Other arguments, the workspace and the errors are those of
+ * pa_paged_mixed_attention.
+ */
+int pa_paged_mixed_attention_fp8(const void* q, const void* k, const void* v, const float* k_scale,
+                                 const float* v_scale, const int32_t* cu_seqlens, const int32_t* block_table,
+                                 const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                                 int64_t total_q_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /*
  * pa_set_timing_events -- measurement hook.  While both events are non-NULL
  * (hipEvent_t handles), each attention call on this thread records `start`
  * just before and `stop` just after its main kernel (the decode partition
- * kernel, or the prefill kernel), on the call's stream, so the caller can time
+ * kernel, the prefill kernel or the mixed kernel), on the call's stream, so the caller can time
  * that kernel alone with hipEventElapsedTime.  Pass NULL, NULL to turn it off.
  */
 int pa_set_timing_events(void* start_event, void* stop_event);

@@ -33,8 +33,10 @@ __all__ = [
     "check_metadata",
     "paged_decode_attention",
     "paged_prefill_attention",
+    "paged_mixed_attention",
     "decode_workspace_size",
     "prefill_workspace_size",
+    "mixed_workspace_size",
     "kernel_timer",
 ]
 
@@ -82,6 +84,17 @@ SIGNATURES = {
         ctypes.c_int,
         [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
          _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _c_void_p, _size, _c_void_p],
+    ),
+    "pa_mixed_workspace_size": (_size, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_paged_mixed_attention": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+         _i32, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _c_void_p, _size, _c_void_p],
+    ),
+    "pa_paged_mixed_attention_fp8": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+         _i32, _i64, _i32, _i32, _i32, _i32, _i64, _i32, _c_void_p, _size, _c_void_p],
     ),
     "pa_prefill_workspace_size": (_size, [_i32, _i64, _i32, _i32]),
     "pa_paged_prefill_attention": (
@@ -172,6 +185,11 @@ def decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_block
 
 def prefill_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads) -> int:
     return int(load_library().pa_prefill_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads))
+
+
+def mixed_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq) -> int:
+    return int(load_library().pa_mixed_workspace_size(num_seqs, num_q_heads, head_dim, block_size,
+                                                      max_blocks_per_seq))
 
 
 def slot_mapping(block_table: torch.Tensor, cu_seqlens: torch.Tensor, context_lens: torch.Tensor,
@@ -361,6 +379,37 @@ def paged_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, c
                                           block_table.data_ptr(), context_lens.data_ptr(), float(scale),
                                           out.data_ptr(), B, T, Hq, Hkv, D, P, N, M, _dtype_code(q),
                                           ws.data_ptr(), ws.numel(), stream))
+    return out
+
+
+def paged_mixed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                          block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                          out: torch.Tensor, k_scale: torch.Tensor | None = None,
+                          v_scale: torch.Tensor | None = None) -> torch.Tensor:
+    """One step's ragged mix of decodes (one-token chunks) and prefill chunks in one
+    persistent launch; same arguments and result as ``paged_prefill_attention``
+    (see ``pa_paged_mixed_attention``).  uint8 pools hold fp8 (OCP E4M3) codes
+    with per-KV-head scales (``pa_paged_mixed_attention_fp8``)."""
+    lib = load_library()
+    B = _attn_common(q, k, v, block_table, context_lens, out)
+    _dev_tensor(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _req(cu_seqlens.shape[0] == B + 1, "cu_seqlens must have num_seqs + 1 entries")
+    N, P, Hkv, D = k.shape
+    T, Hq, _ = q.shape
+    M = block_table.shape[1]
+    stream = _stream(q)
+    ws = _workspace(q.device, stream, mixed_workspace_size(B, Hq, D, P, M))
+    if k.dtype == torch.uint8:
+        _scales(k_scale, v_scale, Hkv, k.device)
+        _check(lib.pa_paged_mixed_attention_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_scale.data_ptr(),
+                                                v_scale.data_ptr(), cu_seqlens.data_ptr(), block_table.data_ptr(),
+                                                context_lens.data_ptr(), float(scale), out.data_ptr(), B, T, Hq,
+                                                Hkv, D, P, N, M, ws.data_ptr(), ws.numel(), stream))
+        return out
+    _check(lib.pa_paged_mixed_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens.data_ptr(),
+                                        block_table.data_ptr(), context_lens.data_ptr(), float(scale),
+                                        out.data_ptr(), B, T, Hq, Hkv, D, P, N, M, _dtype_code(q),
+                                        ws.data_ptr(), ws.numel(), stream))
     return out
 
 

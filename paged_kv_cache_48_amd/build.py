@@ -16,12 +16,12 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
-SOURCES = ["api.hip", "cache_ops.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "cache_ops.hip", "decode.hip", "prefill.hip", "mixed.hip"]
 # per-source extra flags: the attention kernels keep their MFMA results in
 # VGPRs (the softmax reads the scores and rescales the accumulators on the
 # VALU, which would otherwise copy them out of the accumulation registers on
 # every tile)
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in ("decode.hip", "prefill.hip", "mixed.hip")}
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 FLAGS = [

@@ -298,8 +298,11 @@ size_t pa_prefill_workspace_size(int32_t num_seqs, int64_t total_q_tokens, int32
 
 namespace {
 
-int prefill_call(const char* fn, const void* q, const void* k, const void* v, const float* k_scale,
-                 const float* v_scale, const int32_t* cu_seqlens, const int32_t* block_table,
+// Kinds of varlen call: the prefill kernel, or the mixed prefill/decode kernel.
+enum VarlenKind { kVarlenPrefill, kVarlenMixed };
+
+int prefill_call(VarlenKind kind, const char* fn, const void* q, const void* k, const void* v,
+                 const float* k_scale, const float* v_scale, const int32_t* cu_seqlens, const int32_t* block_table,
                  const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int64_t total_q_tokens,
                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                  int32_t max_blocks_per_seq, int32_t dtype, int32_t kv_dtype, void* workspace,
@@ -322,7 +325,18 @@ int prefill_call(const char* fn, const void* q, const void* k, const void* v, co
   PA_REQUIRE(q && k && v && cu_seqlens && block_table && context_lens && out, PA_ERR_INVALID,
              "%s: null pointer argument", fn);
   PA_REQUIRE(kv_dtype != pa::kFP8E4M3 || (k_scale && v_scale), PA_ERR_INVALID, "%s: null scale pointer", fn);
-  const size_t need = pa::prefill_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads);
+  if (kind == kVarlenMixed) {
+    PA_REQUIRE(num_seqs <= pa::mixed_max_seqs(), PA_ERR_UNSUPPORTED,
+               "%s: more than %d requests is not provided (the work lists are derived on chip)", fn,
+               pa::mixed_max_seqs());
+    PA_REQUIRE(pa::mixed_fits(num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim, block_size,
+                              max_blocks_per_seq),
+               PA_ERR_UNSUPPORTED, "%s: the batch's work lists exceed the queue counters' range", fn);
+  }
+  const size_t need =
+      kind == kVarlenMixed
+          ? pa::mixed_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq)
+          : pa::prefill_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads);
   PA_REQUIRE(workspace && workspace_bytes >= need, PA_ERR_WORKSPACE,
              "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
   pa::AttnArgs a{};
@@ -347,6 +361,8 @@ int prefill_call(const char* fn, const void* q, const void* k, const void* v, co
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.workspace = workspace;
+  if (kind == kVarlenMixed)
+    return hip_status(pa::launch_mixed(a, static_cast<hipStream_t>(stream), g_ev_start, g_ev_stop), fn);
   return hip_status(pa::launch_prefill(a, static_cast<hipStream_t>(stream), g_ev_start, g_ev_stop), fn);
 }
 
@@ -361,9 +377,10 @@ int pa_paged_prefill_attention(const void* q, const void* k, const void* v, cons
                                int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
                                void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
-  return prefill_call("pa_paged_prefill_attention", q, k, v, nullptr, nullptr, cu_seqlens, block_table,
-                      context_lens, scale, out, num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim,
-                      block_size, num_blocks, max_blocks_per_seq, dtype, dtype, workspace, workspace_bytes, stream);
+  return prefill_call(kVarlenPrefill, "pa_paged_prefill_attention", q, k, v, nullptr, nullptr, cu_seqlens,
+                      block_table, context_lens, scale, out, num_seqs, total_q_tokens, num_q_heads, num_kv_heads,
+                      head_dim, block_size, num_blocks, max_blocks_per_seq, dtype, dtype, workspace, workspace_bytes,
+                      stream);
 }
 
 int pa_paged_prefill_attention_fp8(const void* q, const void* k, const void* v, const float* k_scale,
@@ -374,9 +391,39 @@ int pa_paged_prefill_attention_fp8(const void* q, const void* k, const void* v, 
                                    int32_t max_blocks_per_seq, void* workspace, size_t workspace_bytes,
                                    void* stream) {
   g_err.clear();
-  return prefill_call("pa_paged_prefill_attention_fp8", q, k, v, k_scale, v_scale, cu_seqlens, block_table,
+  return prefill_call(kVarlenPrefill, "pa_paged_prefill_attention_fp8", q, k, v, k_scale, v_scale, cu_seqlens,
+                      block_table, context_lens, scale, out, num_seqs, total_q_tokens, num_q_heads, num_kv_heads,
+                      head_dim, block_size, num_blocks, max_blocks_per_seq, PA_DTYPE_BF16, pa::kFP8E4M3, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq) {
+  if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || block_size < 1 || max_blocks_per_seq < 1) return 0;
+  return pa::mixed_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq);
+}
+
+int pa_paged_mixed_attention(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                             const int32_t* block_table, const int32_t* context_lens, float scale, void* out,
+                             int32_t num_seqs, int64_t total_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  return prefill_call(kVarlenMixed, "pa_paged_mixed_attention", q, k, v, nullptr, nullptr, cu_seqlens, block_table,
                       context_lens, scale, out, num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim,
-                      block_size, num_blocks, max_blocks_per_seq, PA_DTYPE_BF16, pa::kFP8E4M3, workspace,
+                      block_size, num_blocks, max_blocks_per_seq, dtype, dtype, workspace, workspace_bytes, stream);
+}
+
+int pa_paged_mixed_attention_fp8(const void* q, const void* k, const void* v, const float* k_scale,
+                                 const float* v_scale, const int32_t* cu_seqlens, const int32_t* block_table,
+                                 const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                                 int64_t total_q_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  return prefill_call(kVarlenMixed, "pa_paged_mixed_attention_fp8", q, k, v, k_scale, v_scale, cu_seqlens,
+                      block_table, context_lens, scale, out, num_seqs, total_q_tokens, num_q_heads, num_kv_heads,
+                      head_dim, block_size, num_blocks, max_blocks_per_seq, PA_DTYPE_BF16, pa::kFP8E4M3, workspace,
                       workspace_bytes, stream);
 }
 

@@ -38,66 +38,13 @@
 //   * Tokens past the partition end never load: tail slots of a block may hold
 //     anything (even NaN).  Block ids outside [0, N) are never dereferenced
 //     (their rows read as zeros, so the result is unspecified but safe).
-#include <math.h>
-#include <unistd.h>
-
-#include <atomic>
-#include <chrono>
-#include <type_traits>
-
-#include "common.h"
-#include "launch.h"
+#include "decode_dev.h"
 
 namespace pa {
 
 namespace {
 
-constexpr int kTile = 16;                        // tokens per MFMA tile
-
-constexpr int kWavesPerBlock = 4;
-constexpr int kMaxStaticRounds = 64;  // static items per wave: one descriptor per lane
-constexpr int kDynamicRounds = 0;     // whole rounds of full partitions handed out by the queues
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// Work-queue header in the workspace: kQueues 64-bit counters, each on its
-// own 128-byte line, and the plan kernel's counts in the last words.  A
-// counter holds a tag in bits 24..63 and the count in bits 0..23: the tag
-// names the launch that reset it (zero when the plan kernel did), so a claim
-// that lands on a counter left by an earlier call, or on whatever else the
-// workspace held, is recognised as such and retried.
-constexpr int kQueues = 8;  // one per XCD of the MI355X
-constexpr int kCounterStride = 16;  // uint64 words between counters
-constexpr int kHeaderBytes = 1024;
-constexpr int kItemCountWord = kHeaderBytes / 4 - 1;
-constexpr int kFullCountWord = kHeaderBytes / 4 - 2;  // items that are full partitions
-constexpr int kQueueCountWord = kHeaderBytes / 4 - 3;  // queues in use
-constexpr int kCountBits = 24;
-constexpr int64_t kMaxQueueItems = (int64_t)1 << kCountBits;  // claims per counter
-constexpr int64_t kMaxWaves = 256 * 32;  // resident waves of a launch, at most
-
-struct DecodeLayout {
-  int64_t max_parts;
-  size_t hdr, items, ml, o, total;
-};
-
-DecodeLayout decode_layout(int B, int Hq, int D, int P, int M) {
-  DecodeLayout L;
-  L.max_parts = ((int64_t)M * P + kPartTokens - 1) / kPartTokens;
-  size_t off = 0;
-  L.hdr = off;
-  off += kHeaderBytes;
-  L.items = off;
-  off = align256(off + sizeof(i32x4_t) * (size_t)B * L.max_parts);
-  L.ml = off;
-  off = align256(off + sizeof(float) * 4 * (size_t)B * Hq * L.max_parts);  // (max, sum, scale, -)
-  L.o = off;
-  off = align256(off + sizeof(float) * (size_t)B * Hq * L.max_parts * D);
-  L.total = off;
-  return L;
-}
-
-__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+using namespace dec;
 
 // ---------------------------------------------------------------------------
 // Plan: lists the (request, partition) items in decreasing size -- every full
@@ -110,9 +57,6 @@ __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L
 // which wave computes an item).  It also zeroes the queue counters and picks
 // one queue when items are long enough for a single counter to keep up.
 // ---------------------------------------------------------------------------
-constexpr int kTileBuckets = kPartTokens / 16;  // bucket k >= 1: tails of k tiles; bucket 0: full
-constexpr int kPlanThreads = 1024;
-
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ lens, int B,
                                                                    int cap, uint32_t* hdr,
                                                                    i32x4_t* __restrict__ items) {
@@ -157,559 +101,14 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
 }
 
 // ---------------------------------------------------------------------------
-// fp8 pools: OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
-// bits), one fp32 scale per KV head for K and for V.
-struct fp8_e4m3 {
-  uint8_t bits;
-};
-
-// Element type of q and out: the pool's, except bf16 for fp8 pools.
-template <typename T>
-struct QType {
-  typedef T type;
-};
-template <>
-struct QType<fp8_e4m3> {
-  typedef bf16_bits type;
-};
-
-// ---------------------------------------------------------------------------
-// Tile geometry.  A tile is 16 consecutive tokens of one KV head.  Lane l
-// loads 16-byte piece l % CPR of the head's row slice for tokens
-// (l / CPR) * TPL + j, j < TPL, so each quarter-wave reads whole contiguous
-// row slices (at most two 128-byte lines per 16 lanes).
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-struct Geo {
-  // fp8 pools are staged as 16-bit values (fp16 holding e4m3 * 2^-8)
-  static constexpr bool kFp8 = std::is_same<T, fp8_e4m3>::value;
-  static constexpr int ESZ = kFp8 ? 2 : (int)sizeof(T);  // bytes of a staged element
-  static constexpr int ROWB = D * ESZ;             // staged bytes of one head's row slice
-  static constexpr int GROWB = D * (int)sizeof(T);  // pool bytes of one head's row slice
-  static constexpr int CPR = ROWB / 16;            // 16-byte staged pieces per row slice
-  static constexpr int LOADB = GROWB / CPR;        // pool bytes a lane loads per token (16; 8 for fp8)
-  static constexpr int TPL = 16 * CPR / 64;        // tokens per lane per tile
-  static constexpr int KST = ROWB + 16;            // LDS row stride of K (and of V for fp32)
-  static constexpr int VTS = 40;                   // LDS row stride of transposed V (16-bit): 16 tokens + pad
-  static constexpr bool kBf16 = ESZ == 2;          // 16-bit path (bf16, or fp8 via fp16)
-  static constexpr int KBYTES = 16 * KST;
-  static constexpr int VBYTES = kBf16 ? D * VTS : 16 * KST;
-  static constexpr int LDS_PER_WAVE = KBYTES + VBYTES;
-  static constexpr int NQ = kBf16 ? D / 32 : D / 4;  // QK MFMA steps over the head dimension
-  static constexpr int NQV = kBf16 ? NQ : NQ / 4;    // 16-byte Q pieces per lane
-};
-
-// Byte offsets into the pool: 32-bit when the pool is under 4 GiB (one VGPR
-// per address, added to a scalar base), 64-bit otherwise.
-template <bool kWide>
-struct Off {
-  typedef typename std::conditional<kWide, uint64_t, uint32_t>::type type;
-};
-
-template <typename T, int D>
-struct TileRegs {
-  typedef typename std::conditional<Geo<T, D>::kFp8, u32x2_t, u32x4_t>::type LT;  // one lane's load per token
-  LT k[Geo<T, D>::TPL];
-  LT v[Geo<T, D>::TPL];
-  uint32_t ok;  // bit j: token j of this lane is inside the partition with a valid block id
-};
-
-struct PoolView {
-  const char* k;
-  const char* v;
-  uint32_t row_bytes;   // H_kv * D * elem: one token's row over all KV heads
-};
-
-struct DecodeParams {
-  const void* q;
-  const void* kc;
-  const void* vc;
-  const int32_t* bt;
-  const int32_t* lens;
-  void* out;
-  const uint32_t* hdr;
-  unsigned long long* counter;
-  const i32x4_t* items;
-  float* ml;
-  float* o;
-  float scale_log2;
-  int Hq, Hkv, G, n_hg, P, p_shift, N, M, cap, max_parts;
-  int dyn_rounds;  // full rounds of full partitions left to the queues
-  int nq;          // queues in use (at most kQueues); 0: as the plan chose
-  int B;
-  const float* k_scale;  // fp8 pools: per-KV-head scales (null otherwise)
-  const float* v_scale;
-  int self_plan;   // 1: the workgroups plan (B <= kSelfPlanMax); 0: the plan kernel did
-  unsigned long long salt;  // per call; mixed into the counters' tag
-};
-
-// One work item, wave-uniform (scalar registers).
-struct Item {
-  int b, part, L, nparts;  // request, partition, visible tokens, partitions of the request
-  int hkv, hg, nh;         // KV head, group of query heads, valid heads in the group
-  int tok0, tok_end, ntiles, blk0, nblk;
-  float sl2, vmul;         // score factor (log2 units) and output factor (fp8 scales folded in)
-};
-
-__device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, uint32_t f, uint32_t per_item) {
-  Item it;
-  it.b = uniform(d[0]);
-  it.part = uniform(d[1]);
-  it.L = uniform(d[2]);
-  it.nparts = uniform(d[3]);
-  const int rem = (int)(f % per_item);
-  it.hkv = rem / prm.n_hg;
-  it.hg = rem - it.hkv * prm.n_hg;
-  it.nh = min(4, prm.G - it.hg * 4);
-  it.tok0 = it.part * kPartTokens;
-  it.tok_end = min(it.L, it.tok0 + kPartTokens);
-  it.ntiles = (it.tok_end - it.tok0 + kTile - 1) / kTile;
-  int last;
-  if (prm.p_shift >= 0) {
-    it.blk0 = it.tok0 >> prm.p_shift;
-    last = (it.tok_end - 1) >> prm.p_shift;
-  } else {
-    it.blk0 = it.tok0 / prm.P;
-    last = (it.tok_end - 1) / prm.P;
-  }
-  it.nblk = last - it.blk0 + 1;
-  // fp8 pools hold code * scale; the staged fp16 values are code * 2^-8
-  it.sl2 = prm.k_scale ? prm.scale_log2 * 256.0f * prm.k_scale[it.hkv] : prm.scale_log2;
-  it.vmul = prm.v_scale ? 256.0f * prm.v_scale[it.hkv] : 1.0f;
-  return it;
-}
-
-// The item's block ids, lane i of register r holding entry blk0 + 64r + i.
-// The index is clamped so every lane loads (no divergent load to wait on).
-template <int NR>
-__device__ __forceinline__ void load_ids(const DecodeParams& prm, const Item& it, int (&ids)[NR]) {
-  const int lane = lane_id();
-  const int32_t* row = prm.bt + (int64_t)it.b * prm.M + it.blk0;
-#pragma unroll
-  for (int r = 0; r < NR; ++r) ids[r] = row[min(64 * r + lane, it.nblk - 1)];
-}
-
-// Q^T operand: column n = query head of the group (heads past the group's
-// last read head 0's row; their columns are never stored).
-template <typename T, int D>
-__device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, u32x4_t (&qv)[Geo<T, D>::NQV]) {
-  using Gm = Geo<T, D>;
-  typedef typename QType<T>::type QT;
-  const int lane = lane_id();
-  const int n = lane & 15, g = lane >> 4;
-  const int h = it.hkv * prm.G + it.hg * 4 + (n < it.nh ? n : 0);
-  const QT* qrow = static_cast<const QT*>(prm.q) + ((int64_t)it.b * prm.Hq + h) * D;
-#pragma unroll
-  for (int i = 0; i < Gm::NQV; ++i) {
-    if constexpr (Gm::kFp8) {
-      // bf16 query -> fp16 operand (exact inside the fp16 range)
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + 32 * i + 8 * g);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) qv[i][w] = pack_f16(bf16_lo(x[w]), bf16_hi(x[w]));
-    } else if constexpr (Gm::kBf16) qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * i + 8 * g);
-    else qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + g * (D / 4) + 4 * i);
-  }
-}
-
-// Descriptor held in lane `r` of a per-lane descriptor register (wave-uniform result).
-__device__ __forceinline__ i32x4_t lane_desc(const i32x4_t& d, int r) {
-  return i32x4_t{__builtin_amdgcn_readlane(d[0], r), __builtin_amdgcn_readlane(d[1], r),
-                 __builtin_amdgcn_readlane(d[2], r), __builtin_amdgcn_readlane(d[3], r)};
-}
-
-// Block id of logical block `idx` (relative to the item's first block) for
-// a per-lane index: lane crossbar read from the id registers.
-template <int NR>
-__device__ __forceinline__ int lane_id_lookup(const int (&ids)[NR], int idx) {
-  int blk = __builtin_amdgcn_ds_bpermute((idx & 63) << 2, ids[0]);
-#pragma unroll
-  for (int r = 1; r < NR; ++r) {
-    const int v = __builtin_amdgcn_ds_bpermute((idx & 63) << 2, ids[r]);
-    if ((idx >> 6) == r) blk = v;
-  }
-  return blk;
-}
-
-// Issues the K/V loads of one tile.  Block ids come from registers, so no
-// global load is waited on here (a wait on one would drain the K/V loads
-// already in flight, since loads complete in order).  Invalid tokens load the
-// head's slice of row 0 (always in range, and cached) and are zeroed when
-// staged.  kAligned: the tile lies inside one block (P a multiple of 16).
-template <typename T, int D, bool kWide, bool kAligned, int NR>
-__device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams& prm, const Item& it,
-                                          const int (&ids)[NR], int tile0, TileRegs<T, D>& r) {
-  using Gm = Geo<T, D>;
-  using O = typename Off<kWide>::type;
-  const int lane = lane_id();
-  const int q = lane / Gm::CPR;
-  const int first = tile0 + q * Gm::TPL;  // this lane's first token
-  const O lane_off = (O)(it.hkv * Gm::GROWB + Gm::LOADB * (lane % Gm::CPR));
-  typedef typename TileRegs<T, D>::LT LT;
-  r.ok = 0;
-  if constexpr (kAligned) {
-    int lb, off;
-    if (prm.p_shift >= 0) {
-      lb = tile0 >> prm.p_shift;
-      off = tile0 & ((1 << prm.p_shift) - 1);
-    } else {
-      lb = tile0 / prm.P;
-      off = tile0 - lb * prm.P;
-    }
-    const int blk = __builtin_amdgcn_readlane(ids[0], lb - it.blk0);
-    const bool bok = blk >= 0 && blk < prm.N;
-    const O base = bok ? ((O)blk * (O)prm.P + (O)(off + q * Gm::TPL)) * (O)pv.row_bytes : (O)0;
-#pragma unroll
-    for (int j = 0; j < Gm::TPL; ++j) {
-      const bool ok = bok && first + j < it.tok_end;
-      r.ok |= (ok ? 1u : 0u) << j;
-      const O e = (ok ? base + (O)j * (O)pv.row_bytes : (O)0) + lane_off;
-      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.k + e));
-      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.v + e));
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < Gm::TPL; ++j) {
-      const int pos = first + j;
-      int lb, off;
-      if (prm.p_shift >= 0) {
-        lb = pos >> prm.p_shift;
-        off = pos & ((1 << prm.p_shift) - 1);
-      } else {
-        lb = pos / prm.P;
-        off = pos - lb * prm.P;
-      }
-      const bool in = pos < it.tok_end;
-      const int blk = lane_id_lookup<NR>(ids, in ? lb - it.blk0 : 0);
-      const bool ok = in && blk >= 0 && blk < prm.N;
-      r.ok |= (ok ? 1u : 0u) << j;
-      const O e = (ok ? ((O)blk * (O)prm.P + (O)off) * (O)pv.row_bytes : (O)0) + lane_off;
-      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.k + e));
-      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.v + e));
-    }
-  }
-}
-
-// Registers -> this wave's LDS region: K row-major; V transposed (bf16, d-major
-// so a P.V operand is one 8-byte read) or row-major (fp32).
-template <typename T, int D>
-__device__ __forceinline__ void stage_tile(char* lds, TileRegs<T, D>& r_in, bool full) {
-  using Gm = Geo<T, D>;
-  typedef typename TileRegs<T, D>::LT LT;
-  const int lane = lane_id();
-  const int c = lane % Gm::CPR, q = lane / Gm::CPR;
-  if (!full) {
-#pragma unroll
-    for (int j = 0; j < Gm::TPL; ++j)
-      if (!((r_in.ok >> j) & 1u)) {
-        r_in.k[j] = LT{};
-        r_in.v[j] = LT{};
-      }
-  }
-  struct {
-    u32x4_t k[Gm::TPL], v[Gm::TPL];
-  } r;
-#pragma unroll
-  for (int j = 0; j < Gm::TPL; ++j) {
-    if constexpr (Gm::kFp8) {
-      r.k[j] = e4m3x8_to_f16(r_in.k[j]);
-      r.v[j] = e4m3x8_to_f16(r_in.v[j]);
-    } else {
-      r.k[j] = r_in.k[j];
-      r.v[j] = r_in.v[j];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < Gm::TPL; ++j)
-    *reinterpret_cast<u32x4_t*>(lds + (q * Gm::TPL + j) * Gm::KST + 16 * c) = r.k[j];
-  char* vl = lds + Gm::KBYTES;
-  if constexpr (Gm::kBf16) {
-    // piece c holds head elements 8c..8c+7; this lane owns tokens q*TPL .. q*TPL+TPL-1
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int d = 8 * c + 2 * w;
-      if constexpr (Gm::TPL == 4) {
-        const u32x2_t lo = {__builtin_amdgcn_perm(r.v[1][w], r.v[0][w], 0x05040100u),
-                            __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], 0x05040100u)};
-        const u32x2_t hi = {__builtin_amdgcn_perm(r.v[1][w], r.v[0][w], 0x07060302u),
-                            __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], 0x07060302u)};
-        *reinterpret_cast<u32x2_t*>(vl + d * Gm::VTS + 8 * q) = lo;
-        *reinterpret_cast<u32x2_t*>(vl + (d + 1) * Gm::VTS + 8 * q) = hi;
-      } else {
-        static_assert(Gm::TPL == 2, "bf16 tiles hold 2 or 4 tokens per lane");
-        *reinterpret_cast<uint32_t*>(vl + d * Gm::VTS + 4 * q) = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(vl + (d + 1) * Gm::VTS + 4 * q) =
-            __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], 0x07060302u);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < Gm::TPL; ++j)
-      *reinterpret_cast<u32x4_t*>(vl + (q * Gm::TPL + j) * Gm::KST + 16 * c) = r.v[j];
-  }
-}
-
-// Orders this wave's LDS stores before its later LDS loads (the wave reads
-// what other lanes of the same wave wrote).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Softmax reference max is moved only when a score exceeds it by more than
-// this (log2 units), so probabilities stay below 2^8 and the rescale of the
-// accumulators is rare; the result does not depend on the reference.
-constexpr float kRescaleSlack = 8.0f;
-
-__device__ __forceinline__ unsigned long long uniform64(unsigned long long v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-  return ((unsigned long long)hi << 32) | lo;
-}
-
-// The launch's dispatch id: the packet's index on its hardware queue (every
-// launch, graph replays included, gets a new one).
-extern "C" __device__ unsigned long long llvm_amdgcn_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
-
-// Tag of this launch's queue counters: dispatch id, queue address and the
-// host's per-call salt, mixed with the splitmix64 finaliser and cut to the
-// tag's 40 bits; never zero (zero marks counters the plan kernel reset).
-__device__ __forceinline__ unsigned long long launch_tag(unsigned long long salt) {
-  unsigned long long x = llvm_amdgcn_dispatch_id() * 0x9E3779B97F4A7C15ull;
-  x ^= (unsigned long long)(uintptr_t)__builtin_amdgcn_queue_ptr() ^ salt;
-  x ^= x >> 30;
-  x *= 0xBF58476D1CE4E5B9ull;
-  x ^= x >> 27;
-  x *= 0x94D049BB133111EBull;
-  x ^= x >> 31;
-  x &= (1ull << (64 - kCountBits)) - 1ull;
-  return x ? x : 1ull;
-}
-
-// Sleeps a claim may wait for workgroup 0 to reset the counters (a few
-// atomics of a resident workgroup, so a handful in practice; the bound only
-// guarantees that every wave exits).
-constexpr int kMaxSpins = 1 << 20;
-
-// Takes the next dynamically scheduled item: with nq queues, queue x holds
-// flat items f = first_dyn + nq * c + x; a wave starts at its home queue (its
-// XCD's, when there are eight) and moves to the next one when that is empty.
-// A self-planned launch checks the counter's tag: a counter not yet reset
-// for this launch is tried again after a short sleep.  Returns 0xffffffff
-// when all queues are empty.
-__device__ __forceinline__ uint32_t claim(const DecodeParams& prm, unsigned long long tag, uint32_t nq, uint32_t home,
-                                          uint32_t& queue, uint32_t first_dyn, uint32_t total) {
-  const int lane = lane_id();
-  int spins = 0;
-  while (queue < nq) {
-    const uint32_t x = (home + queue) % nq;
-    unsigned long long old = 0;
-    if (lane == 0) old = atomicAdd(prm.counter + x * kCounterStride, 1ull);
-    old = uniform64(old);
-    if (prm.self_plan && (old >> kCountBits) != tag) {
-      if (++spins < kMaxSpins) __builtin_amdgcn_s_sleep(8);
-      else ++queue;
-      continue;
-    }
-    const unsigned long long c = prm.self_plan ? old & (kMaxQueueItems - 1) : old;
-    const unsigned long long f = first_dyn + nq * c + x;
-    if (f < total) return (uint32_t)f;
-    ++queue;
-  }
-  return 0xffffffffu;
-}
-
-// ---------------------------------------------------------------------------
-// In-kernel plan (batches of at most kSelfPlanMax requests).  Each workgroup
-// derives the item list from the lengths, in LDS: full partitions first,
-// request by request, then the tail partitions by tile count (16 .. 1),
-// requests in increasing order within a count.  The list is a function of
-// the lengths alone, so all workgroups agree on it without communicating.
-// List entry i < F (the full-partition count) is full partition i - pf[b]
-// of the request b with pf[b] <= i < pf[b + 1]; entry F + j is the tail of
-// request tail_b[j].
-// ---------------------------------------------------------------------------
-constexpr int kSelfPlanMax = 1024;
-constexpr int kPlanChunks = kSelfPlanMax / 64;
-
-struct PlanLds {
-  int pf[kSelfPlanMax + 1];                // first list entry of request b's full partitions; pf[B] = F
-  int len[kSelfPlanMax];                   // clamped lengths
-  uint16_t tail_b[kSelfPlanMax];           // requests with a tail partition, in list order
-  uint16_t rk[kSelfPlanMax];               // tile count of the tail | rank among equal counts of its chunk << 5
-  int pre[kPlanChunks][kTileBuckets + 1];  // per 64-request chunk: counts, then exclusive prefixes
-  int bstart[kTileBuckets + 1];            // first tail position of each tile count
-  int nfull, nitems, nq;
-};
-
-// Inclusive prefix sums with DPP row shifts (lanes shifted in from outside
-// the 16-lane row read zero): inside each row, then across the wave.
-template <int CTRL>
-__device__ __forceinline__ int dpp_zero(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
-}
-__device__ __forceinline__ int row16_incl_scan(int v) {
-  v += dpp_zero<0x111>(v);  // row_shr:1
-  v += dpp_zero<0x112>(v);  // row_shr:2
-  v += dpp_zero<0x114>(v);  // row_shr:4
-  v += dpp_zero<0x118>(v);  // row_shr:8
-  return v;
-}
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  v = row16_incl_scan(v);
-  const int r0 = __builtin_amdgcn_readlane(v, 15);
-  const int r1 = __builtin_amdgcn_readlane(v, 31);
-  const int r2 = __builtin_amdgcn_readlane(v, 47);
-  const int row = lane_id() >> 4;
-  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
-}
-
-// Every thread of the workgroup takes part (three barriers).
-__device__ void self_plan(const DecodeParams& prm, PlanLds* pl) {
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int B = prm.B;
-  const int nc = (B + 63) >> 6;
-  // 1: per chunk of 64 requests: lengths, the full-partition prefix inside
-  // the chunk, each tail's rank among the chunk's tails of equal tile count,
-  // and the chunk's counts
-  for (int c = wave; c < nc; c += nw) {
-    const int b = 64 * c + lane;
-    const int L = b < B ? clamp_len(prm.lens[b], prm.cap) : 0;
-    const int full = L / kPartTokens, rest = L - full * kPartTokens;
-    const int bk = rest ? (rest + kTile - 1) / kTile : 0;
-    const int incl = wave_incl_scan(full);
-    // tails of k tiles counted in 8-bit field (k - 1) % 4 of word (k - 1) / 4
-    // (at most 64 per field): one prefix sum per word gives every lane the
-    // number of lower lanes with its tile count, and lane 63 the totals
-    const int kb = bk - 1;
-    int sc[4], tw[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      sc[w] = wave_incl_scan(bk != 0 && (kb >> 2) == w ? 1 << (8 * (kb & 3)) : 0);
-      tw[w] = __builtin_amdgcn_readlane(sc[w], 63);
-    }
-    const int mine = kb < 4 ? sc[0] : kb < 8 ? sc[1] : kb < 12 ? sc[2] : sc[3];
-    const int rank = bk ? ((mine >> (8 * (kb & 3))) & 255) - 1 : 0;
-    // lane k (1..16) takes the chunk's count of tails of k tiles, lane 0 its full partitions
-    const int lk = lane - 1;
-    const int word = lk < 4 ? tw[0] : lk < 8 ? tw[1] : lk < 12 ? tw[2] : tw[3];
-    int cnt = (word >> (8 * (lk & 3))) & 255;
-    if (lane == 0) cnt = __builtin_amdgcn_readlane(incl, 63);
-    if (b < B) {
-      pl->len[b] = L;
-      pl->pf[b] = incl - full;
-      pl->rk[b] = (uint16_t)(bk | rank << 5);
-    }
-    if (lane <= kTileBuckets) pl->pre[c][lane] = cnt;
-  }
-  __syncthreads();
-  // 2: exclusive prefixes over the chunks (lane c < 16: chunk c), totals,
-  // the first tail position of each tile count, and the queue count (one
-  // queue when items average at least 4 tiles: 16 per full partition, k
-  // per tail of k tiles)
-  if (wave == 0) {
-    int tot[kTileBuckets + 1], v[kTileBuckets + 1];
-#pragma unroll
-    for (int k = 0; k <= kTileBuckets; ++k) v[k] = lane < nc ? pl->pre[lane][k] : 0;
-#pragma unroll
-    for (int k = 0; k <= kTileBuckets; ++k) {
-      const int incl = row16_incl_scan(v[k]);
-      if (lane < nc) pl->pre[lane][k] = incl - v[k];
-      tot[k] = __builtin_amdgcn_readlane(incl, kPlanChunks - 1);
-    }
-    if (lane == 0) {
-      int run = 0;
-      long long tiles = (long long)kTileBuckets * tot[0];
-#pragma unroll
-      for (int k = kTileBuckets; k >= 1; --k) {
-        pl->bstart[k] = run;
-        run += tot[k];
-        tiles += (long long)k * tot[k];
-      }
-      pl->nfull = tot[0];
-      pl->nitems = tot[0] + run;
-      pl->nq = tiles >= 4ll * (tot[0] + run) ? 1 : kQueues;
-      pl->pf[B] = tot[0];
-    }
-  }
-  __syncthreads();
-  // 3: global full-partition offsets and the tail order
-  for (int c = wave; c < nc; c += nw) {
-    const int b = 64 * c + lane;
-    if (b < B) {
-      const int rk = pl->rk[b];
-      const int bk = rk & 31;
-      pl->pf[b] += pl->pre[c][0];
-      if (bk) pl->tail_b[pl->bstart[bk] + pl->pre[c][bk] + (rk >> 5)] = (uint16_t)b;
-    }
-  }
-  __syncthreads();
-}
-
-// Descriptor {request, partition, length, partitions} of list entry i.
-__device__ __forceinline__ i32x4_t plan_desc(const PlanLds* pl, int B, int nfull, int i) {
-  int b, part;
-  if (i < nfull) {
-    int lo = 0, hi = B;  // pf[lo] <= i < pf[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pl->pf[mid] <= i) lo = mid;
-      else hi = mid;
-    }
-    b = lo;
-    part = i - pl->pf[lo];
-  } else {
-    b = pl->tail_b[i - nfull];
-    part = pl->len[b] / kPartTokens;
-  }
-  const int L = pl->len[b];
-  return i32x4_t{b, part, L, (L + kPartTokens - 1) / kPartTokens};
-}
-
-__device__ __forceinline__ i32x4_t item_desc(const DecodeParams& prm, const PlanLds* pl, uint32_t nfull, uint32_t i) {
-  if (prm.self_plan) return plan_desc(pl, prm.B, (int)nfull, (int)i);
-  return prm.items[i];
-}
-
-// ---------------------------------------------------------------------------
-// Partition kernel.  One wave = one work item (request, partition, KV head,
-// group of up to 4 query heads) at a time.
-//
-// Schedule: the flat item list (items x KV heads x head groups) starts with
-// the full partitions, all of the same size.  Whole rounds of those are dealt
-// statically (wave w takes w, w + nwaves, ...), which balances exactly; lane
-// r of a register holds the wave's round-r descriptor, so the next static
-// item costs no memory access.  The rest (the last full round and all tail
-// partitions, largest first) is claimed dynamically from per-XCD queues, one
-// item ahead.
-//
-// The loop runs over the wave's stream of tiles, across item boundaries: each
-// iteration stages the tile that has landed, issues the loads of the next
-// tile of the stream (the next item's first tile after an item's last), and
-// computes.  The next item's block ids are fetched at its predecessor's
-// first tile and its query after the predecessor's last S^T product, so
-// items follow one another without draining the loads in flight.
-//
-// Per 16-token tile:
-//   S^T = K Q^T   (A = K rows from LDS, B = Q^T with the group's heads as
-//                  columns 0..3), so lane (n, g) gets the scores of head n for
-//                  tokens 4g .. 4g+3;
-//   online softmax per head (max over the lane's 4 tokens, then across the
-//                  four 16-lane rows);
-//   O^T += V^T P^T (A = V^T from LDS, B = the lane's own probabilities), so
-//                  lane (n, g) accumulates head n's outputs d = 16db + 4g + j.
+// Partition kernel: every wave computes a stream of work items (see
+// decode_stream for the schedule and the per-tile steps).
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool kWide, bool kAligned, int NR>
 __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm) {
   using Gm = Geo<T, D>;
-  typedef typename QType<T>::type QT;
-  constexpr int NDB = D / 16;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* lds = smem + (threadIdx.x >> 6) * Gm::LDS_PER_WAVE;
-  const int lane = lane_id();
-  const int n = lane & 15;  // head column (S^T, O^T) / token row (K operand)
-  const int g = lane >> 4;
   PlanLds* pl = reinterpret_cast<PlanLds*>(smem + (blockDim.x >> 6) * Gm::LDS_PER_WAVE);
   unsigned long long tag = 0;
   uint32_t n_items, n_full, nq_plan;
@@ -718,7 +117,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     // workgroup 0 resets the queue counters for this launch
     if (blockIdx.x == 0 && threadIdx.x < kQueues)
       atomicExch(prm.counter + threadIdx.x * kCounterStride, tag << kCountBits);
-    self_plan(prm, pl);
+    self_plan<false>(prm, pl);
     n_items = (uint32_t)uniform(pl->nitems);
     n_full = (uint32_t)uniform(pl->nfull);
     nq_plan = (uint32_t)uniform(pl->nq);
@@ -727,380 +126,11 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     n_full = prm.hdr[kFullCountWord];
     nq_plan = prm.hdr[kQueueCountWord];
   }
-  const uint32_t per_item = (uint32_t)(prm.Hkv * prm.n_hg);
-  const uint32_t total = n_items * per_item;
   const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
   // (threadIdx.x >> 6 is the same in every lane; readfirstlane tells the compiler)
   const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (uint32_t)uniform((int)(threadIdx.x >> 6));
-  // static rounds: whole rounds of full partitions, at most one per lane;
-  // the queues hand out the rest (the last kDynamicRounds whole rounds, the
-  // partial round and the tails), which balances waves that run at
-  // different speeds.  Measured on the Llama-3-8B batch, leaving no whole
-  // round to the queues is best.
-  uint32_t rounds = min((n_full * per_item) / nwaves, (uint32_t)kMaxStaticRounds);
-  rounds = rounds > (uint32_t)prm.dyn_rounds ? rounds - (uint32_t)prm.dyn_rounds : min(rounds, 1u);
-  const uint32_t first_dyn = rounds * nwaves;
-  const uint32_t nq = prm.nq > 0 ? (uint32_t)prm.nq : nq_plan;
-  const uint32_t home = blockIdx.x % nq;
-  uint32_t queue = 0;
-  PoolView pv;
-  pv.k = static_cast<const char*>(prm.kc);
-  pv.v = static_cast<const char*>(prm.vc);
-  pv.row_bytes = (uint32_t)(prm.Hkv * Gm::GROWB);
-
-  // lane r: descriptor of this wave's item of static round r
-  i32x4_t sdesc = {0, 0, 0, 0};
-  if (rounds > 0) sdesc = item_desc(prm, pl, n_full, (wave + (uint32_t)min(lane, (int)rounds - 1) * nwaves) / per_item);
-
-  // the current item: round r < rounds is static item wave + r * nwaves
-  uint32_t r = 0;
-  uint32_t f = wave;
-  Item it;
-  if (rounds > 0) {
-    it = make_item(prm, lane_desc(sdesc, 0), f, per_item);
-  } else {
-    r = rounds;
-    f = claim(prm, tag, nq, home, queue, first_dyn, total);
-    if (f >= total) return;
-    it = make_item(prm, item_desc(prm, pl, n_full, f / per_item), f, per_item);
-  }
-  int ids[NR];
-  load_ids<NR>(prm, it, ids);
-  u32x4_t qv[Gm::NQV];
-  load_q<T, D>(prm, it, qv);
-  TileRegs<T, D> regs;
-  load_tile<T, D, kWide, kAligned, NR>(pv, prm, it, ids, it.tok0, regs);
-
-  Item nx = it;        // the item after the current one, once known
-  uint32_t fn = 0;     // its flat index
-  bool has_next = false;
-  int pend = 0;        // 1: next item claimed (fn), 2: its descriptor loaded (dn)
-  i32x4_t dn = {0, 0, 0, 0};
-  int idn[NR];         // its block ids
-#pragma unroll
-  for (int i = 0; i < NR; ++i) idn[i] = 0;
-
-  float m = -INFINITY, l = 0.f;
-  f32x4_t o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int t = 0;;) {
-    const int tile0 = it.tok0 + t * kTile;
-    const bool last = t + 1 == it.ntiles;
-    // every token of the tile valid: no zeroing needed (the usual case)
-    bool full;
-    if constexpr (kAligned)
-      full = tile0 + kTile <= it.tok_end && __builtin_amdgcn_readfirstlane((int)regs.ok) == (1 << Gm::TPL) - 1;
-    else
-      full = __builtin_amdgcn_readfirstlane((int)(__ballot(regs.ok != (1u << Gm::TPL) - 1u) == 0));
-    wave_lds_sync();  // previous tile's LDS reads are done
-    stage_tile<T, D>(lds, regs, full);
-    wave_lds_sync();
-
-    // find the next item and fetch its block ids.  A static item is known at
-    // once.  A dynamic one is claimed with an atomic right after tile 1's
-    // loads are issued (its wait then only delays tile 0's arithmetic, not
-    // the memory stream), its descriptor is loaded at tile 1 and its ids at
-    // tile 2; items of one or two tiles claim everything up front.
-    const bool stat_next = r + 1 < rounds;
-    const bool early = it.ntiles >= 3;
-    if (t == 0) {
-      if (stat_next) {
-        fn = f + nwaves;
-        nx = make_item(prm, lane_desc(sdesc, (int)r + 1), fn, per_item);
-        has_next = true;
-        load_ids<NR>(prm, nx, idn);
-      } else if (!early) {
-        fn = claim(prm, tag, nq, home, queue, first_dyn, total);
-        if (fn < total) {
-          nx = make_item(prm, item_desc(prm, pl, n_full, fn / per_item), fn, per_item);
-          has_next = true;
-          load_ids<NR>(prm, nx, idn);
-        }
-      }
-    }
-    if (pend == 1 && t == 1) {
-      dn = item_desc(prm, pl, n_full, fn / per_item);
-      pend = 2;
-    }
-    if (pend == 2 && t == 2) {
-      nx = make_item(prm, dn, fn, per_item);
-      has_next = true;
-      load_ids<NR>(prm, nx, idn);
-      pend = 0;
-    }
-    // the next tile of the stream: this item's, or the next item's first
-    if (last && has_next) {
-      // a real branch, not a select: a select would read idn on every tile
-      // and so wait for its load right after it is issued
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int i = 0; i < NR; ++i) ids[i] = idn[i];
-    }
-    if (!last || has_next)
-      load_tile<T, D, kWide, kAligned, NR>(pv, prm, last ? nx : it, ids, last ? nx.tok0 : tile0 + kTile, regs);
-    if (t == 0 && early && !stat_next) {
-      fn = claim(prm, tag, nq, home, queue, first_dyn, total);
-      if (fn < total) pend = 1;
-    }
-
-    // ---- S^T = K Q^T ----
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (Gm::kFp8) {
-#pragma unroll
-      for (int i = 0; i < Gm::NQ; ++i) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                   __builtin_bit_cast(f16x8_t, qv[i]), s, 0, 0, 0);
-      }
-    } else if constexpr (Gm::kBf16) {
-#pragma unroll
-      for (int i = 0; i < Gm::NQ; ++i) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                    __builtin_bit_cast(bf16x8_t, qv[i]), s, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < Gm::NQ / 4; ++i) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 4 * (g * (D / 4) + 4 * i));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(qv[i][j]), s, 0, 0, 0);
-      }
-    }
-    if (last && has_next) load_q<T, D>(prm, nx, qv);  // this item's query is no longer needed
-
-    // ---- online softmax for head n over tokens tile0 + 4g + j ----
-    float sc[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[j] = (tile0 + 4 * g + j < it.tok_end) ? s[j] * it.sl2 : -INFINITY;
-      mx = fmaxf(mx, sc[j]);
-    }
-    mx = max_over_rows(mx);
-    // move the reference max only when a score exceeds it by the slack
-    // (always on the first tile, m = -inf); uniform branch, rarely taken
-    const bool move = mx > m + kRescaleSlack;
-    if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
-      const float alpha = (move && m != -INFINITY) ? fast_exp2(m - mx) : 1.0f;
-      if (move) m = mx;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-    }
-    float p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = fast_exp2(sc[j] - m);
-      l += p[j];
-    }
-    // ---- O^T += V^T P^T ----
-    const char* vl = lds + Gm::KBYTES;
-    if constexpr (Gm::kFp8) {
-      const u32x2_t pb = {pack_f16(p[0], p[1]), pack_f16(p[2], p[3])};
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vl + (16 * db + n) * Gm::VTS + 8 * g);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
-                                                      __builtin_bit_cast(f16x4_t, pb), o[db], 0, 0, 0);
-      }
-    } else if constexpr (Gm::kBf16) {
-      const u32x2_t pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vl + (16 * db + n) * Gm::VTS + 8 * g);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
-                                                          __builtin_bit_cast(s16x4_t, pb), o[db], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float a = *reinterpret_cast<const float*>(vl + (4 * g + j) * Gm::KST + 4 * (16 * db + n));
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[j], o[db], 0, 0, 0);
-        }
-    }
-    if (!last) {
-      ++t;
-      continue;
-    }
-
-    // ---- item done: total of l over the four 16-lane rows; store head n ----
-    l = sum_over_rows(l);
-    if (n < it.nh) {
-      const int h = it.hkv * prm.G + it.hg * 4 + n;
-      if (it.nparts == 1) {
-        const float inv = it.vmul / l;
-        QT* dst = static_cast<QT*>(prm.out) + ((int64_t)it.b * prm.Hq + h) * D + 4 * g;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          if constexpr (Gm::kBf16) {
-            *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
-                u32x2_t{pack_bf16(o[db][0] * inv, o[db][1] * inv), pack_bf16(o[db][2] * inv, o[db][3] * inv)};
-          } else {
-            *reinterpret_cast<f32x4_t*>(dst + 16 * db) = o[db] * inv;
-          }
-        }
-      } else {
-        const int64_t slot = ((int64_t)it.b * prm.Hq + h) * prm.max_parts + it.part;
-        float rs = 1.0f;  // the stored row is o / l / rs (bf16) or o (fp32)
-        if constexpr (Gm::kBf16) {
-          // bf16 requests: the partial output normalised by its sum, as fp16
-          // (half the bytes of fp32; its rounding is far below bf16's).  A
-          // normalised row is a weighted mean of value rows, so it can exceed
-          // the fp16 range only if the values do; then it is scaled down by a
-          // power of two, kept beside (max, sum), so it stays below 2^15.
-          const float inv = it.vmul / l;
-          float amax = 0.f;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(o[db][j]));
-          amax = max_over_rows(amax * inv);  // the head's whole row (lanes n, n+16, n+32, n+48)
-          if (amax >= 32768.0f) {
-            int ex;
-            frexpf(amax, &ex);  // amax < 2^ex
-            rs = ldexpf(1.0f, ex - 15);
-          }
-          const float sc = inv / rs;
-          uint16_t* dst = reinterpret_cast<uint16_t*>(prm.o) + slot * D + 4 * g;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
-                u32x2_t{pack_f16(o[db][0] * sc, o[db][1] * sc), pack_f16(o[db][2] * sc, o[db][3] * sc)};
-        } else {
-          float* dst = prm.o + slot * D + 4 * g;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db) = o[db];
-        }
-        if (g == 0) *reinterpret_cast<f32x4_t*>(prm.ml + slot * 4) = f32x4_t{m, l, rs, 0.f};
-      }
-    }
-    if (!has_next) break;
-    // the next item's ids, first tile and query are already in flight
-    it = nx;
-    f = fn;
-    r = r + 1 < rounds ? r + 1 : rounds;
-    has_next = false;
-    t = 0;
-    m = -INFINITY;
-    l = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Reduce: merge the partitions of requests that have more than one; write
-// zeros for empty requests.  One wave per (request, query head), four heads
-// per block.  Lane i first turns partition i's (max, sum) into its weight
-// 2^(m_i - m); the weighted sum over partitions then reads each weight with
-// a lane broadcast while the partial outputs stream in, sixteen partitions
-// per round so that many loads are in flight.  Lane l owns output elements
-// D/64 * l .. D/64 * l + D/64 - 1 (one vector load per partition).
-// ---------------------------------------------------------------------------
-// Partial outputs: fp32, unnormalised, for fp32 requests; fp16 normalised by
-// the partition's sum for bf16 requests.  Lane l reads elements PER*l ..
-// PER*l + PER-1 of a partition's row with one load.
-template <bool kHalf, int PER>
-struct RowPiece;
-template <>
-struct RowPiece<false, 1> {
-  typedef float type;
-  static __device__ __forceinline__ float get(const type& v, int) { return v; }
-};
-template <>
-struct RowPiece<false, 2> {
-  typedef f32x2_t type;
-  static __device__ __forceinline__ float get(const type& v, int j) { return v[j]; }
-};
-template <>
-struct RowPiece<true, 1> {
-  typedef uint16_t type;
-  static __device__ __forceinline__ float get(const type& v, int) { return f16_lo(v); }
-};
-template <>
-struct RowPiece<true, 2> {
-  typedef uint32_t type;
-  static __device__ __forceinline__ float get(const type& v, int j) { return j ? f16_hi(v) : f16_lo(v); }
-};
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams prm) {
-  constexpr int PER = D / 64;
-  constexpr int U = 16;  // partitions per round
-  constexpr bool kHalf = sizeof(T) == 2;
-  typedef RowPiece<kHalf, PER> RP;
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6), b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  if (h >= prm.Hq) return;
-  const int64_t slot0 = ((int64_t)b * prm.Hq + h) * prm.max_parts;
-  const f32x4_t* ml = reinterpret_cast<const f32x4_t*>(prm.ml) + slot0;
-  // the (max, sum, scale) entries are read before the length is known (slots
-  // past the request's partition count exist in the workspace and are masked
-  // below), so the two loads overlap
-  const f32x4_t ml0 = ml[min(lane, prm.max_parts - 1)];
-  const int L = clamp_len(prm.lens[b], prm.cap);
-  const int np = (L + kPartTokens - 1) / kPartTokens;
-  if (np == 1) return;
-  T* dst = static_cast<T*>(prm.out) + ((int64_t)b * prm.Hq + h) * D + PER * lane;
-  if (np == 0) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if constexpr (sizeof(T) == 2) dst[j] = 0;
-      else dst[j] = 0.f;
-    }
-    return;
-  }
-  // global max over all partitions
-  float mx = lane < np ? ml0[0] : -INFINITY;
-  for (int i = lane + 64; i < np; i += 64) mx = fmaxf(mx, ml[i][0]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  float acc[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-  float den = 0.f;
-  const typename RP::type* rows =
-      kHalf ? reinterpret_cast<const typename RP::type*>(reinterpret_cast<const uint16_t*>(prm.o) + slot0 * D)
-            : reinterpret_cast<const typename RP::type*>(prm.o + slot0 * D);
-  for (int c0 = 0; c0 < np; c0 += 64) {  // chunks of 64 partitions
-    const int nc = min(64, np - c0);
-    const f32x4_t mine = c0 == 0 ? ml0 : ml[c0 + min(lane, nc - 1)];
-    // lanes past the chunk hold whatever the workspace held: select, never
-    // multiply, their values away
-    const bool in = lane < nc;
-    const float w = in ? fast_exp2(mine[0] - mx) : 0.f;
-    float lw = in ? w * mine[1] : 0.f;
-    // weight of a partial row: 2^(m_i - m) for unnormalised rows, times l_i and
-    // the row's scale for normalised ones
-    const float wr = kHalf ? (in ? lw * mine[2] : 0.f) : w;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) lw += __shfl_xor(lw, off);
-    den += lw;
-    const typename RP::type* src = rows + (size_t)c0 * (D / PER) + lane;
-    for (int i = 0; i < nc; i += U) {
-      typename RP::type v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = src[(size_t)min(i + u, nc - 1) * (D / PER)];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float wu = i + u < nc ? __shfl(wr, i + u) : 0.f;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] = fmaf(wu, RP::get(v[u], j), acc[j]);
-      }
-    }
-  }
-  const float inv = 1.0f / den;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if constexpr (sizeof(T) == 2) dst[j] = (bf16_bits)f32_to_bf16(acc[j] * inv);
-    else dst[j] = acc[j] * inv;
-  }
+  decode_stream<T, D, kWide, kAligned, NR, false>(prm, lds, pl, tag, n_items, n_full, nq_plan, wave, nwaves,
+                                                  (uint32_t)kMaxStaticRounds);
 }
 
 template <typename T, int D, bool kWide, bool kAligned, int NR>
@@ -1133,7 +163,7 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
     const hipError_t e = hipEventRecord(ev1, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_reduce_kernel<typename QType<T>::type, D>), dim3((prm.Hq + 3) / 4, B), dim3(256), 0,
+  hipLaunchKernelGGL((decode_reduce_kernel<typename QType<T>::type, D, false>), dim3((prm.Hq + 3) / 4, B), dim3(256), 0,
                      stream, prm);
   return hipGetLastError();
 }
@@ -1153,15 +183,6 @@ hipError_t launch_sized(const DecodeParams& prm, int B, int64_t max_items, int64
                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   if (pool_bytes < ((int64_t)1 << 32)) return launch_mode<T, D, false>(prm, B, max_items, stream, ev0, ev1);
   return launch_mode<T, D, true>(prm, B, max_items, stream, ev0, ev1);
-}
-
-// Per-call salt of the counters' tag: a process-wide sequence from a start
-// taken from the clock and the process id.
-unsigned long long next_salt() {
-  static std::atomic<unsigned long long> seq{
-      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
-      ((unsigned long long)getpid() << 40)};
-  return seq.fetch_add(0x9E3779B97F4A7C15ull, std::memory_order_relaxed);
 }
 
 }  // namespace
@@ -1201,6 +222,8 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.nq = 0;
   prm.B = a.num_seqs;
   prm.salt = next_salt();
+  prm.cu = nullptr;
+  prm.num_q_tokens = 0;
   const bool fp8 = a.kv_dtype == kFP8E4M3;
   prm.k_scale = fp8 ? a.k_scale : nullptr;
   prm.v_scale = fp8 ? a.v_scale : nullptr;

@@ -47,13 +47,13 @@ struct AttnArgs {
   const void* q;
   const void* k_cache;
   const void* v_cache;
-  const int32_t* cu_seqlens;  // prefill only
+  const int32_t* cu_seqlens;  // prefill and mixed only
   const int32_t* block_table;
   const int32_t* context_lens;
   void* out;
   float scale;
   int num_seqs;
-  int64_t num_q_tokens;  // prefill only
+  int64_t num_q_tokens;  // prefill and mixed only
   int num_q_heads;
   int num_kv_heads;
   int head_dim;
@@ -76,5 +76,15 @@ size_t prefill_workspace_size(int num_seqs, int64_t num_q_tokens, int num_q_head
                               int num_kv_heads);
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_start,
                           hipEvent_t ev_stop);
+
+// Mixed batches (one-token chunks as decodes, longer chunks as prefill) in one
+// persistent launch, then the merge of the decodes' partitions.  Batches of
+// at most mixed_max_seqs() requests whose work lists fit the queue counters
+// (mixed_fits); bf16 q and out, bf16 or fp8 pools.
+size_t mixed_workspace_size(int num_seqs, int num_q_heads, int head_dim, int block_size, int max_blocks);
+int mixed_max_seqs();
+bool mixed_fits(int num_seqs, int64_t num_q_tokens, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                int max_blocks);
+hipError_t launch_mixed(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 }  // namespace pa

@@ -31,82 +31,13 @@
 //     reference max; tiles past every row of a wave are skipped.
 //   * Keys past the causal limit, tail slots and out-of-range block ids are
 //     masked and never multiply a value: masked K/V tile rows are zero-filled.
-#include <math.h>
-
-#include <type_traits>
-
-#include "common.h"
-#include "launch.h"
+#include "prefill_dev.h"
 
 namespace pa {
 
 namespace {
 
-constexpr int kRows = 256;     // rows (chunk token x query head) per work item
-constexpr int kTK = 64;        // keys per tile
-constexpr int kThreads = 512;  // 8 waves, 32 rows each
-constexpr int kIdCap = kPrefillMaxBlocks;  // block ids an item keeps in LDS
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-int tokens_per_tile(int G) { return kRows / G; }
-
-int64_t max_prefill_items(int num_seqs, int64_t num_q_tokens, int G) {
-  const int TQ = tokens_per_tile(G);
-  return (num_q_tokens + TQ - 1) / TQ + num_seqs;
-}
-
-__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
-
-// ---------------------------------------------------------------------------
-// Plan: the (request, q tile) items, requests ordered by their total number of
-// key tiles (largest first; counting sort, ties in any order -- each item is
-// computed independently, so the order never changes a result), and each
-// request's q tiles from the last (largest causal extent) to the first, so
-// that the items sharing a request's keys run at the same time.
-// ---------------------------------------------------------------------------
-constexpr int kBuckets = 1024;
-constexpr int kPlanThreads = 1024;
-constexpr int kXcds = 8;            // queues: one per XCD of the MI355X
-constexpr int kHeaderBytes = 1024;
-constexpr int kCounterStride = 32;  // uint32 words between queue counters (128-byte lines)
-constexpr int kEntryCountWord = kHeaderBytes / 4 - 1;
-
-__device__ __forceinline__ bool chunk_ok(const int32_t* __restrict__ cu, int b, int T, int L,
-                                         int num_q_tokens) {
-  return T > 0 && T <= L && cu[b] >= 0 && cu[b + 1] <= num_q_tokens;
-}
-
-// Key tiles of all q tiles of a chunk of T tokens over a prefix of L - T.
-__device__ __forceinline__ int chunk_work(int T, int L, int TQ) {
-  int w = 0;
-  for (int t0 = 0; t0 < T; t0 += TQ) w += (L - T + min(T, t0 + TQ) + kTK - 1) / kTK;
-  return w;
-}
-
-// Exclusive scan of one value per thread over a kPlanThreads block.
-__device__ __forceinline__ int block_excl_scan(int v, int* wave_tot) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wave_tot[wv] = x;
-  __syncthreads();
-  if (wv == 0) {
-    int t = lane < kPlanThreads / 64 ? wave_tot[lane] : 0;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(t, d);
-      if (lane >= d) t += y;
-    }
-    if (lane < kPlanThreads / 64) wave_tot[lane] = t;  // inclusive totals
-  }
-  __syncthreads();
-  return x - v + (wv > 0 ? wave_tot[wv - 1] : 0);
-}
+using namespace pre;
 
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const int32_t* __restrict__ cu,
                                                                     const int32_t* __restrict__ lens, int B,
@@ -146,274 +77,6 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const int32_
   }
 }
 
-struct PrefillParams {
-  const bf16_bits* q;
-  const char* kc;
-  const char* vc;
-  const int32_t* cu;
-  const int32_t* bt;
-  const int32_t* lens;
-  bf16_bits* out;
-  const uint32_t* hdr;
-  uint32_t* counter;
-  const int2* items;
-  float scale_log2;
-  int Hq, Hkv, G, TQ, P, N, M, cap;
-  uint32_t div_m, div_l;  // pos / P = (mulhi(pos, div_m) + pos) >> div_l for 0 <= pos < 2^31
-  uint32_t row_bytes;     // H_kv * D * element bytes: one token's row of the pool
-  const float* k_scale;   // fp8 pools: per-KV-head scales
-  const float* v_scale;
-};
-
-// Exact unsigned division by the block size with a precomputed multiplier
-// (Granlund and Montgomery, "Division by invariant integers using
-// multiplication", 1994): l = ceil(log2 P), m = ceil(2^(32+l) / P) - 2^32.
-__device__ __forceinline__ int div_block(const PrefillParams& p, int pos) {
-  return (int)((__umulhi((uint32_t)pos, p.div_m) + (uint32_t)pos) >> p.div_l);
-}
-
-// LDS of one workgroup: two K / V^T tile buffers and the item's block ids.
-template <int D>
-struct __attribute__((aligned(16))) PrefillLds {
-  static constexpr int KST = D + 8;    // K row stride (elements)
-  static constexpr int VST = kTK + 8;  // V^T row stride (elements; rows 16-byte aligned)
-  bf16_bits k[2][kTK * KST];
-  bf16_bits vt[2][D * VST];
-  int32_t ids[kIdCap];
-};
-
-// V^T row d holds the tile's 64 keys in 8-byte units of 4 keys.  The P.V
-// operand of lane (n, g) for k-step ks is keys 32 ks + 4 g + (0..3) followed by
-// 32 ks + 16 + 4 g + (0..3), so those two units are placed side by side (unit
-// index u = 2 (4 ks + g) + half) and the operand is one 16-byte read.  The
-// unit index is XORed with an even function of d, so that the transposing
-// stores (rows 8 apart across a wave's lanes) spread over the banks and the
-// operand reads stay conflict-free.
-__device__ __forceinline__ int vt_unit(int kq) { return 2 * (4 * (kq >> 3) + (kq & 3)) + ((kq >> 2) & 1); }
-__device__ __forceinline__ int vt_col(int d, int u) { return 4 * (u ^ (2 * ((d >> 4) & 7))); }
-
-// One tile's gathers in flight, held in registers between the global loads
-// and the LDS stores.  Waves 0-3 gather K (D/32 16-byte pieces per thread),
-// waves 4-7 gather V (4 keys x one 16-byte piece per thread).  ok: bit x set
-// when the key of load x is visible and its block id valid.
-// fp8 pools: the same pieces as 8-byte loads of E4M3 codes, widened to fp16
-// (code * 2^-8) when stored.
-template <bool kF8>
-struct TileSet {
-  typedef typename std::conditional<kF8, u32x2_t, u32x4_t>::type LT;
-  LT k[4];
-  uint32_t ok;
-};
-
-// Gathers of one tile.  Every load is issued unconditionally: a key past kmax
-// or with an out-of-range block id reads the head's slice of row 0 instead --
-// always in bounds -- and is zeroed when the tile is stored.  The block ids of
-// the thread's 4 keys are read from LDS first, all together, so the LDS round
-// trip is paid once per tile.
-template <int D, bool kWide, bool kF8>
-__device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillLds<D>& s, int hkv, int k0,
-                                          int kmax, TileSet<kF8>& r) {
-  typedef typename TileSet<kF8>::LT LT;
-  constexpr int EB = kF8 ? 1 : 2;  // pool bytes per element
-  typedef typename std::conditional<kWide, uint64_t, uint32_t>::type O;
-  constexpr int CPR = D / 8;
-  constexpr int NK = D / 32;
-  const int tid = threadIdx.x;
-  const bool kw = uniform(tid >> 8) == 0;  // waves 0-3: K, waves 4-7: V
-  const int u = tid & 255;
-  const int kq = u / CPR, dc = u % CPR;    // V: keys 4 kq .. 4 kq + 3, elements 8 dc .. 8 dc + 7
-  // V threads with kq >= 16 exist only for D = 64: whole waves 6 and 7
-  const bool v_wave = !kw && uniform((tid & 255) >> 6) < 16 * CPR / 64;
-  int pos[4], off[4], blk[4];
-#pragma unroll
-  for (int x = 0; x < 4; ++x) pos[x] = kw ? k0 + (u + 256 * x) / CPR : k0 + 4 * kq + x;
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int jb = div_block(p, pos[x] < kmax ? pos[x] : 0);
-    off[x] = pos[x] - jb * p.P;
-    blk[x] = s.ids[jb];
-  }
-  const O head = (O)(hkv * D * EB);
-  r.ok = 0;
-  const char* base = kw ? p.kc : p.vc;
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    if (kw && x >= NK) continue;  // D = 64: two K pieces per thread
-    const bool ok = pos[x] < kmax && blk[x] >= 0 && blk[x] < p.N;
-    const O o = (ok ? ((O)blk[x] * (O)p.P + (O)off[x]) * (O)p.row_bytes : (O)0) + head +
-                (O)(8 * EB * (kw ? (u + 256 * x) % CPR : dc));
-    r.ok |= (ok ? 1u : 0u) << x;
-    if (kw || v_wave) r.k[x] = *reinterpret_cast<const LT*>(base + o);
-  }
-}
-
-template <int D, bool kF8>
-__device__ __forceinline__ void store_tile(PrefillLds<D>& s, int buf, TileSet<kF8>& r_in) {
-  constexpr int CPR = D / 8;
-  constexpr int NK = D / 32;
-  const int tid = threadIdx.x;
-  const bool kw = uniform(tid >> 8) == 0;
-  const int u = tid & 255;
-  const bool v_wave = !kw && uniform((tid & 255) >> 6) < 16 * CPR / 64;
-  const uint32_t all = kw ? (1u << NK) - 1u : (v_wave ? 0xfu : 0u);
-  if (__builtin_amdgcn_readfirstlane((int)(__ballot(r_in.ok != all) != 0))) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      if (!((r_in.ok >> x) & 1u)) r_in.k[x] = typename TileSet<kF8>::LT{};
-  }
-  struct {
-    u32x4_t k[4];
-  } r;
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    if constexpr (kF8) r.k[x] = e4m3x8_to_f16(r_in.k[x]);
-    else r.k[x] = r_in.k[x];
-  }
-  if (kw) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = u + 256 * i, key = e / CPR, c = e % CPR;
-      *reinterpret_cast<u32x4_t*>(&s.k[buf][key * PrefillLds<D>::KST + 8 * c]) = r.k[i];
-    }
-  } else if (v_wave) {
-    const int kq = u / CPR, dc = u % CPR;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w0 = r.k[0][i], w1 = r.k[1][i], w2 = r.k[2][i], w3 = r.k[3][i];
-      const u32x2_t lo = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
-      const u32x2_t hi = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
-      const int d = dc * 8 + 2 * i;
-      *reinterpret_cast<u32x2_t*>(&s.vt[buf][d * PrefillLds<D>::VST + vt_col(d, vt_unit(kq))]) = lo;
-      *reinterpret_cast<u32x2_t*>(&s.vt[buf][(d + 1) * PrefillLds<D>::VST + vt_col(d + 1, vt_unit(kq))]) = hi;
-    }
-  }
-}
-
-// Softmax reference max moves only when a score exceeds it by more than this
-// (log2 units): probabilities stay below 2^8, and rescaling is rare.
-constexpr float kRescaleSlack = 8.0f;
-
-// Per-wave state of one item: 32 rows (two blocks of 16), one per lane column.
-template <int D>
-struct RowState {
-  static constexpr int NI = D / 32;
-  static constexpr int NDB = D / 16;
-  u32x4_t q[2][NI];  // Q^T operand of each row block
-  int pos[2];        // absolute position of the lane's row (-1: no row)
-  float m[2], l[2];
-  f32x4_t o[NDB][2];  // O^T: lane (n, g) holds d = 16 db + 4 g + j of row n
-};
-
-// One 64-key tile for this wave's 32 rows: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// 16x16x32 products on bf16 operands, or on fp16 ones for fp8 pools.
-template <bool kF8>
-__device__ __forceinline__ f32x4_t mma32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
-  if constexpr (kF8)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
-                                                  0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-}
-
-template <bool kF8>
-__device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
-  if constexpr (kF8) return pack_f16(lo, hi);
-  else return pack_bf16(lo, hi);
-}
-
-template <int D, bool kF8>
-__device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int k0, float scale_log2,
-                                            RowState<D>& st) {
-  constexpr int NI = RowState<D>::NI, NDB = RowState<D>::NDB;
-  const int lane = lane_id();
-  const int n = lane & 15, g = lane >> 4;
-  f32x4_t sc[4][2];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    sc[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    sc[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&s.k[buf][(kb * 16 + n) * PrefillLds<D>::KST + 32 * i + 8 * g]);
-      sc[kb][0] = mma32<kF8>(av, st.q[0][i], sc[kb][0]);
-      sc[kb][1] = mma32<kF8>(av, st.q[1][i], sc[kb][1]);
-    }
-  }
-  // scheduling: every K operand read first, then the products
-
-  u32x4_t pop[2][2];  // [rb][k-step]: P^T operand, 8 bf16
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    // causal mask, only where this row block's last key position is inside
-    // the tile (keys past a row's position get -inf)
-    // (the lane's keys are kb*16 + 4g + j, kb, j < 4: all visible when lim >= 51)
-    const int lim = st.pos[rb] - k0 - 4 * g;  // key kb*16 + 4g + j is visible when kb*16 + j <= lim
-    if (__builtin_amdgcn_readfirstlane((int)(__ballot(lim < 3 * 16 + 3) != 0))) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sc[kb][rb][j] = kb * 16 + j <= lim ? sc[kb][rb][j] : -INFINITY;
-    }
-    // max of the raw scores (scale_log2 > 0), in log2 units after scaling
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sc[kb][rb][j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    tmax *= scale_log2;
-    const bool move = tmax > st.m[rb] + kRescaleSlack;
-    if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
-      const float alpha = (move && st.m[rb] != -INFINITY) ? fast_exp2(st.m[rb] - tmax) : 1.0f;
-      if (move) st.m[rb] = tmax;
-      st.l[rb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) st.o[db][rb] *= alpha;
-    }
-    const float nm = st.m[rb] == -INFINITY ? 0.f : -st.m[rb];
-    float pv[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pv[kb][j] = fast_exp2(fmaf(sc[kb][rb][j], scale_log2, nm));
-        st.l[rb] += pv[kb][j];
-      }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      pop[rb][ks] = u32x4_t{pack_p<kF8>(pv[2 * ks][0], pv[2 * ks][1]), pack_p<kF8>(pv[2 * ks][2], pv[2 * ks][3]),
-                            pack_p<kF8>(pv[2 * ks + 1][0], pv[2 * ks + 1][1]),
-                            pack_p<kF8>(pv[2 * ks + 1][2], pv[2 * ks + 1][3])};
-  }
-  // k-slots 0..3 of step ks are keys 32 ks + 4 g + j, slots 4..7 keys 32 ks + 16 + 4 g + j
-  u32x4_t va[NDB][2];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int d = db * 16 + n;
-      va[db][ks] = *reinterpret_cast<const u32x4_t*>(&s.vt[buf][d * PrefillLds<D>::VST + vt_col(d, 2 * (4 * ks + g))]);
-    }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      st.o[db][0] = mma32<kF8>(va[db][ks], pop[0][ks], st.o[db][0]);
-      st.o[db][1] = mma32<kF8>(va[db][ks], pop[1][ks], st.o[db][1]);
-    }
-  }
-
-}
-
-template <int D, bool kF8>
-__device__ __forceinline__ void attend(const PrefillLds<D>& s, int buf, int k0, float scale_log2, int wave_max,
-                                       RowState<D>& st) {
-  if (k0 > wave_max) return;  // every row of this wave is causally done
-  attend_tile<D, kF8>(s, buf, k0, scale_log2, st);
-}
-
 // ---------------------------------------------------------------------------
 // Prefill kernel: one persistent workgroup of 8 waves per CU pulls items.
 // An item is (request, tile of TQ chunk tokens, KV head) with 256 rows
@@ -426,11 +89,7 @@ template <int D, bool kWide, bool kF8>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   __shared__ PrefillLds<D> lds;
   __shared__ uint32_t s_item, s_head;
-  constexpr int NI = RowState<D>::NI, NDB = RowState<D>::NDB;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = uniform(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
   const uint32_t entries = p.hdr[kEntryCountWord];
   // With H_kv a multiple of 8, KV head h is worked on by the workgroups of
   // XCD h % 8 (blocks are dealt to the XCDs in turn), so the q tiles that
@@ -463,93 +122,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const uint32_t e = s_item;
     if (e == 0xffffffffu) break;
     const int2 it = p.items[e];
-    const int hkv = (int)s_head;
-    const int b = it.x, qt = it.y;
-    const int cu0 = p.cu[b];
-    const int T = p.cu[b + 1] - cu0;
-    const int L = clamp_len(p.lens[b], p.cap);
-    const int start = L - T;  // position of chunk row 0
-    const int t0 = qt * p.TQ;
-    const int nt = min(p.TQ, T - t0);
-    const int kmax = start + t0 + nt;  // keys 0 .. kmax-1 are visible to some row
-    const int nkt = (kmax + kTK - 1) / kTK;
-    const int32_t* __restrict__ bt_row = p.bt + (int64_t)b * p.M;
-    const int nblk = div_block(p, kmax - 1) + 1;  // kmax <= cap = M * P, so nblk <= M <= kIdCap
-    for (int i = tid; i < nblk; i += kThreads) lds.ids[i] = bt_row[i];
-
-    RowState<D> st;
-    int wave_max = -1;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int r = 32 * w + 16 * rb + n;
-      const int hl = r / p.TQ, tl = r - hl * p.TQ;
-      const bool ok = hl < p.G && tl < nt;
-      st.pos[rb] = ok ? start + t0 + tl : -1;
-      const int64_t qrow = ((int64_t)(cu0 + t0 + tl) * p.Hq + hkv * p.G + hl) * D;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        st.q[rb][i] = ok ? *reinterpret_cast<const u32x4_t*>(p.q + qrow + 32 * i + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
-        if constexpr (kF8) {  // bf16 query -> fp16 operand (exact inside the fp16 range)
-#pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2) st.q[rb][i][w2] = pack_f16(bf16_lo(st.q[rb][i][w2]), bf16_hi(st.q[rb][i][w2]));
-        }
-      }
-      if (ok) wave_max = max(wave_max, st.pos[rb]);
-      st.m[rb] = -INFINITY;
-      st.l[rb] = 0.f;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) st.o[db][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) wave_max = max(wave_max, __shfl_xor(wave_max, off));
-    wave_max = uniform(wave_max);
-    __syncthreads();  // block ids visible
-
-    // fp8 pools: codes * scale, staged as code * 2^-8
-    const float sl2 = kF8 ? p.scale_log2 * 256.0f * p.k_scale[hkv] : p.scale_log2;
-    const float vmul = kF8 ? 256.0f * p.v_scale[hkv] : 1.0f;
-
-    // pipeline: tile j travels in register set j & 1 and LDS buffer j & 1
-    TileSet<kF8> ra, rb;
-    load_tile<D, kWide, kF8>(p, lds, hkv, 0, kmax, ra);
-    if (nkt > 1) load_tile<D, kWide, kF8>(p, lds, hkv, kTK, kmax, rb);
-    store_tile<D, kF8>(lds, 0, ra);
-    if (nkt > 2) load_tile<D, kWide, kF8>(p, lds, hkv, 2 * kTK, kmax, ra);
-    __syncthreads();
-    for (int kt = 0; kt < nkt; kt += 2) {
-      attend<D, kF8>(lds, 0, kt * kTK, sl2, wave_max, st);
-      if (kt + 1 < nkt) {
-        store_tile<D, kF8>(lds, 1, rb);
-        if (kt + 3 < nkt) load_tile<D, kWide, kF8>(p, lds, hkv, (kt + 3) * kTK, kmax, rb);
-      }
-      __syncthreads();
-      if (kt + 1 >= nkt) break;
-      attend<D, kF8>(lds, 1, (kt + 1) * kTK, sl2, wave_max, st);
-      if (kt + 2 < nkt) {
-        store_tile<D, kF8>(lds, 0, ra);
-        if (kt + 4 < nkt) load_tile<D, kWide, kF8>(p, lds, hkv, (kt + 4) * kTK, kmax, ra);
-      }
-      __syncthreads();
-    }
-
-    // ---- normalise and store: lane holds O^T[d = 16db + 4g + j][row n] ----
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float lt = st.l[rb];
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
-      if (st.pos[rb] < 0) continue;
-      const int r = 32 * w + 16 * rb + n;
-      const int hl = r / p.TQ, tl = r - hl * p.TQ;
-      const float inv = vmul / lt;
-      bf16_bits* dst = p.out + ((int64_t)(cu0 + t0 + tl) * p.Hq + hkv * p.G + hl) * D + 4 * g;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t v = {pack_bf16(st.o[db][rb][0] * inv, st.o[db][rb][1] * inv),
-                           pack_bf16(st.o[db][rb][2] * inv, st.o[db][rb][3] * inv)};
-        *reinterpret_cast<u32x2_t*>(dst + 16 * db) = v;
-      }
-    }
+    prefill_item<D, kWide, kF8>(p, lds, it.x, it.y, (int)s_head);
   }
 }
 

@@ -7,7 +7,7 @@ import numpy as np
 import torch
 
 import paged_kv_cache_48_amd as pa
-from oracle import ref_reshape_and_cache, ref_slot_mapping, widen
+from oracle import ref_decode, ref_dequantize, ref_reshape_and_cache, ref_slot_mapping, widen
 from workloads import nan_pool
 
 DEV = "cuda:0"
@@ -106,3 +106,41 @@ def assert_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = "",
             f"got {g[tuple(i)]!r}, ref {ref[tuple(i)]!r}; max err {float(np.nanmax(err))}"
         )
     return float(err.max()) if err.size else 0.0
+
+
+def fp8_scales(H, seed, lo=0.004, hi=0.03):
+    return np.random.default_rng(seed).uniform(lo, hi, H).astype(np.float32)
+
+
+class Fp8Case:
+    """A case's pools written as fp8 through the HIP path (prefix, then new tokens)."""
+
+    def __init__(self, c, ks, vs):
+        self.case, self.ks, self.vs = c, ks, vs
+        shape = (c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim)
+        # unwritten slots hold the largest code (448): a masking mistake would show
+        self.kc = torch.full(shape, 0x7E, dtype=torch.uint8, device=DEV)
+        self.vc = torch.full(shape, 0x7E, dtype=torch.uint8, device=DEV)
+        self.dks, self.dvs = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+        self.bt, self.lens, self.cu = idx(c.block_table), idx(c.context_lens), idx(c.cu_seqlens)
+        kp, vp, cu_pre, lens_pre = c.prefix()
+        if len(kp):
+            sl = pa.slot_mapping(self.bt, idx(cu_pre), idx(lens_pre), c.block_size, len(kp))
+            pa.reshape_and_cache(to_dev(kp, c.dtype), to_dev(vp, c.dtype), sl, self.kc, self.vc, self.dks, self.dvs)
+        kn, vn = c.new_kv()
+        sl = pa.slot_mapping(self.bt, idx(c.cu_seqlens), self.lens, c.block_size, c.T_total)
+        pa.reshape_and_cache(to_dev(kn, c.dtype), to_dev(vn, c.dtype), sl, self.kc, self.vc, self.dks, self.dvs)
+        self.q = to_dev(c.q, c.dtype)
+
+    def decode(self, q=None, bt=None, lens=None):
+        q = self.q if q is None else q
+        out = torch.empty_like(q)
+        pa.paged_decode_attention(q, self.kc, self.vc, self.bt if bt is None else bt,
+                                  self.lens if lens is None else lens, self.case.scale, out, self.dks, self.dvs)
+        return out
+
+    def reference(self, select=None):
+        c = self.case
+        kc, vc = self.kc.cpu().numpy(), self.vc.cpu().numpy()
+        return ref_decode(c.q, ref_dequantize(kc, self.ks), ref_dequantize(vc, self.vs), c.block_table,
+                          c.context_lens, c.scale, select=select)

@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_expected_calls():
     names = declared_functions()
     for want in ("pa_slot_mapping", "pa_reshape_and_cache", "pa_paged_decode_attention",
-                 "pa_paged_prefill_attention", "pa_decode_workspace_size", "pa_prefill_workspace_size"):
+                 "pa_paged_prefill_attention", "pa_decode_workspace_size", "pa_prefill_workspace_size",
+                 "pa_paged_mixed_attention", "pa_paged_mixed_attention_fp8", "pa_mixed_workspace_size"):
         assert want in names
 
 
@@ -119,6 +120,43 @@ def test_prefill_validation(lib, kw, status):
 
 def test_prefill_no_tokens_is_a_noop(lib):
     assert prefill(lib, T=0, q=NUL, k=NUL, v=NUL, cu=NUL, bt=NUL, lens=NUL, out=NUL, ws=NUL, wsb=0) == OK
+
+
+def mixed(lib, **kw):
+    a = dict(q=1, k=1, v=1, cu=1, bt=1, lens=1, scale=0.1, out=1, B=2, T=10, Hq=8, Hkv=2, D=128, P=16,
+             N=100, M=8, dtype=BF16, ws=1, wsb=1 << 30, stream=NUL)
+    a.update(kw)
+    return lib.pa_paged_mixed_attention(a["q"], a["k"], a["v"], a["cu"], a["bt"], a["lens"], a["scale"],
+                                        a["out"], a["B"], a["T"], a["Hq"], a["Hkv"], a["D"], a["P"], a["N"],
+                                        a["M"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=F32), UNSUPPORTED),
+    (dict(Hq=256, Hkv=1), UNSUPPORTED),    # GQA group above 64
+    (dict(B=1025, T=2000), UNSUPPORTED),   # work lists are derived on chip for at most 1024 requests
+    (dict(T=-1), INVALID),
+    (dict(B=0), INVALID),                  # tokens but no sequence
+    (dict(cu=NUL), INVALID),
+    (dict(wsb=8), WORKSPACE),
+    (dict(D=32), UNSUPPORTED),
+    (dict(M=16385), UNSUPPORTED),
+    (dict(scale=0.0), INVALID),
+])
+def test_mixed_validation(lib, kw, status):
+    assert mixed(lib, **kw) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_mixed_no_tokens_is_a_noop(lib):
+    assert mixed(lib, T=0, q=NUL, k=NUL, v=NUL, cu=NUL, bt=NUL, lens=NUL, out=NUL, ws=NUL, wsb=0) == OK
+
+
+def test_mixed_workspace_size(lib):
+    # the decode partials plus one header of prefill queue counters
+    assert lib.pa_mixed_workspace_size(64, 32, 128, 16, 512) == lib.pa_decode_workspace_size(64, 32, 128, 16, 512) \
+        + 1024
+    assert lib.pa_mixed_workspace_size(-1, 32, 128, 16, 512) == 0
 
 
 def test_reshape_validation(lib):

@@ -13,7 +13,8 @@ import paged_kv_cache_48_amd as pa
 from oracle import ref_copy_blocks, ref_decode, ref_prefill, ref_slot_mapping
 from workloads import config_case, make_case, shared_prefix_case
 
-from gpu_util import DEV, DevCase, assert_close, dev_nan_pool, idx, oracle_pool, to_dev, to_host_bits
+from gpu_util import (DEV, DevCase, Fp8Case, assert_close, dev_nan_pool, fp8_scales, idx, oracle_pool, to_dev,
+                      to_host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -478,10 +479,6 @@ def test_mixed_step_full_size_sampled(P):
 from oracle import ref_dequantize, ref_reshape_and_cache_fp8  # noqa: E402
 
 
-def _scales(H, seed, lo=0.004, hi=0.03):
-    return np.random.default_rng(seed).uniform(lo, hi, H).astype(np.float32)
-
-
 @pytest.mark.parametrize("src", ["bf16", "f32"])
 def test_reshape_and_cache_fp8_bit_exact(src):
     N, P, H, D = 40, 7, 4, 64
@@ -497,7 +494,7 @@ def test_reshape_and_cache_fp8_bit_exact(src):
         v = xb[::-1].copy()
     else:
         k, v = x, x[::-1].copy()
-    ks, vs = _scales(H, 51, 0.01, 2.0), _scales(H, 52, 0.01, 2.0)
+    ks, vs = fp8_scales(H, 51, 0.01, 2.0), fp8_scales(H, 52, 0.01, 2.0)
     slots = rng.permutation(N * P)[:T].astype(np.int32)
     slots[5] = -1
     kc0 = rng.integers(0, 256, (N, P, H, D), dtype=np.uint8)
@@ -512,45 +509,11 @@ def test_reshape_and_cache_fp8_bit_exact(src):
     assert np.array_equal(dv.cpu().numpy(), want_v)
 
 
-class Fp8Case:
-    """A case's pools written as fp8 through the HIP path (prefix, then new tokens)."""
-
-    def __init__(self, c, ks, vs):
-        self.case, self.ks, self.vs = c, ks, vs
-        shape = (c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim)
-        # unwritten slots hold the largest code (448): a masking mistake would show
-        self.kc = torch.full(shape, 0x7E, dtype=torch.uint8, device=DEV)
-        self.vc = torch.full(shape, 0x7E, dtype=torch.uint8, device=DEV)
-        self.dks, self.dvs = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
-        self.bt, self.lens = idx(c.block_table), idx(c.context_lens)
-        kp, vp, cu_pre, lens_pre = c.prefix()
-        if len(kp):
-            sl = pa.slot_mapping(self.bt, idx(cu_pre), idx(lens_pre), c.block_size, len(kp))
-            pa.reshape_and_cache(to_dev(kp, c.dtype), to_dev(vp, c.dtype), sl, self.kc, self.vc, self.dks, self.dvs)
-        kn, vn = c.new_kv()
-        sl = pa.slot_mapping(self.bt, idx(c.cu_seqlens), self.lens, c.block_size, c.T_total)
-        pa.reshape_and_cache(to_dev(kn, c.dtype), to_dev(vn, c.dtype), sl, self.kc, self.vc, self.dks, self.dvs)
-        self.q = to_dev(c.q, c.dtype)
-
-    def decode(self, q=None, bt=None, lens=None):
-        q = self.q if q is None else q
-        out = torch.empty_like(q)
-        pa.paged_decode_attention(q, self.kc, self.vc, self.bt if bt is None else bt,
-                                  self.lens if lens is None else lens, self.case.scale, out, self.dks, self.dvs)
-        return out
-
-    def reference(self, select=None):
-        c = self.case
-        kc, vc = self.kc.cpu().numpy(), self.vc.cpu().numpy()
-        return ref_decode(c.q, ref_dequantize(kc, self.ks), ref_dequantize(vc, self.vs), c.block_table,
-                          c.context_lens, c.scale, select=select)
-
-
 @pytest.mark.parametrize("G,Hkv,D,P", [(4, 8, 128, 16), (1, 4, 64, 16), (8, 2, 128, 7), (3, 2, 64, 1),
                                        (16, 1, 128, 64)])
 def test_decode_fp8_matches_oracle(G, Hkv, D, P):
     c = small(P=P, Hq=G * Hkv, Hkv=Hkv, D=D, lens=(1, 16, 255, 256, 257, 700, 1500), seed=60 + G * D + P)
-    f = Fp8Case(c, _scales(Hkv, 61), _scales(Hkv, 62))
+    f = Fp8Case(c, fp8_scales(Hkv, 61), fp8_scales(Hkv, 62))
     # the pools hold exactly the oracle's codes
     kc0 = np.full((c.num_blocks, P, Hkv, D), 0x7E, dtype=np.uint8)
     kp, vp, cu_pre, lens_pre = c.prefix()
@@ -565,7 +528,7 @@ def test_decode_fp8_matches_oracle(G, Hkv, D, P):
 
 def test_decode_fp8_long_contexts_and_batch_invariance_bitwise():
     c = small(P=16, Hq=32, Hkv=8, D=128, lens=(8192, 3000, 17, 4097, 256), seed=63)
-    f = Fp8Case(c, _scales(8, 64), _scales(8, 65))
+    f = Fp8Case(c, fp8_scales(8, 64), fp8_scales(8, 65))
     full = f.decode()
     assert_close(full, f.reference(), "bf16", "fp8 long contexts")
     fb = to_host_bits(full)
@@ -592,7 +555,7 @@ def test_prefill_fp8_matches_oracle(G, Hkv, D, P):
     lens = (70, 300, 45, 9, 620)
     qlens = (70, 100, 33, 1, 300)
     c = small(P=P, Hq=G * Hkv, Hkv=Hkv, D=D, lens=lens, qlens=qlens, seed=70 + G * D + P)
-    f = Fp8Case(c, _scales(Hkv, 71), _scales(Hkv, 72))
+    f = Fp8Case(c, fp8_scales(Hkv, 71), fp8_scales(Hkv, 72))
     out = torch.empty_like(f.q)
     pa.paged_prefill_attention(f.q, f.kc, f.vc, idx(c.cu_seqlens), f.bt, f.lens, c.scale, out, f.dks, f.dvs)
     kc, vc = f.kc.cpu().numpy(), f.vc.cpu().numpy()
