@@ -19,10 +19,12 @@
 //     waits on a global load (a wait on one would drain the loads in flight,
 //     which complete in order).
 //   * Per 64-key tile, four waves gather K rows and four gather V rows through
-//     the block table (16-byte loads); K is stored as is in LDS and V
-//     transposed (d-major) so that both MFMA operands are contiguous LDS
-//     reads.  Two register sets and two LDS buffers keep the loads of the next
-//     two tiles in flight while one tile computes; one barrier per tile.
+//     the block table (16-byte loads), and both are stored row-major in LDS
+//     (the same work for every wave).  The K operand is a contiguous LDS
+//     read; the V^T operand of the P.V product comes from gfx950's
+//     transposing LDS read (ds_read_b64_tr_b16).  Two register sets and two
+//     LDS buffers keep the loads of the next two tiles in flight while one
+//     tile computes; one barrier per tile.
 //   * Each wave owns 32 rows.  S^T = K Q^T and O^T += V^T P^T run as
 //     16x16x32 bf16 MFMAs with fp32 accumulation.  Computing the transposed
 //     scores leaves each lane holding one query row's scores for a run of keys,

@@ -106,30 +106,34 @@ __device__ __forceinline__ int div_block(const PrefillParams& p, int pos) {
   return (int)((__umulhi((uint32_t)pos, p.div_m) + (uint32_t)pos) >> p.div_l);
 }
 
-// LDS of one workgroup: two K / V^T tile buffers and the item's block ids.
+// LDS of one workgroup: two K / V tile buffers (row-major) and the item's
+// block ids.  The V row stride is an odd multiple of 32 bytes modulo 256, so
+// the transposing operand reads (16 rows x 32 bytes per half-wave) and the
+// row stores are free of bank conflicts.
 template <int D>
 struct __attribute__((aligned(16))) PrefillLds {
-  static constexpr int KST = D + 8;    // K row stride (elements)
-  static constexpr int VST = kTK + 8;  // V^T row stride (elements; rows 16-byte aligned)
+  static constexpr int KST = D + 8;   // K row stride (elements)
+  static constexpr int VST = D + 16;  // V row stride (elements)
   bf16_bits k[2][kTK * KST];
-  bf16_bits vt[2][D * VST];
+  bf16_bits v[2][kTK * VST];
   int32_t ids[kIdCap];
 };
 
-// V^T row d holds the tile's 64 keys in 8-byte units of 4 keys.  The P.V
-// operand of lane (n, g) for k-step ks is keys 32 ks + 4 g + (0..3) followed by
-// 32 ks + 16 + 4 g + (0..3), so those two units are placed side by side (unit
-// index u = 2 (4 ks + g) + half) and the operand is one 16-byte read.  The
-// unit index is XORed with an even function of d, so that the transposing
-// stores (rows 8 apart across a wave's lanes) spread over the banks and the
-// operand reads stay conflict-free.
-__device__ __forceinline__ int vt_unit(int kq) { return 2 * (4 * (kq >> 3) + (kq & 3)) + ((kq >> 2) & 1); }
-__device__ __forceinline__ int vt_col(int d, int u) { return 4 * (u ^ (2 * ((d >> 4) & 7))); }
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// gfx950's transposing LDS read: within each 16-lane group, lane l receives
+// element l % 4 of the 8-byte chunks addressed by lanes l / 4, 4 + l / 4,
+// 8 + l / 4 and 12 + l / 4 of the group.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const bf16_bits* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+}
 
 // One tile's gathers in flight, held in registers between the global loads
-// and the LDS stores.  Waves 0-3 gather K (D/32 16-byte pieces per thread),
-// waves 4-7 gather V (4 keys x one 16-byte piece per thread).  ok: bit x set
-// when the key of load x is visible and its block id valid.
+// and the LDS stores.  Waves 0-3 gather K and waves 4-7 gather V, D/32
+// 16-byte pieces per thread: piece e = u + 256 x of thread u is key e / (D/8),
+// elements 8 (e % (D/8)) .. + 7.  ok: bit x set when the key of load x is
+// visible and its block id valid.
 // fp8 pools: the same pieces as 8-byte loads of E4M3 codes, widened to fp16
 // (code * 2^-8) when stored.
 template <bool kF8>
@@ -143,7 +147,7 @@ struct TileSet {
 // or with an out-of-range block id reads the head's slice of row 0 instead --
 // always in bounds -- and is zeroed when the tile is stored.  The block ids of
 // the thread's 4 keys are read from LDS first, all together, so the LDS round
-// trip is paid once per tile.
+// trip is paid once per tile.  The tile is stored row-major, K and V alike.
 template <int D, bool kWide, bool kF8>
 __device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillLds<D>& s, int hkv, int k0,
                                           int kmax, TileSet<kF8>& r) {
@@ -155,14 +159,11 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillL
   const int tid = threadIdx.x;
   const bool kw = uniform(tid >> 8) == 0;  // waves 0-3: K, waves 4-7: V
   const int u = tid & 255;
-  const int kq = u / CPR, dc = u % CPR;    // V: keys 4 kq .. 4 kq + 3, elements 8 dc .. 8 dc + 7
-  // V threads with kq >= 16 exist only for D = 64: whole waves 6 and 7
-  const bool v_wave = !kw && uniform((tid & 255) >> 6) < 16 * CPR / 64;
-  int pos[4], off[4], blk[4];
+  int pos[NK], off[NK], blk[NK];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) pos[x] = kw ? k0 + (u + 256 * x) / CPR : k0 + 4 * kq + x;
+  for (int x = 0; x < NK; ++x) pos[x] = k0 + (u + 256 * x) / CPR;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
+  for (int x = 0; x < NK; ++x) {
     const int jb = div_block(p, pos[x] < kmax ? pos[x] : 0);
     off[x] = pos[x] - jb * p.P;
     blk[x] = s.ids[jb];
@@ -171,13 +172,12 @@ __device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillL
   r.ok = 0;
   const char* base = kw ? p.kc : p.vc;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    if (kw && x >= NK) continue;  // D = 64: two K pieces per thread
+  for (int x = 0; x < NK; ++x) {
     const bool ok = pos[x] < kmax && blk[x] >= 0 && blk[x] < p.N;
     const O o = (ok ? ((O)blk[x] * (O)p.P + (O)off[x]) * (O)p.row_bytes : (O)0) + head +
-                (O)(8 * EB * (kw ? (u + 256 * x) % CPR : dc));
+                (O)(8 * EB * ((u + 256 * x) % CPR));
     r.ok |= (ok ? 1u : 0u) << x;
-    if (kw || v_wave) r.k[x] = *reinterpret_cast<const LT*>(base + o);
+    r.k[x] = *reinterpret_cast<const LT*>(base + o);
   }
 }
 
@@ -188,38 +188,21 @@ __device__ __forceinline__ void store_tile(PrefillLds<D>& s, int buf, TileSet<kF
   const int tid = threadIdx.x;
   const bool kw = uniform(tid >> 8) == 0;
   const int u = tid & 255;
-  const bool v_wave = !kw && uniform((tid & 255) >> 6) < 16 * CPR / 64;
-  const uint32_t all = kw ? (1u << NK) - 1u : (v_wave ? 0xfu : 0u);
+  const uint32_t all = (1u << NK) - 1u;
   if (__builtin_amdgcn_readfirstlane((int)(__ballot(r_in.ok != all) != 0))) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < NK; ++x)
       if (!((r_in.ok >> x) & 1u)) r_in.k[x] = typename TileSet<kF8>::LT{};
   }
-  struct {
-    u32x4_t k[4];
-  } r;
+  bf16_bits* dst = kw ? s.k[buf] : s.v[buf];
+  const int stride = kw ? PrefillLds<D>::KST : PrefillLds<D>::VST;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    if constexpr (kF8) r.k[x] = e4m3x8_to_f16(r_in.k[x]);
-    else r.k[x] = r_in.k[x];
-  }
-  if (kw) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = u + 256 * i, key = e / CPR, c = e % CPR;
-      *reinterpret_cast<u32x4_t*>(&s.k[buf][key * PrefillLds<D>::KST + 8 * c]) = r.k[i];
-    }
-  } else if (v_wave) {
-    const int kq = u / CPR, dc = u % CPR;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w0 = r.k[0][i], w1 = r.k[1][i], w2 = r.k[2][i], w3 = r.k[3][i];
-      const u32x2_t lo = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
-      const u32x2_t hi = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
-      const int d = dc * 8 + 2 * i;
-      *reinterpret_cast<u32x2_t*>(&s.vt[buf][d * PrefillLds<D>::VST + vt_col(d, vt_unit(kq))]) = lo;
-      *reinterpret_cast<u32x2_t*>(&s.vt[buf][(d + 1) * PrefillLds<D>::VST + vt_col(d + 1, vt_unit(kq))]) = hi;
-    }
+  for (int i = 0; i < NK; ++i) {
+    u32x4_t w;
+    if constexpr (kF8) w = e4m3x8_to_f16(r_in.k[i]);
+    else w = r_in.k[i];
+    const int e = u + 256 * i, key = e / CPR, c = e % CPR;
+    *reinterpret_cast<u32x4_t*>(&dst[key * stride + 8 * c]) = w;
   }
 }
 
@@ -295,8 +278,7 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) tmax = fmaxf(tmax, sc[kb][rb][j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_over_rows(tmax);
     tmax *= scale_log2;
     const bool move = tmax > st.m[rb] + kRescaleSlack;
     if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
@@ -322,13 +304,17 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
                             pack_p<kF8>(pv[2 * ks + 1][2], pv[2 * ks + 1][3])};
   }
   // k-slots 0..3 of step ks are keys 32 ks + 4 g + j, slots 4..7 keys 32 ks + 16 + 4 g + j
+  // V^T operand of lane (n, g): keys 32 ks + 4 g + (0..3) and 32 ks + 16 + 4 g + (0..3)
+  // of column 16 db + n, as two transposing reads; lane n of the group
+  // addresses row n / 4 of the 4-row slice, columns 4 (n % 4) .. 4 (n % 4) + 3
   u32x4_t va[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int d = db * 16 + n;
-      va[db][ks] = *reinterpret_cast<const u32x4_t*>(&s.vt[buf][d * PrefillLds<D>::VST + vt_col(d, 2 * (4 * ks + g))]);
+      const bf16_bits* a = &s.v[buf][(32 * ks + 4 * g + (n >> 2)) * PrefillLds<D>::VST + 16 * db + 4 * (n & 3)];
+      const u32x2_t lo = lds_read_tr16(a), hi = lds_read_tr16(a + 16 * PrefillLds<D>::VST);
+      va[db][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     }
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
@@ -430,8 +416,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, PrefillLds<
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     float lt = st.l[rb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    lt = sum_over_rows(lt);
     if (st.pos[rb] < 0) continue;
     const int r = 32 * w + 16 * rb + n;
     const int hl = r / p.TQ, tl = r - hl * p.TQ;
