@@ -30,7 +30,8 @@
 //     scores leaves each lane holding one query row's scores for a run of keys,
 //     which is exactly the B-operand layout the P.V product needs, so P never
 //     leaves registers.  Online softmax in base 2, fp32, with a lazily moved
-//     reference max; tiles past every row of a wave are skipped.
+//     reference max; the row sums of P are products with a ones operand;
+//     tiles past every row of a wave are skipped.
 //   * Keys past the causal limit, tail slots and out-of-range block ids are
 //     masked and never multiply a value: masked K/V tile rows are zero-filled.
 #include "prefill_dev.h"

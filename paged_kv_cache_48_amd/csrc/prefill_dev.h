@@ -217,7 +217,8 @@ struct RowState {
   static constexpr int NDB = D / 16;
   u32x4_t q[2][NI];  // Q^T operand of each row block
   int pos[2];        // absolute position of the lane's row (-1: no row)
-  float m[2], l[2];
+  float m[2];
+  f32x4_t l[2];  // row sums, accumulated by MFMA (every component holds the sum)
   f32x4_t o[NDB][2];  // O^T: lane (n, g) holds d = 16 db + 4 g + j of row n
 };
 
@@ -295,13 +296,17 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         pv[kb][j] = fast_exp2(fmaf(sc[kb][rb][j], scale_log2, nm));
-        st.l[rb] += pv[kb][j];
       }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       pop[rb][ks] = u32x4_t{pack_p<kF8>(pv[2 * ks][0], pv[2 * ks][1]), pack_p<kF8>(pv[2 * ks][2], pv[2 * ks][3]),
                             pack_p<kF8>(pv[2 * ks + 1][0], pv[2 * ks + 1][1]),
                             pack_p<kF8>(pv[2 * ks + 1][2], pv[2 * ks + 1][3])};
+    // row sums of the probabilities as products with a ones operand
+    const uint32_t one2 = kF8 ? 0x3C003C00u : 0x3F803F80u;
+    const u32x4_t ones = {one2, one2, one2, one2};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) st.l[rb] = mma32<kF8>(ones, pop[rb][ks], st.l[rb]);
   }
   // k-slots 0..3 of step ks are keys 32 ks + 4 g + j, slots 4..7 keys 32 ks + 16 + 4 g + j
   // V^T operand of lane (n, g): keys 32 ks + 4 g + (0..3) and 32 ks + 16 + 4 g + (0..3)
@@ -376,7 +381,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, PrefillLds<
     }
     if (ok) wave_max = max(wave_max, st.pos[rb]);
     st.m[rb] = -INFINITY;
-    st.l[rb] = 0.f;
+    st.l[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < NDB; ++db) st.o[db][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -415,8 +420,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, PrefillLds<
   // ---- normalise and store: lane holds O^T[d = 16db + 4g + j][row n] ----
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    float lt = st.l[rb];
-    lt = sum_over_rows(lt);
+    const float lt = st.l[rb][0];
     if (st.pos[rb] < 0) continue;
     const int r = 32 * w + 16 * rb + n;
     const int hl = r / p.TQ, tl = r - hl * p.TQ;
