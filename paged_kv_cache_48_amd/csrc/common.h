@@ -118,6 +118,15 @@ __device__ __forceinline__ float sum_over_rows(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// gfx950's byte-transposing LDS read (ds_read_b64_tr_b8): within each 16-lane
+// group, byte j of lane l's result is byte l % 8 of the 8 bytes addressed by
+// lane 2 j + l / 8 of the group.  p must point into LDS, 8-byte aligned.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+__device__ __forceinline__ u32x2_t lds_read_tr8(const char* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)p));
+}
+
 // Wave-uniform copy of a value (held in a scalar register).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -93,22 +93,25 @@ struct QType<fp8_e4m3> {
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct Geo {
-  // fp8 pools are staged as 16-bit values (fp16 holding e4m3 * 2^-8)
+  // fp8 pools: tiles of 32 tokens (the bytes of a 16-token bf16 tile), staged
+  // as the codes themselves and widened to fp16 (code * 2^-8) when an MFMA
+  // operand is read
   static constexpr bool kFp8 = std::is_same<T, fp8_e4m3>::value;
-  static constexpr int ESZ = kFp8 ? 2 : (int)sizeof(T);  // bytes of a staged element
-  static constexpr int ROWB = D * ESZ;             // staged bytes of one head's row slice
-  static constexpr int GROWB = D * (int)sizeof(T);  // pool bytes of one head's row slice
-  static constexpr int CPR = ROWB / 16;            // 16-byte staged pieces per row slice
-  static constexpr int LOADB = GROWB / CPR;        // pool bytes a lane loads per token (16; 8 for fp8)
-  static constexpr int TPL = 16 * CPR / 64;        // tokens per lane per tile
-  static constexpr int KST = ROWB + 16;            // LDS row stride of K (and of V for fp32)
-  static constexpr int VTS = 40;                   // LDS row stride of transposed V (16-bit): 16 tokens + pad
-  static constexpr bool kBf16 = ESZ == 2;          // 16-bit path (bf16, or fp8 via fp16)
-  static constexpr int KBYTES = 16 * KST;
-  static constexpr int VBYTES = kBf16 ? D * VTS : 16 * KST;
+  static constexpr bool kBf16 = std::is_same<T, bf16_bits>::value;
+  static constexpr bool kHalf = kBf16 || kFp8;     // 16-bit q and out (fp16 MFMAs for fp8)
+  static constexpr int TT = kFp8 ? 32 : 16;        // tokens per tile
+  static constexpr int ROWB = D * (int)sizeof(T);  // bytes of one head's row slice (pool and LDS)
+  static constexpr int GROWB = ROWB;
+  static constexpr int CPR = ROWB / 16;            // 16-byte pieces per row slice
+  static constexpr int LOADB = 16;                 // pool bytes a lane loads per token
+  static constexpr int TPL = TT * CPR / 64;        // tokens per lane per tile
+  static constexpr int KST = ROWB + 16;            // LDS row stride of K (and of V unless bf16)
+  static constexpr int VTS = 40;                   // LDS row stride of transposed bf16 V: 16 tokens + pad
+  static constexpr int KBYTES = TT * KST;
+  static constexpr int VBYTES = kBf16 ? D * VTS : TT * KST;
   static constexpr int LDS_PER_WAVE = KBYTES + VBYTES;
-  static constexpr int NQ = kBf16 ? D / 32 : D / 4;  // QK MFMA steps over the head dimension
-  static constexpr int NQV = kBf16 ? NQ : NQ / 4;    // 16-byte Q pieces per lane
+  static constexpr int NQ = kHalf ? D / 32 : D / 4;  // QK MFMA steps over the head dimension
+  static constexpr int NQV = kHalf ? NQ : NQ / 4;    // 16-byte Q pieces per lane
 };
 
 // Byte offsets into the pool: 32-bit when the pool is under 4 GiB (one VGPR
@@ -120,7 +123,7 @@ struct Off {
 
 template <typename T, int D>
 struct TileRegs {
-  typedef typename std::conditional<Geo<T, D>::kFp8, u32x2_t, u32x4_t>::type LT;  // one lane's load per token
+  typedef u32x4_t LT;  // one lane's load per token
   LT k[Geo<T, D>::TPL];
   LT v[Geo<T, D>::TPL];
   uint32_t ok;  // bit j: token j of this lane is inside the partition with a valid block id
@@ -169,7 +172,7 @@ struct Item {
   float sl2, vmul;         // score factor (log2 units) and output factor (fp8 scales folded in)
 };
 
-template <bool kRowMap>
+template <bool kRowMap, int TT>
 __device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, uint32_t f, uint32_t per_item) {
   Item it;
   it.b = uniform(d[0]);
@@ -183,7 +186,7 @@ __device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, ui
   it.nh = min(4, prm.G - it.hg * 4);
   it.tok0 = it.part * kPartTokens;
   it.tok_end = min(it.L, it.tok0 + kPartTokens);
-  it.ntiles = (it.tok_end - it.tok0 + kTile - 1) / kTile;
+  it.ntiles = (it.tok_end - it.tok0 + TT - 1) / TT;
   int last;
   if (prm.p_shift >= 0) {
     it.blk0 = it.tok0 >> prm.p_shift;
@@ -275,9 +278,19 @@ __device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams
       lb = tile0 / prm.P;
       off = tile0 - lb * prm.P;
     }
-    const int blk = __builtin_amdgcn_readlane(ids[0], lb - it.blk0);
+    int blk = __builtin_amdgcn_readlane(ids[0], lb - it.blk0);
+    int loff = off + q * Gm::TPL;  // block offset of this lane's first token
+    if constexpr (Gm::TT > 16) {
+      // P is a multiple of 16 and a tile spans 32 tokens: the lane's tokens lie
+      // in block lb or lb + 1 (at most 256 / P + 1 <= 17 ids of the item)
+      const int blk1 = __builtin_amdgcn_readlane(ids[0], min(lb + 1 - it.blk0, 63));
+      if (loff >= prm.P) {
+        blk = blk1;
+        loff -= prm.P;
+      }
+    }
     const bool bok = blk >= 0 && blk < prm.N;
-    const O base = bok ? ((O)blk * (O)prm.P + (O)(off + q * Gm::TPL)) * (O)pv.row_bytes : (O)0;
+    const O base = bok ? ((O)blk * (O)prm.P + (O)loff) * (O)pv.row_bytes : (O)0;
 #pragma unroll
     for (int j = 0; j < Gm::TPL; ++j) {
       const bool ok = bok && first + j < it.tok_end;
@@ -310,7 +323,8 @@ __device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams
 }
 
 // Registers -> this wave's LDS region: K row-major; V transposed (bf16, d-major
-// so a P.V operand is one 8-byte read) or row-major (fp32).
+// so a P.V operand is one 8-byte read) or row-major (fp32, and fp8 codes,
+// whose P.V operand comes from the byte-transposing LDS read).
 template <typename T, int D>
 __device__ __forceinline__ void stage_tile(char* lds, TileRegs<T, D>& r_in, bool full) {
   using Gm = Geo<T, D>;
@@ -325,19 +339,7 @@ __device__ __forceinline__ void stage_tile(char* lds, TileRegs<T, D>& r_in, bool
         r_in.v[j] = LT{};
       }
   }
-  struct {
-    u32x4_t k[Gm::TPL], v[Gm::TPL];
-  } r;
-#pragma unroll
-  for (int j = 0; j < Gm::TPL; ++j) {
-    if constexpr (Gm::kFp8) {
-      r.k[j] = e4m3x8_to_f16(r_in.k[j]);
-      r.v[j] = e4m3x8_to_f16(r_in.v[j]);
-    } else {
-      r.k[j] = r_in.k[j];
-      r.v[j] = r_in.v[j];
-    }
-  }
+  TileRegs<T, D>& r = r_in;
 #pragma unroll
   for (int j = 0; j < Gm::TPL; ++j)
     *reinterpret_cast<u32x4_t*>(lds + (q * Gm::TPL + j) * Gm::KST + 16 * c) = r.k[j];
@@ -671,12 +673,12 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
   uint32_t f = wave;
   Item it;
   if (rounds > 0) {
-    it = make_item<kRowMap>(prm, lane_desc(sdesc, 0), f, per_item);
+    it = make_item<kRowMap, Gm::TT>(prm, lane_desc(sdesc, 0), f, per_item);
   } else {
     r = rounds;
     f = claim(prm, tag, nq, home, queue, first_dyn, total);
     if (f >= total) return;
-    it = make_item<kRowMap>(prm, item_desc(prm, pl, n_full, f / per_item), f, per_item);
+    it = make_item<kRowMap, Gm::TT>(prm, item_desc(prm, pl, n_full, f / per_item), f, per_item);
   }
   int ids[NR];
   load_ids<NR>(prm, it, ids);
@@ -700,12 +702,12 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
   for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int t = 0;;) {
-    const int tile0 = it.tok0 + t * kTile;
+    const int tile0 = it.tok0 + t * Gm::TT;
     const bool last = t + 1 == it.ntiles;
     // every token of the tile valid: no zeroing needed (the usual case)
     bool full;
-    if constexpr (kAligned)
-      full = tile0 + kTile <= it.tok_end && __builtin_amdgcn_readfirstlane((int)regs.ok) == (1 << Gm::TPL) - 1;
+    if constexpr (kAligned && Gm::TT == 16)
+      full = tile0 + Gm::TT <= it.tok_end && __builtin_amdgcn_readfirstlane((int)regs.ok) == (1 << Gm::TPL) - 1;
     else
       full = __builtin_amdgcn_readfirstlane((int)(__ballot(regs.ok != (1u << Gm::TPL) - 1u) == 0));
     wave_lds_sync();  // previous tile's LDS reads are done
@@ -722,13 +724,13 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
     if (t == 0) {
       if (stat_next) {
         fn = f + nwaves;
-        nx = make_item<kRowMap>(prm, lane_desc(sdesc, (int)r + 1), fn, per_item);
+        nx = make_item<kRowMap, Gm::TT>(prm, lane_desc(sdesc, (int)r + 1), fn, per_item);
         has_next = true;
         load_ids<NR>(prm, nx, idn);
       } else if (!early) {
         fn = claim(prm, tag, nq, home, queue, first_dyn, total);
         if (fn < total) {
-          nx = make_item<kRowMap>(prm, item_desc(prm, pl, n_full, fn / per_item), fn, per_item);
+          nx = make_item<kRowMap, Gm::TT>(prm, item_desc(prm, pl, n_full, fn / per_item), fn, per_item);
           has_next = true;
           load_ids<NR>(prm, nx, idn);
         }
@@ -739,7 +741,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
       pend = 2;
     }
     if (pend == 2 && t == 2) {
-      nx = make_item<kRowMap>(prm, dn, fn, per_item);
+      nx = make_item<kRowMap, Gm::TT>(prm, dn, fn, per_item);
       has_next = true;
       load_ids<NR>(prm, nx, idn);
       pend = 0;
@@ -753,27 +755,33 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
       for (int i = 0; i < NR; ++i) ids[i] = idn[i];
     }
     if (!last || has_next)
-      load_tile<T, D, kWide, kAligned, NR>(pv, prm, last ? nx : it, ids, last ? nx.tok0 : tile0 + kTile, regs);
+      load_tile<T, D, kWide, kAligned, NR>(pv, prm, last ? nx : it, ids, last ? nx.tok0 : tile0 + Gm::TT, regs);
     if (t == 0 && early && !stat_next) {
       fn = claim(prm, tag, nq, home, queue, first_dyn, total);
       if (fn < total) pend = 1;
     }
 
-    // ---- S^T = K Q^T ----
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (Gm::kFp8) {
+    // ---- S^T = K Q^T, per 16-token half of the tile ----
+    constexpr int NH = Gm::TT / 16;
+    f32x4_t s[NH];
 #pragma unroll
-      for (int i = 0; i < Gm::NQ; ++i) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
-                                                   __builtin_bit_cast(f16x8_t, qv[i]), s, 0, 0, 0);
-      }
+    for (int h = 0; h < NH; ++h) s[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (Gm::kFp8) {
+      // K operand: 8 codes of token 16 h + n, widened to fp16 as they are read
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int i = 0; i < Gm::NQ; ++i) {
+          const u32x2_t c = *reinterpret_cast<const u32x2_t*>(lds + (16 * h + n) * Gm::KST + 32 * i + 8 * g);
+          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, e4m3x8_to_f16(c)),
+                                                        __builtin_bit_cast(f16x8_t, qv[i]), s[h], 0, 0, 0);
+        }
     } else if constexpr (Gm::kBf16) {
 #pragma unroll
       for (int i = 0; i < Gm::NQ; ++i) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                    __builtin_bit_cast(bf16x8_t, qv[i]), s, 0, 0, 0);
+        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, qv[i]), s[0], 0, 0, 0);
       }
     } else {
 #pragma unroll
@@ -781,19 +789,22 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 4 * (g * (D / 4) + 4 * i));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(qv[i][j]), s, 0, 0, 0);
+          s[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(qv[i][j]), s[0], 0, 0,
+                                                      0);
       }
     }
     if (last && has_next) load_q<T, D>(prm, nx, qv);  // this item's query is no longer needed
 
-    // ---- online softmax for head n over tokens tile0 + 4g + j ----
-    float sc[4];
+    // ---- online softmax for head n over tokens tile0 + 16h + 4g + j ----
+    float sc[NH][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[j] = (tile0 + 4 * g + j < it.tok_end) ? s[j] * it.sl2 : -INFINITY;
-      mx = fmaxf(mx, sc[j]);
-    }
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sc[h][j] = (tile0 + 16 * h + 4 * g + j < it.tok_end) ? s[h][j] * it.sl2 : -INFINITY;
+        mx = fmaxf(mx, sc[h][j]);
+      }
     mx = max_over_rows(mx);
     // move the reference max only when a score exceeds it by the slack
     // (always on the first tile, m = -inf); uniform branch, rarely taken
@@ -805,21 +816,30 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
-    float p[4];
+    float pp[NH][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = fast_exp2(sc[j] - m);
-      l += p[j];
-    }
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pp[h][j] = fast_exp2(sc[h][j] - m);
+        l += pp[h][j];
+      }
+    const float* p = pp[0];
     // ---- O^T += V^T P^T ----
     const char* vl = lds + Gm::KBYTES;
     if constexpr (Gm::kFp8) {
-      const u32x2_t pb = {pack_f16(p[0], p[1]), pack_f16(p[2], p[3])};
+      // B operand: the lane's probabilities, k-slots 0-3 = tokens 4g + j and
+      // 4-7 = tokens 16 + 4g + j.  A operand (V^T) in the same token order
+      // from the byte-transposing read: lane n of each 16-lane group addresses
+      // V row 4g + n/2 (n < 8) or 12 + 4g + n/2 (n >= 8), bytes 16db + 8 (n % 2)
+      const u32x4_t pb = {pack_f16(pp[0][0], pp[0][1]), pack_f16(pp[0][2], pp[0][3]), pack_f16(pp[1][0], pp[1][1]),
+                          pack_f16(pp[1][2], pp[1][3])};
+      const char* vrow = vl + ((n < 8 ? 4 * g : 12 + 4 * g) + (n >> 1)) * Gm::KST + 8 * (n & 1);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vl + (16 * db + n) * Gm::VTS + 8 * g);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
-                                                      __builtin_bit_cast(f16x4_t, pb), o[db], 0, 0, 0);
+        const u32x2_t c = lds_read_tr8(vrow + 16 * db);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, e4m3x8_to_f16(c)),
+                                                       __builtin_bit_cast(f16x8_t, pb), o[db], 0, 0, 0);
       }
     } else if constexpr (Gm::kBf16) {
       const u32x2_t pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
@@ -852,7 +872,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
         QT* dst = static_cast<QT*>(prm.out) + ((int64_t)it.row * prm.Hq + h) * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          if constexpr (Gm::kBf16) {
+          if constexpr (Gm::kHalf) {
             *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
                 u32x2_t{pack_bf16(o[db][0] * inv, o[db][1] * inv), pack_bf16(o[db][2] * inv, o[db][3] * inv)};
           } else {
@@ -862,7 +882,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
       } else {
         const int64_t slot = ((int64_t)it.b * prm.Hq + h) * prm.max_parts + it.part;
         float rs = 1.0f;  // the stored row is o / l / rs (bf16) or o (fp32)
-        if constexpr (Gm::kBf16) {
+        if constexpr (Gm::kHalf) {
           // bf16 requests: the partial output normalised by its sum, as fp16
           // (half the bytes of fp32; its rounding is far below bf16's).  A
           // normalised row is a weighted mean of value rows, so it can exceed
