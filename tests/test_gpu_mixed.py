@@ -165,6 +165,26 @@ def test_mixed_workload_full_size(P):
     assert_close(got, oracle(c, rows=rows), "bf16", f"mixed workload P={P}", rows=rows)
 
 
+def test_mixed_large_batch():
+    """1000 requests (the in-LDS plans handle up to 1024): mostly decodes of
+    1 .. 600 tokens, every tenth a chunk of 2 .. 100 tokens over its prefix."""
+    rng = np.random.default_rng(96)
+    B = 1000
+    lens = rng.integers(1, 600, size=B)
+    qlens = np.ones(B, dtype=np.int64)
+    pf = np.arange(0, B, 10)
+    qlens[pf] = rng.integers(2, 100, size=len(pf))
+    lens = np.maximum(lens, qlens)
+    c = case(Hq=8, Hkv=2, D=64, lens=tuple(int(x) for x in lens), qlens=tuple(int(x) for x in qlens), seed=96)
+    d = DevCase(c)
+    got = mixed(d)
+    assert np.array_equal(to_host_bits(got), to_host_bits(separate(d)))
+    cu = c.cu_seqlens
+    rows = sorted(set([0, 1, int(cu[-1]) - 1] + [int(cu[b]) for b in (5, 10, 500, 990, 999)]
+                      + [int(cu[b + 1]) - 1 for b in (10, 990)]))
+    assert_close(got, oracle(c, rows=rows), "bf16", "B=1000", rows=rows)
+
+
 def test_mixed_fp8_pools():
     for G, Hkv, D, P in ((4, 8, 128, 16), (2, 2, 64, 7)):
         c = case(P=P, Hq=G * Hkv, Hkv=Hkv, D=D, lens=LENS, qlens=QLENS, seed=93 + D + P)

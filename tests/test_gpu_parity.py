@@ -510,8 +510,11 @@ def test_reshape_and_cache_fp8_bit_exact(src):
 
 
 @pytest.mark.parametrize("G,Hkv,D,P", [(4, 8, 128, 16), (1, 4, 64, 16), (8, 2, 128, 7), (3, 2, 64, 1),
-                                       (16, 1, 128, 64)])
+                                       (16, 1, 128, 64), (4, 2, 128, 48), (2, 2, 64, 32)])
 def test_decode_fp8_matches_oracle(G, Hkv, D, P):
+    # fp8 tiles hold 32 tokens: P = 16 splits each tile over two blocks, P = 48
+    # puts tiles at block offsets 0, 32 and 16 (some straddling), P = 32 and 64
+    # hold whole tiles
     c = small(P=P, Hq=G * Hkv, Hkv=Hkv, D=D, lens=(1, 16, 255, 256, 257, 700, 1500), seed=60 + G * D + P)
     f = Fp8Case(c, fp8_scales(Hkv, 61), fp8_scales(Hkv, 62))
     # the pools hold exactly the oracle's codes
