@@ -401,16 +401,27 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, PrefillLds<
   store_tile<D, kF8>(lds, 0, ra);
   if (nkt > 2) load_tile<D, kWide, kF8>(p, lds, hkv, 2 * kTK, kmax, ra);
   __syncthreads();
+  // waves 4-7 stage the next tile before their products, waves 0-3 after, so
+  // the two waves of a SIMD are out of phase
+  const bool early = w >= 4;
   for (int kt = 0; kt < nkt; kt += 2) {
+    if (early && kt + 1 < nkt) {
+      store_tile<D, kF8>(lds, 1, rb);
+      if (kt + 3 < nkt) load_tile<D, kWide, kF8>(p, lds, hkv, (kt + 3) * kTK, kmax, rb);
+    }
     attend<D, kF8>(lds, 0, kt * kTK, sl2, wave_max, st);
-    if (kt + 1 < nkt) {
+    if (!early && kt + 1 < nkt) {
       store_tile<D, kF8>(lds, 1, rb);
       if (kt + 3 < nkt) load_tile<D, kWide, kF8>(p, lds, hkv, (kt + 3) * kTK, kmax, rb);
     }
     __syncthreads();
     if (kt + 1 >= nkt) break;
+    if (early && kt + 2 < nkt) {
+      store_tile<D, kF8>(lds, 0, ra);
+      if (kt + 4 < nkt) load_tile<D, kWide, kF8>(p, lds, hkv, (kt + 4) * kTK, kmax, ra);
+    }
     attend<D, kF8>(lds, 1, (kt + 1) * kTK, sl2, wave_max, st);
-    if (kt + 2 < nkt) {
+    if (!early && kt + 2 < nkt) {
       store_tile<D, kF8>(lds, 0, ra);
       if (kt + 4 < nkt) load_tile<D, kWide, kF8>(p, lds, hkv, (kt + 4) * kTK, kmax, ra);
     }
