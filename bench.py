@@ -144,6 +144,62 @@ def cpu_baseline_decode(case, budget_s):
     }
 
 
+def cpu_baseline_mixed(case, budget_s, npf=16):
+    """The oracle (fp64 numpy ``ref_prefill``) on a sample of the mixed step: two
+    of its prefill chunks and six of its decodes, rebuilt with values (untimed),
+    then timed on random rows until the budget is spent.  The whole step's time
+    is extrapolated from the sampled rows' share of the step's (row, visible
+    key) pairs, which the oracle's work is proportional to."""
+    from oracle import ref_prefill, ref_reshape_and_cache, ref_slot_mapping
+    from workloads import make_case, nan_pool
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    pick = np.concatenate([rng.permutation(npf)[:2], npf + rng.permutation(case.B - npf)[:6]])
+    sub = make_case(name="cpu_sample", dtype=case.dtype, block_size=case.block_size,
+                    num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                    context_lens=case.context_lens[pick], query_lens=case.query_lens[pick], seed=0)
+    kc = nan_pool(sub.num_blocks, sub.block_size, sub.num_kv_heads, sub.head_dim, sub.dtype)
+    vc = kc.copy()
+    kp, vp, cu_pre, lens_pre = sub.prefix()
+    if len(kp):
+        kc, vc = ref_reshape_and_cache(kp, vp, ref_slot_mapping(sub.block_table, cu_pre, lens_pre, sub.block_size),
+                                       kc, vc)
+    kn, vn = sub.new_kv()
+    kc, vc = ref_reshape_and_cache(kn, vn, ref_slot_mapping(sub.block_table, sub.cu_seqlens, sub.context_lens,
+                                                            sub.block_size), kc, vc)
+
+    def visible(cu, lens):  # visible keys of every packed row
+        T = np.diff(cu)
+        return np.concatenate([lens[b] - T[b] + 1 + np.arange(T[b]) for b in range(len(T))])
+
+    vis_sub = visible(sub.cu_seqlens, sub.context_lens.astype(np.int64))
+    vis_full = visible(case.cu_seqlens, case.context_lens.astype(np.int64))
+    decode_rows = sub.cu_seqlens[2:8].tolist()
+    keys_done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        rows = sorted(set(rng.integers(0, int(sub.cu_seqlens[2]), 32).tolist() + decode_rows))
+        ref_prefill(sub.q, kc, vc, sub.cu_seqlens, sub.block_table, sub.context_lens, sub.scale, rows=rows)
+        keys_done += int(vis_sub[rows].sum())
+    dt = time.perf_counter() - t0
+    est_ms = dt / keys_done * float(vis_full.sum()) * 1e3
+    return {
+        "value": round(est_ms, 1),
+        "unit": "ms/step",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"2 of the 16 prefill chunks and 6 of the 48 decodes, random rows for {dt:.1f} s "
+                  f"({keys_done} (row, key) pairs of the step's {int(vis_full.sum())}), extrapolated to the "
+                  f"whole step; host has {os.cpu_count()} logical CPUs",
+    }
+
+
 def bench_decode(args):
     import paged_kv_cache_48_amd as pa
     from workloads import config_case
@@ -640,7 +696,11 @@ def main():
         res = bench_cow(args)
     elif args.workload.startswith("mixed"):
         res, case = bench_mixed(args)
-        res["cpu_baseline"] = None
+        if args.no_cpu_baseline or args.workload != "mixed_single":
+            res["cpu_baseline"] = None
+        else:
+            log("timing the oracle on the host")
+            res["cpu_baseline"] = cpu_baseline_mixed(case, args.cpu_seconds)
     else:
         res, case = bench_decode(args)
         if args.no_cpu_baseline or args.workload != "llama3_8b":
