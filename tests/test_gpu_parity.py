@@ -529,6 +529,20 @@ def test_decode_fp8_matches_oracle(G, Hkv, D, P):
     assert_close(f.decode(), f.reference(), "bf16", f"fp8 G={G} D={D} P={P}")
 
 
+def test_decode_fp8_llama3_8b_full_size_sampled():
+    """The full Llama-3-8B-shaped batch with fp8 pools (quantised through the
+    HIP scatter), in the launch configuration the fp8 benchmark times; the
+    oracle checks 12 requests on the dequantised pools."""
+    c = config_case(3)
+    f = Fp8Case(c, fp8_scales(8, 97), fp8_scales(8, 98))
+    out = f.decode()
+    order = np.argsort(c.context_lens)
+    rng = np.random.default_rng(124)
+    pick = sorted(set([int(order[0]), int(order[1]), int(order[-1]), int(order[-2])]
+                      + rng.choice(c.B, 8, replace=False).tolist()))
+    assert_close(out, f.reference(select=pick), "bf16", "fp8 llama3_8b", rows=pick)
+
+
 def test_decode_fp8_long_contexts_and_batch_invariance_bitwise():
     c = small(P=16, Hq=32, Hkv=8, D=128, lens=(8192, 3000, 17, 4097, 256), seed=63)
     f = Fp8Case(c, fp8_scales(8, 64), fp8_scales(8, 65))
