@@ -49,19 +49,17 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 __device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-// Eight E4M3 codes -> eight fp16 values equal to code * 2^-8, exactly: the
-// sign goes to bit 15 and the 7 exponent-and-mantissa bits to bits 7..13, so
-// the e4m3 exponent (bias 7) reads as an fp16 exponent (bias 15) 8 lower, and
-// e4m3 subnormals land on fp16 subnormals.  (The NaN code reads as 480.)
+// Eight OCP E4M3 codes -> the eight fp16 values they encode, exactly (every
+// E4M3 value, subnormals included, is an fp16 value; the NaN codes give NaN),
+// with gfx950's conversion instruction, two codes per instruction.  The
+// result words are taken whole: reading single halves of the builtin's
+// vector result has been compiled into a copy of the low half.
 __device__ __forceinline__ u32x4_t e4m3x8_to_f16(u32x2_t w) {
   u32x4_t r;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    // bytes b0 b1 b2 b3 -> [0, b0, 0, b1] and [0, b2, 0, b3]
-    const uint32_t x01 = __builtin_amdgcn_perm(w[i], w[i], 0x010C000Cu);
-    const uint32_t x23 = __builtin_amdgcn_perm(w[i], w[i], 0x030C020Cu);
-    r[2 * i] = (x01 & 0x80008000u) | ((x01 >> 1) & 0x3F803F80u);
-    r[2 * i + 1] = (x23 & 0x80008000u) | ((x23 >> 1) & 0x3F803F80u);
+    r[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
+    r[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
   }
   return r;
 }

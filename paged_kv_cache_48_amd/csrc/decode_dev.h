@@ -94,7 +94,7 @@ struct QType<fp8_e4m3> {
 template <typename T, int D>
 struct Geo {
   // fp8 pools: tiles of 32 tokens (the bytes of a 16-token bf16 tile), staged
-  // as the codes themselves and widened to fp16 (code * 2^-8) when an MFMA
+  // as the codes themselves and widened to the fp16 values they encode when an MFMA
   // operand is read
   static constexpr bool kFp8 = std::is_same<T, fp8_e4m3>::value;
   static constexpr bool kBf16 = std::is_same<T, bf16_bits>::value;
@@ -196,9 +196,9 @@ __device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, ui
     last = (it.tok_end - 1) / prm.P;
   }
   it.nblk = last - it.blk0 + 1;
-  // fp8 pools hold code * scale; the staged fp16 values are code * 2^-8
-  it.sl2 = prm.k_scale ? prm.scale_log2 * 256.0f * prm.k_scale[it.hkv] : prm.scale_log2;
-  it.vmul = prm.v_scale ? 256.0f * prm.v_scale[it.hkv] : 1.0f;
+  // fp8 pools hold value(code) * scale; the operands are value(code) in fp16
+  it.sl2 = prm.k_scale ? prm.scale_log2 * prm.k_scale[it.hkv] : prm.scale_log2;
+  it.vmul = prm.v_scale ? prm.v_scale[it.hkv] : 1.0f;
   return it;
 }
 

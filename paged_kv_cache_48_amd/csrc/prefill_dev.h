@@ -135,7 +135,7 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const bf16_bits* p) {
 // elements 8 (e % (D/8)) .. + 7.  ok: bit x set when the key of load x is
 // visible and its block id valid.
 // fp8 pools: the same pieces as 8-byte loads of E4M3 codes, widened to fp16
-// (code * 2^-8) when stored.
+// (the values the codes encode) when stored.
 template <bool kF8>
 struct TileSet {
   typedef typename std::conditional<kF8, u32x2_t, u32x4_t>::type LT;
@@ -390,9 +390,9 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, PrefillLds<
   wave_max = uniform(wave_max);
   __syncthreads();  // block ids visible
 
-  // fp8 pools: codes * scale, staged as code * 2^-8
-  const float sl2 = kF8 ? p.scale_log2 * 256.0f * p.k_scale[hkv] : p.scale_log2;
-  const float vmul = kF8 ? 256.0f * p.v_scale[hkv] : 1.0f;
+  // fp8 pools: value(code) * scale, staged as value(code)
+  const float sl2 = kF8 ? p.scale_log2 * p.k_scale[hkv] : p.scale_log2;
+  const float vmul = kF8 ? p.v_scale[hkv] : 1.0f;
 
   // pipeline: tile j travels in register set j & 1 and LDS buffer j & 1
   TileSet<kF8> ra, rb;
