@@ -109,7 +109,8 @@ int pa_reshape_and_cache(const void* k, const void* v, const int32_t* slot_mappi
  * stored as encode(x / scale[h]) -- the quotient correctly rounded to fp32,
  * then rounded to the nearest code with ties to even, magnitudes above 448
  * saturated to +-448 and NaN stored as 0x7F -- and read as decode(code) *
- * scale[h].  Attention over an fp8 pool is attention over those values.
+ * scale[h] (a NaN code reads as NaN).  Attention over an fp8 pool is
+ * attention over those values.
  *
  * pa_reshape_and_cache_fp8 -- pa_reshape_and_cache into fp8 pools.
  *   k, v               [num_tokens, num_kv_heads, head_dim], dtype (F32 or BF16)

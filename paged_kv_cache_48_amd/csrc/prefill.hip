@@ -24,7 +24,9 @@
 //     read; the V^T operand of the P.V product comes from gfx950's
 //     transposing LDS read (ds_read_b64_tr_b16).  Two register sets and two
 //     LDS buffers keep the loads of the next two tiles in flight while one
-//     tile computes; one barrier per tile.
+//     tile computes; one barrier per tile.  Waves 4-7 stage the next tile
+//     before their products and waves 0-3 after them, so the two waves that
+//     share a SIMD overlap staging with matrix work.
 //   * Each wave owns 32 rows.  S^T = K Q^T and O^T += V^T P^T run as
 //     16x16x32 bf16 MFMAs with fp32 accumulation.  Computing the transposed
 //     scores leaves each lane holding one query row's scores for a run of keys,
