@@ -75,6 +75,16 @@ def test_mixed_matches_oracle_and_separate_calls(G, Hkv, D, P):
     assert np.array_equal(to_host_bits(got), to_host_bits(separate(d))), "mixed differs from the separate calls"
 
 
+def test_mixed_largest_group():
+    """A GQA group of 64: decode items take the heads in 16 groups of 4, prefill
+    items are 4 tokens x 64 heads."""
+    c = case(Hq=64, Hkv=1, D=64, lens=(300, 1, 700, 257), qlens=(37, 1, 1, 2), seed=97)
+    d = DevCase(c)
+    got = mixed(d)
+    assert_close(got, oracle(c), "bf16", "G=64")
+    assert np.array_equal(to_host_bits(got), to_host_bits(separate(d)))
+
+
 def test_mixed_all_decode_and_all_prefill_batches():
     lens = (1, 256, 257, 900, 4000, 33)
     for qlens, what in (((1,) * 6, "all decode"), ((1, 200, 2, 900, 64, 33), "all prefill but one"),

@@ -397,6 +397,24 @@ def test_prefill_matches_oracle(G, Hkv, D, P):
     assert_close(d.prefill(), ref, "bf16", f"prefill G={G} D={D} P={P}")
 
 
+def test_prefill_largest_group_and_longest_table():
+    """The limits of the prefill call: a GQA group of 64 (an item is 4 tokens
+    x 64 heads) and a request whose block table has the largest supported
+    length (16384 entries at P = 1, all staged on chip)."""
+    c = small(P=16, Hq=64, Hkv=1, D=64, lens=(300, 1), qlens=(37, 1), seed=42)
+    d = DevCase(c)
+    kc, vc = oracle_pool(c)
+    ref = ref_prefill(c.q, kc, vc, c.cu_seqlens, c.block_table, c.context_lens, c.scale)
+    assert_close(d.prefill(), ref, "bf16", "G=64")
+    c = small(P=1, Hq=4, Hkv=1, D=64, lens=(16384,), qlens=(40,), seed=43)
+    assert c.max_blocks_per_seq == 16384
+    d = DevCase(c)
+    rows = [0, 17, 39]
+    kc, vc = oracle_pool(c)
+    ref = ref_prefill(c.q, kc, vc, c.cu_seqlens, c.block_table, c.context_lens, c.scale, rows=rows)
+    assert_close(d.prefill(), ref, "bf16", "16384 blocks", rows=rows)
+
+
 def test_prefill_single_token_matches_decode():
     c = small(P=16, lens=(77, 400, 1), seed=40)
     d = DevCase(c)
