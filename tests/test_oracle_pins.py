@@ -296,6 +296,24 @@ def test_prefill_single_new_token_equals_decode_bitwise():
     assert np.array_equal(dec, pre)
 
 
+def test_mixed_batch_equals_its_parts_bitwise():
+    """A ragged batch of one-token chunks (decodes) and longer chunks (the
+    single-launch mixed call's reading of a step): each request's rows are
+    those of its chunk computed alone, and the one-token rows are decode."""
+    case = tiny_case(lens=(8, 19, 1, 30, 6), qlens=(1, 7, 1, 30, 2), seed=36)
+    kc, vc = populate(case)
+    cu = case.cu_seqlens
+    mixed = ref_prefill(case.q, kc, vc, cu, case.block_table, case.context_lens, case.scale)
+    for b in range(case.B):
+        s, e = int(cu[b]), int(cu[b + 1])
+        alone = ref_prefill(case.q[s:e], kc, vc, [0, e - s], case.block_table[b:b + 1], case.context_lens[b:b + 1],
+                            case.scale)
+        assert np.array_equal(mixed[s:e], alone), b
+        if e - s == 1:
+            dec = ref_decode(case.q[s:e], kc, vc, case.block_table[b:b + 1], case.context_lens[b:b + 1], case.scale)
+            assert np.array_equal(mixed[s:e], dec), b
+
+
 def test_chunked_prefill_equals_one_shot_bitwise():
     one = tiny_case(G=2, H_kv=2, P=3, lens=(23,), qlens=(23,), seed=33)
     ref = prefill_oracle(one)
