@@ -17,13 +17,15 @@
 //     grid of exactly the resident waves takes one item each to start, then
 //     pulls items with one atomic each from per-XCD queues, stealing from the
 //     other queues at the end.
-//   * Coalesced gathers.  Per 16-token tile each quarter-wave reads whole
-//     contiguous row slices of one KV head (16-byte loads); the tile goes
-//     through a wave-private LDS region, K row-major and V transposed, which
-//     turns it into MFMA operands.  The next tile's loads are in flight while
-//     the current one computes.
+//   * Coalesced gathers.  Per tile (16 tokens; 32 for fp8 pools) groups of
+//     lanes read whole contiguous row slices of one KV head (16-byte loads);
+//     the tile goes through a wave-private LDS region, K row-major and V
+//     transposed (bf16) or row-major (fp32, and fp8 codes, read back with
+//     the byte-transposing LDS read), which turns it into MFMA operands.  The
+//     next tile's loads are in flight while the current one computes.
 //   * S^T = K Q^T and O^T += V^T P^T run on MFMA (bf16: 16x16x32 and
-//     16x16x16; fp32: 16x16x4) with fp32 accumulation.  The group's query
+//     16x16x16; fp8 via fp16: 16x16x32; fp32: 16x16x4) with fp32
+//     accumulation.  The group's query
 //     heads are the B-operand columns, so each lane holds one head's scores
 //     for four tokens, which is exactly the B operand of the P.V product: the
 //     probabilities never leave registers and the outputs need no cross-lane

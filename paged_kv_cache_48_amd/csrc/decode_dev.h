@@ -18,7 +18,7 @@
 namespace pa {
 namespace dec {
 
-constexpr int kTile = 16;                        // tokens per MFMA tile
+constexpr int kTile = 16;  // tokens per tile (bf16, fp32); the plan counts tails in these units
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kMaxStaticRounds = 64;  // static items per wave: one descriptor per lane
@@ -86,10 +86,10 @@ struct QType<fp8_e4m3> {
 };
 
 // ---------------------------------------------------------------------------
-// Tile geometry.  A tile is 16 consecutive tokens of one KV head.  Lane l
-// loads 16-byte piece l % CPR of the head's row slice for tokens
-// (l / CPR) * TPL + j, j < TPL, so each quarter-wave reads whole contiguous
-// row slices (at most two 128-byte lines per 16 lanes).
+// Tile geometry.  A tile is TT consecutive tokens of one KV head (16; 32 for
+// fp8 pools).  Lane l loads 16-byte piece l % CPR of the head's row slice for
+// tokens (l / CPR) * TPL + j, j < TPL, so groups of CPR lanes read whole
+// contiguous row slices.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct Geo {
@@ -626,10 +626,10 @@ __device__ __forceinline__ i32x4_t item_desc(const DecodeParams& prm, const Plan
 // first tile and its query after the predecessor's last S^T product, so
 // items follow one another without draining the loads in flight.
 //
-// Per 16-token tile:
+// Per 16 tokens of a tile (two such halves for fp8):
 //   S^T = K Q^T   (A = K rows from LDS, B = Q^T with the group's heads as
 //                  columns 0..3), so lane (n, g) gets the scores of head n for
-//                  tokens 4g .. 4g+3;
+//                  tokens 4g .. 4g+3 of the half;
 //   online softmax per head (max over the lane's 4 tokens, then across the
 //                  four 16-lane rows);
 //   O^T += V^T P^T (A = V^T from LDS, B = the lane's own probabilities), so
