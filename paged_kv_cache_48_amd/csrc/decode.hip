@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
 // Partition kernel: every wave computes a stream of work items (see
 // decode_stream for the schedule and the per-tile steps).
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool kWide, bool kAligned, int NR>
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP>
 __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm) {
   using Gm = Geo<T, D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -131,11 +131,11 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
   const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
   // (threadIdx.x >> 6 is the same in every lane; readfirstlane tells the compiler)
   const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (uint32_t)uniform((int)(threadIdx.x >> 6));
-  decode_stream<T, D, kWide, kAligned, NR, false>(prm, lds, pl, tag, n_items, n_full, nq_plan, wave, nwaves,
-                                                  (uint32_t)kMaxStaticRounds);
+  decode_stream<T, D, kWide, kAligned, NR, false, HP>(prm, lds, pl, tag, n_items, n_full, nq_plan, wave, nwaves,
+                                                      (uint32_t)kMaxStaticRounds);
 }
 
-template <typename T, int D, bool kWide, bool kAligned, int NR>
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP>
 hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipStream_t stream,
                         hipEvent_t ev0, hipEvent_t ev1) {
   // waves are independent workers; a block holds as many as fit in 64 KiB of LDS (at most 4)
@@ -147,7 +147,7 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partition_kernel<T, D, kWide, kAligned, NR>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partition_kernel<T, D, kWide, kAligned, NR, HP>,
                                                      64 * wpb, lds_bytes) != hipSuccess || nb < 1)
       nb = 1;
     per_cu = nb;
@@ -159,32 +159,33 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
     const hipError_t e = hipEventRecord(ev0, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, kWide, kAligned, NR>), dim3(blocks), dim3(64 * wpb), lds_bytes,
-                     stream, prm);
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, kWide, kAligned, NR, HP>), dim3(blocks), dim3(64 * wpb),
+                     lds_bytes, stream, prm);
   if (ev1) {
     const hipError_t e = hipEventRecord(ev1, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_reduce_kernel<typename QType<T>::type, D, false>), dim3((prm.Hq + 3) / 4, B), dim3(256), 0,
-                     stream, prm);
+  // partial rows are the real heads' (D / HP elements)
+  hipLaunchKernelGGL((decode_reduce_kernel<typename QType<T>::type, D / HP, false>), dim3((prm.Hq + 3) / 4, B),
+                     dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool kWide>
+template <typename T, int D, bool kWide, int HP>
 hipError_t launch_mode(const DecodeParams& prm, int B, int64_t max_items, hipStream_t stream, hipEvent_t ev0,
                        hipEvent_t ev1) {
   // tiles of 16 tokens never straddle a block when P is a multiple of 16; a
   // partition touches at most 256 / P + 1 blocks: one id register for P >= 5
-  if (prm.P % kTile == 0) return launch_typed<T, D, kWide, true, 1>(prm, B, max_items, stream, ev0, ev1);
-  if (prm.P >= 5) return launch_typed<T, D, kWide, false, 1>(prm, B, max_items, stream, ev0, ev1);
-  return launch_typed<T, D, kWide, false, 5>(prm, B, max_items, stream, ev0, ev1);
+  if (prm.P % kTile == 0) return launch_typed<T, D, kWide, true, 1, HP>(prm, B, max_items, stream, ev0, ev1);
+  if (prm.P >= 5) return launch_typed<T, D, kWide, false, 1, HP>(prm, B, max_items, stream, ev0, ev1);
+  return launch_typed<T, D, kWide, false, 5, HP>(prm, B, max_items, stream, ev0, ev1);
 }
 
-template <typename T, int D>
+template <typename T, int D, int HP = 1>
 hipError_t launch_sized(const DecodeParams& prm, int B, int64_t max_items, int64_t pool_bytes,
                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  if (pool_bytes < ((int64_t)1 << 32)) return launch_mode<T, D, false>(prm, B, max_items, stream, ev0, ev1);
-  return launch_mode<T, D, true>(prm, B, max_items, stream, ev0, ev1);
+  if (pool_bytes < ((int64_t)1 << 32)) return launch_mode<T, D, false, HP>(prm, B, max_items, stream, ev0, ev1);
+  return launch_mode<T, D, true, HP>(prm, B, max_items, stream, ev0, ev1);
 }
 
 }  // namespace
@@ -211,9 +212,14 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.o = reinterpret_cast<float*>(ws + Lw.o);
   prm.scale_log2 = a.scale * kLog2e;
   prm.Hq = a.num_q_heads;
-  prm.Hkv = a.num_kv_heads;
   prm.G = a.num_q_heads / a.num_kv_heads;
   prm.n_hg = (prm.G + 3) / 4;
+  const bool fp8 = a.kv_dtype == kFP8E4M3;
+  // bf16 pools with 64-dim heads: adjacent KV heads are read in pairs, as one
+  // 128-dim head (256 contiguous bytes per token, the width the 128-dim
+  // kernel reads); each query column keeps its own head's half
+  const bool pairs = !fp8 && a.dtype == kBF16 && a.head_dim == 64 && a.num_kv_heads % 2 == 0;
+  prm.Hkv = pairs ? a.num_kv_heads / 2 : a.num_kv_heads;
   prm.P = a.block_size;
   prm.p_shift = (a.block_size & (a.block_size - 1)) == 0 ? __builtin_ctz((unsigned)a.block_size) : -1;
   prm.N = (int)a.num_blocks;
@@ -226,7 +232,6 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.salt = next_salt();
   prm.cu = nullptr;
   prm.num_q_tokens = 0;
-  const bool fp8 = a.kv_dtype == kFP8E4M3;
   prm.k_scale = fp8 ? a.k_scale : nullptr;
   prm.v_scale = fp8 ? a.v_scale : nullptr;
 
@@ -248,6 +253,7 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   if (a.dtype == kBF16) {
     if (a.head_dim == 128)
       return launch_sized<bf16_bits, 128>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
+    if (pairs) return launch_sized<bf16_bits, 128, 2>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
     return launch_sized<bf16_bits, 64>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
   }
   if (a.head_dim == 128) return launch_sized<float, 128>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);

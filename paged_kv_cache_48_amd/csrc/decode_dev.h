@@ -214,12 +214,30 @@ __device__ __forceinline__ void load_ids(const DecodeParams& prm, const Item& it
 
 // Q^T operand: column n = query head of the group (heads past the group's
 // last read head 0's row; their columns are never stored).
-template <typename T, int D>
+// HP = 2 (bf16 pools with 64-dim heads, taken in pairs of adjacent KV heads
+// as one 128-dim head): columns 0..3 are the group's query heads of the first
+// KV head of the pair, columns 4..7 those of the second; each column's query
+// fills its own head's 64 dimensions and zeros the other's, so one S^T
+// product gives every column its own head's scores.
+template <typename T, int D, int HP>
 __device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, u32x4_t (&qv)[Geo<T, D>::NQV]) {
   using Gm = Geo<T, D>;
   typedef typename QType<T>::type QT;
   const int lane = lane_id();
   const int n = lane & 15, g = lane >> 4;
+  if constexpr (HP == 2) {
+    static_assert(Gm::kBf16 && D == 128, "head pairs: bf16, two 64-dim heads");
+    const int hi = (n >> 2) & 1, c = n & 3;
+    const bool col = n < 8 && c < it.nh;
+    const int h = (2 * it.hkv + hi) * prm.G + it.hg * 4 + (col ? c : 0);
+    const QT* qrow = static_cast<const QT*>(prm.q) + ((int64_t)it.row * prm.Hq + h) * (D / 2);
+#pragma unroll
+    for (int i = 0; i < Gm::NQV; ++i) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + 32 * (i & 1) + 8 * g);
+      qv[i] = (i >> 1) == hi ? x : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
   const int h = it.hkv * prm.G + it.hg * 4 + (n < it.nh ? n : 0);
   const QT* qrow = static_cast<const QT*>(prm.q) + ((int64_t)it.row * prm.Hq + h) * D;
 #pragma unroll
@@ -635,7 +653,7 @@ __device__ __forceinline__ i32x4_t item_desc(const DecodeParams& prm, const Plan
 //   O^T += V^T P^T (A = V^T from LDS, B = the lane's own probabilities), so
 //                  lane (n, g) accumulates head n's outputs d = 16db + 4g + j.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool kWide, bool kAligned, int NR, bool kRowMap>
+template <typename T, int D, bool kWide, bool kAligned, int NR, bool kRowMap, int HP = 1>
 __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds, const PlanLds* pl,
                                               unsigned long long tag, uint32_t n_items, uint32_t n_full,
                                               uint32_t nq_plan, uint32_t wave, uint32_t nwaves,
@@ -683,7 +701,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
   int ids[NR];
   load_ids<NR>(prm, it, ids);
   u32x4_t qv[Gm::NQV];
-  load_q<T, D>(prm, it, qv);
+  load_q<T, D, HP>(prm, it, qv);
   TileRegs<T, D> regs;
   load_tile<T, D, kWide, kAligned, NR>(pv, prm, it, ids, it.tok0, regs);
 
@@ -793,7 +811,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
                                                       0);
       }
     }
-    if (last && has_next) load_q<T, D>(prm, nx, qv);  // this item's query is no longer needed
+    if (last && has_next) load_q<T, D, HP>(prm, nx, qv);  // this item's query is no longer needed
 
     // ---- online softmax for head n over tokens tile0 + 16h + 4g + j ----
     float sc[NH][4];
@@ -864,19 +882,41 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
     }
 
     // ---- item done: total of l over the four 16-lane rows; store head n ----
+    // (HP = 2: column n's head is the pair's first or second, and its outputs
+    // are rows 0..63 or 64..127 of the 128-dim O^T)
+    constexpr int DH = D / HP, NDBH = NDB / HP;
     l = sum_over_rows(l);
-    if (n < it.nh) {
-      const int h = it.hkv * prm.G + it.hg * 4 + n;
+    f32x4_t ov[NDBH];
+    bool col;
+    int h;
+    if constexpr (HP == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) ov[db] = o[db];
+      col = n < it.nh;
+      h = it.hkv * prm.G + it.hg * 4 + n;
+    } else {
+      const bool hi = ((n >> 2) & 1) != 0;
+#pragma unroll
+      for (int db = 0; db < NDBH; ++db) {
+        // a select of values, not of the two array elements' addresses
+        // (which would put o in scratch memory to index it)
+        const f32x4_t lo = o[db], up = o[NDBH + db];
+        ov[db] = f32x4_t{hi ? up[0] : lo[0], hi ? up[1] : lo[1], hi ? up[2] : lo[2], hi ? up[3] : lo[3]};
+      }
+      col = n < 8 && (n & 3) < it.nh;
+      h = (2 * it.hkv + (hi ? 1 : 0)) * prm.G + it.hg * 4 + (n & 3);
+    }
+    if (col) {
       if (it.nparts == 1) {
         const float inv = it.vmul / l;
-        QT* dst = static_cast<QT*>(prm.out) + ((int64_t)it.row * prm.Hq + h) * D + 4 * g;
+        QT* dst = static_cast<QT*>(prm.out) + ((int64_t)it.row * prm.Hq + h) * DH + 4 * g;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDBH; ++db) {
           if constexpr (Gm::kHalf) {
             *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
-                u32x2_t{pack_bf16(o[db][0] * inv, o[db][1] * inv), pack_bf16(o[db][2] * inv, o[db][3] * inv)};
+                u32x2_t{pack_bf16(ov[db][0] * inv, ov[db][1] * inv), pack_bf16(ov[db][2] * inv, ov[db][3] * inv)};
           } else {
-            *reinterpret_cast<f32x4_t*>(dst + 16 * db) = o[db] * inv;
+            *reinterpret_cast<f32x4_t*>(dst + 16 * db) = ov[db] * inv;
           }
         }
       } else {
@@ -891,9 +931,9 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
           const float inv = it.vmul / l;
           float amax = 0.f;
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
+          for (int db = 0; db < NDBH; ++db)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(o[db][j]));
+            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(ov[db][j]));
           amax = max_over_rows(amax * inv);  // the head's whole row (lanes n, n+16, n+32, n+48)
           if (amax >= 32768.0f) {
             int ex;
@@ -901,15 +941,15 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
             rs = ldexpf(1.0f, ex - 15);
           }
           const float sc = inv / rs;
-          uint16_t* dst = reinterpret_cast<uint16_t*>(prm.o) + slot * D + 4 * g;
+          uint16_t* dst = reinterpret_cast<uint16_t*>(prm.o) + slot * DH + 4 * g;
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
+          for (int db = 0; db < NDBH; ++db)
             *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
-                u32x2_t{pack_f16(o[db][0] * sc, o[db][1] * sc), pack_f16(o[db][2] * sc, o[db][3] * sc)};
+                u32x2_t{pack_f16(ov[db][0] * sc, ov[db][1] * sc), pack_f16(ov[db][2] * sc, ov[db][3] * sc)};
         } else {
-          float* dst = prm.o + slot * D + 4 * g;
+          float* dst = prm.o + slot * DH + 4 * g;
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db) = o[db];
+          for (int db = 0; db < NDBH; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db) = ov[db];
         }
         if (g == 0) *reinterpret_cast<f32x4_t*>(prm.ml + slot * 4) = f32x4_t{m, l, rs, 0.f};
       }

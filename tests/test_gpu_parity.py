@@ -123,6 +123,22 @@ def test_decode_head_layouts(G, Hkv, D, dtype):
     assert_close(d.decode(), decode_ref(c), dtype, f"G={G} D={D} {dtype}")
 
 
+@pytest.mark.parametrize("G,Hkv,P", [(1, 2, 16), (4, 2, 16), (6, 4, 7), (8, 8, 1), (1, 16, 64), (5, 2, 3)])
+def test_decode_paired_64_dim_heads(G, Hkv, P):
+    """bf16 pools with 64-dim heads and an even number of KV heads are read two
+    adjacent heads at a time, as one 128-dim row per token; each query head
+    must still attend to its own KV head only.  Checked against the oracle, and
+    bit for bit against the mixed call, whose decode rows (one-token chunks)
+    read one KV head at a time."""
+    c = small(P=P, Hq=G * Hkv, Hkv=Hkv, D=64, lens=(1, 40, 256, 257, 700, 1500), seed=31 + G * Hkv + P)
+    d = DevCase(c)
+    got = d.decode()
+    assert_close(got, decode_ref(c), "bf16", f"paired heads G={G} Hkv={Hkv} P={P}")
+    one = torch.empty_like(d.q)
+    pa.paged_mixed_attention(d.q, d.kc, d.vc, idx(np.arange(c.B + 1)), d.bt, d.lens, c.scale, one)
+    assert np.array_equal(to_host_bits(got), to_host_bits(one)), "paired read differs from the single-head read"
+
+
 def test_decode_block_size_invariance():
     """ember "Correctness": block_size in {1,2,3,7,16,64}.  Each matches the
     oracle; the kernel tiles by token position only, so results are bitwise
