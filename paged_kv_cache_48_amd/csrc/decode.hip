@@ -215,10 +215,10 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.G = a.num_q_heads / a.num_kv_heads;
   prm.n_hg = (prm.G + 3) / 4;
   const bool fp8 = a.kv_dtype == kFP8E4M3;
-  // bf16 pools with 64-dim heads: adjacent KV heads are read in pairs, as one
-  // 128-dim head (256 contiguous bytes per token, the width the 128-dim
-  // kernel reads); each query column keeps its own head's half
-  const bool pairs = !fp8 && a.dtype == kBF16 && a.head_dim == 64 && a.num_kv_heads % 2 == 0;
+  // bf16 and fp8 pools with 64-dim heads: adjacent KV heads are read in
+  // pairs, as one 128-dim head (the row width the 128-dim kernels read);
+  // each query column keeps its own head's half
+  const bool pairs = (fp8 || a.dtype == kBF16) && a.head_dim == 64 && a.num_kv_heads % 2 == 0;
   prm.Hkv = pairs ? a.num_kv_heads / 2 : a.num_kv_heads;
   prm.P = a.block_size;
   prm.p_shift = (a.block_size & (a.block_size - 1)) == 0 ? __builtin_ctz((unsigned)a.block_size) : -1;
@@ -248,6 +248,7 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   if (fp8) {  // bf16 q and out
     if (a.head_dim == 128)
       return launch_sized<fp8_e4m3, 128>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
+    if (pairs) return launch_sized<fp8_e4m3, 128, 2>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
     return launch_sized<fp8_e4m3, 64>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
   }
   if (a.dtype == kBF16) {

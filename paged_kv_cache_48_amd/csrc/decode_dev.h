@@ -172,7 +172,7 @@ struct Item {
   float sl2, vmul;         // score factor (log2 units) and output factor (fp8 scales folded in)
 };
 
-template <bool kRowMap, int TT>
+template <bool kRowMap, int TT, int HP>
 __device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, uint32_t f, uint32_t per_item) {
   Item it;
   it.b = uniform(d[0]);
@@ -199,6 +199,13 @@ __device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, ui
   // fp8 pools hold value(code) * scale; the operands are value(code) in fp16
   it.sl2 = prm.k_scale ? prm.scale_log2 * prm.k_scale[it.hkv] : prm.scale_log2;
   it.vmul = prm.v_scale ? prm.v_scale[it.hkv] : 1.0f;
+  if constexpr (HP == 2) {
+    // head pairs: the factors are per column (column n of the lane belongs
+    // to KV head 2 hkv + (n / 4) % 2)
+    const int hs = 2 * it.hkv + ((lane_id() >> 2) & 1);
+    if (prm.k_scale) it.sl2 = prm.scale_log2 * prm.k_scale[hs];
+    if (prm.v_scale) it.vmul = prm.v_scale[hs];
+  }
   return it;
 }
 
@@ -214,11 +221,12 @@ __device__ __forceinline__ void load_ids(const DecodeParams& prm, const Item& it
 
 // Q^T operand: column n = query head of the group (heads past the group's
 // last read head 0's row; their columns are never stored).
-// HP = 2 (bf16 pools with 64-dim heads, taken in pairs of adjacent KV heads
-// as one 128-dim head): columns 0..3 are the group's query heads of the first
-// KV head of the pair, columns 4..7 those of the second; each column's query
-// fills its own head's 64 dimensions and zeros the other's, so one S^T
-// product gives every column its own head's scores.
+// HP = 2 (64-dim heads taken in pairs of adjacent KV heads, read as one
+// 128-dim head): columns 0..3 are the group's query heads of the first KV
+// head of the pair, columns 4..7 those of the second.  Each column's query
+// is its own head's 64 dimensions, in both halves of the operand: the score
+// products over dimensions 0..63 and 64..127 go to separate accumulators,
+// and each column keeps the one of its own head.
 template <typename T, int D, int HP>
 __device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, u32x4_t (&qv)[Geo<T, D>::NQV]) {
   using Gm = Geo<T, D>;
@@ -226,15 +234,21 @@ __device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, 
   const int lane = lane_id();
   const int n = lane & 15, g = lane >> 4;
   if constexpr (HP == 2) {
-    static_assert(Gm::kBf16 && D == 128, "head pairs: bf16, two 64-dim heads");
+    static_assert(Gm::kHalf && D == 128, "head pairs: bf16 or fp8 pools, two 64-dim heads");
     const int hi = (n >> 2) & 1, c = n & 3;
     const bool col = n < 8 && c < it.nh;
     const int h = (2 * it.hkv + hi) * prm.G + it.hg * 4 + (col ? c : 0);
     const QT* qrow = static_cast<const QT*>(prm.q) + ((int64_t)it.row * prm.Hq + h) * (D / 2);
 #pragma unroll
-    for (int i = 0; i < Gm::NQV; ++i) {
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + 32 * (i & 1) + 8 * g);
-      qv[i] = (i >> 1) == hi ? x : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < Gm::NQV / 2; ++i) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + 32 * i + 8 * g);
+      if constexpr (Gm::kFp8) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qv[i][w] = pack_f16(bf16_lo(x[w]), bf16_hi(x[w]));
+      } else {
+        qv[i] = x;
+      }
+      qv[i + Gm::NQV / 2] = qv[i];
     }
     return;
   }
@@ -691,12 +705,12 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
   uint32_t f = wave;
   Item it;
   if (rounds > 0) {
-    it = make_item<kRowMap, Gm::TT>(prm, lane_desc(sdesc, 0), f, per_item);
+    it = make_item<kRowMap, Gm::TT, HP>(prm, lane_desc(sdesc, 0), f, per_item);
   } else {
     r = rounds;
     f = claim(prm, tag, nq, home, queue, first_dyn, total);
     if (f >= total) return;
-    it = make_item<kRowMap, Gm::TT>(prm, item_desc(prm, pl, n_full, f / per_item), f, per_item);
+    it = make_item<kRowMap, Gm::TT, HP>(prm, item_desc(prm, pl, n_full, f / per_item), f, per_item);
   }
   int ids[NR];
   load_ids<NR>(prm, it, ids);
@@ -742,13 +756,13 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
     if (t == 0) {
       if (stat_next) {
         fn = f + nwaves;
-        nx = make_item<kRowMap, Gm::TT>(prm, lane_desc(sdesc, (int)r + 1), fn, per_item);
+        nx = make_item<kRowMap, Gm::TT, HP>(prm, lane_desc(sdesc, (int)r + 1), fn, per_item);
         has_next = true;
         load_ids<NR>(prm, nx, idn);
       } else if (!early) {
         fn = claim(prm, tag, nq, home, queue, first_dyn, total);
         if (fn < total) {
-          nx = make_item<kRowMap, Gm::TT>(prm, item_desc(prm, pl, n_full, fn / per_item), fn, per_item);
+          nx = make_item<kRowMap, Gm::TT, HP>(prm, item_desc(prm, pl, n_full, fn / per_item), fn, per_item);
           has_next = true;
           load_ids<NR>(prm, nx, idn);
         }
@@ -759,7 +773,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
       pend = 2;
     }
     if (pend == 2 && t == 2) {
-      nx = make_item<kRowMap, Gm::TT>(prm, dn, fn, per_item);
+      nx = make_item<kRowMap, Gm::TT, HP>(prm, dn, fn, per_item);
       has_next = true;
       load_ids<NR>(prm, nx, idn);
       pend = 0;
@@ -780,26 +794,49 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
     }
 
     // ---- S^T = K Q^T, per 16-token half of the tile ----
+    // (HP = 2: dimensions 0..63 accumulate in s, 64..127 in s2)
     constexpr int NH = Gm::TT / 16;
-    f32x4_t s[NH];
+    constexpr int NQ1 = Gm::NQ / HP;
+    f32x4_t s[NH], s2[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) s[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (HP == 2) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) s2[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     if constexpr (Gm::kFp8) {
       // K operand: 8 codes of token 16 h + n, widened to fp16 as they are read
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
+      for (int h = 0; h < NH; ++h) {
 #pragma unroll
-        for (int i = 0; i < Gm::NQ; ++i) {
+        for (int i = 0; i < NQ1; ++i) {
           const u32x2_t c = *reinterpret_cast<const u32x2_t*>(lds + (16 * h + n) * Gm::KST + 32 * i + 8 * g);
           s[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, e4m3x8_to_f16(c)),
                                                         __builtin_bit_cast(f16x8_t, qv[i]), s[h], 0, 0, 0);
         }
+        if constexpr (HP == 2) {
+#pragma unroll
+          for (int i = NQ1; i < Gm::NQ; ++i) {
+            const u32x2_t c = *reinterpret_cast<const u32x2_t*>(lds + (16 * h + n) * Gm::KST + 32 * i + 8 * g);
+            s2[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, e4m3x8_to_f16(c)),
+                                                           __builtin_bit_cast(f16x8_t, qv[i]), s2[h], 0, 0, 0);
+          }
+        }
+      }
     } else if constexpr (Gm::kBf16) {
 #pragma unroll
-      for (int i = 0; i < Gm::NQ; ++i) {
+      for (int i = 0; i < NQ1; ++i) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
         s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, qv[i]), s[0], 0, 0, 0);
+      }
+      if constexpr (HP == 2) {
+#pragma unroll
+        for (int i = NQ1; i < Gm::NQ; ++i) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
+          s2[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                          __builtin_bit_cast(bf16x8_t, qv[i]), s2[0], 0, 0, 0);
+        }
       }
     } else {
 #pragma unroll
@@ -812,6 +849,14 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
       }
     }
     if (last && has_next) load_q<T, D, HP>(prm, nx, qv);  // this item's query is no longer needed
+    if constexpr (HP == 2) {
+      const bool hi = ((n >> 2) & 1) != 0;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const f32x4_t lo = s[h], up = s2[h];
+        s[h] = f32x4_t{hi ? up[0] : lo[0], hi ? up[1] : lo[1], hi ? up[2] : lo[2], hi ? up[3] : lo[3]};
+      }
+    }
 
     // ---- online softmax for head n over tokens tile0 + 16h + 4g + j ----
     float sc[NH][4];

@@ -123,20 +123,47 @@ def test_decode_head_layouts(G, Hkv, D, dtype):
     assert_close(d.decode(), decode_ref(c), dtype, f"G={G} D={D} {dtype}")
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
 @pytest.mark.parametrize("G,Hkv,P", [(1, 2, 16), (4, 2, 16), (6, 4, 7), (8, 8, 1), (1, 16, 64), (5, 2, 3)])
-def test_decode_paired_64_dim_heads(G, Hkv, P):
-    """bf16 pools with 64-dim heads and an even number of KV heads are read two
-    adjacent heads at a time, as one 128-dim row per token; each query head
-    must still attend to its own KV head only.  Checked against the oracle, and
-    bit for bit against the mixed call, whose decode rows (one-token chunks)
-    read one KV head at a time."""
+def test_decode_paired_64_dim_heads(kind, G, Hkv, P):
+    """bf16 and fp8 pools with 64-dim heads and an even number of KV heads are
+    read two adjacent heads at a time, as one 128-dim row per token; each query
+    head must still attend to its own KV head only (fp8: with its own head's
+    scales).  Checked against the oracle, and bit for bit against the mixed
+    call, whose decode rows (one-token chunks) read one KV head at a time."""
     c = small(P=P, Hq=G * Hkv, Hkv=Hkv, D=64, lens=(1, 40, 256, 257, 700, 1500), seed=31 + G * Hkv + P)
-    d = DevCase(c)
+    if kind == "fp8":
+        d = Fp8Case(c, fp8_scales(Hkv, 63 + P), fp8_scales(Hkv, 64 + P))
+        scales, ref = (d.dks, d.dvs), d.reference()
+    else:
+        d = DevCase(c)
+        scales, ref = (None, None), decode_ref(c)
     got = d.decode()
-    assert_close(got, decode_ref(c), "bf16", f"paired heads G={G} Hkv={Hkv} P={P}")
+    assert_close(got, ref, "bf16", f"paired heads {kind} G={G} Hkv={Hkv} P={P}")
     one = torch.empty_like(d.q)
-    pa.paged_mixed_attention(d.q, d.kc, d.vc, idx(np.arange(c.B + 1)), d.bt, d.lens, c.scale, one)
+    pa.paged_mixed_attention(d.q, d.kc, d.vc, idx(np.arange(c.B + 1)), d.bt, d.lens, c.scale, one, *scales)
     assert np.array_equal(to_host_bits(got), to_host_bits(one)), "paired read differs from the single-head read"
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_decode_paired_heads_keep_a_non_finite_key_to_its_own_head(kind):
+    """An infinite (bf16) or NaN-coded (fp8) key element in one KV head of a
+    pair changes no output of the other head's query heads: the two heads'
+    score products are accumulated apart."""
+    G, Hkv = 4, 2
+    c = small(P=16, Hq=G * Hkv, Hkv=Hkv, D=64, lens=(300, 40, 700), seed=41)
+    if kind == "fp8":
+        d = Fp8Case(c, fp8_scales(Hkv, 65), fp8_scales(Hkv, 66))
+        bad = 0x7F
+    else:
+        d = DevCase(c)
+        bad = float("inf")
+    ref = to_host_bits(d.decode())
+    blk = int(c.block_table[0][3])  # tokens 48 .. 63 of request 0
+    d.kc[blk, 5, 1, 7] = bad
+    got = to_host_bits(d.decode())
+    assert np.array_equal(got[:, :G], ref[:, :G]), "KV head 0's query heads changed"
+    assert np.array_equal(got[1:], ref[1:]), "other requests changed"
 
 
 def test_decode_block_size_invariance():
