@@ -200,6 +200,30 @@ def cpu_baseline_mixed(case, budget_s, npf=16):
     }
 
 
+def hbm_read_ceiling(pa, dev, reps=10, nbytes=4 << 30):
+    """Practical HBM read ceiling: the library's read-only streaming kernel
+    over a 4 GiB buffer (16x the 256 MB Infinity Cache), best of a sweep of
+    grid sizes, each timed with events over `reps` back-to-back launches."""
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = (0.0, 0)
+    for wg in (256, 384, 512, 640, 768, 1024, 2048):
+        pa.hbm_read(buf, sink, wg)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            pa.hbm_read(buf, sink, wg)
+        t1.record()
+        torch.cuda.synchronize()
+        gbs = nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+        log(f"HBM read stream, {wg} workgroups: {gbs:.0f} GB/s")
+        best = max(best, (gbs, wg))
+    del buf
+    torch.cuda.empty_cache()
+    return {"kernel": "hbm_read_kernel (read-only stream, 16-byte nontemporal loads)", "gbs": round(best[0], 1),
+            "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4), "bytes": nbytes, "workgroups": best[1]}
+
+
 def bench_decode(args):
     import paged_kv_cache_48_amd as pa
     from workloads import config_case
@@ -291,6 +315,9 @@ def bench_decode(args):
     torch.cuda.synchronize()
     attn_ms = np.array([amarks[k].elapsed_time(amarks[k + 1]) for k in range(args.steps)])
 
+    ceiling = hbm_read_ceiling(pa, dev)
+    log(f"HBM read ceiling: {ceiling['gbs']} GB/s ({ceiling['workgroups']} workgroups)")
+
     dec_b = decode_bytes(case.context_lens, P, Hq, Hkv, D, s, s_kv)
     sc_b = scatter_bytes(B, Hkv, D, s, s_kv)
     step_bytes = L * (dec_b + sc_b) + 4 * B  # + the slot-mapping output
@@ -338,6 +365,7 @@ def bench_decode(args):
             "algorithmic_bytes_per_launch": dec_b,
             "avg_launch_us": round(kern_avg_ms * 1e3, 2),
         },
+        "hbm_read_ceiling": dict(ceiling, decode_frac_of_ceiling=round(achieved / ceiling["gbs"], 4)),
     }
     return res, case
 

@@ -318,6 +318,19 @@ int pa_paged_mixed_attention_fp8(const void* q, const void* k, const void* v, co
  */
 int pa_set_timing_events(void* start_event, void* stop_event);
 
+/*
+ * pa_hbm_read -- measurement aid, not a step of the attention path: streams
+ * `bytes` (a multiple of 16) from `src` (device, 16-byte aligned) with
+ * nontemporal 16-byte loads over `num_workgroups` workgroups of 256 threads
+ * and stores nothing but, with negligible probability, one word to `sink`
+ * (device, one uint32).  Its rate is the practical HBM read ceiling that the
+ * decode kernel's gathers (which also read from HBM only) are compared with.
+ * Errors: PA_ERR_INVALID for a negative or unaligned size, num_workgroups
+ * outside [1, 2^20], a null pointer or an unaligned src.  bytes == 0 is a
+ * no-op.
+ */
+int pa_hbm_read(const void* src, int64_t bytes, uint32_t* sink, int32_t num_workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

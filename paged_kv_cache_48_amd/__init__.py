@@ -31,6 +31,7 @@ __all__ = [
     "reshape_and_cache",
     "copy_blocks",
     "check_metadata",
+    "hbm_read",
     "paged_decode_attention",
     "paged_prefill_attention",
     "paged_mixed_attention",
@@ -54,6 +55,7 @@ SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_set_timing_events": (ctypes.c_int, [_c_void_p, _c_void_p]),
+    "pa_hbm_read": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _i32, _c_void_p]),
     "pa_slot_mapping": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p]),
     "pa_reshape_and_cache": (
         ctypes.c_int,
@@ -267,6 +269,18 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: tor
     code = 2 if k_cache.dtype == torch.uint8 else _dtype_code(k_cache)  # uint8: fp8 codes
     _check(lib.pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), block_mapping.data_ptr(),
                               block_mapping.shape[0], N, P, H, D, code, _stream(k_cache)))
+
+
+def hbm_read(buf: torch.Tensor, sink: torch.Tensor, num_workgroups: int) -> None:
+    """Measurement aid (see ``pa_hbm_read``): streams every byte of the
+    contiguous device tensor ``buf`` (its size a multiple of 16 bytes) from
+    HBM, storing nothing of consequence to the one-element int32 ``sink``."""
+    lib = load_library()
+    _dev_tensor(buf, "buf")
+    _dev_tensor(sink, "sink", torch.int32)
+    _req(sink.numel() >= 1, "sink must hold at least one element")
+    _check(lib.pa_hbm_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), int(num_workgroups),
+                           _stream(buf)))
 
 
 CHECK_RULES = {1: "context_lens out of range", 2: "block id out of range", 4: "cu_seqlens malformed",

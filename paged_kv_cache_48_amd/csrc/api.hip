@@ -212,6 +212,19 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, i
                     fn);
 }
 
+int pa_hbm_read(const void* src, int64_t bytes, uint32_t* sink, int32_t num_workgroups, void* stream) {
+  g_err.clear();
+  const char* fn = "pa_hbm_read";
+  PA_REQUIRE(bytes >= 0 && bytes % 16 == 0, PA_ERR_INVALID, "%s: bytes must be a non-negative multiple of 16 (got %lld)",
+             fn, (long long)bytes);
+  PA_REQUIRE(num_workgroups >= 1 && num_workgroups <= (1 << 20), PA_ERR_INVALID,
+             "%s: num_workgroups must be in [1, 2^20] (got %d)", fn, num_workgroups);
+  if (bytes == 0) return PA_OK;
+  PA_REQUIRE(src && sink, PA_ERR_INVALID, "%s: null pointer argument", fn);
+  PA_REQUIRE(reinterpret_cast<uintptr_t>(src) % 16 == 0, PA_ERR_INVALID, "%s: src must be 16-byte aligned", fn);
+  return hip_status(pa::launch_hbm_read(src, bytes, sink, num_workgroups, static_cast<hipStream_t>(stream)), fn);
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t block_size, int32_t max_blocks_per_seq) {
   if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || block_size < 1 || max_blocks_per_seq < 1) return 0;

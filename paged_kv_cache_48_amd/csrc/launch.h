@@ -42,6 +42,8 @@ hipError_t launch_check_metadata(const int32_t* block_table, const int32_t* cont
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping, int64_t num_pairs,
                               int64_t num_blocks, int64_t block_bytes, hipStream_t stream);
+// Read-only stream over `bytes` (a multiple of 16) at `src`: HBM read ceiling.
+hipError_t launch_hbm_read(const void* src, int64_t bytes, uint32_t* sink, int num_workgroups, hipStream_t stream);
 
 struct AttnArgs {
   const void* q;

@@ -199,6 +199,18 @@ def test_copy_blocks_validation(lib):
     assert f(NUL, NUL, NUL, 0, 100, 16, 8, 128, BF16, NUL) == OK    # no pairs: no-op
 
 
+def test_hbm_read_validation(lib):
+    f = lib.pa_hbm_read
+    assert f(16, -16, 16, 1024, NUL) == INVALID
+    assert f(16, 24, 16, 1024, NUL) == INVALID          # not a multiple of 16 bytes
+    assert f(16, 1 << 20, 16, 0, NUL) == INVALID         # no workgroups
+    assert f(16, 1 << 20, 16, (1 << 20) + 1, NUL) == INVALID
+    assert f(NUL, 1 << 20, 16, 1024, NUL) == INVALID
+    assert f(16, 1 << 20, NUL, 1024, NUL) == INVALID     # no sink
+    assert f(8, 1 << 20, 16, 1024, NUL) == INVALID       # src not 16-byte aligned
+    assert f(NUL, 0, NUL, 1024, NUL) == OK               # nothing to read: no-op
+
+
 def test_check_metadata_validation(lib):
     f = lib.pa_check_metadata
     assert f(1, 1, NUL, NUL, -1, 0, 10, 16, 4, 1, NUL) == INVALID
