@@ -76,8 +76,17 @@ def scatter_bytes(T, Hkv, D, s, s_kv=None):
     return int(2 * T * Hkv * D * (s + s_kv) + 4 * T)
 
 
+def append_bytes(B, Hkv, D, s, s_kv=None):
+    """The new K and V rows a decode-with-append launch reads (``s``) and writes (``s_kv``)."""
+    s_kv = s if s_kv is None else s_kv
+    return int(2 * B * Hkv * D * (s + s_kv))
+
+
 # sources the decode partition kernel is compiled from
 DECODE_SOURCES = ("decode.hip", "decode_dev.h", "common.h")
+# the partition kernel of the benchmark's decode-with-append call (bf16 pools
+# under 4 GiB, P a multiple of 16), as rocprofv3 names it
+BENCH_DECODE_KERNEL = "decode_partition_kernel<unsigned short, 128, false, true, 1, 1, true>"
 
 
 def sources_sha(files) -> str:
@@ -262,15 +271,16 @@ def bench_decode(args):
     vs = torch.full((Hkv,), 0.02, dtype=torch.float32, device=dev) if fp8 else None
     log(f"llama3_8b: {L} layer pools of {N} blocks ready ({'fp8 e4m3' if fp8 else 'bf16'})")
 
+    # One decode step: per layer, the new tokens' K/V are written to the pool
+    # and attended to in one call (paged_decode_append, bit for bit the scatter
+    # followed by the decode call).
     def step(ev=None, timed_layer=-1):
-        pa.slot_mapping(bt, cu, lens, P, B, out=slots)
         for i, (kc, vc, q, kn, vn, out) in enumerate(layers):
-            pa.reshape_and_cache(kn, vn, slots, kc, vc, ks, vs)
             if i != timed_layer:
-                pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out, ks, vs)
+                pa.paged_decode_append(q, kn, vn, kc, vc, bt, lens, scale, out, ks, vs)
             else:
                 with pa.kernel_timer(*ev):
-                    pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out, ks, vs)
+                    pa.paged_decode_append(q, kn, vn, kc, vc, bt, lens, scale, out, ks, vs)
 
     for _ in range(args.warmup):
         step()
@@ -300,7 +310,8 @@ def bench_decode(args):
     kern_avg_ms = float(np.mean(kern_ms))
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, decode kernel {kern_avg_ms * 1e3:.1f} us avg")
 
-    # attention only: the same sweep without the slot mapping and the scatters
+    # attention only: each layer's decode call over pools that already hold
+    # the new tokens (no append)
     def attn_only():
         for kc, vc, q, kn, vn, out in layers:
             pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out, ks, vs)
@@ -315,14 +326,34 @@ def bench_decode(args):
     torch.cuda.synchronize()
     attn_ms = np.array([amarks[k].elapsed_time(amarks[k + 1]) for k in range(args.steps)])
 
+    # the same step as separate calls: slot mapping, then per layer the
+    # scatter (reshape_and_cache) and the decode call
+    def separate_step():
+        pa.slot_mapping(bt, cu, lens, P, B, out=slots)
+        for kc, vc, q, kn, vn, out in layers:
+            pa.reshape_and_cache(kn, vn, slots, kc, vc, ks, vs)
+            pa.paged_decode_attention(q, kc, vc, bt, lens, scale, out, ks, vs)
+
+    separate_step()
+    smarks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    smarks[0].record()
+    for k in range(args.steps):
+        separate_step()
+        smarks[k + 1].record()
+    torch.cuda.synchronize()
+    sep_ms = np.array([smarks[k].elapsed_time(smarks[k + 1]) for k in range(args.steps)])
+    log(f"as separate calls: {float(np.mean(sep_ms)):.3f} ms/step")
+
     ceiling = hbm_read_ceiling(pa, dev)
     log(f"HBM read ceiling: {ceiling['gbs']} GB/s ({ceiling['workgroups']} workgroups)")
 
     dec_b = decode_bytes(case.context_lens, P, Hq, Hkv, D, s, s_kv)
     sc_b = scatter_bytes(B, Hkv, D, s, s_kv)
-    step_bytes = L * (dec_b + sc_b) + 4 * B  # + the slot-mapping output
+    step_bytes = L * (dec_b + sc_b)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = dec_b / (kern_avg_ms * 1e-3) / 1e9
+    kern_b = dec_b + append_bytes(B, Hkv, D, s, s_kv)  # the launch also reads and writes the new rows
+    achieved = kern_b / (kern_avg_ms * 1e-3) / 1e9
     traffic = None if fp8 else traffic_from_profiles(DECODE_SOURCES, "decode_partition_llama3_8b")
     res = {
         "metric": ("paged decode attn (fp8 e4m3 KV) KV GB/s (% HBM peak) + us/layer-step + tokens/s, Llama-3-8B shape"
@@ -339,7 +370,8 @@ def bench_decode(args):
         "dtype": "fp8_e4m3 KV, bf16 q/out" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"llama3_8b{'_fp8' if fp8 else ''} decode step: {L} layers x (reshape_and_cache + paged decode), B={B}, "
+            "workload": f"llama3_8b{'_fp8' if fp8 else ''} decode step: {L} layers x paged decode with append "
+                        f"(the new token's K/V written and attended to in one call), B={B}, "
                         f"H_q={Hq}, H_kv={Hkv}, D={D}, P={P}, N={N} blocks/layer, context log-normal "
                         f"(median 1024, sigma 1) clipped to [16, 8192], sum L = {int(case.context_lens.sum())}",
             "global_batch": B,
@@ -352,17 +384,20 @@ def bench_decode(args):
         "us_per_layer_step_p10_p50_p90": [round(float(x), 2) for x in np.percentile(1e3 * step_ms / L, [10, 50, 90])],
         "attention_only_us_per_layer_step_p10_p50_p90": [round(float(x), 2)
                                                          for x in np.percentile(1e3 * attn_ms / L, [10, 50, 90])],
+        "separate_calls_us_per_layer_step_p10_p50_p90": [round(float(x), 2)
+                                                          for x in np.percentile(1e3 * sep_ms / L, [10, 50, 90])],
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "roofline_tokens_per_s": round(B / (step_bytes / (HBM_PEAK_GBS * 1e9)), 1),
         "roofline": {
-            "kernel": "decode_partition_kernel<fp8_e4m3,128>" if fp8 else "decode_partition_kernel<bf16,128>",
+            "kernel": ("decode_partition_kernel<fp8_e4m3,128> (decode with append)" if fp8
+                       else "decode_partition_kernel<bf16,128> (decode with append)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": dec_b,
+            "algorithmic_bytes_per_launch": kern_b,
             "avg_launch_us": round(kern_avg_ms * 1e3, 2),
         },
         "hbm_read_ceiling": dict(ceiling, decode_frac_of_ceiling=round(achieved / ceiling["gbs"], 4)),
@@ -623,8 +658,10 @@ def summarize_profiles(d):
     if stats:
         table, _ = _stats_table(stats)
         with open(os.path.join(prof, "decode_llama3_8b_kernel_stats.txt"), "w") as f:
-            f.write("Llama-3-8B-shaped decode step (32 layers x (reshape_and_cache + paged decode: partition with\n"
-                    "in-kernel plan, reduce), B=256, H_q=32, H_kv=8, D=128, P=16, bf16), rocprofv3 kernel statistics.\n")
+            f.write("Llama-3-8B-shaped decode step (32 layers x paged decode with append: partition kernel with\n"
+                    "in-kernel plan and the new token's write, reduce), B=256, H_q=32, H_kv=8, D=128, P=16, bf16;\n"
+                    "the same run also times the step as separate calls (slot mapping, reshape_and_cache, decode\n"
+                    "without append) and an attention-only sweep.  rocprofv3 kernel statistics.\n")
             f.write("command (run from the repository root, DIR = an output folder):\n  "
                     + PROFILE_RUNS["trace"] + "\n")
             f.write(sha_line + "\n\n")
@@ -660,9 +697,9 @@ def summarize_profiles(d):
                     + PROFILE_RUNS["trace_cow"] + "\n\n")
             f.write("\n".join(table) + "\n")
 
-    fetch_kib, nf = _counter_mean(one("pmc_fetch/*counter_collection.csv"), "decode_partition_kernel", "FETCH_SIZE") \
+    fetch_kib, nf = _counter_mean(one("pmc_fetch/*counter_collection.csv"), BENCH_DECODE_KERNEL, "FETCH_SIZE") \
         if one("pmc_fetch/*counter_collection.csv") else (None, 0)
-    write_kib, nw = _counter_mean(one("pmc_write/*counter_collection.csv"), "decode_partition_kernel", "WRITE_SIZE") \
+    write_kib, nw = _counter_mean(one("pmc_write/*counter_collection.csv"), BENCH_DECODE_KERNEL, "WRITE_SIZE") \
         if one("pmc_write/*counter_collection.csv") else (None, 0)
     cf_kib, _ = _counter_mean(one("pmc_copyf/*counter_collection.csv"), "copyBuffer", "FETCH_SIZE") \
         if one("pmc_copyf/*counter_collection.csv") else (None, 0)
@@ -677,9 +714,11 @@ def summarize_profiles(d):
     from workloads import config_case
 
     case = config_case(3, values=False)
-    alg = decode_bytes(case.context_lens, case.block_size, case.num_q_heads, case.num_kv_heads, case.head_dim, 2)
+    alg = (decode_bytes(case.context_lens, case.block_size, case.num_q_heads, case.num_kv_heads, case.head_dim, 2)
+           + append_bytes(case.B, case.num_kv_heads, case.head_dim, 2))
     lines = [
-        "HBM traffic of decode_partition_kernel<bf16, 128> on the Llama-3-8B-shaped batch (one launch = one layer:",
+        "HBM traffic of decode_partition_kernel<bf16, 128> with append on the Llama-3-8B-shaped batch (one launch =",
+        "one layer, the new token's K/V written in the same launch:",
         "B=256, sum of context lengths " + f"{int(case.context_lens.sum())}, H_kv=8, D=128, P=16).",
         "commands (run from the repository root, DIR = an output folder):",
         "  " + PROFILE_RUNS["fetch"], "  " + PROFILE_RUNS["write"],
@@ -687,11 +726,11 @@ def summarize_profiles(d):
         sha_line, "",
         f"calibration: torch copy_ of 1 GiB reads FETCH_SIZE {cf_kib:.0f} KiB and WRITE_SIZE {cw_kib:.0f} KiB "
         f"per dispatch -> scale {kf:.4f} (fetch), {kw:.4f} (write)",
-        f"partition kernel: FETCH_SIZE {fetch_kib:.0f} KiB, WRITE_SIZE {write_kib:.0f} KiB per dispatch "
+        f"{BENCH_DECODE_KERNEL}: FETCH_SIZE {fetch_kib:.0f} KiB, WRITE_SIZE {write_kib:.0f} KiB per dispatch "
         f"(mean of {nf} and {nw} dispatches)",
         f"  -> fetched {fetch_b / 1e9:.4f} GB + written {write_b / 1e9:.4f} GB = {(fetch_b + write_b) / 1e9:.4f} GB "
         f"per launch",
-        f"algorithmic bytes per launch: {alg / 1e9:.4f} GB (KV rows + q/out + block table + lengths); "
+        f"algorithmic bytes per launch: {alg / 1e9:.4f} GB (KV rows + q/out + block table + lengths + new rows); "
         f"measured / algorithmic = {(fetch_b + write_b) / alg:.3f}",
     ]
     with open(os.path.join(prof, "decode_llama3_8b_hbm_traffic.txt"), "w") as f:

@@ -124,6 +124,29 @@ int pa_reshape_and_cache_fp8(const void* k, const void* v, const int32_t* slot_m
                              int32_t dtype, void* stream);
 
 /*
+ * pa_paged_decode_append -- one decode step of a layer in one call: the step's
+ * new token of each request is appended to the pools and attended to, exactly
+ * as pa_reshape_and_cache (with the slots of positions context_lens[b] - 1)
+ * followed by pa_paged_decode_attention, bit for bit (tiny-vllm-py "KV Cache":
+ * the new token's K/V are stored first and the token sees itself; weft "Cache
+ * layouts": the write is a scatter through the block table).
+ *   k_new, v_new       [num_seqs, num_kv_heads, head_dim], dtype: the new token
+ *                      of request b, stored at position context_lens[b] - 1
+ *   k_cache, v_cache   written at those slots only (a block id outside
+ *                      [0, num_blocks) is skipped, as the scatter skips such
+ *                      slots; context_lens[b] == 0 or above max_blocks_per_seq
+ *                      * block_size appends nothing)
+ * Other arguments, the workspace and the errors are those of
+ * pa_paged_decode_attention.  The pools must not hold the slot in more than
+ * one request's table (a shared block is copied before it is appended to).
+ */
+int pa_paged_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* block_table, const int32_t* context_lens, float scale, void* out,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_paged_decode_attention_fp8 -- pa_paged_decode_attention over fp8 pools
  * (format and scales as above).  q and out are bfloat16; q's elements must lie
  * inside the fp16 range (the products run on fp16 matrix cores: the codes
@@ -137,6 +160,21 @@ int pa_paged_decode_attention_fp8(const void* q, const void* k_cache, const void
                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                   int32_t max_blocks_per_seq, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/*
+ * pa_paged_decode_append_fp8 -- pa_paged_decode_append over fp8 pools: equal,
+ * bit for bit, to pa_reshape_and_cache_fp8 of the new rows (quantised with
+ * k_scale / v_scale) followed by pa_paged_decode_attention_fp8.  k_new and
+ * v_new are of type new_dtype (PA_DTYPE_F32 or PA_DTYPE_BF16); q and out are
+ * bfloat16.  Errors: those of pa_paged_decode_append, and PA_ERR_UNSUPPORTED
+ * for another new_dtype.
+ */
+int pa_paged_decode_append_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               const float* k_scale, const float* v_scale, const int32_t* block_table,
+                               const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t new_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * pa_copy_blocks -- copy-on-write support for prefix sharing (tiny-vllm-py,

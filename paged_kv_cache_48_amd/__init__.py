@@ -33,6 +33,7 @@ __all__ = [
     "check_metadata",
     "hbm_read",
     "paged_decode_attention",
+    "paged_decode_append",
     "paged_prefill_attention",
     "paged_mixed_attention",
     "decode_workspace_size",
@@ -86,6 +87,16 @@ SIGNATURES = {
         ctypes.c_int,
         [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
          _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _c_void_p, _size, _c_void_p],
+    ),
+    "pa_paged_decode_append": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+         _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _c_void_p, _size, _c_void_p],
+    ),
+    "pa_paged_decode_append_fp8": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32,
+         _c_void_p, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _c_void_p, _size, _c_void_p],
     ),
     "pa_mixed_workspace_size": (_size, [_i32, _i32, _i32, _i32, _i32]),
     "pa_paged_mixed_attention": (
@@ -362,6 +373,43 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                          block_table.data_ptr(), context_lens.data_ptr(), float(scale),
                                          out.data_ptr(), B, Hq, Hkv, D, P, N, M, _dtype_code(q),
                                          ws.data_ptr(), ws.numel(), stream))
+    return out
+
+
+def paged_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                        out: torch.Tensor, k_scale: torch.Tensor | None = None,
+                        v_scale: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step in one call: the new tokens ``k_new``/``v_new``
+    ``[B, H_kv, D]`` are written at positions ``context_lens - 1`` and attended
+    to, as ``reshape_and_cache`` + ``paged_decode_attention`` would (see
+    ``pa_paged_decode_append``).  uint8 pools hold fp8 (OCP E4M3) codes: the new
+    rows (float32 or bfloat16) are quantised with the per-KV-head scales."""
+    lib = load_library()
+    B = _attn_common(q, k_cache, v_cache, block_table, context_lens, out)
+    _req(q.shape[0] == B, "q must have one row per sequence")
+    N, P, Hkv, D = k_cache.shape
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _dev_tensor(t, name, dim=3)
+        _req(tuple(t.shape) == (B, Hkv, D), f"{name} must be [num_seqs, num_kv_heads, head_dim]")
+    _req(v_new.dtype == k_new.dtype, "k_new and v_new must share a dtype")
+    Hq = q.shape[1]
+    M = block_table.shape[1]
+    stream = _stream(q)
+    ws = _workspace(q.device, stream, decode_workspace_size(B, Hq, D, P, M))
+    if k_cache.dtype == torch.uint8:
+        _scales(k_scale, v_scale, Hkv, k_cache.device)
+        _check(lib.pa_paged_decode_append_fp8(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                                              v_cache.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
+                                              block_table.data_ptr(), context_lens.data_ptr(), float(scale),
+                                              out.data_ptr(), B, Hq, Hkv, D, P, N, M, _dtype_code(k_new),
+                                              ws.data_ptr(), ws.numel(), stream))
+        return out
+    _req(k_new.dtype == k_cache.dtype, "k_new and the caches must share a dtype")
+    _check(lib.pa_paged_decode_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                                      v_cache.data_ptr(), block_table.data_ptr(), context_lens.data_ptr(),
+                                      float(scale), out.data_ptr(), B, Hq, Hkv, D, P, N, M, _dtype_code(q),
+                                      ws.data_ptr(), ws.numel(), stream))
     return out
 
 

@@ -235,11 +235,13 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
 
 namespace {
 
+// k_new / v_new non-null: decode with append (new rows of type new_dtype).
 int decode_call(const char* fn, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
                 const float* v_scale, const int32_t* block_table, const int32_t* context_lens, float scale, void* out,
                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                 int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype, int32_t kv_dtype, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, const void* k_new = nullptr, const void* v_new = nullptr,
+                int32_t new_dtype = 0) {
   int st = check_attn(fn, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                       max_blocks_per_seq, dtype);
   if (st != PA_OK) return st;
@@ -247,6 +249,7 @@ int decode_call(const char* fn, const void* q, const void* k_cache, const void* 
   PA_REQUIRE(q && k_cache && v_cache && block_table && context_lens && out, PA_ERR_INVALID,
              "%s: null pointer argument", fn);
   PA_REQUIRE(kv_dtype != pa::kFP8E4M3 || (k_scale && v_scale), PA_ERR_INVALID, "%s: null scale pointer", fn);
+  PA_REQUIRE((k_new == nullptr) == (v_new == nullptr), PA_ERR_INVALID, "%s: null new-token pointer", fn);
   const size_t need = pa::decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq);
   PA_REQUIRE(workspace && workspace_bytes >= need, PA_ERR_WORKSPACE,
              "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? workspace_bytes : (size_t)0);
@@ -270,6 +273,9 @@ int decode_call(const char* fn, const void* q, const void* k_cache, const void* 
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.workspace = workspace;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_dtype = new_dtype;
   return hip_status(pa::launch_decode(a, static_cast<hipStream_t>(stream), g_ev_start, g_ev_stop), fn);
 }
 
@@ -299,6 +305,34 @@ int pa_paged_decode_attention_fp8(const void* q, const void* k_cache, const void
   return decode_call("pa_paged_decode_attention_fp8", q, k_cache, v_cache, k_scale, v_scale, block_table,
                      context_lens, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, PA_DTYPE_BF16, pa::kFP8E4M3, workspace, workspace_bytes, stream);
+}
+
+int pa_paged_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* block_table, const int32_t* context_lens, float scale, void* out,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "pa_paged_decode_append";
+  PA_REQUIRE(num_seqs == 0 || (k_new && v_new), PA_ERR_INVALID, "%s: null pointer argument", fn);
+  return decode_call(fn, q, k_cache, v_cache, nullptr, nullptr, block_table, context_lens, scale, out, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, dtype, dtype,
+                     workspace, workspace_bytes, stream, k_new, v_new, dtype);
+}
+
+int pa_paged_decode_append_fp8(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               const float* k_scale, const float* v_scale, const int32_t* block_table,
+                               const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t new_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  const char* fn = "pa_paged_decode_append_fp8";
+  PA_REQUIRE(dtype_ok(new_dtype), PA_ERR_UNSUPPORTED, "%s: unsupported dtype %d of the new rows", fn, new_dtype);
+  PA_REQUIRE(num_seqs == 0 || (k_new && v_new), PA_ERR_INVALID, "%s: null pointer argument", fn);
+  return decode_call(fn, q, k_cache, v_cache, k_scale, v_scale, block_table, context_lens, scale, out, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, PA_DTYPE_BF16,
+                     pa::kFP8E4M3, workspace, workspace_bytes, stream, k_new, v_new, new_dtype);
 }
 
 size_t pa_prefill_workspace_size(int32_t num_seqs, int64_t total_q_tokens, int32_t num_q_heads,

@@ -134,4 +134,28 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// fp32 -> OCP FP8 E4M3 code (1 sign bit, 4 exponent bits with bias 7, 3
+// mantissa bits, subnormals m/8 * 2^-6, no infinities, S.1111.111 = NaN):
+// nearest, ties to even; magnitudes above 448 saturate to +-448; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a == a)) return 0x7Fu;
+  if (a > 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);  // subnormal grid of 2^-9 (8 = smallest normal)
+  const uint32_t ua = __float_as_uint(a);
+  int e = (int)(ua >> 23) - 127;
+  const uint32_t mant = ua & 0x7FFFFFu;
+  uint32_t r = mant >> 20;
+  const uint32_t rem = mant & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+  if (r == 8u) {
+    r = 0u;
+    ++e;
+  }
+  const uint32_t code = ((uint32_t)(e + 7) << 3) | r;
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
 }  // namespace pa

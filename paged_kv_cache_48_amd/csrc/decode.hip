@@ -106,12 +106,19 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
 // Partition kernel: every wave computes a stream of work items (see
 // decode_stream for the schedule and the per-tile steps).
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool kWide, bool kAligned, int NR, int HP>
-__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm) {
+// Waves per workgroup: as many as fit in 64 KiB of LDS (at most 4).
+template <typename T, int D>
+constexpr int waves_per_block() {
+  return Geo<T, D>::LDS_PER_WAVE * kWavesPerBlock <= 65536 ? kWavesPerBlock : 2;
+}
+
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend>
+__device__ __forceinline__ void partition_body(const DecodeParams& prm) {
   using Gm = Geo<T, D>;
+  constexpr int wpb = waves_per_block<T, D>();
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* lds = smem + (threadIdx.x >> 6) * Gm::LDS_PER_WAVE;
-  PlanLds* pl = reinterpret_cast<PlanLds*>(smem + (blockDim.x >> 6) * Gm::LDS_PER_WAVE);
+  PlanLds* pl = reinterpret_cast<PlanLds*>(smem + wpb * Gm::LDS_PER_WAVE);
   unsigned long long tag = 0;
   uint32_t n_items, n_full, nq_plan;
   if (prm.self_plan) {
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     // workgroup 0 resets the queue counters for this launch
     if (blockIdx.x == 0 && threadIdx.x < kQueues)
       atomicExch(prm.counter + threadIdx.x * kCounterStride, tag << kCountBits);
-    self_plan<false>(prm, pl);
+    self_plan<false>(prm, pl, wpb);
     n_items = (uint32_t)uniform(pl->nitems);
     n_full = (uint32_t)uniform(pl->nfull);
     nq_plan = (uint32_t)uniform(pl->nq);
@@ -128,29 +135,46 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
     n_full = prm.hdr[kFullCountWord];
     nq_plan = prm.hdr[kQueueCountWord];
   }
-  const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
+  const uint32_t nwaves = gridDim.x * wpb;
   // (threadIdx.x >> 6 is the same in every lane; readfirstlane tells the compiler)
-  const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (uint32_t)uniform((int)(threadIdx.x >> 6));
-  decode_stream<T, D, kWide, kAligned, NR, false, HP>(prm, lds, pl, tag, n_items, n_full, nq_plan, wave, nwaves,
-                                                      (uint32_t)kMaxStaticRounds);
+  const uint32_t wave = blockIdx.x * wpb + (uint32_t)uniform((int)(threadIdx.x >> 6));
+  decode_stream<T, D, kWide, kAligned, NR, false, HP, kAppend>(prm, lds, pl, tag, n_items, n_full, nq_plan, wave,
+                                                               nwaves, (uint32_t)kMaxStaticRounds);
 }
 
-template <typename T, int D, bool kWide, bool kAligned, int NR, int HP>
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend>
+__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm) {
+  partition_body<T, D, kWide, kAligned, NR, HP, kAppend>(prm);
+}
+
+// fp8 pools with append: making the new token's codes would take the kernel
+// just past 168 VGPRs, from three waves per SIMD to two; it is held to three.
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend>
+__global__ __launch_bounds__(256, 3) void decode_partition_kernel_w3(DecodeParams prm) {
+  partition_body<T, D, kWide, kAligned, NR, HP, kAppend>(prm);
+}
+
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend>
 hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipStream_t stream,
                         hipEvent_t ev0, hipEvent_t ev1) {
-  // waves are independent workers; a block holds as many as fit in 64 KiB of LDS (at most 4)
-  constexpr int wpb = Geo<T, D>::LDS_PER_WAVE * kWavesPerBlock <= 65536 ? kWavesPerBlock : 2;
+  // waves are independent workers
+  constexpr int wpb = waves_per_block<T, D>();
   // per-wave tile buffers, then the in-kernel plan
   constexpr unsigned lds_bytes = Geo<T, D>::LDS_PER_WAVE * wpb + (unsigned)sizeof(PlanLds);
   // exactly the blocks that can be resident at once: every wave starts on its
   // first item immediately, and none waits for a slot while holding one
+  constexpr bool kW3 = kAppend && Geo<T, D>::kFp8;
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_partition_kernel<T, D, kWide, kAligned, NR, HP>,
-                                                     64 * wpb, lds_bytes) != hipSuccess || nb < 1)
-      nb = 1;
-    per_cu = nb;
+    hipError_t e;
+    if constexpr (kW3)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &nb, decode_partition_kernel_w3<T, D, kWide, kAligned, NR, HP, kAppend>, 64 * wpb, lds_bytes);
+    else
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &nb, decode_partition_kernel<T, D, kWide, kAligned, NR, HP, kAppend>, 64 * wpb, lds_bytes);
+    per_cu = e != hipSuccess || nb < 1 ? 1 : nb;
   }
   const int64_t want = (max_items + wpb - 1) / wpb;
   const int64_t cap = (int64_t)device_cu_count() * per_cu;
@@ -159,8 +183,12 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
     const hipError_t e = hipEventRecord(ev0, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, kWide, kAligned, NR, HP>), dim3(blocks), dim3(64 * wpb),
-                     lds_bytes, stream, prm);
+  if constexpr (kW3)
+    hipLaunchKernelGGL((decode_partition_kernel_w3<T, D, kWide, kAligned, NR, HP, kAppend>), dim3(blocks),
+                       dim3(64 * wpb), lds_bytes, stream, prm);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, kWide, kAligned, NR, HP, kAppend>), dim3(blocks),
+                       dim3(64 * wpb), lds_bytes, stream, prm);
   if (ev1) {
     const hipError_t e = hipEventRecord(ev1, stream);
     if (e != hipSuccess) return e;
@@ -171,21 +199,44 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
   return hipGetLastError();
 }
 
-template <typename T, int D, bool kWide, int HP>
+template <typename T, int D, bool kWide, int HP, bool kAppend>
 hipError_t launch_mode(const DecodeParams& prm, int B, int64_t max_items, hipStream_t stream, hipEvent_t ev0,
                        hipEvent_t ev1) {
   // tiles of 16 tokens never straddle a block when P is a multiple of 16; a
   // partition touches at most 256 / P + 1 blocks: one id register for P >= 5
-  if (prm.P % kTile == 0) return launch_typed<T, D, kWide, true, 1, HP>(prm, B, max_items, stream, ev0, ev1);
-  if (prm.P >= 5) return launch_typed<T, D, kWide, false, 1, HP>(prm, B, max_items, stream, ev0, ev1);
-  return launch_typed<T, D, kWide, false, 5, HP>(prm, B, max_items, stream, ev0, ev1);
+  if (prm.P % kTile == 0)
+    return launch_typed<T, D, kWide, true, 1, HP, kAppend>(prm, B, max_items, stream, ev0, ev1);
+  if (prm.P >= 5) return launch_typed<T, D, kWide, false, 1, HP, kAppend>(prm, B, max_items, stream, ev0, ev1);
+  return launch_typed<T, D, kWide, false, 5, HP, kAppend>(prm, B, max_items, stream, ev0, ev1);
 }
 
-template <typename T, int D, int HP = 1>
+template <typename T, int D, int HP, bool kAppend>
 hipError_t launch_sized(const DecodeParams& prm, int B, int64_t max_items, int64_t pool_bytes,
                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  if (pool_bytes < ((int64_t)1 << 32)) return launch_mode<T, D, false, HP>(prm, B, max_items, stream, ev0, ev1);
-  return launch_mode<T, D, true, HP>(prm, B, max_items, stream, ev0, ev1);
+  if (pool_bytes < ((int64_t)1 << 32))
+    return launch_mode<T, D, false, HP, kAppend>(prm, B, max_items, stream, ev0, ev1);
+  return launch_mode<T, D, true, HP, kAppend>(prm, B, max_items, stream, ev0, ev1);
+}
+
+// Kernel choice by pool element type, head size and head pairing.
+template <bool kAppend>
+hipError_t launch_kinds(const AttnArgs& a, const DecodeParams& prm, bool fp8, bool pairs, int64_t max_items,
+                        int64_t pool_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const int B = a.num_seqs;
+  if (fp8) {  // bf16 q and out
+    if (a.head_dim == 128)
+      return launch_sized<fp8_e4m3, 128, 1, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
+    if (pairs) return launch_sized<fp8_e4m3, 128, 2, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
+    return launch_sized<fp8_e4m3, 64, 1, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
+  }
+  if (a.dtype == kBF16) {
+    if (a.head_dim == 128)
+      return launch_sized<bf16_bits, 128, 1, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
+    if (pairs) return launch_sized<bf16_bits, 128, 2, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
+    return launch_sized<bf16_bits, 64, 1, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
+  }
+  if (a.head_dim == 128) return launch_sized<float, 128, 1, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
+  return launch_sized<float, 64, 1, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
 }
 
 }  // namespace
@@ -232,6 +283,9 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.salt = next_salt();
   prm.cu = nullptr;
   prm.num_q_tokens = 0;
+  prm.knew = a.k_new;
+  prm.vnew = a.v_new;
+  prm.new_f32 = a.new_dtype == kF32;
   prm.k_scale = fp8 ? a.k_scale : nullptr;
   prm.v_scale = fp8 ? a.v_scale : nullptr;
 
@@ -245,20 +299,8 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
                        reinterpret_cast<i32x4_t*>(ws + Lw.items));
   const int64_t pool_bytes =
       a.num_blocks * a.block_size * a.num_kv_heads * a.head_dim * (fp8 ? 1 : (a.dtype == kBF16 ? 2 : 4));
-  if (fp8) {  // bf16 q and out
-    if (a.head_dim == 128)
-      return launch_sized<fp8_e4m3, 128>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
-    if (pairs) return launch_sized<fp8_e4m3, 128, 2>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
-    return launch_sized<fp8_e4m3, 64>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
-  }
-  if (a.dtype == kBF16) {
-    if (a.head_dim == 128)
-      return launch_sized<bf16_bits, 128>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
-    if (pairs) return launch_sized<bf16_bits, 128, 2>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
-    return launch_sized<bf16_bits, 64>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
-  }
-  if (a.head_dim == 128) return launch_sized<float, 128>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
-  return launch_sized<float, 64>(prm, a.num_seqs, max_items, pool_bytes, stream, ev0, ev1);
+  if (a.k_new) return launch_kinds<true>(a, prm, fp8, pairs, max_items, pool_bytes, stream, ev0, ev1);
+  return launch_kinds<false>(a, prm, fp8, pairs, max_items, pool_bytes, stream, ev0, ev1);
 }
 
 }  // namespace pa

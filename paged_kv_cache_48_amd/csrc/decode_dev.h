@@ -161,6 +161,14 @@ struct DecodeParams {
   // requests have no decode items.  Null for plain decode (row b).
   const int32_t* cu;
   int num_q_tokens;
+  // decode with append: request b's new token, at position L_b - 1, is row b
+  // of knew / vnew [B, H_kv, D] (the pool's element type; fp8 pools: bf16
+  // values, or fp32 when new_f32, quantised with the head's scale as the
+  // scatter does).  The last partition's items take it from there instead of
+  // the pool, and those of query-head group 0 write it to its slot.
+  const void* knew;
+  const void* vnew;
+  int new_f32;
 };
 
 // One work item, wave-uniform (scalar registers).
@@ -530,11 +538,11 @@ __device__ __forceinline__ int decode_len(const DecodeParams& prm, int b) {
   return clamp_len(prm.lens[b], prm.cap);
 }
 
-// Every thread of the workgroup takes part (three barriers).
+// Every thread of the workgroup (nw waves) takes part (three barriers).
 template <bool kRowMap>
-__device__ void self_plan(const DecodeParams& prm, PlanLds* pl) {
+__device__ void self_plan(const DecodeParams& prm, PlanLds* pl, int nw) {
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6;
   const int B = prm.B;
   const int nc = (B + 63) >> 6;
   // 1: per chunk of 64 requests: lengths, the full-partition prefix inside
@@ -667,7 +675,111 @@ __device__ __forceinline__ i32x4_t item_desc(const DecodeParams& prm, const Plan
 //   O^T += V^T P^T (A = V^T from LDS, B = the lane's own probabilities), so
 //                  lane (n, g) accumulates head n's outputs d = 16db + 4g + j.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool kWide, bool kAligned, int NR, bool kRowMap, int HP = 1>
+// Decode with append (bf16 and fp32 pools): the new token's 16-byte piece of
+// the item's head slice that this lane stages (piece lane % CPR).
+template <typename T, int D, int HP>
+__device__ __forceinline__ void load_new(const DecodeParams& prm, const Item& it, u32x4_t& nk, u32x4_t& nv) {
+  using Gm = Geo<T, D>;
+  static_assert(!Gm::kFp8, "fp8 pools make the new codes in append_lds");
+  // the new rows have the pool rows' layout: the item's slice of row b
+  const int64_t off = (int64_t)it.b * (prm.Hkv * Gm::GROWB) + it.hkv * Gm::GROWB + 16 * (lane_id() % Gm::CPR);
+  nk = *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(prm.knew) + off);
+  nv = *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(prm.vnew) + off);
+}
+
+// Decode with append, at the last tile of a request's last partition (tile0
+// holds position L - 1).  Items of query-head group 0 write the new token to
+// its slot, unless the block id is out of range (as the scatter skips such
+// slots); the lanes that stage the token's pieces hold (nk, nv).
+template <typename T, int D, int NR>
+__device__ __forceinline__ void append_store(const DecodeParams& prm, const PoolView& pv, const Item& it,
+                                             const int (&ids)[NR], bool mine, const u32x4_t& nk, const u32x4_t& nv) {
+  using Gm = Geo<T, D>;
+  if (it.hg != 0) return;
+  const int pos = it.L - 1;
+  const int lb = pos / prm.P, off = pos - lb * prm.P;
+  const int blk = lane_id_lookup<NR>(ids, lb - it.blk0);
+  if (mine && blk >= 0 && blk < prm.N) {
+    const uint64_t e = ((uint64_t)blk * (uint64_t)prm.P + (uint64_t)off) * pv.row_bytes +
+                       (uint64_t)(it.hkv * Gm::GROWB + 16 * (lane_id() % Gm::CPR));
+    *reinterpret_cast<u32x4_t*>(const_cast<char*>(pv.k) + e) = nk;
+    *reinterpret_cast<u32x4_t*>(const_cast<char*>(pv.v) + e) = nv;
+  }
+}
+
+// bf16 and fp32 pools: before the last tile is staged, the lane that stages
+// the new token takes its piece from (nk, nv), loaded with the item's first
+// tile.  A length beyond the block table (clamped when read) appends nothing.
+template <typename T, int D, int NR>
+__device__ __forceinline__ void append_regs(const DecodeParams& prm, const PoolView& pv, const Item& it,
+                                            const int (&ids)[NR], int tile0, const u32x4_t& nk, const u32x4_t& nv,
+                                            TileRegs<T, D>& regs) {
+  using Gm = Geo<T, D>;
+  if (prm.lens[it.b] > prm.cap) return;
+  const int tL = it.L - 1 - tile0;  // in [0, TT)
+  const int qL = tL / Gm::TPL, jL = tL - qL * Gm::TPL;
+  const bool mine = lane_id() / Gm::CPR == qL;
+#pragma unroll
+  for (int j = 0; j < Gm::TPL; ++j)
+    if (mine && j == jL) {
+      regs.k[j] = nk;
+      regs.v[j] = nv;
+    }
+  append_store<T, D, NR>(prm, pv, it, ids, mine, nk, nv);
+}
+
+// fp8 pools: after the last tile is staged, the new token's codes are made
+// here, four per lane (lanes 0-31 K, 32-63 V), and written over its staged K
+// and V rows (unless the token was zeroed: invalid block id) and, by items of
+// query-head group 0, to its slot.  Each code is x / scale[h], correctly
+// rounded, then encoded, as the fp8 scatter makes it.
+template <typename T, int D, int NR, int HP>
+__device__ __forceinline__ void append_lds(const DecodeParams& prm, const PoolView& pv, const Item& it,
+                                           const int (&ids)[NR], int tile0, uint32_t ok, char* lds) {
+  using Gm = Geo<T, D>;
+  static_assert(Gm::kFp8, "fp8 pools");
+  if (prm.lens[it.b] > prm.cap) return;
+  constexpr int W = Gm::ROWB / 4;  // 4-code words of the item's row slice
+  const int lane = lane_id();
+  const int tL = it.L - 1 - tile0;  // in [0, TT)
+  const int qL = tL / Gm::TPL, jL = tL - qL * Gm::TPL;
+  const bool tok_ok = ((__builtin_amdgcn_readlane((int)ok, qL * Gm::CPR) >> jL) & 1) != 0;
+  const bool isv = lane >= 32;
+  const int w = lane & 31;
+  const bool act = w < W;
+  const int e = 4 * (act ? w : 0);  // code index within the slice
+  const int h = HP == 2 ? 2 * it.hkv + (e >= D / 2 ? 1 : 0) : it.hkv;
+  const float sc = isv ? prm.v_scale[h] : prm.k_scale[h];
+  const int64_t e0 = ((int64_t)it.b * prm.Hkv + it.hkv) * D + e;
+  const void* src = isv ? prm.vnew : prm.knew;
+  float x[4];
+  if (prm.new_f32) {
+    const f32x4_t f = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(src) + e0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = f[j];
+  } else {
+    const u32x2_t u = *reinterpret_cast<const u32x2_t*>(static_cast<const bf16_bits*>(src) + e0);
+    x[0] = bf16_lo(u[0]);
+    x[1] = bf16_hi(u[0]);
+    x[2] = bf16_lo(u[1]);
+    x[3] = bf16_hi(u[1]);
+  }
+  uint32_t code = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) code |= e4m3_from_f32(x[j] / sc) << (8 * j);
+  if (act && tok_ok) *reinterpret_cast<uint32_t*>(lds + (isv ? Gm::KBYTES : 0) + tL * Gm::KST + e) = code;
+  if (it.hg != 0) return;
+  const int pos = it.L - 1;
+  const int lb = pos / prm.P, off = pos - lb * prm.P;
+  const int blk = lane_id_lookup<NR>(ids, lb - it.blk0);
+  if (act && blk >= 0 && blk < prm.N) {
+    const uint64_t a = ((uint64_t)blk * (uint64_t)prm.P + (uint64_t)off) * pv.row_bytes +
+                       (uint64_t)(it.hkv * Gm::GROWB + e);
+    *reinterpret_cast<uint32_t*>(const_cast<char*>(isv ? pv.v : pv.k) + a) = code;
+  }
+}
+
+template <typename T, int D, bool kWide, bool kAligned, int NR, bool kRowMap, int HP = 1, bool kAppend = false>
 __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds, const PlanLds* pl,
                                               unsigned long long tag, uint32_t n_items, uint32_t n_full,
                                               uint32_t nq_plan, uint32_t wave, uint32_t nwaves,
@@ -718,6 +830,10 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
   load_q<T, D, HP>(prm, it, qv);
   TileRegs<T, D> regs;
   load_tile<T, D, kWide, kAligned, NR>(pv, prm, it, ids, it.tok0, regs);
+  u32x4_t nk, nv;  // decode with append: the new token's piece (last partitions)
+  if constexpr (kAppend && !Gm::kFp8) {
+    if (it.part == it.nparts - 1) load_new<T, D, HP>(prm, it, nk, nv);
+  }
 
   Item nx = it;        // the item after the current one, once known
   uint32_t fn = 0;     // its flat index
@@ -742,8 +858,14 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
       full = tile0 + Gm::TT <= it.tok_end && __builtin_amdgcn_readfirstlane((int)regs.ok) == (1 << Gm::TPL) - 1;
     else
       full = __builtin_amdgcn_readfirstlane((int)(__ballot(regs.ok != (1u << Gm::TPL) - 1u) == 0));
+    if constexpr (kAppend && !Gm::kFp8) {
+      if (last && it.part == it.nparts - 1) append_regs<T, D, NR>(prm, pv, it, ids, tile0, nk, nv, regs);
+    }
     wave_lds_sync();  // previous tile's LDS reads are done
     stage_tile<T, D>(lds, regs, full);
+    if constexpr (kAppend && Gm::kFp8) {
+      if (last && it.part == it.nparts - 1) append_lds<T, D, NR, HP>(prm, pv, it, ids, tile0, regs.ok, lds);
+    }
     wave_lds_sync();
 
     // find the next item and fetch its block ids.  A static item is known at
@@ -788,6 +910,9 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
     }
     if (!last || has_next)
       load_tile<T, D, kWide, kAligned, NR>(pv, prm, last ? nx : it, ids, last ? nx.tok0 : tile0 + Gm::TT, regs);
+    if constexpr (kAppend && !Gm::kFp8) {
+      if (last && has_next && nx.part == nx.nparts - 1) load_new<T, D, HP>(prm, nx, nk, nv);
+    }
     if (t == 0 && early && !stat_next) {
       fn = claim(prm, tag, nq, home, queue, first_dyn, total);
       if (fn < total) pend = 1;

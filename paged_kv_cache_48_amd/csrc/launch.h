@@ -67,6 +67,11 @@ struct AttnArgs {
   const float* k_scale;  // kFP8E4M3 pools: per-KV-head scales
   const float* v_scale;
   void* workspace;
+  // decode with append: each request's new token [num_seqs, H_kv, D] (null
+  // otherwise), of type new_dtype (the pools' type; fp8 pools: kF32 or kBF16)
+  const void* k_new;
+  const void* v_new;
+  int new_dtype;
 };
 
 size_t decode_workspace_size(int num_seqs, int num_q_heads, int head_dim, int block_size,

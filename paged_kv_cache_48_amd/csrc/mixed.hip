@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kMixThreads) void mixed_kernel(MixedParams mp) {
                                                : mp.pcounter + (tid - dec::kQueues) * dec::kCounterStride;
     atomicExch(c, tag << dec::kCountBits);
   }
-  dec::self_plan<true>(mp.d, dpl);
+  dec::self_plan<true>(mp.d, dpl, pre::kThreads / 64);
   prefill_self_plan(mp.p, mp.B, mp.num_q_tokens, ppl);
 
   // ---- phase 1: prefill items, one per workgroup at a time ----
@@ -355,6 +355,9 @@ hipError_t launch_mixed(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, h
   d.salt = dec::next_salt();
   d.cu = a.cu_seqlens;
   d.num_q_tokens = (int)a.num_q_tokens;
+  d.knew = nullptr;
+  d.vnew = nullptr;
+  d.new_f32 = 0;
 
   pre::PrefillParams& p = mp.p;
   p.q = static_cast<const bf16_bits*>(a.q);

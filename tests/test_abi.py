@@ -35,7 +35,8 @@ def test_header_declares_the_expected_calls():
     names = declared_functions()
     for want in ("pa_slot_mapping", "pa_reshape_and_cache", "pa_paged_decode_attention",
                  "pa_paged_prefill_attention", "pa_decode_workspace_size", "pa_prefill_workspace_size",
-                 "pa_paged_mixed_attention", "pa_paged_mixed_attention_fp8", "pa_mixed_workspace_size"):
+                 "pa_paged_mixed_attention", "pa_paged_mixed_attention_fp8", "pa_mixed_workspace_size",
+                 "pa_paged_decode_append", "pa_paged_decode_append_fp8"):
         assert want in names
 
 
@@ -197,6 +198,25 @@ def test_copy_blocks_validation(lib):
     assert f(1, 1, 1, 4, 100, 16, 1, 4, BF16, NUL) == UNSUPPORTED   # 8-byte rows
     assert f(NUL, 1, 1, 4, 100, 16, 8, 128, BF16, NUL) == INVALID
     assert f(NUL, NUL, NUL, 0, 100, 16, 8, 128, BF16, NUL) == OK    # no pairs: no-op
+
+
+def test_decode_append_validation(lib):
+    def app(kn=1, vn=1, B=2, D=128, ws=1, wsb=1 << 30):
+        return lib.pa_paged_decode_append(1, kn, vn, 1, 1, 1, 1, 0.1, 1, B, 8, 2, D, 16, 100, 8, BF16, ws, wsb, NUL)
+
+    def app8(kn=1, vn=1, new_dtype=BF16, B=2):
+        return lib.pa_paged_decode_append_fp8(1, kn, vn, 1, 1, 1, 1, 1, 1, 0.1, 1, B, 8, 2, 128, 16, 100, 8,
+                                              new_dtype, 1, 1 << 30, NUL)
+
+    assert app(kn=NUL) == INVALID
+    assert app(vn=NUL) == INVALID
+    assert app(D=96) == UNSUPPORTED
+    assert app(wsb=16) == WORKSPACE
+    assert app(kn=NUL, vn=NUL, B=0) == OK            # empty batch: no-op
+    assert app8(new_dtype=7) == UNSUPPORTED
+    assert app8(kn=NUL) == INVALID
+    assert lib.pa_paged_decode_append_fp8(1, 1, 1, 1, 1, NUL, 1, 1, 1, 0.1, 1, 2, 8, 2, 128, 16, 100, 8, BF16, 1,
+                                          1 << 30, NUL) == INVALID   # no k_scale
 
 
 def test_hbm_read_validation(lib):

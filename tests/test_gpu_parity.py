@@ -668,3 +668,95 @@ def test_check_metadata_flags_each_rule():
     s2[3] = N * P
     s2[4] = -1  # padding is fine
     assert pa.check_metadata(bt, lens, N, P, cu, s2) == (16, 1)
+
+
+# ----------------------------------------------------------------------------
+# decode with append: the step's scatter and decode in one call
+# ----------------------------------------------------------------------------
+
+def prefix_pools(c, scales=(None, None)):
+    """Pools holding only the cached prefix (positions < L - 1) of a decode case."""
+    if scales[0] is not None:
+        shape = (c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim)
+        kc = torch.full(shape, 0x7E, dtype=torch.uint8, device=DEV)
+        vc = torch.full(shape, 0x7E, dtype=torch.uint8, device=DEV)
+    else:
+        kc, vc = dev_nan_pool(c), dev_nan_pool(c)
+    kp, vp, cu_pre, lens_pre = c.prefix()
+    if len(kp):
+        slots = pa.slot_mapping(idx(c.block_table), idx(cu_pre), idx(lens_pre), c.block_size, len(kp))
+        pa.reshape_and_cache(to_dev(kp, c.dtype), to_dev(vp, c.dtype), slots, kc, vc, *scales)
+    return kc, vc
+
+
+def append_both_ways(c, q, kn, vn, bt, lens, scales=(None, None)):
+    """(out, k pool, v pool) of the slot mapping + scatter + decode calls, and
+    of one decode-with-append call, from the same prefix pools."""
+    k1, v1 = prefix_pools(c, scales)
+    slots = pa.slot_mapping(bt, idx(np.arange(c.B + 1)), lens, c.block_size, c.B)
+    pa.reshape_and_cache(kn, vn, slots, k1, v1, *scales)
+    o1 = torch.empty_like(q)
+    pa.paged_decode_attention(q, k1, v1, bt, lens, c.scale, o1, *scales)
+    k2, v2 = prefix_pools(c, scales)
+    o2 = torch.empty_like(q)
+    pa.paged_decode_append(q, kn, vn, k2, v2, bt, lens, c.scale, o2, *scales)
+    torch.cuda.synchronize()
+    return (o1, k1, v1), (o2, k2, v2)
+
+
+def same_bits(a, b):
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+@pytest.mark.parametrize("kind,G,Hkv,D,P", [("bf16", 4, 8, 128, 16), ("f32", 1, 4, 64, 7), ("bf16", 4, 2, 64, 1),
+                                            ("bf16", 8, 2, 128, 48), ("bf16", 3, 3, 64, 5), ("fp8", 4, 8, 128, 16),
+                                            ("fp8-f32", 2, 2, 64, 3), ("fp8", 5, 3, 64, 32), ("fp8", 8, 1, 128, 48)])
+def test_decode_append_equals_scatter_then_decode(kind, G, Hkv, D, P):
+    """pa_paged_decode_append writes each request's new token at position L - 1
+    and attends to it in one call: bit for bit the outputs and the pools of the
+    slot mapping, the scatter and the decode call (tiles of the new token that
+    straddle blocks, query-head groups past the first, paired heads, fp8 codes
+    quantised from bf16 or fp32 rows), and the oracle."""
+    fp8 = kind.startswith("fp8")
+    c = small(dtype="f32" if kind == "f32" else "bf16", P=P, Hq=G * Hkv, Hkv=Hkv, D=D,
+              lens=(1, 2, 16, 17, 31, 33, 255, 256, 257, 700, 1500), seed=70 + G * D + P)
+    q, bt, lens = to_dev(c.q, c.dtype), idx(c.block_table), idx(c.context_lens)
+    kn, vn = (to_dev(x, c.dtype) for x in c.new_kv())
+    if kind == "fp8-f32":  # fp32 rows that bf16 cannot hold
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(7)
+        kn = torch.randn(kn.shape, generator=gen, device=DEV, dtype=torch.float32)
+        vn = torch.randn(vn.shape, generator=gen, device=DEV, dtype=torch.float32)
+    ks, vs = fp8_scales(Hkv, 71), fp8_scales(Hkv, 72)
+    scales = (torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)) if fp8 else (None, None)
+    (o1, k1, v1), (o2, k2, v2) = append_both_ways(c, q, kn, vn, bt, lens, scales)
+    assert same_bits(k1, k2) and same_bits(v1, v2), "pools differ"
+    assert same_bits(o1, o2), "outputs differ"
+    if fp8:
+        ref = ref_decode(c.q, ref_dequantize(k2.cpu().numpy(), ks), ref_dequantize(v2.cpu().numpy(), vs),
+                         c.block_table, c.context_lens, c.scale)
+        assert_close(o2, ref, "bf16", f"append {kind} G={G} D={D} P={P}")
+    elif kind != "fp8-f32":
+        assert_close(o2, decode_ref(c), c.dtype, f"append {kind} G={G} D={D} P={P}")
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_decode_append_edge_metadata(kind):
+    """A request with no context appends nothing and gives a zero row; a new
+    token whose block id is out of range is not written (as the scatter skips
+    its slot) and is masked; a length beyond the block table appends nothing.
+    Both ways agree bit for bit on outputs and pools."""
+    fp8 = kind == "fp8"
+    c = small(P=16, Hq=8, Hkv=2, D=128, lens=(40, 300, 33, 700, 64), seed=77)
+    q, bt_np, lens_np = to_dev(c.q, c.dtype), c.block_table.copy(), c.context_lens.copy()
+    lens_np[0] = 0                         # no context
+    bt_np[2, (33 - 1) // 16] = -1          # the new token's block id is invalid
+    bt_np[4, (64 - 1) // 16] = c.num_blocks + 3
+    lens_np[3] = bt_np.shape[1] * 16 + 5   # beyond the block table
+    kn, vn = (to_dev(x, c.dtype) for x in c.new_kv())
+    scales = ((torch.from_numpy(fp8_scales(2, 73)).to(DEV), torch.from_numpy(fp8_scales(2, 74)).to(DEV))
+              if fp8 else (None, None))
+    (o1, k1, v1), (o2, k2, v2) = append_both_ways(c, q, kn, vn, idx(bt_np), idx(lens_np), scales)
+    assert same_bits(k1, k2) and same_bits(v1, v2), "pools differ"
+    assert same_bits(o1, o2), "outputs differ"
+    assert not o2[0].float().abs().sum().item()
