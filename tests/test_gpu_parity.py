@@ -760,3 +760,36 @@ def test_decode_append_edge_metadata(kind):
     assert same_bits(k1, k2) and same_bits(v1, v2), "pools differ"
     assert same_bits(o1, o2), "outputs differ"
     assert not o2[0].float().abs().sum().item()
+
+
+def test_decode_append_graph_replays():
+    """Captured in a HIP graph, every replay of the append call writes the new
+    tokens again and gives the eager result of the separate calls, with the
+    pools reset to the prefix and other eager calls between replays."""
+    c = small(P=16, lens=(5, 300, 1025, 77, 4000), seed=78)
+    q, bt, lens = to_dev(c.q, c.dtype), idx(c.block_table), idx(c.context_lens)
+    kn, vn = (to_dev(x, c.dtype) for x in c.new_kv())
+    (o1, k1, v1), _ = append_both_ways(c, q, kn, vn, bt, lens)
+    k0, v0 = prefix_pools(c)
+    k2, v2 = k0.clone(), v0.clone()
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pa.paged_decode_append(q, kn, vn, k2, v2, bt, lens, c.scale, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.paged_decode_append(q, kn, vn, k2, v2, bt, lens, c.scale, out)
+    for rep in range(3):
+        out.fill_(0)
+        k2.copy_(k0)
+        v2.copy_(v0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert same_bits(out, o1) and same_bits(k2, k1) and same_bits(v2, v1), rep
+        other = torch.empty_like(q)
+        pa.paged_decode_attention(q, k1, v1, bt, lens, c.scale, other)
+        torch.cuda.synchronize()
+        assert same_bits(other, o1), rep
