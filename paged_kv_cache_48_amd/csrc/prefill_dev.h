@@ -258,7 +258,6 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
       sc[kb][1] = mma32<kF8>(av, st.q[1][i], sc[kb][1]);
     }
   }
-  // scheduling: every K operand read first, then the products
 
   u32x4_t pop[2][2];  // [rb][k-step]: P^T operand, 8 bf16
 #pragma unroll
@@ -329,7 +328,6 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
       st.o[db][1] = mma32<kF8>(va[db][ks], pop[1][ks], st.o[db][1]);
     }
   }
-
 }
 
 template <int D, bool kF8>
