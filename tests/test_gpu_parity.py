@@ -793,3 +793,21 @@ def test_decode_append_graph_replays():
         pa.paged_decode_attention(q, k1, v1, bt, lens, c.scale, other)
         torch.cuda.synchronize()
         assert same_bits(other, o1), rep
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_decode_append_large_batch_plan_kernel_path(kind):
+    """Above 1024 requests the items come from the plan kernel: decode with
+    append still equals the separate calls bit for bit (64-dim heads, read in
+    pairs)."""
+    rng = np.random.default_rng(79)
+    lens = rng.integers(1, 700, size=1100)
+    lens[:5] = [1, 16, 256, 257, 699]
+    c = small(P=16, Hq=8, Hkv=2, D=64, lens=tuple(int(x) for x in lens), seed=79)
+    q, bt, lens_d = to_dev(c.q, c.dtype), idx(c.block_table), idx(c.context_lens)
+    kn, vn = (to_dev(x, c.dtype) for x in c.new_kv())
+    scales = ((torch.from_numpy(fp8_scales(2, 80)).to(DEV), torch.from_numpy(fp8_scales(2, 81)).to(DEV))
+              if kind == "fp8" else (None, None))
+    (o1, k1, v1), (o2, k2, v2) = append_both_ways(c, q, kn, vn, bt, lens_d, scales)
+    assert same_bits(k1, k2) and same_bits(v1, v2), "pools differ"
+    assert same_bits(o1, o2), "outputs differ"
