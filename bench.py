@@ -149,7 +149,8 @@ def cpu_baseline_decode(case, budget_s):
         "kind": "oracle",
         "sample": f"{sub.B} requests drawn from the workload's 256 ({int(sub.context_lens.sum())} cached tokens, "
                   f"one layer), {len(done) / sub.B:.0f} passes of fp64 numpy decode in {dt:.1f} s; "
-                  f"host has {os.cpu_count()} logical CPUs",
+                  f"host has {os.cpu_count()} logical CPUs, {len(os.sched_getaffinity(0))} allowed to this process, "
+                  f"BLAS threads {threads}",
     }
 
 
