@@ -148,9 +148,10 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm)
 }
 
 // fp8 pools with append: making the new token's codes would take the kernel
-// just past 168 VGPRs, from three waves per SIMD to two; it is held to three.
-template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend>
-__global__ __launch_bounds__(256, 3) void decode_partition_kernel_w3(DecodeParams prm) {
+// just past 168 VGPRs (three waves per SIMD to two), or for 128-dim heads read
+// in pairs just past 256 (two to one); it is held to kWaves waves per SIMD.
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend, int kWaves>
+__global__ __launch_bounds__(256, kWaves) void decode_partition_kernel_wb(DecodeParams prm) {
   partition_body<T, D, kWide, kAligned, NR, HP, kAppend>(prm);
 }
 
@@ -163,14 +164,15 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
   constexpr unsigned lds_bytes = Geo<T, D>::LDS_PER_WAVE * wpb + (unsigned)sizeof(PlanLds);
   // exactly the blocks that can be resident at once: every wave starts on its
   // first item immediately, and none waits for a slot while holding one
-  constexpr bool kW3 = kAppend && Geo<T, D>::kFp8;
+  constexpr bool kWb = kAppend && Geo<T, D>::kFp8;
+  constexpr int kWaves = D <= 128 ? 3 : 2;
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
     hipError_t e;
-    if constexpr (kW3)
+    if constexpr (kWb)
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &nb, decode_partition_kernel_w3<T, D, kWide, kAligned, NR, HP, kAppend>, 64 * wpb, lds_bytes);
+          &nb, decode_partition_kernel_wb<T, D, kWide, kAligned, NR, HP, kAppend, kWaves>, 64 * wpb, lds_bytes);
     else
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &nb, decode_partition_kernel<T, D, kWide, kAligned, NR, HP, kAppend>, 64 * wpb, lds_bytes);
@@ -183,8 +185,8 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
     const hipError_t e = hipEventRecord(ev0, stream);
     if (e != hipSuccess) return e;
   }
-  if constexpr (kW3)
-    hipLaunchKernelGGL((decode_partition_kernel_w3<T, D, kWide, kAligned, NR, HP, kAppend>), dim3(blocks),
+  if constexpr (kWb)
+    hipLaunchKernelGGL((decode_partition_kernel_wb<T, D, kWide, kAligned, NR, HP, kAppend, kWaves>), dim3(blocks),
                        dim3(64 * wpb), lds_bytes, stream, prm);
   else
     hipLaunchKernelGGL((decode_partition_kernel<T, D, kWide, kAligned, NR, HP, kAppend>), dim3(blocks),
@@ -224,6 +226,8 @@ hipError_t launch_kinds(const AttnArgs& a, const DecodeParams& prm, bool fp8, bo
                         int64_t pool_bytes, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int B = a.num_seqs;
   if (fp8) {  // bf16 q and out
+    if (a.head_dim == 128 && pairs)
+      return launch_sized<fp8_e4m3, 256, 2, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
     if (a.head_dim == 128)
       return launch_sized<fp8_e4m3, 128, 1, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
     if (pairs) return launch_sized<fp8_e4m3, 128, 2, kAppend>(prm, B, max_items, pool_bytes, stream, ev0, ev1);
@@ -266,10 +270,10 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.G = a.num_q_heads / a.num_kv_heads;
   prm.n_hg = (prm.G + 3) / 4;
   const bool fp8 = a.kv_dtype == kFP8E4M3;
-  // bf16 and fp8 pools with 64-dim heads: adjacent KV heads are read in
-  // pairs, as one 128-dim head (the row width the 128-dim kernels read);
-  // each query column keeps its own head's half
-  const bool pairs = (fp8 || a.dtype == kBF16) && a.head_dim == 64 && a.num_kv_heads % 2 == 0;
+  // bf16 pools with 64-dim heads and fp8 pools: adjacent KV heads are read in
+  // pairs, as one head of twice the dimension (256-byte token rows, as the
+  // bf16 128-dim kernel reads); each query column keeps its own head's half
+  const bool pairs = (fp8 || (a.dtype == kBF16 && a.head_dim == 64)) && a.num_kv_heads % 2 == 0;
   prm.Hkv = pairs ? a.num_kv_heads / 2 : a.num_kv_heads;
   prm.P = a.block_size;
   prm.p_shift = (a.block_size & (a.block_size - 1)) == 0 ? __builtin_ctz((unsigned)a.block_size) : -1;

@@ -229,12 +229,13 @@ __device__ __forceinline__ void load_ids(const DecodeParams& prm, const Item& it
 
 // Q^T operand: column n = query head of the group (heads past the group's
 // last read head 0's row; their columns are never stored).
-// HP = 2 (64-dim heads taken in pairs of adjacent KV heads, read as one
-// 128-dim head): columns 0..3 are the group's query heads of the first KV
-// head of the pair, columns 4..7 those of the second.  Each column's query
-// is its own head's 64 dimensions, in both halves of the operand: the score
-// products over dimensions 0..63 and 64..127 go to separate accumulators,
-// and each column keeps the one of its own head.
+// HP = 2 (adjacent KV heads taken in pairs, read as one head of dimension D:
+// 64-dim bf16 or fp8 heads as D = 128, 128-dim fp8 heads as D = 256): columns
+// 0..3 are the group's query heads of the first KV head of the pair, columns
+// 4..7 those of the second.  Each column's query is its own head's D / 2
+// dimensions, in both halves of the operand: the score products over the
+// first and the second half go to separate accumulators, and each column
+// keeps the one of its own head.
 template <typename T, int D, int HP>
 __device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, u32x4_t (&qv)[Geo<T, D>::NQV]) {
   using Gm = Geo<T, D>;
@@ -242,7 +243,7 @@ __device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, 
   const int lane = lane_id();
   const int n = lane & 15, g = lane >> 4;
   if constexpr (HP == 2) {
-    static_assert(Gm::kHalf && D == 128, "head pairs: bf16 or fp8 pools, two 64-dim heads");
+    static_assert(Gm::kHalf && (D == 128 || (Gm::kFp8 && D == 256)), "head pairs");
     const int hi = (n >> 2) & 1, c = n & 3;
     const bool col = n < 8 && c < it.nh;
     const int h = (2 * it.hkv + hi) * prm.G + it.hg * 4 + (col ? c : 0);
@@ -729,7 +730,7 @@ __device__ __forceinline__ void append_regs(const DecodeParams& prm, const PoolV
 }
 
 // fp8 pools: after the last tile is staged, the new token's codes are made
-// here, four per lane (lanes 0-31 K, 32-63 V), and written over its staged K
+// here, four per lane and word (lanes 0-31 K, 32-63 V), and written over its staged K
 // and V rows (unless the token was zeroed: invalid block id) and, by items of
 // query-head group 0, to its slot.  Each code is x / scale[h], correctly
 // rounded, then encoded, as the fp8 scatter makes it.
@@ -745,7 +746,10 @@ __device__ __forceinline__ void append_lds(const DecodeParams& prm, const PoolVi
   const int qL = tL / Gm::TPL, jL = tL - qL * Gm::TPL;
   const bool tok_ok = ((__builtin_amdgcn_readlane((int)ok, qL * Gm::CPR) >> jL) & 1) != 0;
   const bool isv = lane >= 32;
-  const int w = lane & 31;
+  static_assert(W <= 64, "at most two words per lane");
+#pragma unroll
+  for (int w2 = 0; w2 < (W + 31) / 32; ++w2) {  // (two for 256-code slices)
+  const int w = (lane & 31) + 32 * w2;
   const bool act = w < W;
   const int e = 4 * (act ? w : 0);  // code index within the slice
   const int h = HP == 2 ? 2 * it.hkv + (e >= D / 2 ? 1 : 0) : it.hkv;
@@ -768,14 +772,16 @@ __device__ __forceinline__ void append_lds(const DecodeParams& prm, const PoolVi
 #pragma unroll
   for (int j = 0; j < 4; ++j) code |= e4m3_from_f32(x[j] / sc) << (8 * j);
   if (act && tok_ok) *reinterpret_cast<uint32_t*>(lds + (isv ? Gm::KBYTES : 0) + tL * Gm::KST + e) = code;
-  if (it.hg != 0) return;
-  const int pos = it.L - 1;
-  const int lb = pos / prm.P, off = pos - lb * prm.P;
-  const int blk = lane_id_lookup<NR>(ids, lb - it.blk0);
-  if (act && blk >= 0 && blk < prm.N) {
-    const uint64_t a = ((uint64_t)blk * (uint64_t)prm.P + (uint64_t)off) * pv.row_bytes +
-                       (uint64_t)(it.hkv * Gm::GROWB + e);
-    *reinterpret_cast<uint32_t*>(const_cast<char*>(isv ? pv.v : pv.k) + a) = code;
+  if (it.hg == 0) {
+    const int pos = it.L - 1;
+    const int lb = pos / prm.P, off = pos - lb * prm.P;
+    const int blk = lane_id_lookup<NR>(ids, lb - it.blk0);
+    if (act && blk >= 0 && blk < prm.N) {
+      const uint64_t a = ((uint64_t)blk * (uint64_t)prm.P + (uint64_t)off) * pv.row_bytes +
+                         (uint64_t)(it.hkv * Gm::GROWB + e);
+      *reinterpret_cast<uint32_t*>(const_cast<char*>(isv ? pv.v : pv.k) + a) = code;
+    }
+  }
   }
 }
 
@@ -919,7 +925,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
     }
 
     // ---- S^T = K Q^T, per 16-token half of the tile ----
-    // (HP = 2: dimensions 0..63 accumulate in s, 64..127 in s2)
+    // (HP = 2: the first D / 2 dimensions accumulate in s, the others in s2)
     constexpr int NH = Gm::TT / 16;
     constexpr int NQ1 = Gm::NQ / HP;
     f32x4_t s[NH], s2[NH];
@@ -1053,7 +1059,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
 
     // ---- item done: total of l over the four 16-lane rows; store head n ----
     // (HP = 2: column n's head is the pair's first or second, and its outputs
-    // are rows 0..63 or 64..127 of the 128-dim O^T)
+    // are the first or the second half of the rows of O^T)
     constexpr int DH = D / HP, NDBH = NDB / HP;
     l = sum_over_rows(l);
     f32x4_t ov[NDBH];
