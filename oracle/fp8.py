@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/paged_attention.py``).
 
 The pages only name the feature: ember, "Deliberately out of scope (for now)",
 lists paged KV quantisation (fp8/int8) as a next step.  Everything below is
-this build's reading, stated here and in the design doc:
+a reading of that one line (format, scales, rounding):
 
 * format: OCP 8-bit floating point, E4M3 with the "fn" encoding (1 sign bit,
   4 exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is

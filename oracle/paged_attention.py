@@ -23,7 +23,7 @@ What it computes, and where that comes from (page title, then section):
   ``softmax(scale * q K^T) V`` directly, in fp64.
 * weft, "Shapes and symbols": ``H_q / H_kv`` is the GQA group size ``G``.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 
 * slot encoding: ``slot = physical_block * P + offset`` indexes the flattened
   ``[N * P]`` token rows of the pool;
