@@ -88,6 +88,54 @@ def test_slot_mapping_chunk_over_prefix():
 
 
 # ----------------------------------------------------------------------------
+# bf16 -> fp64 conversion (the first step of every bf16 oracle result)
+# ----------------------------------------------------------------------------
+
+def _same_fp64(a, b):
+    """Equal as values, NaN where either is NaN, and zeros with the same sign."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nan = np.isnan(a)
+    return (np.array_equal(nan, np.isnan(b)) and np.array_equal(a[~nan], b[~nan])
+            and np.array_equal(np.signbit(a[~nan]), np.signbit(b[~nan])))
+
+
+ALL_BF16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+
+
+def test_widen_matches_torch_on_every_bf16_pattern():
+    import torch
+
+    want = torch.from_numpy(ALL_BF16.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    assert _same_fp64(widen(ALL_BF16), want)
+
+
+def test_widen_matches_field_decoder_on_every_bf16_pattern():
+    from oracle.brute_force import bf16_value
+
+    assert _same_fp64(widen(ALL_BF16), [bf16_value(int(b)) for b in ALL_BF16])
+
+
+def test_widen_hand_constants():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F80, 0xFF80, 0x7F7F, 0x0080, 0x0001,
+                     0x3EAB, 0x4049], dtype=np.uint16)
+    want = [1.0, -2.0, 0.0, -0.0, math.inf, -math.inf, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -126,
+            2.0 ** -133, (1 + 0x2B / 128) * 2.0 ** -2, (1 + 0x49 / 128) * 2.0]
+    assert _same_fp64(widen(bits), want)
+    assert np.all(np.isnan(widen(np.array([0x7FC0, 0x7F81, 0xFFFF], dtype=np.uint16))))
+    f = np.array([1.5, -0.0, 3.0e38, 1e-45], dtype=np.float32)
+    assert _same_fp64(widen(f), [1.5, -0.0, float(np.float32(3.0e38)), float(np.float32(1e-45))])
+
+
+def test_widen_pin_catches_a_wrong_width():
+    # shifting the uint16 left by 16 without first widening wraps to zero
+    wrong = (ALL_BF16 << np.uint16(16)).astype(np.uint32).view(np.float32).astype(np.float64)
+    from oracle.brute_force import bf16_value
+
+    assert not _same_fp64(wrong, [bf16_value(int(b)) for b in ALL_BF16])
+
+
+# ----------------------------------------------------------------------------
 # scatter
 # ----------------------------------------------------------------------------
 
