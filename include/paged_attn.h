@@ -71,7 +71,10 @@ const char* pa_last_error(void);
  * at position p = context_lens[b] - T_b + i and gets
  *     slot_mapping[cu_seqlens[b] + i] = block_table[b][p / P] * P + p % P,
  * the row index into the flattened [N * P] token rows of the pool.  Positions
- * outside [0, max_blocks_per_seq * P) get slot -1.
+ * outside [0, max_blocks_per_seq * P), negative block ids and slots beyond
+ * 2^31 - 1 get slot -1; a block id at or past num_blocks gives a slot at or
+ * past num_blocks * P.  pa_reshape_and_cache skips both, so such a token is
+ * stored nowhere, as in pa_paged_decode_append.
  *   block_table  int32 [num_seqs, max_blocks_per_seq]
  *   cu_seqlens   int32 [num_seqs + 1], non-decreasing, cu_seqlens[0] = 0,
  *                cu_seqlens[num_seqs] = num_tokens

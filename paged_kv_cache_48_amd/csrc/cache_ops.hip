@@ -28,10 +28,15 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
   const int b = lo;
   const int64_t T = (int64_t)cu[b + 1] - cu[b];
   const int64_t pos = (int64_t)lens[b] - T + (t - cu[b]);
+  // A negative block id, or one whose slot does not fit in int32, gives -1;
+  // any other id at or past the pool's end gives a slot >= N * P (pools are
+  // limited to N * P <= 2^31 - 1), which the scatter skips.  Either way the
+  // token lands in no block, as in the decode-with-append call.
   int32_t slot = -1;
   if (pos >= 0 && pos < (int64_t)max_blocks * block_size) {
     const int64_t blk = block_table[(int64_t)b * max_blocks + pos / block_size];
-    slot = (int32_t)(blk * block_size + pos % block_size);
+    const int64_t s = blk * block_size + pos % block_size;
+    if (blk >= 0 && s <= (int64_t)INT32_MAX) slot = (int32_t)s;
   }
   slots[t] = slot;
 }

@@ -100,18 +100,28 @@ def test_decode_config_shapes_reduced(cfg):
     assert_close(d.decode(), decode_ref(c), c.dtype, f"config {cfg} shape")
 
 
-def test_decode_llama3_8b_full_size_sampled():
-    """Full Llama-3-8B-shaped batch (B=256, log-normal lengths, 90% pool) in the
-    launch configuration the benchmark times; the oracle checks 12 requests."""
-    c = config_case(3)
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_decode_config_full_size(cfg):
+    """The seeded batch of the GPT-2-124M (B=64), Llama-3.2-1B (B=128) and
+    Llama-3-8B (B=256, 90% pool) workloads at full size, one layer (every layer
+    has the same shape), in the launch configuration the benchmark times: every
+    row of the decode call against the oracle, and decode with append equal bit
+    for bit to the slot mapping, the scatter and the decode call, outputs and
+    pools."""
+    c = config_case(cfg)
+    print(f"config {c.name}: B={c.B} N={c.num_blocks} sum L={int(c.context_lens.sum())}", flush=True)
     d = DevCase(c)
     out = d.decode()
-    order = np.argsort(c.context_lens)
-    rng = np.random.default_rng(123)
-    pick = sorted(set([int(order[0]), int(order[1]), int(order[-1]), int(order[-2])]
-                      + rng.choice(c.B, 8, replace=False).tolist()))
-    ref = decode_ref(c, select=pick)
-    assert_close(out, ref, "bf16", "llama3_8b", rows=pick)
+    ref = decode_ref(c)
+    assert_close(out, ref, c.dtype, f"{c.name} decode")
+    del d
+    kn, vn = (to_dev(x, c.dtype) for x in c.new_kv())
+    q, bt, lens = to_dev(c.q, c.dtype), idx(c.block_table), idx(c.context_lens)
+    (o1, k1, v1), (o2, k2, v2) = append_both_ways(c, q, kn, vn, bt, lens)
+    assert same_bits(k1, k2) and same_bits(v1, v2), "pools differ"
+    assert same_bits(o1, o2), "outputs differ"
+    assert same_bits(o1, out), "decode of the same pools differs"
+    assert_close(o2, ref, c.dtype, f"{c.name} decode with append")
 
 
 @pytest.mark.parametrize("G,Hkv,D,dtype", [(1, 12, 64, "f32"), (1, 4, 128, "bf16"), (3, 2, 64, "bf16"),
@@ -760,6 +770,34 @@ def test_decode_append_edge_metadata(kind):
     assert same_bits(k1, k2) and same_bits(v1, v2), "pools differ"
     assert same_bits(o1, o2), "outputs differ"
     assert not o2[0].float().abs().sum().item()
+
+
+@pytest.mark.parametrize("bad", [1 << 28, -(1 << 28), (1 << 31) - 1, -(1 << 31)])
+def test_slot_mapping_huge_block_ids_store_nothing(bad):
+    """A block id far outside the pool (whose slot would wrap in int32) gives a
+    slot the scatter skips, so the new token lands in no block: the separate
+    calls and decode with append leave the same pools, and both equal the
+    prefix pools with only the valid requests' tokens written."""
+    c = small(P=16, Hq=8, Hkv=2, D=128, lens=(40, 300, 33, 17), seed=82)
+    bt_np = c.block_table.copy()
+    for b in (1, 3):
+        bt_np[b, (int(c.context_lens[b]) - 1) // 16] = bad
+    bt, lens = idx(bt_np), idx(c.context_lens)
+    slots = pa.slot_mapping(bt, idx(np.arange(c.B + 1)), lens, 16, c.B).cpu().numpy().astype(np.int64)
+    N = c.num_blocks
+    for b in (1, 3):
+        assert slots[b] < 0 or slots[b] >= N * 16, (b, slots[b])
+    q = to_dev(c.q, c.dtype)
+    kn, vn = (to_dev(x, c.dtype) for x in c.new_kv())
+    (o1, k1, v1), (o2, k2, v2) = append_both_ways(c, q, kn, vn, bt, lens)
+    assert same_bits(k1, k2) and same_bits(v1, v2), "pools differ"
+    assert same_bits(o1, o2), "outputs differ"
+    k3, v3 = prefix_pools(c)
+    good = ref_slot_mapping(c.block_table, np.arange(c.B + 1), c.context_lens, 16)
+    good[[1, 3]] = -1
+    pa.reshape_and_cache(kn, vn, idx(good), k3, v3)
+    torch.cuda.synchronize()
+    assert same_bits(k1, k3) and same_bits(v1, v3), "a token with an invalid block id was stored"
 
 
 def test_decode_append_graph_replays():
