@@ -177,16 +177,33 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
-# one workspace per (device, stream): calls on one stream run in order, so
-# they can share it; calls on different streams must not.
+# One cached workspace per (device, stream): calls on one stream run in order,
+# so they can share it; calls on different streams must not.  A workspace may
+# be baked into a captured HIP graph (torch.cuda.graph), so a cached workspace
+# is never freed: when a call needs more, a larger one (rounded up to a power
+# of two, so at most a few dozen ever exist) replaces it in the cache and the
+# old one stays alive in ``_retired`` until the process ends.  Graphs that
+# were captured on one stream share that stream's workspace and must not be
+# replayed concurrently; a caller that needs otherwise passes ``workspace=``.
 _workspaces: dict = {}
+_retired: list = []
 
 
-def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+def _workspace(device: torch.device, stream: int, nbytes: int, given: torch.Tensor | None = None) -> torch.Tensor:
+    if given is not None:
+        _dev_tensor(given, "workspace", torch.uint8)
+        _req(given.device == device, "workspace must be on the call's device")
+        _req(given.numel() >= nbytes, f"workspace holds {given.numel()} bytes, the call needs {nbytes}")
+        return given
     key = (device.index, stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        size = 256
+        while size < nbytes:
+            size *= 2
+        if ws is not None:
+            _retired.append(ws)
+        ws = torch.empty(size, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -349,10 +366,13 @@ def _attn_common(q, k_cache, v_cache, block_table, context_lens, out):
 def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                            out: torch.Tensor, k_scale: torch.Tensor | None = None,
-                           v_scale: torch.Tensor | None = None) -> torch.Tensor:
+                           v_scale: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Decode attention: ``q``/``out`` ``[B, H_q, D]``; see ``pa_paged_decode_attention``.
     uint8 pools hold fp8 (OCP E4M3) codes with per-KV-head scales
-    (``pa_paged_decode_attention_fp8``; q and out bfloat16)."""
+    (``pa_paged_decode_attention_fp8``; q and out bfloat16).
+    ``workspace``, if given, is a caller-owned uint8 device tensor at least the
+    call's workspace size; otherwise the stream's cached workspace is used."""
     lib = load_library()
     B = _attn_common(q, k_cache, v_cache, block_table, context_lens, out)
     _req(q.shape[0] == B, "q must have one row per sequence")
@@ -361,7 +381,7 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     M = block_table.shape[1]
     stream = _stream(q)
     need = decode_workspace_size(B, Hq, D, P, M)
-    ws = _workspace(q.device, stream, need)
+    ws = _workspace(q.device, stream, need, workspace)
     if k_cache.dtype == torch.uint8:
         _scales(k_scale, v_scale, Hkv, k_cache.device)
         _check(lib.pa_paged_decode_attention_fp8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -379,12 +399,15 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
 def paged_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
                         v_cache: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                         out: torch.Tensor, k_scale: torch.Tensor | None = None,
-                        v_scale: torch.Tensor | None = None) -> torch.Tensor:
+                        v_scale: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
     """One decode step in one call: the new tokens ``k_new``/``v_new``
     ``[B, H_kv, D]`` are written at positions ``context_lens - 1`` and attended
     to, as ``reshape_and_cache`` + ``paged_decode_attention`` would (see
     ``pa_paged_decode_append``).  uint8 pools hold fp8 (OCP E4M3) codes: the new
-    rows (float32 or bfloat16) are quantised with the per-KV-head scales."""
+    rows (float32 or bfloat16) are quantised with the per-KV-head scales.
+    ``workspace``, if given, is a caller-owned uint8 device tensor at least the
+    call's workspace size; otherwise the stream's cached workspace is used."""
     lib = load_library()
     B = _attn_common(q, k_cache, v_cache, block_table, context_lens, out)
     _req(q.shape[0] == B, "q must have one row per sequence")
@@ -396,7 +419,7 @@ def paged_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tenso
     Hq = q.shape[1]
     M = block_table.shape[1]
     stream = _stream(q)
-    ws = _workspace(q.device, stream, decode_workspace_size(B, Hq, D, P, M))
+    ws = _workspace(q.device, stream, decode_workspace_size(B, Hq, D, P, M), workspace)
     if k_cache.dtype == torch.uint8:
         _scales(k_scale, v_scale, Hkv, k_cache.device)
         _check(lib.pa_paged_decode_append_fp8(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
@@ -416,10 +439,13 @@ def paged_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tenso
 def paged_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                             block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                             out: torch.Tensor, k_scale: torch.Tensor | None = None,
-                            v_scale: torch.Tensor | None = None) -> torch.Tensor:
+                            v_scale: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Varlen / chunked prefill: ``q``/``out`` ``[T_total, H_q, D]``; ``k``, ``v`` are the
     paged pools; see ``pa_paged_prefill_attention``.  uint8 pools hold fp8
-    (OCP E4M3) codes with per-KV-head scales (``pa_paged_prefill_attention_fp8``)."""
+    (OCP E4M3) codes with per-KV-head scales (``pa_paged_prefill_attention_fp8``).
+    ``workspace``, if given, is a caller-owned uint8 device tensor at least the
+    call's workspace size; otherwise the stream's cached workspace is used."""
     lib = load_library()
     B = _attn_common(q, k, v, block_table, context_lens, out)
     _dev_tensor(cu_seqlens, "cu_seqlens", torch.int32, 1)
@@ -429,7 +455,7 @@ def paged_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, c
     M = block_table.shape[1]
     stream = _stream(q)
     need = prefill_workspace_size(B, T, Hq, Hkv)
-    ws = _workspace(q.device, stream, need)
+    ws = _workspace(q.device, stream, need, workspace)
     if k.dtype == torch.uint8:
         _scales(k_scale, v_scale, Hkv, k.device)
         _check(lib.pa_paged_prefill_attention_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_scale.data_ptr(),
@@ -447,11 +473,14 @@ def paged_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, c
 def paged_mixed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                           block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                           out: torch.Tensor, k_scale: torch.Tensor | None = None,
-                          v_scale: torch.Tensor | None = None) -> torch.Tensor:
+                          v_scale: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None) -> torch.Tensor:
     """One step's ragged mix of decodes (one-token chunks) and prefill chunks in one
     persistent launch; same arguments and result as ``paged_prefill_attention``
     (see ``pa_paged_mixed_attention``).  uint8 pools hold fp8 (OCP E4M3) codes
-    with per-KV-head scales (``pa_paged_mixed_attention_fp8``)."""
+    with per-KV-head scales (``pa_paged_mixed_attention_fp8``).
+    ``workspace``, if given, is a caller-owned uint8 device tensor at least the
+    call's workspace size; otherwise the stream's cached workspace is used."""
     lib = load_library()
     B = _attn_common(q, k, v, block_table, context_lens, out)
     _dev_tensor(cu_seqlens, "cu_seqlens", torch.int32, 1)
@@ -460,7 +489,7 @@ def paged_mixed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_
     T, Hq, _ = q.shape
     M = block_table.shape[1]
     stream = _stream(q)
-    ws = _workspace(q.device, stream, mixed_workspace_size(B, Hq, D, P, M))
+    ws = _workspace(q.device, stream, mixed_workspace_size(B, Hq, D, P, M), workspace)
     if k.dtype == torch.uint8:
         _scales(k_scale, v_scale, Hkv, k.device)
         _check(lib.pa_paged_mixed_attention_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), k_scale.data_ptr(),

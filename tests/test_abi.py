@@ -237,3 +237,32 @@ def test_check_metadata_validation(lib):
     assert f(1, 1, NUL, NUL, 2, 0, 10, 0, 4, 1, NUL) == INVALID
     assert f(1, 1, NUL, NUL, 2, 0, 10, 16, 4, NUL, NUL) == INVALID   # no result buffer
     assert f(NUL, 1, NUL, NUL, 2, 0, 10, 16, 4, 1, NUL) == INVALID
+
+
+def test_workspace_cache_never_frees_a_workspace():
+    """A cached workspace may be baked into a captured graph, so growing the
+    cache keeps the old tensor alive; sizes are powers of two, and a call that
+    fits reuses the cached tensor."""
+    import torch
+
+    dev = torch.device("cpu")
+    key = (dev.index, 12345)
+    saved_ws, saved_ret = dict(pa._workspaces), list(pa._retired)
+    try:
+        pa._workspaces.pop(key, None)
+        a = pa._workspace(dev, 12345, 1000)
+        assert a.numel() == 1024
+        assert pa._workspace(dev, 12345, 1024).data_ptr() == a.data_ptr()
+        n_ret = len(pa._retired)
+        b = pa._workspace(dev, 12345, 5000)
+        assert b.numel() == 8192 and b.data_ptr() != a.data_ptr()
+        assert pa._retired[n_ret] is a, "the replaced workspace must stay alive"
+        assert pa._workspace(dev, 12345, 100).data_ptr() == b.data_ptr()
+        assert pa._workspace(dev, 54321, 100).data_ptr() != b.data_ptr(), "streams must not share"
+        with pytest.raises(ValueError):
+            pa._workspace(dev, 12345, 100, given=torch.empty(100, dtype=torch.uint8))  # not a device tensor
+    finally:
+        pa._workspaces.clear()
+        pa._workspaces.update(saved_ws)
+        pa._retired[:] = saved_ret
+

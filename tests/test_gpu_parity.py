@@ -315,6 +315,44 @@ def test_decode_graph_replays_match_eager():
         assert np.array_equal(to_host_bits(d2.decode()), ref2), rep
 
 
+def test_graphs_of_two_sizes_on_one_pool_replay_correctly():
+    """Two graphs captured on one memory pool, the small batch first: the
+    larger batch's capture replaces the cached workspace, and the smaller
+    graph's workspace must stay allocated, so that a third capture on the same
+    pool cannot take its memory.  Replays of all three, interleaved, keep
+    both outputs equal to the eager results and the third graph's tensor
+    intact."""
+    ca = small(P=16, lens=(5, 300, 77), seed=30)
+    cb = small(P=16, lens=tuple(range(200, 8200, 50)), seed=31)
+    da, db = DevCase(ca), DevCase(cb)
+    ref_a, ref_b = to_host_bits(da.decode()), to_host_bits(db.decode())
+    out_a, out_b = torch.empty_like(da.q), torch.empty_like(db.q)
+    need_a = pa.decode_workspace_size(ca.B, ca.num_q_heads, ca.head_dim, 16, ca.max_blocks_per_seq)
+    need_b = pa.decode_workspace_size(cb.B, cb.num_q_heads, cb.head_dim, 16, cb.max_blocks_per_seq)
+    assert need_b > 2 * need_a
+    torch.cuda.synchronize()
+    pool = torch.cuda.graph_pool_handle()
+    ga, gb, gc = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga, pool=pool):
+        pa.paged_decode_attention(da.q, da.kc, da.vc, da.bt, da.lens, ca.scale, out_a)
+    with torch.cuda.graph(gb, pool=pool):
+        pa.paged_decode_attention(db.q, db.kc, db.vc, db.bt, db.lens, cb.scale, out_b)
+    with torch.cuda.graph(gc, pool=pool):
+        x = torch.full((need_a,), 7, dtype=torch.uint8, device=DEV)
+    for rep in range(3):
+        out_a.fill_(0)
+        out_b.fill_(0)
+        gc.replay()
+        ga.replay()
+        gb.replay()
+        ga.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(out_a), ref_a), rep
+        assert np.array_equal(to_host_bits(out_b), ref_b), rep
+        assert bool((x == 7).all()), rep
+        assert np.array_equal(to_host_bits(da.decode()), ref_a), rep
+
+
 def _scale_bf16(bits: np.ndarray, pow2: int) -> np.ndarray:
     """bf16 bits times 2**pow2 (exact while in range)."""
     f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** pow2)
