@@ -255,6 +255,31 @@ int pa_paged_decode_attention(const void* q, const void* k_cache, const void* v_
                               int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_paged_decode_attention_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc): pa_paged_decode_attention with the same arguments but no
+ * workspace, giving the same result bit for bit.  Its workspace is a static
+ * device array of PA_NOALLOC_SCRATCH_BYTES bytes inside the library, of which
+ * each GPU the call runs on holds one copy until the process ends.  The call
+ * allocates nothing.
+ *   Batches whose pa_decode_workspace_size() exceeds PA_NOALLOC_SCRATCH_BYTES
+ *   return PA_ERR_WORKSPACE before any HIP call (160 MiB holds, e.g., 256
+ *   requests of up to 8192 tokens with 32 query heads of 128 dims).
+ *   Every call on one GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (other streams, concurrent graph replays) race and must not be
+ *   made.  The array needs no clearing between calls.
+ *   The first call on a device resolves the array's address there (with that
+ *   device current) and keeps it; later calls reuse it.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (160u << 20)
+int pa_paged_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* context_lens,
+                                      float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
+                                      void* stream);
+
 /* Bytes of workspace pa_paged_prefill_attention needs for these shapes. */
 size_t pa_prefill_workspace_size(int32_t num_seqs, int64_t total_q_tokens,
                                  int32_t num_q_heads, int32_t num_kv_heads);

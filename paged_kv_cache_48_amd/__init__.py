@@ -34,6 +34,7 @@ __all__ = [
     "hbm_read",
     "paged_decode_attention",
     "paged_decode_append",
+    "paged_decode_attention_noalloc",
     "paged_prefill_attention",
     "paged_mixed_attention",
     "decode_workspace_size",
@@ -87,6 +88,11 @@ SIGNATURES = {
         ctypes.c_int,
         [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
          _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _c_void_p, _size, _c_void_p],
+    ),
+    "pa_paged_decode_attention_noalloc": (
+        ctypes.c_int,
+        [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+         _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _c_void_p],
     ),
     "pa_paged_decode_append": (
         ctypes.c_int,
@@ -393,6 +399,25 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                                          block_table.data_ptr(), context_lens.data_ptr(), float(scale),
                                          out.data_ptr(), B, Hq, Hkv, D, P, N, M, _dtype_code(q),
                                          ws.data_ptr(), ws.numel(), stream))
+    return out
+
+
+def paged_decode_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                                   out: torch.Tensor) -> torch.Tensor:
+    """``paged_decode_attention`` for callers that cannot allocate: the
+    workspace is the library's static device array (see
+    ``pa_paged_decode_attention_noalloc``), so this call allocates no device
+    memory.  float32 or bfloat16 pools.  Calls that may overlap on one GPU race."""
+    lib = load_library()
+    B = _attn_common(q, k_cache, v_cache, block_table, context_lens, out)
+    _req(q.shape[0] == B, "q must have one row per sequence")
+    _req(k_cache.dtype != torch.uint8, "the allocation-free call takes float32 or bfloat16 pools")
+    N, P, Hkv, D = k_cache.shape
+    _check(lib.pa_paged_decode_attention_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                                 block_table.data_ptr(), context_lens.data_ptr(), float(scale),
+                                                 out.data_ptr(), B, q.shape[1], Hkv, D, P, N, block_table.shape[1],
+                                                 _dtype_code(q), _stream(q)))
     return out
 
 

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <climits>
+#include <mutex>
 #include <string>
 
 #include "../../include/paged_attn.h"
@@ -475,3 +476,70 @@ int pa_paged_mixed_attention_fp8(const void* q, const void* k, const void* v, co
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode attention for callers that cannot allocate (code under HIP graph
+// capture, serving loops that forbid hipMalloc).  The decode workspace lives
+// in a file-scope device array; each device holds its own copy until the
+// process ends.  Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, resolved once per device
+// with that device current, and is what the kernels receive.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (the stream's device).
+int scratch_address(const char* fn, hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  PA_REQUIRE(dev >= 0 && dev < kMaxDevices, PA_ERR_UNSUPPORTED, "%s: device %d beyond the first %d", fn, dev,
+             kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, fn);
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess) return hip_status(e, fn);
+    if (es != hipSuccess) return hip_status(es, fn);
+    PA_REQUIRE(p != nullptr, PA_ERR_HIP, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int pa_paged_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                                 const int32_t* block_table, const int32_t* context_lens, float scale,
+                                                 void* out, int32_t num_seqs, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                 int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
+                                                 void* stream) {
+  g_err.clear();
+  const char* fn = "pa_paged_decode_attention_noalloc";
+  int st = check_attn(fn, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, dtype);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  const size_t need = pa::decode_workspace_size(num_seqs, num_q_heads, head_dim, block_size, max_blocks_per_seq);
+  PA_REQUIRE(need <= (size_t)PA_NOALLOC_SCRATCH_BYTES, PA_ERR_WORKSPACE,
+             "%s: this batch needs %zu bytes of workspace, beyond the %zu-byte static scratch (use "
+             "pa_paged_decode_attention with a workspace of that size)",
+             fn, need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_address(fn, static_cast<hipStream_t>(stream), &ws);
+  if (st != PA_OK) return st;
+  return decode_call(fn, q, k_cache, v_cache, nullptr, nullptr, block_table, context_lens, scale, out, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, dtype, dtype,
+                     ws, (size_t)PA_NOALLOC_SCRATCH_BYTES, stream);
+}

@@ -266,3 +266,23 @@ def test_workspace_cache_never_frees_a_workspace():
         pa._workspaces.update(saved_ws)
         pa._retired[:] = saved_ret
 
+
+def test_decode_noalloc_validation(lib):
+    """Shapes are checked, and a batch whose workspace exceeds the static
+    scratch is refused, before any HIP call."""
+    f = lib.pa_paged_decode_attention_noalloc
+    args = dict(q=1, k=1, v=1, bt=1, lens=1, scale=0.1, out=1, B=4, Hq=32, Hkv=8, D=128, P=16, N=100, M=512,
+                dtype=BF16, stream=NUL)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["scale"], a["out"], a["B"], a["Hq"], a["Hkv"],
+                 a["D"], a["P"], a["N"], a["M"], a["dtype"], a["stream"])
+
+    assert call(B=0) == OK
+    assert call(Hq=30) == INVALID
+    assert call(D=96) == UNSUPPORTED
+    assert call(B=1024) == WORKSPACE
+    assert b"static scratch" in lib.pa_last_error()
+    assert lib.pa_decode_workspace_size(1024, 32, 128, 16, 512) > (160 << 20)
+    assert lib.pa_decode_workspace_size(256, 32, 128, 16, 512) <= (160 << 20)
