@@ -1,21 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention hot path on one MI355X.
 
-Default workload: Llama-3-8B-shaped decode at large batch (32 layers, H_q=32,
+Headline workload: Llama-3-8B-shaped decode at large batch (32 layers, H_q=32,
 H_kv=8, D=128, block size 16, B=256, log-normal context lengths with median
 1024 and sigma 1, clipped to [16, 8192], pool at 90% occupancy), bf16.
 
-One step = one decode step of the whole model's attention:
-    slot mapping of the 256 new tokens, then for each of the 32 layers
-    reshape_and_cache (scatter the new K/V) + paged_decode_attention.
-Every layer owns its pool, queries and outputs, so no layer's data is still in
-the 256 MB Infinity Cache when it is read.
+One step = one decode step of the whole model's attention: for each of the 32
+layers, one decode-with-append call, which writes the 256 new tokens' K/V to
+the layer's pool and computes decode attention over it (bit for bit the
+scatter followed by the decode call).  Every layer owns its pool, queries and
+outputs, so no layer's data is still in the 256 MB Infinity Cache when it is
+read.  The same run also times the step as separate calls (slot mapping, then
+per layer reshape_and_cache and paged_decode_attention) and attention alone.
 
 Prints ONE JSON line.  ``value`` is the algorithmic HBM bytes of the step
-(KV read by decode + q/out + block table + lengths + scatter bytes) divided by
+(KV read by decode + q/out + block table + lengths + the new rows) divided by
 the step time, in GB/s.  ``roofline`` reports the decode partition kernel alone
 (its average duration from HIP events recorded around it inside the timed
 region).  ``cpu_baseline`` times the fp64 oracle on a bounded sample.
+
+The default run (``--workload all``) also measures every other seeded workload
+and adds them under ``workloads``: tiny (fp32), GPT-2-124M, Llama-3.2-1B, the
+Llama-3-8B batch with fp8 pools, and the mixed chunked-prefill + decode step
+(as prefill and decode calls, and as one mixed call).  Each entry gives KV
+GB/s, us per layer-step (p10/p50/p90), decode tokens/s, the roofline fraction
+of its dominant kernel and the oracle's time on the host cores.
 """
 
 from __future__ import annotations
@@ -48,9 +57,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["llama3_8b", "llama3_8b_fp8", "mixed", "mixed_fp8", "mixed_single",
-                                           "mixed_single_fp8", "cow", "copy"],
-                    default="llama3_8b")
+    ap.add_argument("--workload", choices=["all", "llama3_8b", "llama3_8b_fp8", "tiny", "gpt2_124m", "llama32_1b",
+                                           "mixed", "mixed_fp8", "mixed_single", "mixed_single_fp8", "cow", "copy"],
+                    default="all")
     ap.add_argument("--layers", type=int, default=None, help="profile runs only: fewer layers")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -112,46 +121,105 @@ def traffic_from_profiles(files, key: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline_decode(case, budget_s):
-    """The oracle (fp64 numpy) on a sample of the workload's requests, taken in a
-    fixed random order until the time budget is spent; GB/s of algorithmic
-    decode bytes.  The sample's pool is built beforehand (untimed)."""
-    from oracle import ref_decode, ref_reshape_and_cache, ref_slot_mapping
-    from workloads import make_case, nan_pool
-
+def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    order = np.random.default_rng(0).permutation(case.B)[:64]
+        return os.cpu_count() or 1
+
+
+def host_line() -> str:
+    return (f"host has {os.cpu_count()} logical CPUs, {len(os.sched_getaffinity(0))} allowed to this process, "
+            f"BLAS threads {blas_threads()}")
+
+
+def cpu_baseline_decode(case, budget_s, fp8=False):
+    """The oracle (fp64 numpy) on a sample of the workload's requests, taken in a
+    fixed random order until the time budget is spent; GB/s of algorithmic
+    decode bytes, and the whole batch's layer-step time at that rate.  The
+    sample's pool is built beforehand (untimed); fp8 pools are quantised with
+    the oracle's encoder and dequantised once, also untimed, so the timed work
+    is attention over the dequantised values."""
+    from oracle import ref_decode, ref_dequantize, ref_reshape_and_cache, ref_slot_mapping
+    from workloads import draw_values, make_case, nan_pool
+
+    threads = blas_threads()
+    order = np.random.default_rng(0).permutation(case.B)[:16 if fp8 else 64]
     sub = make_case(name="cpu_sample", dtype=case.dtype, block_size=case.block_size,
                     num_q_heads=case.num_q_heads, num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
-                    context_lens=case.context_lens[order], seed=0)
-    kc = nan_pool(sub.num_blocks, sub.block_size, sub.num_kv_heads, sub.head_dim, sub.dtype)
-    vc = kc.copy()
-    slots = ref_slot_mapping(sub.block_table, sub.cu_ctx, sub.context_lens, sub.block_size)
-    kc, vc = ref_reshape_and_cache(sub.k_tok, sub.v_tok, slots, kc, vc)
+                    context_lens=case.context_lens[order], seed=0, values=not fp8)
+    if fp8:  # random finite E4M3 codes, as the GPU benchmark's pools hold
+        rng = np.random.default_rng(7)
+        q = draw_values(rng, (sub.B, sub.num_q_heads, sub.head_dim), "bf16")
+        shape = (sub.num_blocks, sub.block_size, sub.num_kv_heads, sub.head_dim)
+        sc = np.full(sub.num_kv_heads, 0.02, dtype=np.float32)
+        pools = []
+        for _ in range(2):
+            codes = rng.integers(0, 256, size=shape, dtype=np.uint8)
+            codes[(codes & 0x7F) == 0x7F] -= 1
+            pools.append(ref_dequantize(codes, sc))
+        kc, vc = pools
+    else:
+        q = sub.q
+        slots = ref_slot_mapping(sub.block_table, sub.cu_ctx, sub.context_lens, sub.block_size)
+        kc = nan_pool(sub.num_blocks, sub.block_size, sub.num_kv_heads, sub.head_dim, sub.dtype)
+        vc = kc.copy()
+        kc, vc = ref_reshape_and_cache(sub.k_tok, sub.v_tok, slots, kc, vc)
     done = []
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:  # repeat passes over the sample until the budget is spent
         for i in range(sub.B):
-            ref_decode(sub.q, kc, vc, sub.block_table, sub.context_lens, sub.scale, select=[i])
+            ref_decode(q, kc, vc, sub.block_table, sub.context_lens, sub.scale, select=[i])
             done.append(i)
     dt = time.perf_counter() - t0
+    s_kv = 1 if fp8 else 2
     lens_done = sub.context_lens[done]
-    nbytes = decode_bytes(lens_done, case.block_size, case.num_q_heads, case.num_kv_heads, case.head_dim, 2)
+    nbytes = decode_bytes(lens_done, case.block_size, case.num_q_heads, case.num_kv_heads, case.head_dim, 2, s_kv)
+    full = decode_bytes(case.context_lens, case.block_size, case.num_q_heads, case.num_kv_heads, case.head_dim, 2,
+                        s_kv)
+    rate = nbytes / dt
     return {
-        "value": round(nbytes / dt / 1e9, 4),
+        "value": round(rate / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{sub.B} requests drawn from the workload's 256 ({int(sub.context_lens.sum())} cached tokens, "
-                  f"one layer), {len(done) / sub.B:.0f} passes of fp64 numpy decode in {dt:.1f} s; "
-                  f"host has {os.cpu_count()} logical CPUs, {len(os.sched_getaffinity(0))} allowed to this process, "
-                  f"BLAS threads {threads}",
+        "us_per_layer_step": round(full / rate * 1e6, 1),
+        "sample": f"{sub.B} requests drawn from the workload's {case.B} ({int(sub.context_lens.sum())} cached tokens, "
+                  f"one layer{', fp8 pools dequantised beforehand' if fp8 else ''}), {len(done) / sub.B:.1f} passes "
+                  f"of fp64 numpy decode in {dt:.1f} s; the whole batch's layer-step time is extrapolated at that "
+                  f"rate; {host_line()}",
     }
+
+
+def cpu_baseline_config(idx, repeats=3):
+    """The oracle (fp64 numpy ``ref_decode``) on one whole layer-step of seeded
+    workload ``idx`` (every layer has the same shape), median of ``repeats``;
+    the pool is written beforehand by the oracle's own slot math and scatter
+    (untimed)."""
+    from oracle import ref_decode, ref_reshape_and_cache, ref_slot_mapping
+    from workloads import config_case, nan_pool
+
+    case = config_case(idx)
+    kc = nan_pool(case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim, case.dtype)
+    vc = kc.copy()
+    kp, vp, cu_pre, lens_pre = case.prefix()
+    if len(kp):
+        kc, vc = ref_reshape_and_cache(kp, vp, ref_slot_mapping(case.block_table, cu_pre, lens_pre,
+                                                                 case.block_size), kc, vc)
+    kn, vn = case.new_kv()
+    kc, vc = ref_reshape_and_cache(kn, vn, ref_slot_mapping(case.block_table, case.cu_seqlens, case.context_lens,
+                                                             case.block_size), kc, vc)
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        ref_decode(case.q, kc, vc, case.block_table, case.context_lens, case.scale)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"us_per_layer_step": round(t * 1e6, 1), "cores": blas_threads(), "kind": "oracle",
+            "sample": f"the whole batch ({case.B} requests, one layer), median of {repeats} runs of fp64 numpy "
+                      f"decode ({', '.join(f'{x:.3f}' for x in times)} s); {host_line()}"}
 
 
 def cpu_baseline_mixed(case, budget_s, npf=16):
@@ -234,7 +302,141 @@ def hbm_read_ceiling(pa, dev, reps=10, nbytes=4 << 30):
             "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4), "bytes": nbytes, "workgroups": best[1]}
 
 
-def bench_decode(args):
+def graph_step_ms(step, reps, per_graph=1):
+    """Per-step times (ms) from HIP-graph replays of ``per_graph`` consecutive
+    steps, with an event between consecutive replays: the host launches one
+    graph per replay, so short steps are not stretched by per-call host work."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            step()
+    for _ in range(3):
+        g.replay()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    marks[0].record()
+    for k in range(reps):
+        g.replay()
+        marks[k + 1].record()
+    torch.cuda.synchronize()
+    return np.array([marks[k].elapsed_time(marks[k + 1]) / per_graph for k in range(reps)])
+
+
+def eager_step_ms(step, reps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    marks[0].record()
+    for k in range(reps):
+        step()
+        marks[k + 1].record()
+    torch.cuda.synchronize()
+    return np.array([marks[k].elapsed_time(marks[k + 1]) for k in range(reps)])
+
+
+def guarded_kernel_ms(pa, call, reps, dev):
+    """Average duration (ms) of the partition kernel of ``call(layer)``, from the
+    events the library records around it.  Each call follows a read-only stream
+    over 1 GiB (about 150 us of GPU work, which also evicts the Infinity
+    Cache), so that the host has enqueued the call before the GPU reaches it;
+    on an idle stream the start event would also count the host's launch time."""
+    gbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for k in range(reps):
+        pa.hbm_read(gbuf, sink, 512)
+        with pa.kernel_timer(*evs[k]):
+            call(k)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+SMALL_DECODE = {"tiny": 0, "gpt2_124m": 1, "llama32_1b": 2}
+
+
+def bench_decode_small(args, name):
+    """Decode step of a smaller seeded workload (tiny, GPT-2-124M, Llama-3.2-1B):
+    per layer one decode-with-append call, every layer with its own pool.  Steps
+    take tens of microseconds per layer, less than the host needs to issue a
+    call from Python, so the step is timed as HIP-graph replays (the eager time
+    is reported beside it).  The partition kernel's own duration comes from the
+    guarded event loop."""
+    import paged_kv_cache_48_amd as pa
+    from workloads import config_case
+
+    idx = SMALL_DECODE[name]
+    case = config_case(idx, values=False)
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, D, P, N = case.B, case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size, case.num_blocks
+    L = case.num_layers
+    tdt = torch.float32 if case.dtype == "f32" else torch.bfloat16
+    s = 4 if case.dtype == "f32" else 2
+    gen = torch.Generator(device=dev)
+    bt = torch.as_tensor(case.block_table, device=dev)
+    lens = torch.as_tensor(case.context_lens, device=dev)
+    layers = []
+    for layer in range(L):
+        gen.manual_seed(2000 + 100 * idx + layer)
+        kc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=tdt)
+        vc = torch.randn((N, P, Hkv, D), generator=gen, device=dev, dtype=tdt)
+        q = torch.randn((B, Hq, D), generator=gen, device=dev, dtype=tdt)
+        kn = torch.randn((B, Hkv, D), generator=gen, device=dev, dtype=tdt)
+        vn = torch.randn((B, Hkv, D), generator=gen, device=dev, dtype=tdt)
+        layers.append((kc, vc, q, kn, vn, torch.empty_like(q)))
+    scale = case.scale
+
+    def call(i):
+        kc, vc, q, kn, vn, out = layers[i % L]
+        pa.paged_decode_append(q, kn, vn, kc, vc, bt, lens, scale, out)
+
+    def step():
+        for i in range(L):
+            call(i)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    per_graph = max(1, 12 // L)  # at least 12 layer-calls per replay
+    g_ms = graph_step_ms(step, args.steps, per_graph)
+    e_ms = eager_step_ms(step, args.steps)
+    kern_ms = guarded_kernel_ms(pa, call, max(args.steps, 2 * L), dev)
+    dec_b = decode_bytes(case.context_lens, P, Hq, Hkv, D, s)
+    step_bytes = L * (dec_b + scatter_bytes(B, Hkv, D, s))
+    kern_b = dec_b + append_bytes(B, Hkv, D, s)
+    ms = float(np.median(g_ms))
+    achieved = kern_b / (kern_ms * 1e-3) / 1e9
+    log(f"{name}: {1e3 * ms / L:.2f} us/layer-step (graph), {1e3 * float(np.median(e_ms)) / L:.2f} (eager), "
+        f"partition kernel {kern_ms * 1e3:.2f} us")
+    return {
+        "config": f"{name}: {L} layer(s) x paged decode with append, B={B}, H_q={Hq}, H_kv={Hkv}, D={D}, P={P}, "
+                  f"N={N} blocks/layer, {case.dtype}, sum L = {int(case.context_lens.sum())}",
+        "layers": L,
+        "dtype": case.dtype,
+        "timing": f"HIP-graph replays of {per_graph} step(s), {args.steps} replays",
+        "kv_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "us_per_layer_step_p10_p50_p90": [round(float(x), 2) for x in np.percentile(1e3 * g_ms / L, [10, 50, 90])],
+        "eager_us_per_layer_step_p50": round(1e3 * float(np.median(e_ms)) / L, 2),
+        "decode_tokens_per_s": round(B / (ms * 1e-3), 1),
+        "roofline_tokens_per_s": round(B / (step_bytes / (HBM_PEAK_GBS * 1e9)), 1),
+        "roofline": {"kernel": f"decode_partition_kernel<{case.dtype},{D}> (decode with append)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": kern_b,
+                     "avg_launch_us": round(kern_ms * 1e3, 2),
+                     "timing": "library events around the kernel, each launch after a 1 GiB read-only stream"},
+    }
+
+
+def bench_decode(args, ceiling_run=True):
     import paged_kv_cache_48_amd as pa
     from workloads import config_case
 
@@ -346,8 +548,9 @@ def bench_decode(args):
     sep_ms = np.array([smarks[k].elapsed_time(smarks[k + 1]) for k in range(args.steps)])
     log(f"as separate calls: {float(np.mean(sep_ms)):.3f} ms/step")
 
-    ceiling = hbm_read_ceiling(pa, dev)
-    log(f"HBM read ceiling: {ceiling['gbs']} GB/s ({ceiling['workgroups']} workgroups)")
+    ceiling = hbm_read_ceiling(pa, dev) if ceiling_run else None
+    if ceiling:
+        log(f"HBM read ceiling: {ceiling['gbs']} GB/s ({ceiling['workgroups']} workgroups)")
 
     dec_b = decode_bytes(case.context_lens, P, Hq, Hkv, D, s, s_kv)
     sc_b = scatter_bytes(B, Hkv, D, s, s_kv)
@@ -401,8 +604,9 @@ def bench_decode(args):
             "algorithmic_bytes_per_launch": kern_b,
             "avg_launch_us": round(kern_avg_ms * 1e3, 2),
         },
-        "hbm_read_ceiling": dict(ceiling, decode_frac_of_ceiling=round(achieved / ceiling["gbs"], 4)),
     }
+    if ceiling:
+        res["hbm_read_ceiling"] = dict(ceiling, decode_frac_of_ceiling=round(achieved / ceiling["gbs"], 4))
     return res, case
 
 
@@ -743,6 +947,74 @@ def summarize_profiles(d):
     log("profiles written")
 
 
+def decode_summary(res):
+    """The ``workloads`` entry of a Llama-3-8B-shaped decode result."""
+    keys = ("pct_hbm_peak", "us_per_layer_step_p10_p50_p90", "attention_only_us_per_layer_step_p10_p50_p90",
+            "separate_calls_us_per_layer_step_p10_p50_p90", "decode_tokens_per_s", "roofline_tokens_per_s",
+            "roofline", "cpu_baseline")
+    out = {"config": res["config"]["workload"], "layers": res["config"]["layers"], "dtype": res["dtype"],
+           "timing": f"eager calls, {res['steps']} steps", "kv_gbs": res["value"]}
+    out.update({k: res[k] for k in keys if k in res})
+    return out
+
+
+def mixed_summary(res):
+    out = {"config": res["config"]["workload"], "ms_per_step": res["value"], "roofline": res["roofline"],
+           "cpu_baseline": res.get("cpu_baseline")}
+    if res.get("cpu_baseline"):
+        out["oracle_ms_per_step"] = res["cpu_baseline"]["value"]
+    return out
+
+
+def with_oracle_speedup(entry):
+    cb = entry.get("cpu_baseline") or {}
+    if "us_per_layer_step" in cb and "us_per_layer_step_p10_p50_p90" in entry:
+        entry["oracle_us_per_layer_step"] = cb["us_per_layer_step"]
+        entry["gpu_speedup_vs_oracle"] = round(cb["us_per_layer_step"] / entry["us_per_layer_step_p10_p50_p90"][1], 1)
+    return entry
+
+
+def free_gpu():
+    import gc
+
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def run_all(args):
+    """The headline decode step, then every other seeded workload as extra keys."""
+    sub = lambda **kw: argparse.Namespace(**dict(vars(args), **kw))  # noqa: E731
+    res, case = bench_decode(sub(workload="llama3_8b"))
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_decode(case, args.cpu_seconds)
+    free_gpu()
+    wl = {"llama3_8b": with_oracle_speedup(decode_summary(res))}
+    for name in SMALL_DECODE:
+        entry = bench_decode_small(args, name)
+        free_gpu()
+        if not args.no_cpu_baseline:
+            log(f"timing the oracle on {name}")
+            entry["cpu_baseline"] = cpu_baseline_config(SMALL_DECODE[name])
+        wl[name] = with_oracle_speedup(entry)
+    r8, c8 = bench_decode(sub(workload="llama3_8b_fp8"), ceiling_run=False)
+    free_gpu()
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the fp8 batch")
+        r8["cpu_baseline"] = cpu_baseline_decode(c8, args.cpu_seconds / 2, fp8=True)
+    wl["llama3_8b_fp8"] = with_oracle_speedup(decode_summary(r8))
+    rm, _ = bench_mixed(sub(workload="mixed", block_size=16))
+    free_gpu()
+    wl["mixed"] = mixed_summary(rm)
+    rs, cs = bench_mixed(sub(workload="mixed_single", block_size=16))
+    free_gpu()
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the mixed step")
+        rs["cpu_baseline"] = cpu_baseline_mixed(cs, args.cpu_seconds / 2)
+    wl["mixed_single"] = mixed_summary(rs)
+    res["workloads"] = wl
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_profiles:
@@ -758,10 +1030,16 @@ def main():
     import paged_kv_cache_48_amd as pa
 
     pa.load_library()
-    if args.workload == "copy":
+    if args.workload == "all":
+        res = run_all(args)
+    elif args.workload == "copy":
         res = bench_copy(args)
     elif args.workload == "cow":
         res = bench_cow(args)
+    elif args.workload in SMALL_DECODE:
+        res = bench_decode_small(args, args.workload)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_config(SMALL_DECODE[args.workload])
     elif args.workload.startswith("mixed"):
         res, case = bench_mixed(args)
         if args.no_cpu_baseline or args.workload != "mixed_single":
@@ -771,11 +1049,11 @@ def main():
             res["cpu_baseline"] = cpu_baseline_mixed(case, args.cpu_seconds)
     else:
         res, case = bench_decode(args)
-        if args.no_cpu_baseline or args.workload != "llama3_8b":
+        if args.no_cpu_baseline:
             res["cpu_baseline"] = None
         else:
             log("timing the oracle on the host")
-            res["cpu_baseline"] = cpu_baseline_decode(case, args.cpu_seconds)
+            res["cpu_baseline"] = cpu_baseline_decode(case, args.cpu_seconds, fp8=args.workload.endswith("_fp8"))
     print(json.dumps(res), flush=True)
 
 
