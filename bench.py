@@ -91,13 +91,6 @@ def append_bytes(B, Hkv, D, s, s_kv=None):
     return int(2 * B * Hkv * D * (s + s_kv))
 
 
-# sources the decode partition kernel is compiled from
-DECODE_SOURCES = ("decode.hip", "decode_dev.h", "common.h")
-# the partition kernel of the benchmark's decode-with-append call (bf16 pools
-# under 4 GiB, P a multiple of 16), as rocprofv3 names it
-BENCH_DECODE_KERNEL = "decode_partition_kernel<unsigned short, 128, false, true, 1, 1, true>"
-
-
 def sources_sha(files) -> str:
     h = hashlib.sha256()
     for name in files:
@@ -558,7 +551,7 @@ def bench_decode(args, ceiling_run=True):
     value = step_bytes / (ms_step * 1e-3) / 1e9
     kern_b = dec_b + append_bytes(B, Hkv, D, s, s_kv)  # the launch also reads and writes the new rows
     achieved = kern_b / (kern_avg_ms * 1e-3) / 1e9
-    traffic = None if fp8 else traffic_from_profiles(DECODE_SOURCES, "decode_partition_llama3_8b")
+    traffic = traffic_from_profiles(DECODE_SOURCES, "decode_llama3_8b_fp8" if fp8 else "decode_llama3_8b")
     res = {
         "metric": ("paged decode attn (fp8 e4m3 KV) KV GB/s (% HBM peak) + us/layer-step + tokens/s, Llama-3-8B shape"
                    if fp8 else "paged decode attn KV GB/s (% HBM peak) + us/layer-step, Llama-3-8B shape"),
@@ -802,25 +795,68 @@ def bench_copy(args):
 
 
 # ---------------------------------------------------------------------------
-# Profile summaries.  The GPU runs that feed them (each writes CSVs under DIR):
-PROFILE_RUNS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_decode -o decode -- "
-             "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
-    "trace_mixed": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_mixed -o mixed -- "
-                   "python3 bench.py --workload mixed --steps 10 --warmup 2",
-    "trace_mixsingle": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_mixsingle -o mixsingle -- "
-                       "python3 bench.py --workload mixed_single --steps 10 --warmup 2",
-    "trace_cow": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_cow -o cow -- "
-                 "python3 bench.py --workload cow --steps 20 --warmup 3",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch -o fetch -- "
-             "python3 bench.py --layers 2 --steps 2 --warmup 1 --no-cpu-baseline",
-    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write -o write -- "
-             "python3 bench.py --layers 2 --steps 2 --warmup 1 --no-cpu-baseline",
-    "copyf": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_copyf -o copyf -- "
-             "python3 bench.py --workload copy --steps 3 --warmup 1",
-    "copyw": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_copyw -o copyw -- "
-             "python3 bench.py --workload copy --steps 3 --warmup 1",
+# Profile summaries.  Each GPU run below writes CSVs under DIR (run from the
+# repository root); ``--summarize-profiles DIR`` turns them into profiles/.
+B_CMD = "python3 bench.py --no-cpu-baseline --workload "
+# kernel statistics: key -> (workload, steps, description)
+TRACES = {
+    "decode_llama3_8b": ("llama3_8b", 10, "Llama-3-8B-shaped decode step: 32 layers x paged decode with append "
+                         "(partition kernel with in-kernel plan and the new token's write, then the merge), B=256, "
+                         "H_q=32, H_kv=8, D=128, P=16, bf16; the same run times the step as separate calls (slot "
+                         "mapping, reshape_and_cache, decode without append) and attention alone."),
+    "decode_llama3_8b_fp8": ("llama3_8b_fp8", 10, "The same Llama-3-8B-shaped decode step over fp8 (OCP E4M3) pools "
+                             "with per-KV-head scales; adjacent KV heads read in pairs."),
+    "decode_gpt2_124m": ("gpt2_124m", 20, "GPT-2-124M-shaped decode step: 12 layers x paged decode with append, "
+                         "B=64, H_q=H_kv=12, D=64 (KV heads read in pairs), P=16, N=4096, bf16; graph replays, eager "
+                         "steps, then the guarded per-kernel loop."),
+    "decode_llama32_1b": ("llama32_1b", 20, "Llama-3.2-1B-shaped decode step: 16 layers x paged decode with append, "
+                          "B=128, H_q=32, H_kv=8, D=64 (KV heads read in pairs), P=16, bf16; graph replays, eager "
+                          "steps, then the guarded per-kernel loop."),
+    "decode_tiny": ("tiny", 20, "Tiny decode step: 1 layer, paged decode with append, B=4, H_q=H_kv=12, D=64, P=16, "
+                    "N=64, fp32 (launch-latency bound)."),
+    "prefill_mixed": ("mixed", 10, "Mixed chunked-prefill + decode step as two calls: 16 prefill chunks over cached "
+                      "prefixes (paged_prefill_attention) and 48 decodes (paged_decode_attention), after the slot "
+                      "mapping and the scatter of all new tokens; Llama-3-8B heads, P=16, bf16."),
+    "mixed_single_launch": ("mixed_single", 10, "The same mixed step as one single-launch mixed call over the whole "
+                            "ragged batch (64 requests: 16 prefill chunks + 48 one-token decodes), then the merge of "
+                            "the decodes' partitions."),
+    "copy_blocks_cow": ("cow", 20, "Copy-on-write block copies: pa_copy_blocks with 4096 (src, dst) pairs of 32 KiB "
+                        "blocks per pool (P=16, H_kv=8, D=128, bf16), K and V: 512 MiB moved per launch."),
 }
+# HBM traffic (FETCH_SIZE, WRITE_SIZE per dispatch): key -> (workload, kernel name pattern)
+TRAFFIC = {
+    "decode_llama3_8b": ("llama3_8b", "decode_partition_kernel<unsigned short, 128, false, true, 1, 1, true>"),
+    "decode_llama3_8b_fp8": ("llama3_8b_fp8", "fp8_e4m3, 256, false, true, 1, 2, true"),
+}
+# prefill counters, two passes (each within one pass's counter limits)
+PREFILL_PMC = {
+    "a": "MfmaUtil VALUBusy LdsBankConflict SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES SQ_WAVE_CYCLES",
+    "b": "SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_ANY SQ_INSTS_LDS "
+         "SQ_INSTS_VALU SQ_INSTS_MFMA",
+}
+PREFILL_SOURCES = ("prefill.hip", "prefill_dev.h", "common.h")
+# sources the decode partition kernel is compiled from
+DECODE_SOURCES = ("decode.hip", "decode_dev.h", "common.h")
+
+
+def profile_commands():
+    cmds = {}
+    for key, (wl, steps, _) in TRACES.items():
+        cmds[f"trace_{key}"] = (f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace_{key} -o {key} -- "
+                                f"{B_CMD}{wl} --steps {steps} --warmup 2")
+    for key, (wl, _) in TRAFFIC.items():
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            tag = c.split("_")[0].lower()
+            cmds[f"{tag}_{key}"] = (f"rocprofv3 --pmc {c} --output-format csv -d DIR/{tag}_{key} -o {tag}_{key} -- "
+                                    f"{B_CMD}{wl} --layers 2 --steps 2 --warmup 1")
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        tag = c.split("_")[0].lower()
+        cmds[f"{tag}_copy"] = (f"rocprofv3 --pmc {c} --output-format csv -d DIR/{tag}_copy -o {tag}_copy -- "
+                               f"{B_CMD}copy --steps 3 --warmup 1")
+    for p, ctr in PREFILL_PMC.items():
+        cmds[f"pmc_prefill_{p}"] = (f"rocprofv3 --pmc {ctr} --output-format csv -d DIR/pmc_prefill_{p} -o "
+                                    f"pmc_prefill_{p} -- {B_CMD}mixed --steps 2 --warmup 1")
+    return cmds
 
 
 def _short_kernel(name):
@@ -840,14 +876,21 @@ def _stats_table(path, top=8):
     return out, rows
 
 
-def _counter_mean(path, kernel_substr, counter):
-    """Mean over dispatches of one counter (KiB per dispatch) for the kernels
-    whose name contains kernel_substr."""
+def _counter_means(path, kernel_substr):
+    """Mean over dispatches of every counter for the kernels whose name contains
+    kernel_substr: {counter: (mean, dispatches)}."""
+    import collections
     import csv
 
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
-            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
-    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+    vals = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if kernel_substr in r["Kernel_Name"].replace("pa::", ""):
+            vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def _sha_line(files):
+    return f"kernel sources ({', '.join(files)}) sha256: {sources_sha(files)}"
 
 
 def summarize_profiles(d):
@@ -855,96 +898,112 @@ def summarize_profiles(d):
 
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
-    sha = sources_sha(DECODE_SOURCES)
-    sha_line = f"decode kernel sources ({', '.join(DECODE_SOURCES)}) sha256: {sha}"
+    cmds = profile_commands()
     one = lambda pat: (glob.glob(os.path.join(d, pat)) or [None])[0]  # noqa: E731
-
-    stats = one("prof_decode/*kernel_stats.csv")
-    if stats:
+    for key, (wl, _, desc) in TRACES.items():
+        stats = one(f"trace_{key}/*kernel_stats.csv")
+        if not stats:
+            continue
         table, _ = _stats_table(stats)
-        with open(os.path.join(prof, "decode_llama3_8b_kernel_stats.txt"), "w") as f:
-            f.write("Llama-3-8B-shaped decode step (32 layers x paged decode with append: partition kernel with\n"
-                    "in-kernel plan and the new token's write, reduce), B=256, H_q=32, H_kv=8, D=128, P=16, bf16;\n"
-                    "the same run also times the step as separate calls (slot mapping, reshape_and_cache, decode\n"
-                    "without append) and an attention-only sweep.  rocprofv3 kernel statistics.\n")
-            f.write("command (run from the repository root, DIR = an output folder):\n  "
-                    + PROFILE_RUNS["trace"] + "\n")
-            f.write(sha_line + "\n\n")
+        srcs = PREFILL_SOURCES if key == "prefill_mixed" else DECODE_SOURCES
+        with open(os.path.join(prof, f"{key}_kernel_stats.txt"), "w") as f:
+            f.write(desc + "\nrocprofv3 kernel statistics.\n")
+            f.write("command (run from the repository root, DIR = an output folder):\n  " + cmds[f"trace_{key}"] + "\n")
+            f.write(_sha_line(srcs) + "\n\n")
             f.write("\n".join(table) + "\n")
-    stats = one("prof_mixed/*kernel_stats.csv")
-    if stats:
-        table, _ = _stats_table(stats)
-        with open(os.path.join(prof, "prefill_mixed_kernel_stats.txt"), "w") as f:
-            f.write("Mixed chunked-prefill + decode step (16 prefill chunks over cached prefixes + 48 decodes,\n"
-                    "Llama-3-8B heads, P=16, bf16), rocprofv3 kernel statistics.\n")
-            f.write("command (run from the repository root, DIR = an output folder):\n  "
-                    + PROFILE_RUNS["trace_mixed"] + "\n\n")
-            f.write("\n".join(table) + "\n")
+        log(f"profiles/{key}_kernel_stats.txt written")
 
-    stats = one("prof_mixsingle/*kernel_stats.csv")
-    if stats:
-        table, _ = _stats_table(stats)
-        with open(os.path.join(prof, "mixed_single_launch_kernel_stats.txt"), "w") as f:
-            f.write("The same mixed step as one single-launch mixed call over the whole ragged batch (64 requests:\n"
-                    "16 prefill chunks + 48 one-token decodes, Llama-3-8B heads, P=16, bf16), then the merge of the\n"
-                    "decodes' partitions, rocprofv3 kernel statistics.\n")
-            f.write("command (run from the repository root, DIR = an output folder):\n  "
-                    + PROFILE_RUNS["trace_mixsingle"] + "\n\n")
-            f.write("\n".join(table) + "\n")
+    # prefill counters
+    pa_csv, pb_csv = one("pmc_prefill_a/*counter_collection.csv"), one("pmc_prefill_b/*counter_collection.csv")
+    if pa_csv and pb_csv:
+        a = _counter_means(pa_csv, "prefill_kernel")
+        b = _counter_means(pb_csv, "prefill_kernel")
+        from workloads import config_case
 
-    stats = one("prof_cow/*kernel_stats.csv")
-    if stats:
-        table, _ = _stats_table(stats)
-        with open(os.path.join(prof, "copy_blocks_cow_kernel_stats.txt"), "w") as f:
-            f.write("Copy-on-write block copies: pa_copy_blocks with 4096 (src, dst) pairs of 32 KiB blocks per pool\n"
-                    "(P=16, H_kv=8, D=128, bf16), K and V: 512 MiB moved per launch, rocprofv3 kernel statistics.\n")
-            f.write("command (run from the repository root, DIR = an output folder):\n  "
-                    + PROFILE_RUNS["trace_cow"] + "\n\n")
-            f.write("\n".join(table) + "\n")
+        case = config_case(4, values=False)
+        Tb = case.query_lens[:16].astype(np.int64)
+        Lb = case.context_lens[:16].astype(np.int64)
+        D, Hq = case.head_dim, case.num_q_heads
+        alg = int(np.sum(4 * D * Hq * (Tb * (Lb - Tb) + Tb * (Tb + 1) // 2)))
+        g = lambda m, k: m[k][0] if k in m else float("nan")  # noqa: E731
+        mops = g(a, "SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+        wave = g(a, "SQ_WAVE_CYCLES")
+        lines = [
+            "Counters of prefill_kernel<128> on the mixed step's 16 prefill chunks (sum T = "
+            f"{int(Tb.sum())}, Llama-3-8B heads, P=16, bf16), mean per dispatch.",
+            "commands (run from the repository root, DIR = an output folder):",
+            "  " + cmds["pmc_prefill_a"], "  " + cmds["pmc_prefill_b"],
+            _sha_line(PREFILL_SOURCES), "",
+            f"MfmaUtil        {g(a, 'MfmaUtil'):8.2f} %   MFMA busy cycles / (GPU active cycles x 1024 SIMDs)",
+            f"VALUBusy        {g(a, 'VALUBusy'):8.2f} %   VALU instruction cycles / (GPU active cycles x 256 CUs)",
+            f"LdsBankConflict {g(a, 'LdsBankConflict'):8.4f}     bank-conflict cycles per LDS access cycle",
+            f"bf16 MFMA flops executed {mops:.4e} (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) against {alg:.4e} algorithmic "
+            f"(causal half only): {mops / alg:.3f}x",
+            "",
+            "fractions of wave-resident cycles (SQ_WAVE_CYCLES):",
+        ]
+        for k in ("SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS"):
+            lines.append(f"  {k:<22} {g(b, k) / wave:8.4f}")
+        lines.append("instructions per dispatch:")
+        for k in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS"):
+            lines.append(f"  {k:<22} {g(b, k):.4e}")
+        lines.append("raw means: " + ", ".join(f"{k}={v[0]:.6g}" for k, v in sorted({**a, **b}.items())))
+        with open(os.path.join(prof, "prefill_mixed_counters.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log("profiles/prefill_mixed_counters.txt written")
 
-    fetch_kib, nf = _counter_mean(one("pmc_fetch/*counter_collection.csv"), BENCH_DECODE_KERNEL, "FETCH_SIZE") \
-        if one("pmc_fetch/*counter_collection.csv") else (None, 0)
-    write_kib, nw = _counter_mean(one("pmc_write/*counter_collection.csv"), BENCH_DECODE_KERNEL, "WRITE_SIZE") \
-        if one("pmc_write/*counter_collection.csv") else (None, 0)
-    cf_kib, _ = _counter_mean(one("pmc_copyf/*counter_collection.csv"), "copyBuffer", "FETCH_SIZE") \
-        if one("pmc_copyf/*counter_collection.csv") else (None, 0)
-    cw_kib, _ = _counter_mean(one("pmc_copyw/*counter_collection.csv"), "copyBuffer", "WRITE_SIZE") \
-        if one("pmc_copyw/*counter_collection.csv") else (None, 0)
-    if None in (fetch_kib, write_kib, cf_kib, cw_kib):
-        log("counter CSVs incomplete; traffic summary not written")
+    # HBM traffic of the decode partition kernels
+    cf, cw = one("fetch_copy/*counter_collection.csv"), one("write_copy/*counter_collection.csv")
+    if not (cf and cw):
+        log("copy calibration CSVs missing; traffic summaries not written")
         return
+    cf_kib = _counter_means(cf, "copyBuffer").get("FETCH_SIZE", (None, 0))[0]
+    cw_kib = _counter_means(cw, "copyBuffer").get("WRITE_SIZE", (None, 0))[0]
     gib = float(1 << 30)
     kf, kw = gib / (cf_kib * 1024), gib / (cw_kib * 1024)  # true bytes per counted byte
-    fetch_b, write_b = fetch_kib * 1024 * kf, write_kib * 1024 * kw
     from workloads import config_case
 
     case = config_case(3, values=False)
-    alg = (decode_bytes(case.context_lens, case.block_size, case.num_q_heads, case.num_kv_heads, case.head_dim, 2)
-           + append_bytes(case.B, case.num_kv_heads, case.head_dim, 2))
-    lines = [
-        "HBM traffic of decode_partition_kernel<bf16, 128> with append on the Llama-3-8B-shaped batch (one launch =",
-        "one layer, the new token's K/V written in the same launch:",
-        "B=256, sum of context lengths " + f"{int(case.context_lens.sum())}, H_kv=8, D=128, P=16).",
-        "commands (run from the repository root, DIR = an output folder):",
-        "  " + PROFILE_RUNS["fetch"], "  " + PROFILE_RUNS["write"],
-        "  " + PROFILE_RUNS["copyf"], "  " + PROFILE_RUNS["copyw"],
-        sha_line, "",
-        f"calibration: torch copy_ of 1 GiB reads FETCH_SIZE {cf_kib:.0f} KiB and WRITE_SIZE {cw_kib:.0f} KiB "
-        f"per dispatch -> scale {kf:.4f} (fetch), {kw:.4f} (write)",
-        f"{BENCH_DECODE_KERNEL}: FETCH_SIZE {fetch_kib:.0f} KiB, WRITE_SIZE {write_kib:.0f} KiB per dispatch "
-        f"(mean of {nf} and {nw} dispatches)",
-        f"  -> fetched {fetch_b / 1e9:.4f} GB + written {write_b / 1e9:.4f} GB = {(fetch_b + write_b) / 1e9:.4f} GB "
-        f"per launch",
-        f"algorithmic bytes per launch: {alg / 1e9:.4f} GB (KV rows + q/out + block table + lengths + new rows); "
-        f"measured / algorithmic = {(fetch_b + write_b) / alg:.3f}",
-    ]
-    with open(os.path.join(prof, "decode_llama3_8b_hbm_traffic.txt"), "w") as f:
-        f.write("\n".join(lines) + "\n")
-    with open(os.path.join(prof, "traffic.json"), "w") as f:
-        json.dump({"decode_partition_llama3_8b": {
-            "source_sha256": sha, "bytes_per_launch": int(fetch_b + write_b), "fetch_bytes": int(fetch_b),
-            "write_bytes": int(write_b), "fetch_scale": kf, "write_scale": kw}}, f, indent=1)
-    log("profiles written")
+    path = os.path.join(prof, "traffic.json")
+    rec_all = json.load(open(path)) if os.path.exists(path) else {}
+    for key, (wl, pat) in TRAFFIC.items():
+        fe, wr = one(f"fetch_{key}/*counter_collection.csv"), one(f"write_{key}/*counter_collection.csv")
+        if not (fe and wr):
+            continue
+        fetch_kib, nf = _counter_means(fe, pat).get("FETCH_SIZE", (None, 0))
+        write_kib, nw = _counter_means(wr, pat).get("WRITE_SIZE", (None, 0))
+        if fetch_kib is None or write_kib is None:
+            log(f"{key}: no dispatch of a kernel matching {pat!r}")
+            continue
+        s_kv = 1 if wl.endswith("fp8") else 2
+        alg = (decode_bytes(case.context_lens, case.block_size, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                            2, s_kv) + append_bytes(case.B, case.num_kv_heads, case.head_dim, 2, s_kv))
+        fetch_b, write_b = fetch_kib * 1024 * kf, write_kib * 1024 * kw
+        lines = [
+            f"HBM traffic of the decode partition kernel with append ({pat}) on the Llama-3-8B-shaped batch",
+            f"({'fp8 e4m3' if s_kv == 1 else 'bf16'} pools; one launch = one layer, the new token's K/V written in "
+            f"the same launch: B=256, sum of context lengths {int(case.context_lens.sum())}, H_kv=8, D=128, P=16).",
+            "commands (run from the repository root, DIR = an output folder):",
+            "  " + cmds[f"fetch_{key}"], "  " + cmds[f"write_{key}"], "  " + cmds["fetch_copy"],
+            "  " + cmds["write_copy"], _sha_line(DECODE_SOURCES), "",
+            f"calibration: torch copy_ of 1 GiB reads FETCH_SIZE {cf_kib:.0f} KiB and WRITE_SIZE {cw_kib:.0f} KiB "
+            f"per dispatch -> scale {kf:.4f} (fetch), {kw:.4f} (write)",
+            f"FETCH_SIZE {fetch_kib:.0f} KiB, WRITE_SIZE {write_kib:.0f} KiB per dispatch (mean of {nf} and {nw} "
+            f"dispatches)",
+            f"  -> fetched {fetch_b / 1e9:.4f} GB + written {write_b / 1e9:.4f} GB = {(fetch_b + write_b) / 1e9:.4f} "
+            f"GB per launch",
+            f"algorithmic bytes per launch: {alg / 1e9:.4f} GB (KV rows + q/out + block table + lengths + new rows); "
+            f"measured / algorithmic = {(fetch_b + write_b) / alg:.3f}",
+        ]
+        with open(os.path.join(prof, f"{key}_hbm_traffic.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        rec_all[key] = {"source_sha256": sources_sha(DECODE_SOURCES), "bytes_per_launch": int(fetch_b + write_b),
+                        "fetch_bytes": int(fetch_b), "write_bytes": int(write_b), "fetch_scale": kf,
+                        "write_scale": kw}
+        log(f"profiles/{key}_hbm_traffic.txt written")
+    rec_all.pop("decode_partition_llama3_8b", None)
+    with open(path, "w") as f:
+        json.dump(rec_all, f, indent=1)
 
 
 def decode_summary(res):
