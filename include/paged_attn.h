@@ -280,6 +280,31 @@ int pa_paged_decode_attention_noalloc(const void* q, const void* k_cache, const 
                                       int64_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
                                       void* stream);
 
+/*
+ * pa_workspace_status -- reports whether a call that used this workspace left
+ * work uncomputed.  The decode, decode-with-append and mixed calls hand out
+ * their work items through queue counters that the first workgroup of each
+ * launch resets; a wave that finds a counter not yet reset sleeps and tries
+ * again, and after 2^20 sleeps gives that queue up, so that every wave
+ * terminates.  The queue's remaining items are then not computed and the
+ * output is wrong.  (The grid never exceeds the resident workgroups and the
+ * first one resets the counters before its own claims, so this is not
+ * expected to happen.)  Each give-up sets a bit of a status word in the
+ * workspace header: 1 = a decode queue, 2 = a prefill queue of the mixed call.
+ *   workspace  a workspace of pa_paged_decode_attention(_fp8),
+ *              pa_paged_decode_append(_fp8) or pa_paged_mixed_attention(_fp8),
+ *              or NULL for the static scratch of
+ *              pa_paged_decode_attention_noalloc on the stream's device
+ *   result     int32 device pointer; receives the bits set since the previous
+ *              pa_workspace_status call on this workspace, and the word is
+ *              cleared.  A new workspace holds arbitrary bits: its first status
+ *              call only clears them (the static scratch starts at zero).
+ * Runs asynchronously on stream, after the calls enqueued before it.
+ * Setting the environment variable PA_TEST_QUEUE_GIVEUP=1 makes every queue
+ * claim give up at once (for tests of this path).
+ */
+int pa_workspace_status(void* workspace, int32_t* result, void* stream);
+
 /* Bytes of workspace pa_paged_prefill_attention needs for these shapes. */
 size_t pa_prefill_workspace_size(int32_t num_seqs, int64_t total_q_tokens,
                                  int32_t num_q_heads, int32_t num_kv_heads);

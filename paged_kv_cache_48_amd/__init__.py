@@ -41,6 +41,7 @@ __all__ = [
     "prefill_workspace_size",
     "mixed_workspace_size",
     "kernel_timer",
+    "workspace_status",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpaged_attn.so")
@@ -94,6 +95,7 @@ SIGNATURES = {
         [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
          _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _c_void_p],
     ),
+    "pa_workspace_status": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p]),
     "pa_paged_decode_append": (
         ctypes.c_int,
         [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
@@ -527,6 +529,31 @@ def paged_mixed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_
                                         out.data_ptr(), B, T, Hq, Hkv, D, P, N, M, _dtype_code(q),
                                         ws.data_ptr(), ws.numel(), stream))
     return out
+
+
+GAVE_UP = {1: "a decode work queue was given up", 2: "a prefill work queue of the mixed call was given up"}
+
+
+def workspace_status(workspace: torch.Tensor | None = None, device=None, noalloc: bool = False) -> int:
+    """Bits of the workspace's status word (see ``pa_workspace_status``),
+    gathered since the previous query; the word is cleared.  ``workspace``
+    defaults to the cached workspace of ``device``'s current stream; with
+    ``noalloc`` the static scratch of ``paged_decode_attention_noalloc`` is
+    read.  Synchronises the stream."""
+    lib = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    if noalloc:
+        ptr = None
+    else:
+        if workspace is None:
+            workspace = _workspaces.get((dev.index, stream))
+            _req(workspace is not None, "no cached workspace on this stream yet")
+        _dev_tensor(workspace, "workspace", torch.uint8)
+        ptr = workspace.data_ptr()
+    result = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib.pa_workspace_status(ptr, result.data_ptr(), stream))
+    return int(result.item())
 
 
 @contextlib.contextmanager

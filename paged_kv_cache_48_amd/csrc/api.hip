@@ -543,3 +543,15 @@ extern "C" int pa_paged_decode_attention_noalloc(const void* q, const void* k_ca
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, dtype, dtype,
                      ws, (size_t)PA_NOALLOC_SCRATCH_BYTES, stream);
 }
+
+extern "C" int pa_workspace_status(void* workspace, int32_t* result, void* stream) {
+  g_err.clear();
+  const char* fn = "pa_workspace_status";
+  PA_REQUIRE(result, PA_ERR_INVALID, "%s: null result pointer", fn);
+  void* ws = workspace;
+  if (!ws) {
+    const int st = scratch_address(fn, static_cast<hipStream_t>(stream), &ws);
+    if (st != PA_OK) return st;
+  }
+  return hip_status(pa::launch_workspace_status(ws, result, static_cast<hipStream_t>(stream)), fn);
+}

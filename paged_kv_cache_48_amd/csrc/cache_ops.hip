@@ -289,4 +289,18 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, const int32_t*
   return hipGetLastError();
 }
 
+// Reads and clears a workspace's sticky status word (one thread).
+__global__ __launch_bounds__(64) void workspace_status_kernel(uint32_t* word, int32_t* result) {
+  if (threadIdx.x == 0) {
+    result[0] = (int32_t)*word;
+    *word = 0u;
+  }
+}
+
+hipError_t launch_workspace_status(void* workspace, int32_t* result, hipStream_t stream) {
+  uint32_t* word = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kStatusWordOffset);
+  hipLaunchKernelGGL(workspace_status_kernel, dim3(1), dim3(64), 0, stream, word, result);
+  return hipGetLastError();
+}
+
 }  // namespace pa

@@ -292,6 +292,8 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.new_f32 = a.new_dtype == kF32;
   prm.k_scale = fp8 ? a.k_scale : nullptr;
   prm.v_scale = fp8 ? a.v_scale : nullptr;
+  prm.status = reinterpret_cast<uint32_t*>(ws + Lw.hdr) + kStatusWord;
+  prm.force_giveup = test_queue_giveup();
 
   const int64_t max_items = (int64_t)a.num_seqs * Lw.max_parts * prm.Hkv * prm.n_hg;
   // the workgroups plan small batches themselves (their counters then carry

@@ -6,6 +6,7 @@
 #pragma once
 
 #include <math.h>
+#include <stdlib.h>
 #include <unistd.h>
 
 #include <atomic>
@@ -38,6 +39,13 @@ constexpr int kHeaderBytes = 1024;
 constexpr int kItemCountWord = kHeaderBytes / 4 - 1;
 constexpr int kFullCountWord = kHeaderBytes / 4 - 2;  // items that are full partitions
 constexpr int kQueueCountWord = kHeaderBytes / 4 - 3;  // queues in use
+// Sticky status bits: a wave that gives up waiting on a queue (see claim)
+// ORs in kGaveUpDecode, a mixed workgroup that gives up on a prefill queue
+// kGaveUpPrefill.  Only pa_workspace_status reads and clears the word.
+constexpr int kStatusWord = kHeaderBytes / 4 - 4;
+static_assert(kStatusWord * 4 == (int)kStatusWordOffset, "status word offset");
+constexpr uint32_t kGaveUpDecode = 1u;
+constexpr uint32_t kGaveUpPrefill = 2u;
 constexpr int kCountBits = 24;
 constexpr int64_t kMaxQueueItems = (int64_t)1 << kCountBits;  // claims per counter
 constexpr int64_t kMaxWaves = 256 * 32;  // resident waves of a launch, at most
@@ -169,6 +177,8 @@ struct DecodeParams {
   const void* knew;
   const void* vnew;
   int new_f32;
+  uint32_t* status;  // the header's kStatusWord
+  int force_giveup;  // test knob: every claim sees a stale counter and gives up at once
 };
 
 // One work item, wave-uniform (scalar registers).
@@ -451,7 +461,8 @@ __device__ __forceinline__ unsigned long long launch_tag(unsigned long long salt
 
 // Sleeps a claim may wait for workgroup 0 to reset the counters (a few
 // atomics of a resident workgroup, so a handful in practice; the bound only
-// guarantees that every wave exits).
+// guarantees that every wave exits).  A wave that reaches it leaves the
+// queue's remaining items uncomputed and records that in the status word.
 constexpr int kMaxSpins = 1 << 20;
 
 // Takes the next dynamically scheduled item: with nq queues, queue x holds
@@ -469,9 +480,13 @@ __device__ __forceinline__ uint32_t claim(const DecodeParams& prm, unsigned long
     unsigned long long old = 0;
     if (lane == 0) old = atomicAdd(prm.counter + x * kCounterStride, 1ull);
     old = uniform64(old);
-    if (prm.self_plan && (old >> kCountBits) != tag) {
-      if (++spins < kMaxSpins) __builtin_amdgcn_s_sleep(8);
-      else ++queue;
+    if (prm.force_giveup || (prm.self_plan && (old >> kCountBits) != tag)) {
+      if (!prm.force_giveup && ++spins < kMaxSpins) {
+        __builtin_amdgcn_s_sleep(8);
+      } else {
+        ++queue;
+        if (lane == 0) atomicOr(prm.status, kGaveUpDecode);
+      }
       continue;
     }
     const unsigned long long c = prm.self_plan ? old & (kMaxQueueItems - 1) : old;
@@ -1258,6 +1273,15 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams prm) {
 
 // Per-call salt of the counters' tag: a process-wide sequence from a start
 // taken from the clock and the process id.
+// Test knob, read on every call: PA_TEST_QUEUE_GIVEUP=1 makes every queue
+// claim give up at once (the status word then reports it; the items left in
+// the queues are not computed).  Lets a test see the give-up path with every
+// kernel exiting normally.
+inline int test_queue_giveup() {
+  const char* e = getenv("PA_TEST_QUEUE_GIVEUP");
+  return e && e[0] == '1' ? 1 : 0;
+}
+
 inline unsigned long long next_salt() {
   static std::atomic<unsigned long long> seq{
       (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^

@@ -94,4 +94,10 @@ bool mixed_fits(int num_seqs, int64_t num_q_tokens, int num_q_heads, int num_kv_
                 int max_blocks);
 hipError_t launch_mixed(const AttnArgs& a, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// Decode and mixed workspaces keep a sticky status word (give-ups of a work
+// queue) at this byte offset of their header; prefill leaves it alone.  The
+// kernel copies it to result[0] and clears it.
+constexpr size_t kStatusWordOffset = 1008;
+hipError_t launch_workspace_status(void* workspace, int32_t* result, hipStream_t stream);
+
 }  // namespace pa

@@ -226,9 +226,13 @@ __global__ __launch_bounds__(kMixThreads) void mixed_kernel(MixedParams mp) {
       while (queue < nqueues) {
         const uint32_t x = (home + queue) % nqueues;
         const unsigned long long old = atomicAdd(mp.pcounter + x * dec::kCounterStride, 1ull);
-        if ((old >> dec::kCountBits) != tag) {  // not yet reset for this launch
-          if (++spins < dec::kMaxSpins) __builtin_amdgcn_s_sleep(8);
-          else ++queue;
+        if (mp.d.force_giveup || (old >> dec::kCountBits) != tag) {  // not yet reset for this launch
+          if (!mp.d.force_giveup && ++spins < dec::kMaxSpins) {
+            __builtin_amdgcn_s_sleep(8);
+          } else {
+            ++queue;
+            atomicOr(mp.d.status, dec::kGaveUpPrefill);
+          }
           continue;
         }
         const uint32_t c = (uint32_t)(old & (dec::kMaxQueueItems - 1));
@@ -358,6 +362,10 @@ hipError_t launch_mixed(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, h
   d.knew = nullptr;
   d.vnew = nullptr;
   d.new_f32 = 0;
+  // both kinds of give-up go to the status word of the mixed header (at the
+  // same offset as in a decode workspace)
+  d.status = reinterpret_cast<uint32_t*>(ws) + dec::kStatusWord;
+  d.force_giveup = dec::test_queue_giveup();
 
   pre::PrefillParams& p = mp.p;
   p.q = static_cast<const bf16_bits*>(a.q);

@@ -286,3 +286,7 @@ def test_decode_noalloc_validation(lib):
     assert b"static scratch" in lib.pa_last_error()
     assert lib.pa_decode_workspace_size(1024, 32, 128, 16, 512) > (160 << 20)
     assert lib.pa_decode_workspace_size(256, 32, 128, 16, 512) <= (160 << 20)
+
+
+def test_workspace_status_validation(lib):
+    assert lib.pa_workspace_status(1, None, NUL) == INVALID

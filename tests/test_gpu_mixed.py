@@ -205,3 +205,42 @@ def test_mixed_fp8_pools():
                           c.context_lens, c.scale)
         assert_close(got, ref, "bf16", f"fp8 mixed G={G} D={D} P={P}")
         assert np.array_equal(to_host_bits(got), to_host_bits(separate(f, scales=(f.dks, f.dvs))))
+
+
+def test_queue_giveup_is_reported(monkeypatch):
+    """A wave that gives up waiting on a work queue leaves that queue's items
+    uncomputed; the workspace's status word must say so.  PA_TEST_QUEUE_GIVEUP=1
+    forces every claim to give up at once (every kernel still exits): the
+    decode call reports bit 1, the mixed call bits 1 and 2, the allocation-free
+    call bit 1 in the static scratch.  Normal calls leave the word clear and
+    compute the right rows again."""
+    c = case(lens=(5, 300, 1025, 4000, 77, 512, 2048, 700), qlens=(1, 1, 1, 300, 1, 100, 1, 1), seed=93)
+    d = DevCase(c)
+    ref = to_host_bits(separate(d))
+    B, Hq, D, P, M = c.B, c.num_q_heads, c.head_dim, c.block_size, c.max_blocks_per_seq
+    wsm = torch.empty(pa.mixed_workspace_size(B, Hq, D, P, M), dtype=torch.uint8, device=DEV)
+    dd = DevCase(case(lens=(5, 300, 1025, 4000), qlens=(1, 1, 1, 1), seed=94))
+    cd = dd.case
+    wsd = torch.empty(pa.decode_workspace_size(cd.B, Hq, D, P, cd.max_blocks_per_seq), dtype=torch.uint8, device=DEV)
+    outd = torch.empty_like(dd.q)
+    outm = torch.empty_like(d.q)
+
+    def run():
+        pa.paged_decode_attention(dd.q, dd.kc, dd.vc, dd.bt, dd.lens, cd.scale, outd, workspace=wsd)
+        pa.paged_mixed_attention(d.q, d.kc, d.vc, d.cu, d.bt, d.lens, c.scale, outm, workspace=wsm)
+        pa.paged_decode_attention_noalloc(dd.q, dd.kc, dd.vc, dd.bt, dd.lens, cd.scale, outd)
+
+    for ws in (wsd, wsm):
+        pa.workspace_status(ws)  # a new workspace holds arbitrary bits: the first query clears them
+    pa.workspace_status(noalloc=True)
+    run()
+    assert (pa.workspace_status(wsd), pa.workspace_status(wsm), pa.workspace_status(noalloc=True)) == (0, 0, 0)
+    monkeypatch.setenv("PA_TEST_QUEUE_GIVEUP", "1")
+    run()
+    monkeypatch.delenv("PA_TEST_QUEUE_GIVEUP")
+    assert pa.workspace_status(wsd) == 1
+    assert pa.workspace_status(wsm) == 3
+    assert pa.workspace_status(noalloc=True) == 1
+    run()
+    assert (pa.workspace_status(wsd), pa.workspace_status(wsm), pa.workspace_status(noalloc=True)) == (0, 0, 0)
+    assert np.array_equal(to_host_bits(outm), ref)
