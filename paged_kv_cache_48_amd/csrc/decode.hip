@@ -112,7 +112,7 @@ constexpr int waves_per_block() {
   return Geo<T, D>::LDS_PER_WAVE * kWavesPerBlock <= 65536 ? kWavesPerBlock : 2;
 }
 
-template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend>
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend, bool kTwo>
 __device__ __forceinline__ void partition_body(const DecodeParams& prm) {
   using Gm = Geo<T, D>;
   constexpr int wpb = waves_per_block<T, D>();
@@ -138,24 +138,31 @@ __device__ __forceinline__ void partition_body(const DecodeParams& prm) {
   const uint32_t nwaves = gridDim.x * wpb;
   // (threadIdx.x >> 6 is the same in every lane; readfirstlane tells the compiler)
   const uint32_t wave = blockIdx.x * wpb + (uint32_t)uniform((int)(threadIdx.x >> 6));
-  decode_stream<T, D, kWide, kAligned, NR, false, HP, kAppend>(prm, lds, pl, tag, n_items, n_full, nq_plan, wave,
+  // kTwo (bf16 pools, small batches): two tiles in flight per wave (the same
+  // items and arithmetic, so the same bits as one)
+  if constexpr (kTwo)
+    decode_stream2<T, D, kWide, kAligned, NR, HP, kAppend>(prm, lds, pl, tag, n_items, n_full, nq_plan, wave,
+                                                           nwaves, (uint32_t)kMaxStaticRounds);
+  else
+    decode_stream<T, D, kWide, kAligned, NR, false, HP, kAppend>(prm, lds, pl, tag, n_items, n_full, nq_plan, wave,
                                                                nwaves, (uint32_t)kMaxStaticRounds);
 }
 
 template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend>
 __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams prm) {
-  partition_body<T, D, kWide, kAligned, NR, HP, kAppend>(prm);
+  partition_body<T, D, kWide, kAligned, NR, HP, kAppend, false>(prm);
 }
 
 // fp8 pools with append: making the new token's codes would take the kernel
 // just past 168 VGPRs (three waves per SIMD to two), or for 128-dim heads read
 // in pairs just past 256 (two to one); it is held to kWaves waves per SIMD.
-template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend, int kWaves>
+// bf16 pools with two tiles in flight are held to two.
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend, int kWaves, bool kTwo = false>
 __global__ __launch_bounds__(256, kWaves) void decode_partition_kernel_wb(DecodeParams prm) {
-  partition_body<T, D, kWide, kAligned, NR, HP, kAppend>(prm);
+  partition_body<T, D, kWide, kAligned, NR, HP, kAppend, kTwo>(prm);
 }
 
-template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend>
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP, bool kAppend, bool kTwo>
 hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipStream_t stream,
                         hipEvent_t ev0, hipEvent_t ev1) {
   // waves are independent workers
@@ -164,15 +171,17 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
   constexpr unsigned lds_bytes = Geo<T, D>::LDS_PER_WAVE * wpb + (unsigned)sizeof(PlanLds);
   // exactly the blocks that can be resident at once: every wave starts on its
   // first item immediately, and none waits for a slot while holding one
-  constexpr bool kWb = kAppend && Geo<T, D>::kFp8;
-  constexpr int kWaves = D <= 128 ? 3 : 2;
+  // two tiles in flight (two register sets): held to two waves per SIMD,
+  // where the compiler would otherwise go just past 256 registers
+  constexpr bool kWb = (kAppend && Geo<T, D>::kFp8) || kTwo;
+  constexpr int kWaves = kTwo ? 2 : (D <= 128 ? 3 : 2);
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
     hipError_t e;
     if constexpr (kWb)
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &nb, decode_partition_kernel_wb<T, D, kWide, kAligned, NR, HP, kAppend, kWaves>, 64 * wpb, lds_bytes);
+          &nb, decode_partition_kernel_wb<T, D, kWide, kAligned, NR, HP, kAppend, kWaves, kTwo>, 64 * wpb, lds_bytes);
     else
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &nb, decode_partition_kernel<T, D, kWide, kAligned, NR, HP, kAppend>, 64 * wpb, lds_bytes);
@@ -186,7 +195,7 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
     if (e != hipSuccess) return e;
   }
   if constexpr (kWb)
-    hipLaunchKernelGGL((decode_partition_kernel_wb<T, D, kWide, kAligned, NR, HP, kAppend, kWaves>), dim3(blocks),
+    hipLaunchKernelGGL((decode_partition_kernel_wb<T, D, kWide, kAligned, NR, HP, kAppend, kWaves, kTwo>), dim3(blocks),
                        dim3(64 * wpb), lds_bytes, stream, prm);
   else
     hipLaunchKernelGGL((decode_partition_kernel<T, D, kWide, kAligned, NR, HP, kAppend>), dim3(blocks),
@@ -201,23 +210,36 @@ hipError_t launch_typed(const DecodeParams& prm, int B, int64_t max_items, hipSt
   return hipGetLastError();
 }
 
-template <typename T, int D, bool kWide, int HP, bool kAppend>
+template <typename T, int D, bool kWide, int HP, bool kAppend, bool kTwo>
 hipError_t launch_mode(const DecodeParams& prm, int B, int64_t max_items, hipStream_t stream, hipEvent_t ev0,
                        hipEvent_t ev1) {
   // tiles of 16 tokens never straddle a block when P is a multiple of 16; a
   // partition touches at most 256 / P + 1 blocks: one id register for P >= 5
   if (prm.P % kTile == 0)
-    return launch_typed<T, D, kWide, true, 1, HP, kAppend>(prm, B, max_items, stream, ev0, ev1);
-  if (prm.P >= 5) return launch_typed<T, D, kWide, false, 1, HP, kAppend>(prm, B, max_items, stream, ev0, ev1);
-  return launch_typed<T, D, kWide, false, 5, HP, kAppend>(prm, B, max_items, stream, ev0, ev1);
+    return launch_typed<T, D, kWide, true, 1, HP, kAppend, kTwo>(prm, B, max_items, stream, ev0, ev1);
+  if (prm.P >= 5) return launch_typed<T, D, kWide, false, 1, HP, kAppend, kTwo>(prm, B, max_items, stream, ev0, ev1);
+  return launch_typed<T, D, kWide, false, 5, HP, kAppend, kTwo>(prm, B, max_items, stream, ev0, ev1);
 }
+
+// bf16 pools: batches of at most this many work items (upper bound from the
+// shapes: requests x partitions of the longest context x KV heads x head
+// groups) run with two tiles in flight per wave.  Their waves have few items
+// each, and a wave with one tile in flight waits a memory latency per tile;
+// larger batches keep more waves resident with one tile each, which measured
+// faster on them.  Both compute the same bits.
+constexpr int64_t kTwoTileMaxItems = 8192;
 
 template <typename T, int D, int HP, bool kAppend>
 hipError_t launch_sized(const DecodeParams& prm, int B, int64_t max_items, int64_t pool_bytes,
                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  if (pool_bytes < ((int64_t)1 << 32))
-    return launch_mode<T, D, false, HP, kAppend>(prm, B, max_items, stream, ev0, ev1);
-  return launch_mode<T, D, true, HP, kAppend>(prm, B, max_items, stream, ev0, ev1);
+  const bool wide = pool_bytes >= ((int64_t)1 << 32);
+  if constexpr (std::is_same<T, bf16_bits>::value) {
+    if (max_items <= kTwoTileMaxItems)
+      return wide ? launch_mode<T, D, true, HP, kAppend, true>(prm, B, max_items, stream, ev0, ev1)
+                  : launch_mode<T, D, false, HP, kAppend, true>(prm, B, max_items, stream, ev0, ev1);
+  }
+  return wide ? launch_mode<T, D, true, HP, kAppend, false>(prm, B, max_items, stream, ev0, ev1)
+              : launch_mode<T, D, false, HP, kAppend, false>(prm, B, max_items, stream, ev0, ev1);
 }
 
 // Kernel choice by pool element type, head size and head pairing.

@@ -309,9 +309,14 @@ __device__ __forceinline__ int lane_id_lookup(const int (&ids)[NR], int idx) {
 // already in flight, since loads complete in order).  Invalid tokens load the
 // head's slice of row 0 (always in range, and cached) and are zeroed when
 // staged.  kAligned: the tile lies inside one block (P a multiple of 16).
-template <typename T, int D, bool kWide, bool kAligned, int NR>
+// kNew (decode with append, bf16): the lanes that load token npos (the new
+// token, L - 1) load it from the new rows (knew / vnew: this lane's piece of
+// the item's slice of row b) instead of the pool; every lane issues the same
+// loads either way.
+template <typename T, int D, bool kWide, bool kAligned, int NR, bool kNew = false>
 __device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams& prm, const Item& it,
-                                          const int (&ids)[NR], int tile0, TileRegs<T, D>& r) {
+                                          const int (&ids)[NR], int tile0, TileRegs<T, D>& r, int npos = -1,
+                                          const char* knew = nullptr, const char* vnew = nullptr) {
   using Gm = Geo<T, D>;
   using O = typename Off<kWide>::type;
   const int lane = lane_id();
@@ -347,8 +352,14 @@ __device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams
       const bool ok = bok && first + j < it.tok_end;
       r.ok |= (ok ? 1u : 0u) << j;
       const O e = (ok ? base + (O)j * (O)pv.row_bytes : (O)0) + lane_off;
-      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.k + e));
-      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.v + e));
+      if constexpr (kNew) {
+        const bool nw = first + j == npos;
+        r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(nw ? knew : pv.k + e));
+        r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(nw ? vnew : pv.v + e));
+      } else {
+        r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.k + e));
+        r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.v + e));
+      }
     }
   } else {
 #pragma unroll
@@ -367,8 +378,14 @@ __device__ __forceinline__ void load_tile(const PoolView& pv, const DecodeParams
       const bool ok = in && blk >= 0 && blk < prm.N;
       r.ok |= (ok ? 1u : 0u) << j;
       const O e = (ok ? ((O)blk * (O)prm.P + (O)off) * (O)pv.row_bytes : (O)0) + lane_off;
-      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.k + e));
-      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.v + e));
+      if constexpr (kNew) {
+        const bool nw = pos == npos;
+        r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(nw ? knew : pv.k + e));
+        r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(nw ? vnew : pv.v + e));
+      } else {
+        r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.k + e));
+        r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const LT*>(pv.v + e));
+      }
     }
   }
 }
@@ -418,6 +435,42 @@ __device__ __forceinline__ void stage_tile(char* lds, TileRegs<T, D>& r_in, bool
 #pragma unroll
     for (int j = 0; j < Gm::TPL; ++j)
       *reinterpret_cast<u32x4_t*>(vl + (q * Gm::TPL + j) * Gm::KST + 16 * c) = r.v[j];
+  }
+}
+
+// stage_tile for the two-tile stream (bf16 pools): the same LDS contents, but
+// the registers are only read (a masked token's values are replaced by zeros
+// as they are written to LDS).  Only the loads write a register set there, so
+// the wait before staging a set covers that set's loads alone and leaves the
+// other set's in flight.
+template <typename T, int D, bool kMasked>
+__device__ __forceinline__ void stage_tile_ro(char* lds, const TileRegs<T, D>& r) {
+  using Gm = Geo<T, D>;
+  static_assert(Gm::kBf16, "bf16 pools");
+  const int lane = lane_id();
+  const int c = lane % Gm::CPR, q = lane / Gm::CPR;
+  auto okj = [&](int j) { return !kMasked || ((r.ok >> j) & 1u) != 0; };
+#pragma unroll
+  for (int j = 0; j < Gm::TPL; ++j)
+    *reinterpret_cast<u32x4_t*>(lds + (q * Gm::TPL + j) * Gm::KST + 16 * c) =
+        okj(j) ? r.k[j] : u32x4_t{0u, 0u, 0u, 0u};
+  char* vl = lds + Gm::KBYTES;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int d = 8 * c + 2 * w;
+    uint32_t v[Gm::TPL];
+#pragma unroll
+    for (int j = 0; j < Gm::TPL; ++j) v[j] = okj(j) ? r.v[j][w] : 0u;
+    if constexpr (Gm::TPL == 4) {
+      const u32x2_t lo = {__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
+      const u32x2_t hi = {__builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+      *reinterpret_cast<u32x2_t*>(vl + d * Gm::VTS + 8 * q) = lo;
+      *reinterpret_cast<u32x2_t*>(vl + (d + 1) * Gm::VTS + 8 * q) = hi;
+    } else {
+      static_assert(Gm::TPL == 2, "bf16 tiles hold 2 or 4 tokens per lane");
+      *reinterpret_cast<uint32_t*>(vl + d * Gm::VTS + 4 * q) = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(vl + (d + 1) * Gm::VTS + 4 * q) = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+    }
   }
 }
 
@@ -473,6 +526,7 @@ constexpr int kMaxSpins = 1 << 20;
 // when all queues are empty.
 __device__ __forceinline__ uint32_t claim(const DecodeParams& prm, unsigned long long tag, uint32_t nq, uint32_t home,
                                           uint32_t& queue, uint32_t first_dyn, uint32_t total) {
+  if (first_dyn >= total) return 0xffffffffu;  // every item is dealt statically
   const int lane = lane_id();
   int spins = 0;
   while (queue < nq) {
@@ -480,6 +534,53 @@ __device__ __forceinline__ uint32_t claim(const DecodeParams& prm, unsigned long
     unsigned long long old = 0;
     if (lane == 0) old = atomicAdd(prm.counter + x * kCounterStride, 1ull);
     old = uniform64(old);
+    if (prm.force_giveup || (prm.self_plan && (old >> kCountBits) != tag)) {
+      if (!prm.force_giveup && ++spins < kMaxSpins) {
+        __builtin_amdgcn_s_sleep(8);
+      } else {
+        ++queue;
+        if (lane == 0) atomicOr(prm.status, kGaveUpDecode);
+      }
+      continue;
+    }
+    const unsigned long long c = prm.self_plan ? old & (kMaxQueueItems - 1) : old;
+    const unsigned long long f = first_dyn + nq * c + x;
+    if (f < total) return (uint32_t)f;
+    ++queue;
+  }
+  return 0xffffffffu;
+}
+
+// claim() in two halves, so that a stream with two tiles in flight can read
+// the atomic's result later: loads complete in order, so reading it at once
+// would also wait for the tile loads issued before it.  claim_start issues
+// the first attempt (lane 0's atomic on the wave's current queue);
+// claim_finish reads it and continues exactly as claim() does.
+__device__ __forceinline__ bool claim_start(const DecodeParams& prm, uint32_t nq, uint32_t home, uint32_t queue,
+                                            uint32_t first_dyn, uint32_t total, unsigned long long& pending) {
+  if (queue >= nq || first_dyn >= total) return false;
+  const uint32_t x = (home + queue) % nq;
+  if (lane_id() == 0) pending = atomicAdd(prm.counter + x * kCounterStride, 1ull);
+  return true;
+}
+
+__device__ __forceinline__ uint32_t claim_finish(const DecodeParams& prm, unsigned long long tag, uint32_t nq,
+                                                 uint32_t home, uint32_t& queue, uint32_t first_dyn, uint32_t total,
+                                                 bool started, unsigned long long pending) {
+  if (!started) return 0xffffffffu;
+  const int lane = lane_id();
+  int spins = 0;
+  bool first = true;
+  while (queue < nq) {
+    const uint32_t x = (home + queue) % nq;
+    unsigned long long old = 0;
+    if (first) {
+      old = uniform64(pending);
+      first = false;
+    } else {
+      if (lane == 0) old = atomicAdd(prm.counter + x * kCounterStride, 1ull);
+      old = uniform64(old);
+    }
     if (prm.force_giveup || (prm.self_plan && (old >> kCountBits) != tag)) {
       if (!prm.force_giveup && ++spins < kMaxSpins) {
         __builtin_amdgcn_s_sleep(8);
@@ -707,14 +808,20 @@ __device__ __forceinline__ void load_new(const DecodeParams& prm, const Item& it
 // holds position L - 1).  Items of query-head group 0 write the new token to
 // its slot, unless the block id is out of range (as the scatter skips such
 // slots); the lanes that stage the token's pieces hold (nk, nv).
-template <typename T, int D, int NR>
-__device__ __forceinline__ void append_store(const DecodeParams& prm, const PoolView& pv, const Item& it,
-                                             const int (&ids)[NR], bool mine, const u32x4_t& nk, const u32x4_t& nv) {
+// Block id of the item's position L - 1 (the new token's), from its block ids.
+template <int NR>
+__device__ __forceinline__ int append_block(const DecodeParams& prm, const Item& it, const int (&ids)[NR]) {
+  const int lb = (it.L - 1) / prm.P;
+  return lane_id_lookup<NR>(ids, lb - it.blk0);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void append_store(const DecodeParams& prm, const PoolView& pv, const Item& it, int blk,
+                                             bool mine, const u32x4_t& nk, const u32x4_t& nv) {
   using Gm = Geo<T, D>;
   if (it.hg != 0) return;
   const int pos = it.L - 1;
   const int lb = pos / prm.P, off = pos - lb * prm.P;
-  const int blk = lane_id_lookup<NR>(ids, lb - it.blk0);
   if (mine && blk >= 0 && blk < prm.N) {
     const uint64_t e = ((uint64_t)blk * (uint64_t)prm.P + (uint64_t)off) * pv.row_bytes +
                        (uint64_t)(it.hkv * Gm::GROWB + 16 * (lane_id() % Gm::CPR));
@@ -726,12 +833,12 @@ __device__ __forceinline__ void append_store(const DecodeParams& prm, const Pool
 // bf16 and fp32 pools: before the last tile is staged, the lane that stages
 // the new token takes its piece from (nk, nv), loaded with the item's first
 // tile.  A length beyond the block table (clamped when read) appends nothing.
-template <typename T, int D, int NR>
-__device__ __forceinline__ void append_regs(const DecodeParams& prm, const PoolView& pv, const Item& it,
-                                            const int (&ids)[NR], int tile0, const u32x4_t& nk, const u32x4_t& nv,
+template <typename T, int D>
+__device__ __forceinline__ void append_regs(const DecodeParams& prm, const PoolView& pv, const Item& it, int blk,
+                                            int len, int tile0, const u32x4_t& nk, const u32x4_t& nv,
                                             TileRegs<T, D>& regs) {
   using Gm = Geo<T, D>;
-  if (prm.lens[it.b] > prm.cap) return;
+  if (len > prm.cap) return;  // the request's unclamped length: beyond the block table, nothing is appended
   const int tL = it.L - 1 - tile0;  // in [0, TT)
   const int qL = tL / Gm::TPL, jL = tL - qL * Gm::TPL;
   const bool mine = lane_id() / Gm::CPR == qL;
@@ -741,7 +848,59 @@ __device__ __forceinline__ void append_regs(const DecodeParams& prm, const PoolV
       regs.k[j] = nk;
       regs.v[j] = nv;
     }
-  append_store<T, D, NR>(prm, pv, it, ids, mine, nk, nv);
+  append_store<T, D>(prm, pv, it, blk, mine, nk, nv);
+}
+
+// Decode with append, two-tile stream (bf16): the item's last tile was loaded
+// with the new token (position L - 1) taken from the new rows.  Items of
+// query-head group 0 write it to its slot (unless the block id is out of
+// range), from the tile's registers, which are only read.
+template <typename T, int D>
+__device__ __forceinline__ void append_from_regs(const DecodeParams& prm, const PoolView& pv, const Item& it, int blk,
+                                                 int tile0, const TileRegs<T, D>& regs) {
+  using Gm = Geo<T, D>;
+  const int tL = it.L - 1 - tile0;  // in [0, TT)
+  const int qL = tL / Gm::TPL, jL = tL - qL * Gm::TPL;
+  const bool mine = lane_id() / Gm::CPR == qL;
+  u32x4_t nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < Gm::TPL; ++j)
+    if (j == jL) {
+      nk = regs.k[j];
+      nv = regs.v[j];
+    }
+  append_store<T, D>(prm, pv, it, blk, mine, nk, nv);
+}
+
+// A request whose length is beyond its block table appends nothing (its
+// clamped last position is an old token), so the staged row of that position
+// is put back from the pool: the K row and the V^T column, after staging,
+// read synchronously (a caller error, never on a valid batch).
+template <typename T, int D>
+__device__ __forceinline__ void unappend_lds(const DecodeParams& prm, const PoolView& pv, const Item& it, int blk,
+                                             int tile0, char* lds) {
+  using Gm = Geo<T, D>;
+  static_assert(Gm::kBf16, "bf16 pools");
+  if (blk < 0 || blk >= prm.N) return;  // the token is masked (zero) anyway
+  const int lane = lane_id();
+  const int tL = it.L - 1 - tile0;
+  const int pos = it.L - 1;
+  const int lb = pos / prm.P, off = pos - lb * prm.P;
+  const int c = lane % Gm::CPR;
+  const uint64_t e = ((uint64_t)blk * (uint64_t)prm.P + (uint64_t)off) * pv.row_bytes +
+                     (uint64_t)(it.hkv * Gm::GROWB + 16 * c);
+  const u32x4_t pk = *reinterpret_cast<const u32x4_t*>(pv.k + e);
+  const u32x4_t pvv = *reinterpret_cast<const u32x4_t*>(pv.v + e);
+  if (lane < Gm::CPR) {
+    *reinterpret_cast<u32x4_t*>(lds + tL * Gm::KST + 16 * c) = pk;
+    char* vl = lds + Gm::KBYTES;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int d = 8 * c + 2 * w;
+      *reinterpret_cast<uint16_t*>(vl + d * Gm::VTS + 2 * tL) = (uint16_t)(pvv[w] & 0xffffu);
+      *reinterpret_cast<uint16_t*>(vl + (d + 1) * Gm::VTS + 2 * tL) = (uint16_t)(pvv[w] >> 16);
+    }
+  }
 }
 
 // fp8 pools: after the last tile is staged, the new token's codes are made
@@ -800,6 +959,246 @@ __device__ __forceinline__ void append_lds(const DecodeParams& prm, const PoolVi
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-tile arithmetic of a decode item, shared by the decode streams (so that
+// every stream computes an item the same way, bit for bit).
+// ---------------------------------------------------------------------------
+// S^T = K Q^T for the staged tile, per 16-token half: lane (n, g) gets the
+// scores of column n for tokens 16h + 4g + j (HP = 2: the products over the
+// first D / 2 dimensions in s, over the others in s2).
+template <typename T, int D, int HP>
+__device__ __forceinline__ void tile_scores(const char* lds, const u32x4_t (&qv)[Geo<T, D>::NQV],
+                                            f32x4_t (&s)[Geo<T, D>::TT / 16], f32x4_t (&s2)[Geo<T, D>::TT / 16]) {
+  using Gm = Geo<T, D>;
+  constexpr int NH = Gm::TT / 16;
+  constexpr int NQ1 = Gm::NQ / HP;
+  const int lane = lane_id();
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < NH; ++h) s[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (HP == 2) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) s2[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  if constexpr (Gm::kFp8) {
+    // K operand: 8 codes of token 16 h + n, widened to fp16 as they are read
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+      for (int i = 0; i < NQ1; ++i) {
+        const u32x2_t c = *reinterpret_cast<const u32x2_t*>(lds + (16 * h + n) * Gm::KST + 32 * i + 8 * g);
+        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, e4m3x8_to_f16(c)),
+                                                      __builtin_bit_cast(f16x8_t, qv[i]), s[h], 0, 0, 0);
+      }
+      if constexpr (HP == 2) {
+#pragma unroll
+        for (int i = NQ1; i < Gm::NQ; ++i) {
+          const u32x2_t c = *reinterpret_cast<const u32x2_t*>(lds + (16 * h + n) * Gm::KST + 32 * i + 8 * g);
+          s2[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, e4m3x8_to_f16(c)),
+                                                         __builtin_bit_cast(f16x8_t, qv[i]), s2[h], 0, 0, 0);
+        }
+      }
+    }
+  } else if constexpr (Gm::kBf16) {
+#pragma unroll
+    for (int i = 0; i < NQ1; ++i) {
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
+      s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                     __builtin_bit_cast(bf16x8_t, qv[i]), s[0], 0, 0, 0);
+    }
+    if constexpr (HP == 2) {
+#pragma unroll
+      for (int i = NQ1; i < Gm::NQ; ++i) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
+        s2[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                        __builtin_bit_cast(bf16x8_t, qv[i]), s2[0], 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < Gm::NQ / 4; ++i) {
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 4 * (g * (D / 4) + 4 * i));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        s[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(qv[i][j]), s[0], 0, 0,
+                                                    0);
+    }
+  }
+}
+
+// HP = 2: each column keeps the scores of its own KV head of the pair.
+template <int NH, int HP>
+__device__ __forceinline__ void own_half(f32x4_t (&s)[NH], const f32x4_t (&s2)[NH]) {
+  const int n = lane_id() & 15;
+  if constexpr (HP == 2) {
+    const bool hi = ((n >> 2) & 1) != 0;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const f32x4_t lo = s[h], up = s2[h];
+      s[h] = f32x4_t{hi ? up[0] : lo[0], hi ? up[1] : lo[1], hi ? up[2] : lo[2], hi ? up[3] : lo[3]};
+    }
+  }
+}
+
+// Online softmax of the tile's scores for column n (tokens tile0 + 16h + 4g +
+// j; tokens at or past it.tok_end are masked), then O^T += V^T P^T.
+template <typename T, int D>
+__device__ __forceinline__ void tile_softmax_pv(const char* lds, const Item& it, int tile0,
+                                                const f32x4_t (&s)[Geo<T, D>::TT / 16], float& m, float& l,
+                                                f32x4_t (&o)[D / 16]) {
+  using Gm = Geo<T, D>;
+  constexpr int NH = Gm::TT / 16;
+  constexpr int NDB = D / 16;
+  const int lane = lane_id();
+  const int n = lane & 15, g = lane >> 4;
+  float sc[NH][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sc[h][j] = (tile0 + 16 * h + 4 * g + j < it.tok_end) ? s[h][j] * it.sl2 : -INFINITY;
+      mx = fmaxf(mx, sc[h][j]);
+    }
+  mx = max_over_rows(mx);
+  // move the reference max only when a score exceeds it by the slack
+  // (always on the first tile, m = -inf); uniform branch, rarely taken
+  const bool move = mx > m + kRescaleSlack;
+  if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
+    const float alpha = (move && m != -INFINITY) ? fast_exp2(m - mx) : 1.0f;
+    if (move) m = mx;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+  }
+  float pp[NH][4];
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pp[h][j] = fast_exp2(sc[h][j] - m);
+      l += pp[h][j];
+    }
+  const float* p = pp[0];
+  // ---- O^T += V^T P^T ----
+  const char* vl = lds + Gm::KBYTES;
+  if constexpr (Gm::kFp8) {
+    // B operand: the lane's probabilities, k-slots 0-3 = tokens 4g + j and
+    // 4-7 = tokens 16 + 4g + j.  A operand (V^T) in the same token order
+    // from the byte-transposing read: lane n of each 16-lane group addresses
+    // V row 4g + n/2 (n < 8) or 12 + 4g + n/2 (n >= 8), bytes 16db + 8 (n % 2)
+    const u32x4_t pb = {pack_f16(pp[0][0], pp[0][1]), pack_f16(pp[0][2], pp[0][3]), pack_f16(pp[1][0], pp[1][1]),
+                        pack_f16(pp[1][2], pp[1][3])};
+    const char* vrow = vl + ((n < 8 ? 4 * g : 12 + 4 * g) + (n >> 1)) * Gm::KST + 8 * (n & 1);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const u32x2_t c = lds_read_tr8(vrow + 16 * db);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, e4m3x8_to_f16(c)),
+                                                     __builtin_bit_cast(f16x8_t, pb), o[db], 0, 0, 0);
+    }
+  } else if constexpr (Gm::kBf16) {
+    const u32x2_t pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vl + (16 * db + n) * Gm::VTS + 8 * g);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                        __builtin_bit_cast(s16x4_t, pb), o[db], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = *reinterpret_cast<const float*>(vl + (4 * g + j) * Gm::KST + 4 * (16 * db + n));
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[j], o[db], 0, 0, 0);
+      }
+  }
+}
+
+// Item done: total of l over the four 16-lane rows, then column n's output
+// row (one partition) or its partial row and (max, sum, scale) entry.
+template <typename T, int D, int HP>
+__device__ __forceinline__ void store_item(const DecodeParams& prm, const Item& it, float m, float l,
+                                           const f32x4_t (&o)[D / 16]) {
+  using Gm = Geo<T, D>;
+  typedef typename QType<T>::type QT;
+  constexpr int NDB = D / 16;
+  const int lane = lane_id();
+  const int n = lane & 15, g = lane >> 4;
+  // (HP = 2: column n's head is the pair's first or second, and its outputs
+  // are the first or the second half of the rows of O^T)
+  constexpr int DH = D / HP, NDBH = NDB / HP;
+  l = sum_over_rows(l);
+  f32x4_t ov[NDBH];
+  bool col;
+  int h;
+  if constexpr (HP == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) ov[db] = o[db];
+    col = n < it.nh;
+    h = it.hkv * prm.G + it.hg * 4 + n;
+  } else {
+    const bool hi = ((n >> 2) & 1) != 0;
+#pragma unroll
+    for (int db = 0; db < NDBH; ++db) {
+      // a select of values, not of the two array elements' addresses
+      // (which would put o in scratch memory to index it)
+      const f32x4_t lo = o[db], up = o[NDBH + db];
+      ov[db] = f32x4_t{hi ? up[0] : lo[0], hi ? up[1] : lo[1], hi ? up[2] : lo[2], hi ? up[3] : lo[3]};
+    }
+    col = n < 8 && (n & 3) < it.nh;
+    h = (2 * it.hkv + (hi ? 1 : 0)) * prm.G + it.hg * 4 + (n & 3);
+  }
+  if (col) {
+    if (it.nparts == 1) {
+      const float inv = it.vmul / l;
+      QT* dst = static_cast<QT*>(prm.out) + ((int64_t)it.row * prm.Hq + h) * DH + 4 * g;
+#pragma unroll
+      for (int db = 0; db < NDBH; ++db) {
+        if constexpr (Gm::kHalf) {
+          *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
+              u32x2_t{pack_bf16(ov[db][0] * inv, ov[db][1] * inv), pack_bf16(ov[db][2] * inv, ov[db][3] * inv)};
+        } else {
+          *reinterpret_cast<f32x4_t*>(dst + 16 * db) = ov[db] * inv;
+        }
+      }
+    } else {
+      const int64_t slot = ((int64_t)it.b * prm.Hq + h) * prm.max_parts + it.part;
+      float rs = 1.0f;  // the stored row is o / l / rs (bf16) or o (fp32)
+      if constexpr (Gm::kHalf) {
+        // bf16 requests: the partial output normalised by its sum, as fp16
+        // (half the bytes of fp32; its rounding is far below bf16's).  A
+        // normalised row is a weighted mean of value rows, so it can exceed
+        // the fp16 range only if the values do; then it is scaled down by a
+        // power of two, kept beside (max, sum), so it stays below 2^15.
+        const float inv = it.vmul / l;
+        float amax = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDBH; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(ov[db][j]));
+        amax = max_over_rows(amax * inv);  // the head's whole row (lanes n, n+16, n+32, n+48)
+        if (amax >= 32768.0f) {
+          int ex;
+          frexpf(amax, &ex);  // amax < 2^ex
+          rs = ldexpf(1.0f, ex - 15);
+        }
+        const float sc = inv / rs;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(prm.o) + slot * DH + 4 * g;
+#pragma unroll
+        for (int db = 0; db < NDBH; ++db)
+          *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
+              u32x2_t{pack_f16(ov[db][0] * sc, ov[db][1] * sc), pack_f16(ov[db][2] * sc, ov[db][3] * sc)};
+      } else {
+        float* dst = prm.o + slot * DH + 4 * g;
+#pragma unroll
+        for (int db = 0; db < NDBH; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db) = ov[db];
+      }
+      if (g == 0) *reinterpret_cast<f32x4_t*>(prm.ml + slot * 4) = f32x4_t{m, l, rs, 0.f};
+    }
+  }
+}
+
 template <typename T, int D, bool kWide, bool kAligned, int NR, bool kRowMap, int HP = 1, bool kAppend = false>
 __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds, const PlanLds* pl,
                                               unsigned long long tag, uint32_t n_items, uint32_t n_full,
@@ -820,7 +1219,14 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
   // round to the queues is best.
   uint32_t rounds = min((n_full * per_item) / nwaves, max_rounds);
   rounds = rounds > (uint32_t)prm.dyn_rounds ? rounds - (uint32_t)prm.dyn_rounds : min(rounds, 1u);
-  const uint32_t first_dyn = rounds * nwaves;
+  // With no whole static round (a batch whose full partitions do not fill
+  // one), each wave's first item is still dealt statically: wave w takes
+  // list entry w, the largest items first.  Otherwise every wave would start
+  // by claiming from the queue at once, and the claims on one counter are
+  // served one at a time.  (Decode calls only: in a mixed launch a wave may
+  // still be busy with a prefill item, and its item would wait for it.)
+  const bool first_static = !kRowMap && rounds == 0;
+  const uint32_t first_dyn = first_static ? min(total, nwaves) : rounds * nwaves;
   const uint32_t nq = prm.nq > 0 ? (uint32_t)prm.nq : nq_plan;
   const uint32_t home = blockIdx.x % nq;
   uint32_t queue = 0;
@@ -841,8 +1247,12 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
     it = make_item<kRowMap, Gm::TT, HP>(prm, lane_desc(sdesc, 0), f, per_item);
   } else {
     r = rounds;
-    f = claim(prm, tag, nq, home, queue, first_dyn, total);
-    if (f >= total) return;
+    if (first_static) {
+      if (wave >= first_dyn) return;  // more waves than items
+    } else {
+      f = claim(prm, tag, nq, home, queue, first_dyn, total);
+      if (f >= total) return;
+    }
     it = make_item<kRowMap, Gm::TT, HP>(prm, item_desc(prm, pl, n_full, f / per_item), f, per_item);
   }
   int ids[NR];
@@ -880,7 +1290,8 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
     else
       full = __builtin_amdgcn_readfirstlane((int)(__ballot(regs.ok != (1u << Gm::TPL) - 1u) == 0));
     if constexpr (kAppend && !Gm::kFp8) {
-      if (last && it.part == it.nparts - 1) append_regs<T, D, NR>(prm, pv, it, ids, tile0, nk, nv, regs);
+      if (last && it.part == it.nparts - 1)
+        append_regs<T, D>(prm, pv, it, append_block<NR>(prm, it, ids), prm.lens[it.b], tile0, nk, nv, regs);
     }
     wave_lds_sync();  // previous tile's LDS reads are done
     stage_tile<T, D>(lds, regs, full);
@@ -939,212 +1350,19 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
       if (fn < total) pend = 1;
     }
 
-    // ---- S^T = K Q^T, per 16-token half of the tile ----
-    // (HP = 2: the first D / 2 dimensions accumulate in s, the others in s2)
+    // ---- S^T = K Q^T, online softmax, O^T += V^T P^T ----
     constexpr int NH = Gm::TT / 16;
-    constexpr int NQ1 = Gm::NQ / HP;
     f32x4_t s[NH], s2[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) s[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if constexpr (HP == 2) {
-#pragma unroll
-      for (int h = 0; h < NH; ++h) s2[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    if constexpr (Gm::kFp8) {
-      // K operand: 8 codes of token 16 h + n, widened to fp16 as they are read
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-#pragma unroll
-        for (int i = 0; i < NQ1; ++i) {
-          const u32x2_t c = *reinterpret_cast<const u32x2_t*>(lds + (16 * h + n) * Gm::KST + 32 * i + 8 * g);
-          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, e4m3x8_to_f16(c)),
-                                                        __builtin_bit_cast(f16x8_t, qv[i]), s[h], 0, 0, 0);
-        }
-        if constexpr (HP == 2) {
-#pragma unroll
-          for (int i = NQ1; i < Gm::NQ; ++i) {
-            const u32x2_t c = *reinterpret_cast<const u32x2_t*>(lds + (16 * h + n) * Gm::KST + 32 * i + 8 * g);
-            s2[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, e4m3x8_to_f16(c)),
-                                                           __builtin_bit_cast(f16x8_t, qv[i]), s2[h], 0, 0, 0);
-          }
-        }
-      }
-    } else if constexpr (Gm::kBf16) {
-#pragma unroll
-      for (int i = 0; i < NQ1; ++i) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
-        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, qv[i]), s[0], 0, 0, 0);
-      }
-      if constexpr (HP == 2) {
-#pragma unroll
-        for (int i = NQ1; i < Gm::NQ; ++i) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 2 * (32 * i + 8 * g));
-          s2[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                          __builtin_bit_cast(bf16x8_t, qv[i]), s2[0], 0, 0, 0);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < Gm::NQ / 4; ++i) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lds + n * Gm::KST + 4 * (g * (D / 4) + 4 * i));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          s[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(qv[i][j]), s[0], 0, 0,
-                                                      0);
-      }
-    }
+    tile_scores<T, D, HP>(lds, qv, s, s2);
     if (last && has_next) load_q<T, D, HP>(prm, nx, qv);  // this item's query is no longer needed
-    if constexpr (HP == 2) {
-      const bool hi = ((n >> 2) & 1) != 0;
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const f32x4_t lo = s[h], up = s2[h];
-        s[h] = f32x4_t{hi ? up[0] : lo[0], hi ? up[1] : lo[1], hi ? up[2] : lo[2], hi ? up[3] : lo[3]};
-      }
-    }
-
-    // ---- online softmax for head n over tokens tile0 + 16h + 4g + j ----
-    float sc[NH][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sc[h][j] = (tile0 + 16 * h + 4 * g + j < it.tok_end) ? s[h][j] * it.sl2 : -INFINITY;
-        mx = fmaxf(mx, sc[h][j]);
-      }
-    mx = max_over_rows(mx);
-    // move the reference max only when a score exceeds it by the slack
-    // (always on the first tile, m = -inf); uniform branch, rarely taken
-    const bool move = mx > m + kRescaleSlack;
-    if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
-      const float alpha = (move && m != -INFINITY) ? fast_exp2(m - mx) : 1.0f;
-      if (move) m = mx;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-    }
-    float pp[NH][4];
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pp[h][j] = fast_exp2(sc[h][j] - m);
-        l += pp[h][j];
-      }
-    const float* p = pp[0];
-    // ---- O^T += V^T P^T ----
-    const char* vl = lds + Gm::KBYTES;
-    if constexpr (Gm::kFp8) {
-      // B operand: the lane's probabilities, k-slots 0-3 = tokens 4g + j and
-      // 4-7 = tokens 16 + 4g + j.  A operand (V^T) in the same token order
-      // from the byte-transposing read: lane n of each 16-lane group addresses
-      // V row 4g + n/2 (n < 8) or 12 + 4g + n/2 (n >= 8), bytes 16db + 8 (n % 2)
-      const u32x4_t pb = {pack_f16(pp[0][0], pp[0][1]), pack_f16(pp[0][2], pp[0][3]), pack_f16(pp[1][0], pp[1][1]),
-                          pack_f16(pp[1][2], pp[1][3])};
-      const char* vrow = vl + ((n < 8 ? 4 * g : 12 + 4 * g) + (n >> 1)) * Gm::KST + 8 * (n & 1);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t c = lds_read_tr8(vrow + 16 * db);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, e4m3x8_to_f16(c)),
-                                                       __builtin_bit_cast(f16x8_t, pb), o[db], 0, 0, 0);
-      }
-    } else if constexpr (Gm::kBf16) {
-      const u32x2_t pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x2_t a = *reinterpret_cast<const u32x2_t*>(vl + (16 * db + n) * Gm::VTS + 8 * g);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
-                                                          __builtin_bit_cast(s16x4_t, pb), o[db], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float a = *reinterpret_cast<const float*>(vl + (4 * g + j) * Gm::KST + 4 * (16 * db + n));
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[j], o[db], 0, 0, 0);
-        }
-    }
+    own_half<NH, HP>(s, s2);
+    tile_softmax_pv<T, D>(lds, it, tile0, s, m, l, o);
     if (!last) {
       ++t;
       continue;
     }
 
-    // ---- item done: total of l over the four 16-lane rows; store head n ----
-    // (HP = 2: column n's head is the pair's first or second, and its outputs
-    // are the first or the second half of the rows of O^T)
-    constexpr int DH = D / HP, NDBH = NDB / HP;
-    l = sum_over_rows(l);
-    f32x4_t ov[NDBH];
-    bool col;
-    int h;
-    if constexpr (HP == 1) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) ov[db] = o[db];
-      col = n < it.nh;
-      h = it.hkv * prm.G + it.hg * 4 + n;
-    } else {
-      const bool hi = ((n >> 2) & 1) != 0;
-#pragma unroll
-      for (int db = 0; db < NDBH; ++db) {
-        // a select of values, not of the two array elements' addresses
-        // (which would put o in scratch memory to index it)
-        const f32x4_t lo = o[db], up = o[NDBH + db];
-        ov[db] = f32x4_t{hi ? up[0] : lo[0], hi ? up[1] : lo[1], hi ? up[2] : lo[2], hi ? up[3] : lo[3]};
-      }
-      col = n < 8 && (n & 3) < it.nh;
-      h = (2 * it.hkv + (hi ? 1 : 0)) * prm.G + it.hg * 4 + (n & 3);
-    }
-    if (col) {
-      if (it.nparts == 1) {
-        const float inv = it.vmul / l;
-        QT* dst = static_cast<QT*>(prm.out) + ((int64_t)it.row * prm.Hq + h) * DH + 4 * g;
-#pragma unroll
-        for (int db = 0; db < NDBH; ++db) {
-          if constexpr (Gm::kHalf) {
-            *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
-                u32x2_t{pack_bf16(ov[db][0] * inv, ov[db][1] * inv), pack_bf16(ov[db][2] * inv, ov[db][3] * inv)};
-          } else {
-            *reinterpret_cast<f32x4_t*>(dst + 16 * db) = ov[db] * inv;
-          }
-        }
-      } else {
-        const int64_t slot = ((int64_t)it.b * prm.Hq + h) * prm.max_parts + it.part;
-        float rs = 1.0f;  // the stored row is o / l / rs (bf16) or o (fp32)
-        if constexpr (Gm::kHalf) {
-          // bf16 requests: the partial output normalised by its sum, as fp16
-          // (half the bytes of fp32; its rounding is far below bf16's).  A
-          // normalised row is a weighted mean of value rows, so it can exceed
-          // the fp16 range only if the values do; then it is scaled down by a
-          // power of two, kept beside (max, sum), so it stays below 2^15.
-          const float inv = it.vmul / l;
-          float amax = 0.f;
-#pragma unroll
-          for (int db = 0; db < NDBH; ++db)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(ov[db][j]));
-          amax = max_over_rows(amax * inv);  // the head's whole row (lanes n, n+16, n+32, n+48)
-          if (amax >= 32768.0f) {
-            int ex;
-            frexpf(amax, &ex);  // amax < 2^ex
-            rs = ldexpf(1.0f, ex - 15);
-          }
-          const float sc = inv / rs;
-          uint16_t* dst = reinterpret_cast<uint16_t*>(prm.o) + slot * DH + 4 * g;
-#pragma unroll
-          for (int db = 0; db < NDBH; ++db)
-            *reinterpret_cast<u32x2_t*>(dst + 16 * db) =
-                u32x2_t{pack_f16(ov[db][0] * sc, ov[db][1] * sc), pack_f16(ov[db][2] * sc, ov[db][3] * sc)};
-        } else {
-          float* dst = prm.o + slot * DH + 4 * g;
-#pragma unroll
-          for (int db = 0; db < NDBH; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db) = ov[db];
-        }
-        if (g == 0) *reinterpret_cast<f32x4_t*>(prm.ml + slot * 4) = f32x4_t{m, l, rs, 0.f};
-      }
-    }
+    store_item<T, D, HP>(prm, it, m, l, o);
     if (!has_next) break;
     // the next item's ids, first tile and query are already in flight
     it = nx;
@@ -1156,6 +1374,256 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
     l = 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode stream with two tiles in flight per wave (bf16 pools).  It computes
+// the same items in the same order as decode_stream, each with the same
+// arithmetic (the helpers above), so its results are the same bits.  The
+// difference is in the loads: decode_stream issues a tile's loads after it
+// has staged the tile before it, so one tile is in flight while a tile is
+// computed; here a producer cursor runs two tiles ahead of the tile being
+// computed.  After the consumer has staged tile g of the stream from register
+// set g % 2, the producer issues tile g + 2 into that set.  A wave whose
+// tiles arrive one memory latency apart (few items per wave: small batches)
+// then waits half as long per tile, and fewer waves per SIMD keep as many
+// bytes in flight.
+//
+// The producer fetches the next item (claim, descriptor, block ids) relative
+// to its own item's tiles, as decode_stream does relative to the computed
+// one.  Items whose first tile is issued but which the consumer has not yet
+// started wait in a queue of two (the producer is at most two tiles ahead, and
+// every item has at least one tile); the consumer rebuilds an item from its
+// descriptor and flat index when it gets to it.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+struct TileSet {
+  TileRegs<T, D> regs;
+  int alen;        // decode with append: the request's unclamped length (the item's last tile)
+  int ablk;        // decode with append: block id of the item's position L - 1
+};
+
+template <typename T, int D, bool kWide, bool kAligned, int NR, int HP = 1, bool kAppend = false>
+__device__ __forceinline__ void decode_stream2(const DecodeParams& prm, char* lds, const PlanLds* pl,
+                                               unsigned long long tag, uint32_t n_items, uint32_t n_full,
+                                               uint32_t nq_plan, uint32_t wave, uint32_t nwaves,
+                                               uint32_t max_rounds) {
+  using Gm = Geo<T, D>;
+  static_assert(!Gm::kFp8, "fp8 pools make the new token's codes in LDS; they use decode_stream");
+  constexpr int NDB = D / 16;
+  constexpr int NH = Gm::TT / 16;
+  const int lane = lane_id();
+  const uint32_t per_item = (uint32_t)(prm.Hkv * prm.n_hg);
+  const uint32_t total = n_items * per_item;
+  // the schedule of decode_stream (plain decode: first item static when no
+  // whole round is)
+  uint32_t rounds = min((n_full * per_item) / nwaves, max_rounds);
+  rounds = rounds > (uint32_t)prm.dyn_rounds ? rounds - (uint32_t)prm.dyn_rounds : min(rounds, 1u);
+  const bool first_static = rounds == 0;
+  const uint32_t first_dyn = first_static ? min(total, nwaves) : rounds * nwaves;
+  const uint32_t nq = prm.nq > 0 ? (uint32_t)prm.nq : nq_plan;
+  const uint32_t home = blockIdx.x % nq;
+  uint32_t queue = 0;
+  PoolView pv;
+  pv.k = static_cast<const char*>(prm.kc);
+  pv.v = static_cast<const char*>(prm.vc);
+  pv.row_bytes = (uint32_t)(prm.Hkv * Gm::GROWB);
+  i32x4_t sdesc = {0, 0, 0, 0};
+  if (rounds > 0) sdesc = item_desc(prm, pl, n_full, (wave + (uint32_t)min(lane, (int)rounds - 1) * nwaves) / per_item);
+
+  // ---- producer: the item whose tiles it issues ----
+  uint32_t r = 0;        // its static round (rounds once dynamic)
+  uint32_t pf = wave;    // its flat index
+  i32x4_t pd;            // the first item's descriptor
+  if (rounds > 0) {
+    pd = lane_desc(sdesc, 0);
+  } else {
+    r = rounds;
+    if (first_static) {
+      if (wave >= first_dyn) return;  // more waves than items
+    } else {
+      pf = claim(prm, tag, nq, home, queue, first_dyn, total);
+      if (pf >= total) return;
+    }
+    pd = item_desc(prm, pl, n_full, pf / per_item);
+  }
+  Item pit = make_item<false, Gm::TT, HP>(prm, pd, pf, per_item);
+  int pids[NR];
+  load_ids<NR>(prm, pit, pids);
+  int pt = 0;            // next tile of pit to issue
+  bool pdone = false;    // the stream is fully issued
+  // its next item, once known (descriptor and flat index; the item itself
+  // is rebuilt from them when the producer gets to it)
+  uint32_t fn = 0;
+  i32x4_t nd = {0, 0, 0, 0};
+  bool has_next = false;
+  int idn[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) idn[i] = 0;
+  // items issued but not yet started by the consumer (descriptor, flat index)
+  i32x4_t qd0 = {0, 0, 0, 0}, qd1 = {0, 0, 0, 0};
+  uint32_t qf0 = 0, qf1 = 0;
+  int nqueued = 0;
+  unsigned long long pending = 0;  // a claim's first atomic, issued but not yet read
+  bool claimed = false;
+
+  // ---- consumer: the item being computed ----
+  Item it = pit;
+  u32x4_t qv[Gm::NQV];   // its query
+  load_q<T, D, HP>(prm, it, qv);
+  int ct = 0;            // its tile being computed
+  float m = -INFINITY, l = 0.f;
+  f32x4_t o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  TileSet<T, D> sa, sb;
+
+  // Issues the stream's next tile into S (nothing once the stream is issued).
+  auto produce = [&](TileSet<T, D>& S) {
+    if (pt == pit.ntiles && !has_next) pdone = true;
+    if (pdone) {
+      // the stream is fully issued: the same loads as a tile, every token
+      // masked (each lane reads its piece of row 0, which stays in cache).
+      // The set is never staged again; the loads are there so that every
+      // path issues as many loads after a set's as the wait for it assumes
+      // (otherwise the wait before staging would drain both sets).
+      load_tile<T, D, kWide, kAligned, NR>(pv, prm, pit, pids, pit.tok_end, S.regs);
+      return;
+    }
+    if (pt == pit.ntiles) {
+      // a real branch, not a select: a select would read idn at every tile
+      // and so wait for its load right after it is issued
+      asm volatile("" ::: "memory");
+      pit = make_item<false, Gm::TT, HP>(prm, nd, fn, per_item);
+      pf = fn;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) pids[i] = idn[i];
+      r = r + 1 < rounds ? r + 1 : rounds;
+      has_next = false;
+      pt = 0;
+      if (nqueued == 0) {
+        qd0 = nd;
+        qf0 = fn;
+      } else {
+        qd1 = nd;
+        qf1 = fn;
+      }
+      ++nqueued;
+    }
+    if constexpr (kAppend) {
+      if (pt + 1 == pit.ntiles && pit.part == pit.nparts - 1) {
+        // the item's last tile holds the new token (position L - 1): its
+        // lanes load it from the new rows, as the scatter would have written it
+        const int64_t off = (int64_t)pit.b * (prm.Hkv * Gm::GROWB) + pit.hkv * Gm::GROWB + 16 * (lane % Gm::CPR);
+        load_tile<T, D, kWide, kAligned, NR, true>(pv, prm, pit, pids, pit.tok0 + pt * Gm::TT, S.regs, pit.L - 1,
+                                                   static_cast<const char*>(prm.knew) + off,
+                                                   static_cast<const char*>(prm.vnew) + off);
+        S.alen = prm.lens[pit.b];  // behind the tile's loads, read when the tile is staged
+        S.ablk = __builtin_amdgcn_readfirstlane(append_block<NR>(prm, pit, pids));
+      } else {
+        load_tile<T, D, kWide, kAligned, NR>(pv, prm, pit, pids, pit.tok0 + pt * Gm::TT, S.regs);
+      }
+    } else {
+      load_tile<T, D, kWide, kAligned, NR>(pv, prm, pit, pids, pit.tok0 + pt * Gm::TT, S.regs);
+    }
+    // the next item: a static one is known at once.  A dynamic one is
+    // claimed near the end of this item, so that the claims of waves that
+    // started together do not all reach the counter at once: the atomic is
+    // issued with tile n - 5, and its result read with tile n - 3, when the
+    // consumer has staged the tile issued before it (reading it waits for
+    // nothing in flight); the ids are loaded then too, two tiles before they
+    // are needed.  Items of fewer than five tiles claim everything up front.
+    const bool stat_next = r + 1 < rounds;
+    const int n = pit.ntiles;
+    if (stat_next) {
+      if (pt == 0) {
+        fn = pf + nwaves;
+        nd = lane_desc(sdesc, (int)r + 1);
+        has_next = true;
+        load_ids<NR>(prm, make_item<false, Gm::TT, HP>(prm, nd, fn, per_item), idn);
+      }
+    } else if (n < 5) {
+      if (pt == 0) {
+        fn = claim(prm, tag, nq, home, queue, first_dyn, total);
+        if (fn < total) {
+          nd = item_desc(prm, pl, n_full, fn / per_item);
+          has_next = true;
+          load_ids<NR>(prm, make_item<false, Gm::TT, HP>(prm, nd, fn, per_item), idn);
+        }
+      }
+    } else if (pt == n - 5) {
+      claimed = claim_start(prm, nq, home, queue, first_dyn, total, pending);
+    } else if (pt == n - 3) {
+      fn = claim_finish(prm, tag, nq, home, queue, first_dyn, total, claimed, pending);
+      if (fn < total) {
+        nd = item_desc(prm, pl, n_full, fn / per_item);
+        has_next = true;
+        load_ids<NR>(prm, make_item<false, Gm::TT, HP>(prm, nd, fn, per_item), idn);
+      }
+    }
+    ++pt;
+  };
+
+  // Stages and computes the stream's tile held in S, after refilling S with
+  // the tile two ahead.  Returns true once the stream is done.
+  auto consume = [&](TileSet<T, D>& S) -> bool {
+    const int tile0 = it.tok0 + ct * Gm::TT;
+    const bool last = ct + 1 == it.ntiles;
+    bool full;
+    if constexpr (kAligned && Gm::TT == 16)
+      full = tile0 + Gm::TT <= it.tok_end && __builtin_amdgcn_readfirstlane((int)S.regs.ok) == (1 << Gm::TPL) - 1;
+    else
+      full = __builtin_amdgcn_readfirstlane((int)(__ballot(S.regs.ok != (1u << Gm::TPL) - 1u) == 0));
+    const bool app = kAppend && last && it.part == it.nparts - 1;
+    if constexpr (kAppend) {
+      if (app && S.alen <= prm.cap) append_from_regs<T, D>(prm, pv, it, S.ablk, tile0, S.regs);
+    }
+    wave_lds_sync();  // previous tile's LDS reads are done
+    if (full) stage_tile_ro<T, D, false>(lds, S.regs);
+    else stage_tile_ro<T, D, true>(lds, S.regs);
+    if constexpr (kAppend) {
+      if (app && S.alen > prm.cap) {
+        wave_lds_sync();
+        unappend_lds<T, D>(prm, pv, it, S.ablk, tile0, lds);
+      }
+    }
+    wave_lds_sync();
+    // ---- S^T = K Q^T, online softmax, O^T += V^T P^T ----
+    f32x4_t s[NH], s2[NH];
+    tile_scores<T, D, HP>(lds, qv, s, s2);
+    // the next item's query, once this item's is no longer needed, and before
+    // the tile issued next: reading it then waits only for the tile already
+    // in flight, which is staged first anyway (the next item's first tile is
+    // issued, so it is queued, when this is the last tile)
+    if (last && nqueued > 0) load_q<T, D, HP>(prm, make_item<false, Gm::TT, HP>(prm, qd0, qf0, per_item), qv);
+    produce(S);
+    own_half<NH, HP>(s, s2);
+    tile_softmax_pv<T, D>(lds, it, tile0, s, m, l, o);
+    if (!last) {
+      ++ct;
+      return false;
+    }
+    store_item<T, D, HP>(prm, it, m, l, o);
+    if (nqueued == 0) return true;  // the producer is ahead: no queued item, no next item
+    it = make_item<false, Gm::TT, HP>(prm, qd0, qf0, per_item);
+    qd0 = qd1;
+    qf0 = qf1;
+    --nqueued;
+    ct = 0;
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    return false;
+  };
+
+  produce(sa);
+  produce(sb);
+  for (;;) {
+    if (consume(sa)) break;
+    if (consume(sb)) break;
   }
 }
 

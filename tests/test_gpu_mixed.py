@@ -211,36 +211,48 @@ def test_queue_giveup_is_reported(monkeypatch):
     """A wave that gives up waiting on a work queue leaves that queue's items
     uncomputed; the workspace's status word must say so.  PA_TEST_QUEUE_GIVEUP=1
     forces every claim to give up at once (every kernel still exits): the
-    decode call reports bit 1, the mixed call bits 1 and 2, the allocation-free
-    call bit 1 in the static scratch.  Normal calls leave the word clear and
-    compute the right rows again."""
+    decode call reports bit 1 (with one and with two tiles in flight per wave:
+    block tables of 512 and of 256 entries), the mixed call bits 1 and 2, the
+    allocation-free call bit 1 in the static scratch.  Batches whose items are
+    all dealt statically make no claim and lose nothing.  Normal calls leave
+    the word clear and compute the right rows again."""
     c = case(lens=(5, 300, 1025, 4000, 77, 512, 2048, 700), qlens=(1, 1, 1, 300, 1, 100, 1, 1), seed=93)
     d = DevCase(c)
     ref = to_host_bits(separate(d))
     B, Hq, D, P, M = c.B, c.num_q_heads, c.head_dim, c.block_size, c.max_blocks_per_seq
     wsm = torch.empty(pa.mixed_workspace_size(B, Hq, D, P, M), dtype=torch.uint8, device=DEV)
-    dd = DevCase(case(lens=(5, 300, 1025, 4000), qlens=(1, 1, 1, 1), seed=94))
+    # 40 requests of 4000 tokens: 5000 items, more than the waves, so the queues are used
+    dd = DevCase(case(lens=(4000,) * 40, qlens=(1,) * 40, seed=94, max_blocks_per_seq=512))
     cd = dd.case
-    wsd = torch.empty(pa.decode_workspace_size(cd.B, Hq, D, P, cd.max_blocks_per_seq), dtype=torch.uint8, device=DEV)
-    outd = torch.empty_like(dd.q)
+    bt256 = dd.bt[:, :256].contiguous()
+    outs = {w: torch.empty_like(dd.q) for w in (256, 512)}
+    ws = {w: torch.empty(pa.decode_workspace_size(cd.B, Hq, D, P, w), dtype=torch.uint8, device=DEV)
+          for w in (256, 512)}
     outm = torch.empty_like(d.q)
+    tiny = DevCase(case(lens=(5, 300, 1025), qlens=(1, 1, 1), seed=96))
+    wst = torch.empty(pa.decode_workspace_size(3, Hq, D, P, tiny.case.max_blocks_per_seq), dtype=torch.uint8,
+                      device=DEV)
+    outt = torch.empty_like(tiny.q)
 
     def run():
-        pa.paged_decode_attention(dd.q, dd.kc, dd.vc, dd.bt, dd.lens, cd.scale, outd, workspace=wsd)
+        for w, bt in ((256, bt256), (512, dd.bt)):
+            pa.paged_decode_attention(dd.q, dd.kc, dd.vc, bt, dd.lens, cd.scale, outs[w], workspace=ws[w])
+        pa.paged_decode_attention(tiny.q, tiny.kc, tiny.vc, tiny.bt, tiny.lens, tiny.case.scale, outt, workspace=wst)
         pa.paged_mixed_attention(d.q, d.kc, d.vc, d.cu, d.bt, d.lens, c.scale, outm, workspace=wsm)
-        pa.paged_decode_attention_noalloc(dd.q, dd.kc, dd.vc, dd.bt, dd.lens, cd.scale, outd)
+        pa.paged_decode_attention_noalloc(dd.q, dd.kc, dd.vc, dd.bt, dd.lens, cd.scale, outs[512])
 
-    for ws in (wsd, wsm):
-        pa.workspace_status(ws)  # a new workspace holds arbitrary bits: the first query clears them
-    pa.workspace_status(noalloc=True)
+    def status():
+        return (pa.workspace_status(ws[256]), pa.workspace_status(ws[512]), pa.workspace_status(wst),
+                pa.workspace_status(wsm), pa.workspace_status(noalloc=True))
+
+    status()  # a new workspace holds arbitrary bits: the first query clears them
     run()
-    assert (pa.workspace_status(wsd), pa.workspace_status(wsm), pa.workspace_status(noalloc=True)) == (0, 0, 0)
+    assert status() == (0, 0, 0, 0, 0)
     monkeypatch.setenv("PA_TEST_QUEUE_GIVEUP", "1")
     run()
     monkeypatch.delenv("PA_TEST_QUEUE_GIVEUP")
-    assert pa.workspace_status(wsd) == 1
-    assert pa.workspace_status(wsm) == 3
-    assert pa.workspace_status(noalloc=True) == 1
+    assert status() == (1, 1, 0, 3, 1)
     run()
-    assert (pa.workspace_status(wsd), pa.workspace_status(wsm), pa.workspace_status(noalloc=True)) == (0, 0, 0)
+    assert status() == (0, 0, 0, 0, 0)
     assert np.array_equal(to_host_bits(outm), ref)
+    assert np.array_equal(to_host_bits(outs[256]), to_host_bits(outs[512]))

@@ -887,3 +887,37 @@ def test_decode_append_large_batch_plan_kernel_path(kind):
     (o1, k1, v1), (o2, k2, v2) = append_both_ways(c, q, kn, vn, bt, lens_d, scales)
     assert same_bits(k1, k2) and same_bits(v1, v2), "pools differ"
     assert same_bits(o1, o2), "outputs differ"
+
+
+@pytest.mark.parametrize("append", [False, True])
+def test_decode_one_and_two_tiles_in_flight_agree_bitwise(append):
+    """bf16 batches whose shapes bound the work at 8192 items or fewer run with
+    two tiles in flight per wave, larger ones with one; the items and their
+    arithmetic are the same, so the bits are.  The same requests with a block
+    table of 64 entries (40 x 4 partitions x 8 KV heads = 1280 items) and of
+    512 entries (10240) take the two paths and must give identical outputs
+    and pools, against the oracle too."""
+    lens = [1, 15, 16, 17, 255, 256, 257, 300, 511, 512, 513, 700, 1000, 1024] + list(range(33, 1024, 39))
+    c = small(P=16, Hq=32, Hkv=8, D=128, lens=tuple(lens), seed=95)
+    assert c.max_blocks_per_seq <= 64
+    outs = []
+    for M in (64, 512):
+        bt_np = np.full((c.B, M), c.filler_block, dtype=np.int32)
+        bt_np[:, :c.max_blocks_per_seq] = c.block_table
+        bt, lens_d = idx(bt_np), idx(c.context_lens)
+        q = to_dev(c.q, c.dtype)
+        out = torch.empty_like(q)
+        if append:
+            kc, vc = prefix_pools(c)
+            kn, vn = (to_dev(x, c.dtype) for x in c.new_kv())
+            pa.paged_decode_append(q, kn, vn, kc, vc, bt, lens_d, c.scale, out)
+        else:
+            d = DevCase(c)
+            kc, vc = d.kc, d.vc
+            pa.paged_decode_attention(q, kc, vc, bt, lens_d, c.scale, out)
+        torch.cuda.synchronize()
+        outs.append((out, kc, vc))
+    (o1, k1, v1), (o2, k2, v2) = outs
+    assert same_bits(o1, o2), "one and two tiles in flight differ"
+    assert same_bits(k1, k2) and same_bits(v1, v2)
+    assert_close(o1, decode_ref(c), c.dtype, f"decode append={append}")
