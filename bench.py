@@ -57,8 +57,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["all", "llama3_8b", "llama3_8b_fp8", "tiny", "gpt2_124m", "llama32_1b",
-                                           "mixed", "mixed_fp8", "mixed_single", "mixed_single_fp8", "cow", "copy"],
+    ap.add_argument("--workload", choices=["all", "llama3_8b", "llama3_8b_fp8", "llama3_8b_g8", "tiny", "gpt2_124m",
+                                           "llama32_1b", "mixed", "mixed_fp8", "mixed_single", "mixed_single_fp8",
+                                           "cow", "copy"],
                     default="all")
     ap.add_argument("--layers", type=int, default=None, help="profile runs only: fewer layers")
     ap.add_argument("--block-size", type=int, default=None)
@@ -354,23 +355,30 @@ def guarded_kernel_ms(pa, call, reps, dev):
 
 
 SMALL_DECODE = {"tiny": 0, "gpt2_124m": 1, "llama32_1b": 2}
+# A GQA group of 8: the Llama-3-8B batch, pool and lengths with 64 query
+# heads over its 8 KV heads (the head layout of the 70B and 405B models), one
+# layer.  Each KV slice is read once for all 8 query heads it serves.
+WIDE_GROUP = {"llama3_8b_g8": dict(idx=3, Hq=64, layers=1)}
 
 
 def bench_decode_small(args, name):
-    """Decode step of a smaller seeded workload (tiny, GPT-2-124M, Llama-3.2-1B):
-    per layer one decode-with-append call, every layer with its own pool.  Steps
-    take tens of microseconds per layer, less than the host needs to issue a
-    call from Python, so the step is timed as HIP-graph replays (the eager time
-    is reported beside it).  The partition kernel's own duration comes from the
-    guarded event loop."""
+    """Decode step of a smaller seeded workload (tiny, GPT-2-124M, Llama-3.2-1B,
+    or one layer of the GQA-8 batch): per layer one decode-with-append call,
+    every layer with its own pool.  Steps take tens of microseconds per layer,
+    less than the host needs to issue a call from Python, so the step is timed
+    as HIP-graph replays (the eager time is reported beside it).  The partition
+    kernel's own duration comes from the guarded event loop."""
     import paged_kv_cache_48_amd as pa
     from workloads import config_case
 
-    idx = SMALL_DECODE[name]
+    wide = WIDE_GROUP.get(name)
+    idx = wide["idx"] if wide else SMALL_DECODE[name]
     case = config_case(idx, values=False)
     dev = torch.device("cuda:0")
     B, Hq, Hkv, D, P, N = case.B, case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size, case.num_blocks
     L = case.num_layers
+    if wide:
+        Hq, L = wide["Hq"], wide["layers"]
     tdt = torch.float32 if case.dtype == "f32" else torch.bfloat16
     s = 4 if case.dtype == "f32" else 2
     gen = torch.Generator(device=dev)
@@ -1055,6 +1063,9 @@ def run_all(args):
             log(f"timing the oracle on {name}")
             entry["cpu_baseline"] = cpu_baseline_config(SMALL_DECODE[name])
         wl[name] = with_oracle_speedup(entry)
+    for name in WIDE_GROUP:
+        wl[name] = bench_decode_small(args, name)
+        free_gpu()
     r8, c8 = bench_decode(sub(workload="llama3_8b_fp8"), ceiling_run=False)
     free_gpu()
     if not args.no_cpu_baseline:
@@ -1095,9 +1106,9 @@ def main():
         res = bench_copy(args)
     elif args.workload == "cow":
         res = bench_cow(args)
-    elif args.workload in SMALL_DECODE:
+    elif args.workload in SMALL_DECODE or args.workload in WIDE_GROUP:
         res = bench_decode_small(args, args.workload)
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and args.workload in SMALL_DECODE:
             res["cpu_baseline"] = cpu_baseline_config(SMALL_DECODE[args.workload])
     elif args.workload.startswith("mixed"):
         res, case = bench_mixed(args)

@@ -9,7 +9,7 @@
 // Design (MI355X):
 //   * Split context.  Each request is cut into partitions of kPartTokens tokens
 //     (a count that depends on L_b only).  A (request, partition, KV head, group
-//     of up to 4 query heads) is one work item; a single wave64 computes it.
+//     of up to 16 query heads) is one work item; a single wave64 computes it.
 //   * Work queue.  The (request, partition) items are listed full partitions
 //     first and short tail partitions last: for batches of up to
 //     kSelfPlanMax requests every workgroup derives the list itself in LDS
@@ -289,14 +289,16 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, 
   prm.o = reinterpret_cast<float*>(ws + Lw.o);
   prm.scale_log2 = a.scale * kLog2e;
   prm.Hq = a.num_q_heads;
-  prm.G = a.num_q_heads / a.num_kv_heads;
-  prm.n_hg = (prm.G + 3) / 4;
+  const int G = a.num_q_heads / a.num_kv_heads;
   const bool fp8 = a.kv_dtype == kFP8E4M3;
   // bf16 pools with 64-dim heads and fp8 pools: adjacent KV heads are read in
   // pairs, as one head of twice the dimension (256-byte token rows, as the
-  // bf16 128-dim kernel reads); each query column keeps its own head's half
-  const bool pairs = (fp8 || (a.dtype == kBF16 && a.head_dim == 64)) && a.num_kv_heads % 2 == 0;
+  // bf16 128-dim kernel reads); each query column keeps its own head's half.
+  // A pair's two groups share the 16 columns, so pairs are taken only while
+  // the group fits in 8: beyond that, single heads read each slice once.
+  const bool pairs = (fp8 || (a.dtype == kBF16 && a.head_dim == 64)) && a.num_kv_heads % 2 == 0 && G <= 8;
   prm.Hkv = pairs ? a.num_kv_heads / 2 : a.num_kv_heads;
+  set_query_groups(prm, G, pairs ? 2 : 1);
   prm.P = a.block_size;
   prm.p_shift = (a.block_size & (a.block_size - 1)) == 0 ? __builtin_ctz((unsigned)a.block_size) : -1;
   prm.N = (int)a.num_blocks;

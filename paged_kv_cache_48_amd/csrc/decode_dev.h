@@ -157,6 +157,7 @@ struct DecodeParams {
   float* o;
   float scale_log2;
   int Hq, Hkv, G, n_hg, P, p_shift, N, M, cap, max_parts;
+  int gw, gs;       // query heads per group (4, 8 or 16) and its log2
   int dyn_rounds;  // full rounds of full partitions left to the queues
   int nq;          // queues in use (at most kQueues); 0: as the plan chose
   int B;
@@ -181,6 +182,19 @@ struct DecodeParams {
   int force_giveup;  // test knob: every claim sees a stale counter and gives up at once
 };
 
+// Query heads per item: the G query heads that share a KV head take
+// columns of one 16-column MFMA operand, so a group of up to 16 (8 per head
+// of a pair) reads each KV slice once; larger G splits into groups of 16.
+// The width is a power of two (4, 8 or 16) so a column's head is a shift
+// and a mask of its index.
+inline void set_query_groups(DecodeParams& prm, int G, int HP) {
+  const int cols = 16 / HP;
+  prm.gw = G <= 4 ? 4 : (G <= 8 || cols == 8) ? 8 : 16;
+  prm.gs = prm.gw == 4 ? 2 : prm.gw == 8 ? 3 : 4;
+  prm.G = G;
+  prm.n_hg = (G + prm.gw - 1) / prm.gw;
+}
+
 // One work item, wave-uniform (scalar registers).
 struct Item {
   int b, part, L, nparts;  // request, partition, visible tokens, partitions of the request
@@ -201,7 +215,7 @@ __device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, ui
   const int rem = (int)(f % per_item);
   it.hkv = rem / prm.n_hg;
   it.hg = rem - it.hkv * prm.n_hg;
-  it.nh = min(4, prm.G - it.hg * 4);
+  it.nh = min(prm.gw, prm.G - it.hg * prm.gw);
   it.tok0 = it.part * kPartTokens;
   it.tok_end = min(it.L, it.tok0 + kPartTokens);
   it.ntiles = (it.tok_end - it.tok0 + TT - 1) / TT;
@@ -219,8 +233,8 @@ __device__ __forceinline__ Item make_item(const DecodeParams& prm, i32x4_t d, ui
   it.vmul = prm.v_scale ? prm.v_scale[it.hkv] : 1.0f;
   if constexpr (HP == 2) {
     // head pairs: the factors are per column (column n of the lane belongs
-    // to KV head 2 hkv + (n / 4) % 2)
-    const int hs = 2 * it.hkv + ((lane_id() >> 2) & 1);
+    // to KV head 2 hkv + (n / gw) % 2)
+    const int hs = 2 * it.hkv + (((lane_id() & 15) >> prm.gs) & 1);
     if (prm.k_scale) it.sl2 = prm.scale_log2 * prm.k_scale[hs];
     if (prm.v_scale) it.vmul = prm.v_scale[hs];
   }
@@ -241,8 +255,8 @@ __device__ __forceinline__ void load_ids(const DecodeParams& prm, const Item& it
 // last read head 0's row; their columns are never stored).
 // HP = 2 (adjacent KV heads taken in pairs, read as one head of dimension D:
 // 64-dim bf16 or fp8 heads as D = 128, 128-dim fp8 heads as D = 256): columns
-// 0..3 are the group's query heads of the first KV head of the pair, columns
-// 4..7 those of the second.  Each column's query is its own head's D / 2
+// 0 .. gw-1 are the group's query heads of the first KV head of the pair,
+// columns gw .. 2gw-1 those of the second.  Each column's query is its own head's D / 2
 // dimensions, in both halves of the operand: the score products over the
 // first and the second half go to separate accumulators, and each column
 // keeps the one of its own head.
@@ -254,9 +268,9 @@ __device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, 
   const int n = lane & 15, g = lane >> 4;
   if constexpr (HP == 2) {
     static_assert(Gm::kHalf && (D == 128 || (Gm::kFp8 && D == 256)), "head pairs");
-    const int hi = (n >> 2) & 1, c = n & 3;
-    const bool col = n < 8 && c < it.nh;
-    const int h = (2 * it.hkv + hi) * prm.G + it.hg * 4 + (col ? c : 0);
+    const int hi = (n >> prm.gs) & 1, c = n & (prm.gw - 1);
+    const bool col = n < 2 * prm.gw && c < it.nh;
+    const int h = (2 * it.hkv + hi) * prm.G + it.hg * prm.gw + (col ? c : 0);
     const QT* qrow = static_cast<const QT*>(prm.q) + ((int64_t)it.row * prm.Hq + h) * (D / 2);
 #pragma unroll
     for (int i = 0; i < Gm::NQV / 2; ++i) {
@@ -271,7 +285,7 @@ __device__ __forceinline__ void load_q(const DecodeParams& prm, const Item& it, 
     }
     return;
   }
-  const int h = it.hkv * prm.G + it.hg * 4 + (n < it.nh ? n : 0);
+  const int h = it.hkv * prm.G + it.hg * prm.gw + (n < it.nh ? n : 0);
   const QT* qrow = static_cast<const QT*>(prm.q) + ((int64_t)it.row * prm.Hq + h) * D;
 #pragma unroll
   for (int i = 0; i < Gm::NQV; ++i) {
@@ -766,7 +780,7 @@ __device__ __forceinline__ i32x4_t item_desc(const DecodeParams& prm, const Plan
 
 // ---------------------------------------------------------------------------
 // Partition kernel.  One wave = one work item (request, partition, KV head,
-// group of up to 4 query heads) at a time.
+// group of up to 16 query heads) at a time.
 //
 // Schedule: the flat item list (items x KV heads x head groups) starts with
 // the full partitions, all of the same size.  Whole rounds of those are dealt
@@ -1028,10 +1042,10 @@ __device__ __forceinline__ void tile_scores(const char* lds, const u32x4_t (&qv)
 
 // HP = 2: each column keeps the scores of its own KV head of the pair.
 template <int NH, int HP>
-__device__ __forceinline__ void own_half(f32x4_t (&s)[NH], const f32x4_t (&s2)[NH]) {
+__device__ __forceinline__ void own_half(f32x4_t (&s)[NH], const f32x4_t (&s2)[NH], int gs) {
   const int n = lane_id() & 15;
   if constexpr (HP == 2) {
-    const bool hi = ((n >> 2) & 1) != 0;
+    const bool hi = ((n >> gs) & 1) != 0;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const f32x4_t lo = s[h], up = s2[h];
@@ -1136,9 +1150,9 @@ __device__ __forceinline__ void store_item(const DecodeParams& prm, const Item& 
 #pragma unroll
     for (int db = 0; db < NDB; ++db) ov[db] = o[db];
     col = n < it.nh;
-    h = it.hkv * prm.G + it.hg * 4 + n;
+    h = it.hkv * prm.G + it.hg * prm.gw + n;
   } else {
-    const bool hi = ((n >> 2) & 1) != 0;
+    const bool hi = ((n >> prm.gs) & 1) != 0;
 #pragma unroll
     for (int db = 0; db < NDBH; ++db) {
       // a select of values, not of the two array elements' addresses
@@ -1146,8 +1160,8 @@ __device__ __forceinline__ void store_item(const DecodeParams& prm, const Item& 
       const f32x4_t lo = o[db], up = o[NDBH + db];
       ov[db] = f32x4_t{hi ? up[0] : lo[0], hi ? up[1] : lo[1], hi ? up[2] : lo[2], hi ? up[3] : lo[3]};
     }
-    col = n < 8 && (n & 3) < it.nh;
-    h = (2 * it.hkv + (hi ? 1 : 0)) * prm.G + it.hg * 4 + (n & 3);
+    col = n < 2 * prm.gw && (n & (prm.gw - 1)) < it.nh;
+    h = (2 * it.hkv + (hi ? 1 : 0)) * prm.G + it.hg * prm.gw + (n & (prm.gw - 1));
   }
   if (col) {
     if (it.nparts == 1) {
@@ -1355,7 +1369,7 @@ __device__ __forceinline__ void decode_stream(const DecodeParams& prm, char* lds
     f32x4_t s[NH], s2[NH];
     tile_scores<T, D, HP>(lds, qv, s, s2);
     if (last && has_next) load_q<T, D, HP>(prm, nx, qv);  // this item's query is no longer needed
-    own_half<NH, HP>(s, s2);
+    own_half<NH, HP>(s, s2, prm.gs);
     tile_softmax_pv<T, D>(lds, it, tile0, s, m, l, o);
     if (!last) {
       ++t;
@@ -1599,7 +1613,7 @@ __device__ __forceinline__ void decode_stream2(const DecodeParams& prm, char* ld
     // issued, so it is queued, when this is the last tile)
     if (last && nqueued > 0) load_q<T, D, HP>(prm, make_item<false, Gm::TT, HP>(prm, qd0, qf0, per_item), qv);
     produce(S);
-    own_half<NH, HP>(s, s2);
+    own_half<NH, HP>(s, s2, prm.gs);
     tile_softmax_pv<T, D>(lds, it, tile0, s, m, l, o);
     if (!last) {
       ++ct;

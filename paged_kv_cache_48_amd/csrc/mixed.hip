@@ -310,7 +310,9 @@ bool mixed_fits(int num_seqs, int64_t num_q_tokens, int num_q_heads, int num_kv_
   const int G = num_q_heads / num_kv_heads;
   const dec::DecodeLayout Lw = dec::decode_layout(num_seqs, num_q_heads, head_dim, block_size, max_blocks);
   // claims per tagged counter (24-bit count): items, plus one failed claim per wave
-  const int64_t dec_items = (int64_t)num_seqs * Lw.max_parts * num_kv_heads * ((G + 3) / 4);
+  dec::DecodeParams groups;
+  dec::set_query_groups(groups, G, 1);
+  const int64_t dec_items = (int64_t)num_seqs * Lw.max_parts * num_kv_heads * groups.n_hg;
   const int64_t pre_items = pre::max_prefill_items(num_seqs, num_q_tokens, G) * num_kv_heads;
   return dec_items + dec::kMaxWaves < dec::kMaxQueueItems && pre_items + dec::kMaxWaves < dec::kMaxQueueItems;
 }
@@ -342,8 +344,7 @@ hipError_t launch_mixed(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0, h
   d.scale_log2 = a.scale * kLog2e;
   d.Hq = a.num_q_heads;
   d.Hkv = a.num_kv_heads;
-  d.G = G;
-  d.n_hg = (G + 3) / 4;
+  dec::set_query_groups(d, G, 1);
   d.P = a.block_size;
   d.p_shift = (a.block_size & (a.block_size - 1)) == 0 ? __builtin_ctz((unsigned)a.block_size) : -1;
   d.N = (int)a.num_blocks;

@@ -76,7 +76,7 @@ def test_mixed_matches_oracle_and_separate_calls(G, Hkv, D, P):
 
 
 def test_mixed_largest_group():
-    """A GQA group of 64: decode items take the heads in 16 groups of 4, prefill
+    """A GQA group of 64: decode items take the heads in 4 groups of 16, prefill
     items are 4 tokens x 64 heads."""
     c = case(Hq=64, Hkv=1, D=64, lens=(300, 1, 700, 257), qlens=(37, 1, 1, 2), seed=97)
     d = DevCase(c)

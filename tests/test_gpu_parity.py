@@ -133,6 +133,60 @@ def test_decode_head_layouts(G, Hkv, D, dtype):
     assert_close(d.decode(), decode_ref(c), dtype, f"G={G} D={D} {dtype}")
 
 
+@pytest.mark.parametrize("kind,G,Hkv,D,P", [
+    ("bf16", 8, 8, 128, 16), ("bf16", 16, 2, 128, 16), ("bf16", 12, 2, 64, 7), ("bf16", 7, 4, 64, 16),
+    ("bf16", 32, 1, 128, 32), ("bf16", 20, 2, 64, 16), ("f32", 8, 2, 64, 16), ("f32", 16, 1, 128, 5),
+    ("fp8", 8, 8, 128, 16), ("fp8", 16, 2, 128, 32), ("fp8", 6, 2, 64, 16), ("fp8", 12, 2, 64, 16)])
+def test_decode_wide_query_groups(kind, G, Hkv, D, P):
+    """GQA groups of 5 to 32 query heads: a work item takes up to 16 of them (8
+    per head of a pair), so each KV slice is read once per 16 query heads.
+    Against the oracle, and (bf16 queries) bit for bit against the mixed call,
+    whose decode rows read one KV head at a time."""
+    c = small(dtype="f32" if kind == "f32" else "bf16", P=P, Hq=G * Hkv, Hkv=Hkv, D=D,
+              lens=(1, 16, 255, 256, 257, 700, 1500), seed=110 + G * D + P)
+    print(f"wide group {kind} G={G} Hkv={Hkv} D={D} P={P}", flush=True)
+    if kind == "fp8":
+        d = Fp8Case(c, fp8_scales(Hkv, 111), fp8_scales(Hkv, 112))
+        scales, ref = (d.dks, d.dvs), d.reference()
+    else:
+        d = DevCase(c)
+        scales, ref = (None, None), decode_ref(c)
+    got = d.decode()
+    assert_close(got, ref, "bf16" if kind == "fp8" else c.dtype, f"{kind} G={G} Hkv={Hkv} D={D} P={P}")
+    if kind != "f32":
+        one = torch.empty_like(d.q)
+        pa.paged_mixed_attention(d.q, d.kc, d.vc, idx(np.arange(c.B + 1)), d.bt, d.lens, c.scale, one, *scales)
+        assert np.array_equal(to_host_bits(got), to_host_bits(one)), "decode differs from the mixed call"
+
+
+@pytest.mark.parametrize("kind,G,Hkv,D", [("bf16", 8, 8, 128), ("bf16", 16, 2, 64), ("bf16", 8, 2, 64),
+                                          ("fp8", 8, 8, 128), ("fp8", 16, 1, 128)])
+def test_decode_group_width_does_not_change_bits(kind, G, Hkv, D):
+    """A query head's output does not depend on which other query heads share
+    its work item: the call with G query heads per KV head equals, bit for bit,
+    G / 4 calls of 4 heads per KV head (each taking every KV head's heads
+    4i .. 4i+3), whose items hold 4 heads each."""
+    c = small(P=16, Hq=G * Hkv, Hkv=Hkv, D=D, lens=(1, 40, 256, 257, 700, 1500, 3000), seed=120 + G + D)
+    print(f"group split {kind} G={G} Hkv={Hkv} D={D}", flush=True)
+    if kind == "fp8":
+        d = Fp8Case(c, fp8_scales(Hkv, 121), fp8_scales(Hkv, 122))
+        scales = (d.dks, d.dvs)
+    else:
+        d = DevCase(c)
+        scales = (None, None)
+
+    def decode(q):
+        out = torch.empty_like(q)
+        pa.paged_decode_attention(q, d.kc, d.vc, d.bt, d.lens, c.scale, out, *scales)
+        return to_host_bits(out)
+
+    whole = decode(d.q).reshape(c.B, Hkv, G, D)
+    for i in range(G // 4):
+        q4 = d.q.view(c.B, Hkv, G, D)[:, :, 4 * i:4 * i + 4].contiguous().view(c.B, Hkv * 4, D)
+        part = decode(q4).reshape(c.B, Hkv, 4, D)
+        assert np.array_equal(part, whole[:, :, 4 * i:4 * i + 4]), f"heads {4 * i}..{4 * i + 3} differ"
+
+
 @pytest.mark.parametrize("kind", ["bf16", "fp8"])
 @pytest.mark.parametrize("G,Hkv,P", [(1, 2, 16), (4, 2, 16), (6, 4, 7), (8, 8, 1), (1, 16, 64), (5, 2, 3)])
 def test_decode_paired_64_dim_heads(kind, G, Hkv, P):
