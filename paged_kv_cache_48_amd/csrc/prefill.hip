@@ -177,7 +177,7 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, hipEvent_t ev0,
                      a.num_seqs, p.cap, p.TQ, (int)a.num_q_tokens, (int)item_cap,
                      reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int2*>(ws + kHeaderBytes));
   const int64_t max_items = item_cap * p.Hkv;
-  const int64_t cap = (int64_t)device_cu_count();  // one workgroup (8 waves, 135 KB of LDS) per CU
+  const int64_t cap = (int64_t)device_cu_count();  // one workgroup (8 waves, 136 KiB of LDS) per CU
   const unsigned blocks = (unsigned)(max_items < cap ? max_items : cap);
   // 32-bit pool offsets when one pool is under 4 GiB
   const bool wide = a.num_blocks * a.block_size * (int64_t)p.row_bytes >= ((int64_t)1 << 32);

@@ -107,12 +107,13 @@ __device__ __forceinline__ int div_block(const PrefillParams& p, int pos) {
 }
 
 // LDS of one workgroup: two K / V tile buffers (row-major) and the item's
-// block ids.  The V row stride is an odd multiple of 32 bytes modulo 256, so
-// the transposing operand reads (16 rows x 32 bytes per half-wave) and the
-// row stores are free of bank conflicts.
+// block ids.  Both row strides are an odd multiple of 32 bytes modulo 256:
+// measured on gfx950, the K operand reads (16 rows x 16 bytes per quarter
+// wave) then run without bank conflicts (a 16-byte pad leaves them 2-way
+// conflicted), and so do the transposing V reads and the row stores.
 template <int D>
 struct __attribute__((aligned(16))) PrefillLds {
-  static constexpr int KST = D + 8;   // K row stride (elements)
+  static constexpr int KST = D + 16;  // K row stride (elements)
   static constexpr int VST = D + 16;  // V row stride (elements)
   bf16_bits k[2][kTK * KST];
   bf16_bits v[2][kTK * VST];
@@ -240,12 +241,36 @@ __device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
   else return pack_bf16(lo, hi);
 }
 
-template <int D, bool kF8>
-__device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int k0, float scale_log2,
-                                            RowState<D>& st) {
+// Operand reads of one staged tile pair, for lane (n, g) of the wave:
+//   k(kb, i):   K rows kb*16 + n, elements 32 i + 8 g .. + 7 (the A operand
+//               of S^T = K Q^T, k-step i);
+//   v(db, ks):  the V^T A operand of O^T += V^T P^T for output dims 16 db ..
+//               + 15 and keys 32 ks + 4 g + (0..3), 32 ks + 16 + 4 g + (0..3),
+//               from two transposing reads (lane n of the group addresses row
+//               n / 4 of a 4-row slice, elements 4 (n % 4) .. + 3).
+// PaddedTiles: row-major tiles with padded rows (register-staged path).
+template <int D>
+struct PaddedTiles {
+  const bf16_bits* kt;
+  const bf16_bits* vt;
+  __device__ __forceinline__ PaddedTiles(const PrefillLds<D>& s, int buf) : kt(s.k[buf]), vt(s.v[buf]) {}
+  __device__ __forceinline__ u32x4_t k(int kb, int i) const {
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    return *reinterpret_cast<const u32x4_t*>(&kt[(kb * 16 + n) * PrefillLds<D>::KST + 32 * i + 8 * g]);
+  }
+  __device__ __forceinline__ u32x4_t v(int db, int ks) const {
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const bf16_bits* a = &vt[(32 * ks + 4 * g + (n >> 2)) * PrefillLds<D>::VST + 16 * db + 4 * (n & 3)];
+    const u32x2_t lo = lds_read_tr16(a), hi = lds_read_tr16(a + 16 * PrefillLds<D>::VST);
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  }
+};
+
+template <int D, bool kF8, class Tiles>
+__device__ __forceinline__ void attend_tile(const Tiles& tl, int k0, float scale_log2, RowState<D>& st) {
   constexpr int NI = RowState<D>::NI, NDB = RowState<D>::NDB;
   const int lane = lane_id();
-  const int n = lane & 15, g = lane >> 4;
+  const int g = lane >> 4;
   f32x4_t sc[4][2];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -253,7 +278,7 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
     sc[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&s.k[buf][(kb * 16 + n) * PrefillLds<D>::KST + 32 * i + 8 * g]);
+      const u32x4_t av = tl.k(kb, i);
       sc[kb][0] = mma32<kF8>(av, st.q[0][i], sc[kb][0]);
       sc[kb][1] = mma32<kF8>(av, st.q[1][i], sc[kb][1]);
     }
@@ -308,18 +333,11 @@ __device__ __forceinline__ void attend_tile(const PrefillLds<D>& s, int buf, int
     for (int ks = 0; ks < 2; ++ks) st.l[rb] = mma32<kF8>(ones, pop[rb][ks], st.l[rb]);
   }
   // k-slots 0..3 of step ks are keys 32 ks + 4 g + j, slots 4..7 keys 32 ks + 16 + 4 g + j
-  // V^T operand of lane (n, g): keys 32 ks + 4 g + (0..3) and 32 ks + 16 + 4 g + (0..3)
-  // of column 16 db + n, as two transposing reads; lane n of the group
-  // addresses row n / 4 of the 4-row slice, columns 4 (n % 4) .. 4 (n % 4) + 3
   u32x4_t va[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16_bits* a = &s.v[buf][(32 * ks + 4 * g + (n >> 2)) * PrefillLds<D>::VST + 16 * db + 4 * (n & 3)];
-      const u32x2_t lo = lds_read_tr16(a), hi = lds_read_tr16(a + 16 * PrefillLds<D>::VST);
-      va[db][ks] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-    }
+    for (int ks = 0; ks < 2; ++ks) va[db][ks] = tl.v(db, ks);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -334,41 +352,50 @@ template <int D, bool kF8>
 __device__ __forceinline__ void attend(const PrefillLds<D>& s, int buf, int k0, float scale_log2, int wave_max,
                                        RowState<D>& st) {
   if (k0 > wave_max) return;  // every row of this wave is causally done
-  attend_tile<D, kF8>(s, buf, k0, scale_log2, st);
+  attend_tile<D, kF8>(PaddedTiles<D>(s, buf), k0, scale_log2, st);
 }
 
-// One item: rows of q tile qt of request b's chunk for KV head hkv, every
-// key tile of its causal extent, normalised outputs stored.  All threads of
-// the workgroup take part (barriers inside); on entry no thread may still be
-// reading the LDS buffers of a previous item.
-template <int D, bool kWide, bool kF8>
-__device__ __forceinline__ void prefill_item(const PrefillParams& p, PrefillLds<D>& lds, int b, int qt, int hkv) {
+// The part of an item both tile pipelines share: its geometry, its block
+// ids copied to LDS, the wave's rows and their queries loaded, and (at the
+// end) the normalised outputs stored.
+struct ItemGeo {
+  int cu0;       // packed row of chunk token 0
+  int start;     // position of chunk row 0
+  int t0;        // first chunk token of the q tile
+  int kmax;      // keys 0 .. kmax-1 are visible to some row
+  int nkt;       // key tiles
+  int wave_max;  // largest position of this wave's rows (-1: none)
+};
+
+template <int D, bool kF8>
+__device__ __forceinline__ ItemGeo begin_item(const PrefillParams& p, int32_t* ids, int b, int qt, int hkv,
+                                              RowState<D>& st) {
   constexpr int NI = RowState<D>::NI, NDB = RowState<D>::NDB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = uniform(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int cu0 = p.cu[b];
-  const int T = p.cu[b + 1] - cu0;
+  ItemGeo ig;
+  ig.cu0 = p.cu[b];
+  const int T = p.cu[b + 1] - ig.cu0;
   const int L = clamp_len(p.lens[b], p.cap);
-  const int start = L - T;  // position of chunk row 0
-  const int t0 = qt * p.TQ;
-  const int nt = min(p.TQ, T - t0);
-  const int kmax = start + t0 + nt;  // keys 0 .. kmax-1 are visible to some row
-  const int nkt = (kmax + kTK - 1) / kTK;
+  ig.start = L - T;
+  ig.t0 = qt * p.TQ;
+  const int nt = min(p.TQ, T - ig.t0);
+  ig.kmax = ig.start + ig.t0 + nt;
+  ig.nkt = (ig.kmax + kTK - 1) / kTK;
   const int32_t* __restrict__ bt_row = p.bt + (int64_t)b * p.M;
-  const int nblk = div_block(p, kmax - 1) + 1;  // kmax <= cap = M * P, so nblk <= M <= kIdCap
-  for (int i = tid; i < nblk; i += kThreads) lds.ids[i] = bt_row[i];
+  const int nblk = div_block(p, ig.kmax - 1) + 1;  // kmax <= cap = M * P, so nblk <= M
+  for (int i = tid; i < nblk; i += kThreads) ids[i] = bt_row[i];
 
-  RowState<D> st;
   int wave_max = -1;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int r = 32 * w + 16 * rb + n;
     const int hl = r / p.TQ, tl = r - hl * p.TQ;
     const bool ok = hl < p.G && tl < nt;
-    st.pos[rb] = ok ? start + t0 + tl : -1;
-    const int64_t qrow = ((int64_t)(cu0 + t0 + tl) * p.Hq + hkv * p.G + hl) * D;
+    st.pos[rb] = ok ? ig.start + ig.t0 + tl : -1;
+    const int64_t qrow = ((int64_t)(ig.cu0 + ig.t0 + tl) * p.Hq + hkv * p.G + hl) * D;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       st.q[rb][i] = ok ? *reinterpret_cast<const u32x4_t*>(p.q + qrow + 32 * i + 8 * g) : u32x4_t{0u, 0u, 0u, 0u};
@@ -385,7 +412,46 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, PrefillLds<
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) wave_max = max(wave_max, __shfl_xor(wave_max, off));
-  wave_max = uniform(wave_max);
+  ig.wave_max = uniform(wave_max);
+  return ig;
+}
+
+// Normalise and store: lane holds O^T[d = 16db + 4g + j][row n].
+template <int D>
+__device__ __forceinline__ void finish_item(const PrefillParams& p, const ItemGeo& ig, int hkv, float vmul,
+                                            const RowState<D>& st) {
+  constexpr int NDB = RowState<D>::NDB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float lt = st.l[rb][0];
+    if (st.pos[rb] < 0) continue;
+    const int r = 32 * w + 16 * rb + n;
+    const int hl = r / p.TQ, tl = r - hl * p.TQ;
+    const float inv = vmul / lt;
+    bf16_bits* dst = p.out + ((int64_t)(ig.cu0 + ig.t0 + tl) * p.Hq + hkv * p.G + hl) * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const u32x2_t v = {pack_bf16(st.o[db][rb][0] * inv, st.o[db][rb][1] * inv),
+                         pack_bf16(st.o[db][rb][2] * inv, st.o[db][rb][3] * inv)};
+      *reinterpret_cast<u32x2_t*>(dst + 16 * db) = v;
+    }
+  }
+}
+
+// One item: rows of q tile qt of request b's chunk for KV head hkv, every
+// key tile of its causal extent, normalised outputs stored.  All threads of
+// the workgroup take part (barriers inside); on entry no thread may still be
+// reading the LDS buffers of a previous item.
+template <int D, bool kWide, bool kF8>
+__device__ __forceinline__ void prefill_item(const PrefillParams& p, PrefillLds<D>& lds, int b, int qt, int hkv) {
+  const int w = uniform(threadIdx.x >> 6);
+  RowState<D> st;
+  const ItemGeo ig = begin_item<D, kF8>(p, lds.ids, b, qt, hkv, st);
+  const int kmax = ig.kmax, nkt = ig.nkt, wave_max = ig.wave_max;
   __syncthreads();  // block ids visible
 
   // fp8 pools: value(code) * scale, staged as value(code)
@@ -425,23 +491,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, PrefillLds<
     }
     __syncthreads();
   }
-
-  // ---- normalise and store: lane holds O^T[d = 16db + 4g + j][row n] ----
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float lt = st.l[rb][0];
-    if (st.pos[rb] < 0) continue;
-    const int r = 32 * w + 16 * rb + n;
-    const int hl = r / p.TQ, tl = r - hl * p.TQ;
-    const float inv = vmul / lt;
-    bf16_bits* dst = p.out + ((int64_t)(cu0 + t0 + tl) * p.Hq + hkv * p.G + hl) * D + 4 * g;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const u32x2_t v = {pack_bf16(st.o[db][rb][0] * inv, st.o[db][rb][1] * inv),
-                         pack_bf16(st.o[db][rb][2] * inv, st.o[db][rb][3] * inv)};
-      *reinterpret_cast<u32x2_t*>(dst + 16 * db) = v;
-    }
-  }
+  finish_item<D>(p, ig, hkv, vmul, st);
 }
 
 }  // namespace pre
