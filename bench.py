@@ -415,6 +415,7 @@ def bench_decode_small(args, name):
     kern_b = dec_b + append_bytes(B, Hkv, D, s)
     ms = float(np.median(g_ms))
     achieved = kern_b / (kern_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(DECODE_SOURCES, f"decode_{name}") if wide else None
     log(f"{name}: {1e3 * ms / L:.2f} us/layer-step (graph), {1e3 * float(np.median(e_ms)) / L:.2f} (eager), "
         f"partition kernel {kern_ms * 1e3:.2f} us")
     return {
@@ -431,8 +432,8 @@ def bench_decode_small(args, name):
         "roofline_tokens_per_s": round(B / (step_bytes / (HBM_PEAK_GBS * 1e9)), 1),
         "roofline": {"kernel": f"decode_partition_kernel<{case.dtype},{D}> (decode with append)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": kern_b,
-                     "avg_launch_us": round(kern_ms * 1e3, 2),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": kern_b, "avg_launch_us": round(kern_ms * 1e3, 2),
                      "timing": "library events around the kernel, each launch after a 1 GiB read-only stream"},
     }
 
@@ -822,6 +823,9 @@ TRACES = {
                           "steps, then the guarded per-kernel loop."),
     "decode_tiny": ("tiny", 20, "Tiny decode step: 1 layer, paged decode with append, B=4, H_q=H_kv=12, D=64, P=16, "
                     "N=64, fp32 (launch-latency bound)."),
+    "decode_llama3_8b_g8": ("llama3_8b_g8", 5, "GQA group of 8: one layer of the Llama-3-8B batch (B=256, 90% pool, "
+                            "H_kv=8, D=128, P=16, bf16) with 64 query heads, paged decode with append; graph replays, "
+                            "eager steps, then the guarded per-kernel loop."),
     "prefill_mixed": ("mixed", 10, "Mixed chunked-prefill + decode step as two calls: 16 prefill chunks over cached "
                       "prefixes (paged_prefill_attention) and 48 decodes (paged_decode_attention), after the slot "
                       "mapping and the scatter of all new tokens; Llama-3-8B heads, P=16, bf16."),
@@ -835,6 +839,7 @@ TRACES = {
 TRAFFIC = {
     "decode_llama3_8b": ("llama3_8b", "decode_partition_kernel<unsigned short, 128, false, true, 1, 1, true>"),
     "decode_llama3_8b_fp8": ("llama3_8b_fp8", "fp8_e4m3, 256, false, true, 1, 2, true"),
+    "decode_llama3_8b_g8": ("llama3_8b_g8", "decode_partition_kernel<unsigned short, 128, false, true, 1, 1, true>"),
 }
 # prefill counters, two passes (each within one pass's counter limits)
 PREFILL_PMC = {
@@ -984,13 +989,15 @@ def summarize_profiles(d):
             log(f"{key}: no dispatch of a kernel matching {pat!r}")
             continue
         s_kv = 1 if wl.endswith("fp8") else 2
-        alg = (decode_bytes(case.context_lens, case.block_size, case.num_q_heads, case.num_kv_heads, case.head_dim,
+        Hq = WIDE_GROUP[wl]["Hq"] if wl in WIDE_GROUP else case.num_q_heads
+        alg = (decode_bytes(case.context_lens, case.block_size, Hq, case.num_kv_heads, case.head_dim,
                             2, s_kv) + append_bytes(case.B, case.num_kv_heads, case.head_dim, 2, s_kv))
         fetch_b, write_b = fetch_kib * 1024 * kf, write_kib * 1024 * kw
         lines = [
             f"HBM traffic of the decode partition kernel with append ({pat}) on the Llama-3-8B-shaped batch",
             f"({'fp8 e4m3' if s_kv == 1 else 'bf16'} pools; one launch = one layer, the new token's K/V written in "
-            f"the same launch: B=256, sum of context lengths {int(case.context_lens.sum())}, H_kv=8, D=128, P=16).",
+            f"the same launch: B=256, sum of context lengths {int(case.context_lens.sum())}, H_q={Hq}, H_kv=8, "
+            f"D=128, P=16).",
             "commands (run from the repository root, DIR = an output folder):",
             "  " + cmds[f"fetch_{key}"], "  " + cmds[f"write_{key}"], "  " + cmds["fetch_copy"],
             "  " + cmds["write_copy"], _sha_line(DECODE_SOURCES), "",
