@@ -66,7 +66,7 @@ QLENS = (1, 70, 1, 33, 1, 300, 1, 1, 2, 2, 1, 130)
 
 
 @pytest.mark.parametrize("G,Hkv,D,P", [(4, 8, 128, 16), (4, 2, 128, 16), (1, 3, 64, 16), (2, 2, 128, 7),
-                                       (8, 1, 64, 1), (3, 2, 128, 64)])
+                                       (8, 1, 64, 1), (3, 2, 128, 64), (8, 4, 128, 16), (16, 2, 64, 16)])
 def test_mixed_matches_oracle_and_separate_calls(G, Hkv, D, P):
     c = case(P=P, Hq=G * Hkv, Hkv=Hkv, D=D, lens=LENS, qlens=QLENS, seed=80 + G * D + P)
     d = DevCase(c)

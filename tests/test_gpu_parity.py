@@ -812,13 +812,16 @@ def same_bits(a, b):
 
 @pytest.mark.parametrize("kind,G,Hkv,D,P", [("bf16", 4, 8, 128, 16), ("f32", 1, 4, 64, 7), ("bf16", 4, 2, 64, 1),
                                             ("bf16", 8, 2, 128, 48), ("bf16", 3, 3, 64, 5), ("fp8", 4, 8, 128, 16),
-                                            ("fp8-f32", 2, 2, 64, 3), ("fp8", 5, 3, 64, 32), ("fp8", 8, 1, 128, 48)])
+                                            ("fp8-f32", 2, 2, 64, 3), ("fp8", 5, 3, 64, 32), ("fp8", 8, 1, 128, 48),
+                                            ("bf16", 16, 1, 64, 16), ("bf16", 32, 1, 128, 16), ("fp8", 12, 2, 64, 7),
+                                            ("fp8", 7, 4, 64, 16)])
 def test_decode_append_equals_scatter_then_decode(kind, G, Hkv, D, P):
     """pa_paged_decode_append writes each request's new token at position L - 1
     and attends to it in one call: bit for bit the outputs and the pools of the
     slot mapping, the scatter and the decode call (tiles of the new token that
-    straddle blocks, query-head groups past the first, paired heads, fp8 codes
-    quantised from bf16 or fp32 rows), and the oracle."""
+    straddle blocks, query-head groups past the first (G=32: two groups of
+    16), groups of 8 and 16 heads, paired heads, fp8 codes quantised from bf16
+    or fp32 rows), and the oracle."""
     fp8 = kind.startswith("fp8")
     c = small(dtype="f32" if kind == "f32" else "bf16", P=P, Hq=G * Hkv, Hkv=Hkv, D=D,
               lens=(1, 2, 16, 17, 31, 33, 255, 256, 257, 700, 1500), seed=70 + G * D + P)
